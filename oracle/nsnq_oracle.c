@@ -1,0 +1,460 @@
+/*
+ * nsnq_oracle.c -- plain, slow CPU reference of the NSNQuant hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, calls or
+ * includes this file; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark use it.  It shares no code, header, table or helper with the
+ * GPU path: fp16 conversion, the Hadamard matrix, layouts and argmin are all
+ * written out again here.
+ *
+ * Everything is computed in double precision with straightforward loops.  The
+ * stored format (fp16 scalars, uint8 codes) is rounded with this file's own
+ * round-to-nearest-even conversion.
+ *
+ * Sources (page title, then the section it falls in):
+ *   [P2] "NSNQuant: A Double Normalization Approach for Calibration-Free Low-Bit
+ *        Vector Quantization of KV Cache", research-map summary, "Approach".
+ *   [P3] same title, technical summary ("Technische Samenvatting"), sections
+ *        1 (NSN), 2 (Hadamard), 3 (VQ and codebook), 4 (implementation:
+ *        residuals, attention).
+ *   [P4] same title, machine review: "What carries the argument", referee
+ *        minor comment 1 (paper Section 2, Eq. (1)), Lemma 1 (App. A.1).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- fp16 --- */
+
+/* IEEE binary16 -> double, exact. */
+double orc_h2d(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int m = h & 0x3ff;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+  } else if (e == 31) {
+    v = m ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(m + 1024), e - 25); /* (1.m) * 2^(e-15) */
+  }
+  return sign ? -v : v;
+}
+
+/* double -> IEEE binary16, round to nearest, ties to even.  Works by scanning
+ * the representable magnitudes: finds the two fp16 neighbours of |x| and picks
+ * the nearer one (the even one on a tie).  Slow but plainly correct. */
+uint16_t orc_d2h(double x) {
+  if (isnan(x)) return 0x7e00;
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  /* largest finite fp16 is 65504; values at or above 65520 round to inf */
+  if (a >= 65520.0) return sign | 0x7c00;
+  /* binary search over the 0x7c00 finite non-negative codes (monotone) */
+  int lo = 0, hi = 0x7bff;
+  if (a >= orc_h2d((uint16_t)hi)) return sign | (uint16_t)hi;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (orc_h2d((uint16_t)mid) <= a) lo = mid; else hi = mid;
+  }
+  double dlo = a - orc_h2d((uint16_t)lo);
+  double dhi = orc_h2d((uint16_t)hi) - a;
+  int pick;
+  if (dlo < dhi) pick = lo;
+  else if (dhi < dlo) pick = hi;
+  else pick = (lo % 2 == 0) ? lo : hi;
+  return sign | (uint16_t)pick;
+}
+
+void orc_d2h_array(const double* x, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_d2h(x[i]);
+}
+
+void orc_h2d_array(const uint16_t* h, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_h2d(h[i]);
+}
+
+/* ------------------------------------------------------------ Hadamard --- */
+
+static int popcount_int(int v) {
+  int c = 0;
+  while (v) { c += v & 1; v >>= 1; }
+  return c;
+}
+
+/* The orthonormal Sylvester-ordered Hadamard matrix of size d (a power of 2):
+ * H[i][j] = (-1)^popcount(i & j) / sqrt(d), written into Hm [d][d].
+ * [P3 sec. 2; P4 "What carries the argument"]: after NSN the head vector is
+ * rotated by a fixed (non-randomised) Hadamard transform.  H is symmetric and
+ * its own inverse. */
+void orc_hadamard_matrix(int d, double* Hm) {
+  double scale = 1.0 / sqrt((double)d);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j)
+      Hm[(size_t)i * d + j] = ((popcount_int(i & j) & 1) ? -1.0 : 1.0) * scale;
+}
+
+/* u = Hm w, plain matrix-vector product. */
+static void matvec(const double* Hm, const double* w, double* u, int d) {
+  for (int i = 0; i < d; ++i) {
+    double acc = 0.0;
+    for (int j = 0; j < d; ++j) acc += Hm[(size_t)i * d + j] * w[j];
+    u[i] = acc;
+  }
+}
+
+/* u = H w for one vector (builds H each call; for tests). */
+void orc_hadamard(const double* w, double* u, int d) {
+  double* Hm = (double*)malloc(sizeof(double) * (size_t)d * d);
+  orc_hadamard_matrix(d, Hm);
+  matvec(Hm, w, u, d);
+  free(Hm);
+}
+
+/* ----------------------------------------------------------------- NSN --- */
+
+/* Normalize-Shift-Normalize of one block of R tokens, x fp16 [R][d].
+ * [P3 sec. 1; P4 "What carries the argument"; P2 "Approach"]:
+ *   1. each token is rescaled to Euclidean norm sqrt(d); the factor is kept
+ *      as n1 = ||x|| / sqrt(d) so that x = n1 * y;
+ *   2. the channel-wise mean mu of the block is subtracted, z = y - mu;
+ *   3. each token is rescaled to norm sqrt(d) again, n2 = ||z|| / sqrt(d),
+ *      w = z / n2.
+ * A zero token (n1 = 0) gives y = 0.  A token equal to the block mean has
+ * z = 0 up to rounding; when its n2 rounds to zero in the stored fp16 format
+ * (n2 <= 2^-25) the direction is meaningless and w is set to 0.  The pages do
+ * not cover these cases; this is the reading under which reconstruction from
+ * the stored values stays exact (x_hat = N1 * MU) and both precisions agree.
+ * Any output pointer may be NULL. */
+void orc_nsn_block(const uint16_t* x, int R, int d,
+                   double* n1_out, double* y_out, double* mu_out,
+                   double* z_out, double* n2_out, double* w_out) {
+  double* y = (double*)malloc(sizeof(double) * (size_t)R * d);
+  double* mu = (double*)calloc((size_t)d, sizeof(double));
+  double sqrt_d = sqrt((double)d);
+  for (int t = 0; t < R; ++t) {
+    double ss = 0.0;
+    for (int c = 0; c < d; ++c) {
+      double v = orc_h2d(x[(size_t)t * d + c]);
+      ss += v * v;
+    }
+    double n1 = sqrt(ss) / sqrt_d;
+    if (n1_out) n1_out[t] = n1;
+    for (int c = 0; c < d; ++c) {
+      double v = orc_h2d(x[(size_t)t * d + c]);
+      y[(size_t)t * d + c] = (n1 > 0.0) ? v / n1 : 0.0;
+    }
+  }
+  for (int c = 0; c < d; ++c) {
+    double s = 0.0;
+    for (int t = 0; t < R; ++t) s += y[(size_t)t * d + c];
+    mu[c] = s / (double)R;
+  }
+  if (mu_out) memcpy(mu_out, mu, sizeof(double) * d);
+  for (int t = 0; t < R; ++t) {
+    double ss = 0.0;
+    for (int c = 0; c < d; ++c) {
+      double zc = y[(size_t)t * d + c] - mu[c];
+      if (z_out) z_out[(size_t)t * d + c] = zc;
+      ss += zc * zc;
+    }
+    double n2 = sqrt(ss) / sqrt_d;
+    if (n2_out) n2_out[t] = n2;
+    if (w_out) {
+      for (int c = 0; c < d; ++c) {
+        double zc = y[(size_t)t * d + c] - mu[c];
+        w_out[(size_t)t * d + c] = (orc_d2h(n2) != 0) ? zc / n2 : 0.0;
+      }
+    }
+    if (y_out) memcpy(y_out + (size_t)t * d, y + (size_t)t * d, sizeof(double) * d);
+  }
+  free(y);
+  free(mu);
+}
+
+/* ------------------------------------------------------------------ VQ --- */
+
+/* Eq. (1) of the paper as given in [P4 referee minor comment 1] and [P3 sec. 3]:
+ * the code of a sub-vector v (length s) is the index of the nearest codeword,
+ * with D the squared Euclidean distance; equal distances go to the lowest
+ * index.  Also returns the smallest distance and the relative gap between the
+ * best and second-best distance, (D2 - D1) / D1 (+inf when D1 = 0 < D2). */
+static int vq_dbl(const double* v, int s, const double* cbd, int ncw, double* dmin_out, double* gap_out) {
+  int best = 0;
+  double d1 = INFINITY, d2 = INFINITY;
+  for (int k = 0; k < ncw; ++k) {
+    double dist = 0.0;
+    for (int i = 0; i < s; ++i) {
+      double diff = v[i] - cbd[(size_t)k * s + i];
+      dist += diff * diff;
+    }
+    if (dist < d1) {
+      d2 = d1;
+      d1 = dist;
+      best = k;
+    } else if (dist < d2) {
+      d2 = dist;
+    }
+  }
+  if (dmin_out) *dmin_out = d1;
+  if (gap_out) {
+    if (d1 > 0.0) *gap_out = (d2 - d1) / d1;
+    else *gap_out = (d2 > 0.0) ? INFINITY : 0.0;
+  }
+  return best;
+}
+
+/* Same, with the fp16 codebook cb [ncw][s] taken exactly. */
+int orc_vq(const double* v, int s, const uint16_t* cb, int ncw, double* dmin_out, double* gap_out) {
+  double* cbd = (double*)malloc(sizeof(double) * (size_t)ncw * s);
+  for (size_t e = 0; e < (size_t)ncw * s; ++e) cbd[e] = orc_h2d(cb[e]);
+  int code = vq_dbl(v, s, cbd, ncw, dmin_out, gap_out);
+  free(cbd);
+  return code;
+}
+
+/* -------------------------------------------------------------- encode --- */
+
+/* Number of tokens that stay in the fp16 residual window after a prefill of L
+ * tokens with window R: r = ((L - 1) mod R) + 1 (0 when L = 0).  [P3 sec. 4,
+ * residuals]: recent tokens are kept at full precision and the window is
+ * quantised and appended only once it is full and another token arrives, so a
+ * prefill leaves between 1 and R tokens in it. */
+int orc_resid_count(int L, int R) {
+  if (L <= 0) return 0;
+  return ((L - 1) % R) + 1;
+}
+
+/* Encode one (batch row, head) stream, K or V, of L tokens x fp16 [L][d].
+ * Outputs, for the nq = L - r flushed tokens, in blocks of R:
+ *   codes  [nq][d/s]  uint8, slot j covers u[j*s .. j*s+s-1]
+ *   scales [nq][2]    fp16 (n1, n2)
+ *   mu     [nq/R][d]  fp16 channel mean of each block (original domain)
+ *   gap    [nq][d/s]  relative best/second gap (may be NULL)
+ *   u_out  [nq][d]    Hadamard output, before VQ (may be NULL)
+ * and resid [R][d] fp16: the last r tokens, verbatim (rows >= r untouched).
+ * Returns nq. */
+int orc_encode_unit(const uint16_t* x, int L, int d, int R, int s,
+                    const uint16_t* cb, int ncw,
+                    uint8_t* codes, uint16_t* scales, uint16_t* mu_st,
+                    uint16_t* resid, double* gap, double* u_out) {
+  int r = orc_resid_count(L, R);
+  int nq = L - r;
+  int S = d / s;
+  double* n1 = (double*)malloc(sizeof(double) * R);
+  double* n2 = (double*)malloc(sizeof(double) * R);
+  double* mu = (double*)malloc(sizeof(double) * d);
+  double* w = (double*)malloc(sizeof(double) * (size_t)R * d);
+  double* u = (double*)malloc(sizeof(double) * d);
+  double* Hm = (double*)malloc(sizeof(double) * (size_t)d * d);
+  double* cbd = (double*)malloc(sizeof(double) * (size_t)ncw * s);
+  orc_hadamard_matrix(d, Hm);
+  for (size_t e = 0; e < (size_t)ncw * s; ++e) cbd[e] = orc_h2d(cb[e]);
+  for (int blk = 0; blk < nq / R; ++blk) {
+    const uint16_t* xb = x + (size_t)blk * R * d;
+    orc_nsn_block(xb, R, d, n1, NULL, mu, NULL, n2, w);
+    for (int c = 0; c < d; ++c) mu_st[(size_t)blk * d + c] = orc_d2h(mu[c]);
+    for (int t = 0; t < R; ++t) {
+      size_t tok = (size_t)blk * R + t;
+      scales[tok * 2 + 0] = orc_d2h(n1[t]);
+      scales[tok * 2 + 1] = orc_d2h(n2[t]);
+      matvec(Hm, w + (size_t)t * d, u, d);
+      if (u_out) memcpy(u_out + tok * d, u, sizeof(double) * d);
+      for (int j = 0; j < S; ++j) {
+        double g;
+        int code = vq_dbl(u + (size_t)j * s, s, cbd, ncw, NULL, &g);
+        codes[tok * S + j] = (uint8_t)code;
+        if (gap) gap[tok * S + j] = g;
+      }
+    }
+  }
+  for (int t = 0; t < r; ++t)
+    memcpy(resid + (size_t)t * d, x + (size_t)(nq + t) * d, sizeof(uint16_t) * d);
+  free(n1); free(n2); free(mu); free(w); free(u); free(Hm); free(cbd);
+  return nq;
+}
+
+/* Batched encode over n_units independent streams laid out back to back:
+ * x [n_units][L][d]; outputs [n_units][...] with the per-unit shapes above
+ * (codes/scales/gap/u sized for nq = L - r tokens per unit, mu for nq/R
+ * blocks, resid for R rows).  OpenMP over units only. */
+int orc_encode(const uint16_t* x, int64_t n_units, int L, int d, int R, int s,
+               const uint16_t* cb, int ncw,
+               uint8_t* codes, uint16_t* scales, uint16_t* mu_st, uint16_t* resid,
+               double* gap, double* u_out) {
+  int r = orc_resid_count(L, R);
+  int nq = L - r;
+  int S = d / s;
+  int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (i = 0; i < n_units; ++i) {
+    orc_encode_unit(x + (size_t)i * L * d, L, d, R, s, cb, ncw,
+                    codes + (size_t)i * nq * S, scales + (size_t)i * nq * 2,
+                    mu_st + (size_t)i * (nq / R) * d, resid + (size_t)i * R * d,
+                    gap ? gap + (size_t)i * nq * S : NULL,
+                    u_out ? u_out + (size_t)i * nq * d : NULL);
+  }
+  return nq;
+}
+
+/* ------------------------------------------------------------- dequant --- */
+
+/* Reconstruct tokens [tok0, tok0 + ntok) of one stream from stored values only:
+ *   x_hat = N1 * (N2 * H^T c_hat + MU_block),  c_hat = concat_j C[code_j]
+ * [P3 sec. 1: the byproducts (s1, o, s2) rebuild the tensor; sec. 4: dequant
+ * kernel].  H^T = H for the Sylvester matrix. */
+void orc_dequant_unit(const uint8_t* codes, const uint16_t* scales, const uint16_t* mu_st,
+                      int tok0, int ntok, int d, int R, int s,
+                      const uint16_t* cb, double* out) {
+  int S = d / s;
+  double* chat = (double*)malloc(sizeof(double) * d);
+  double* rot = (double*)malloc(sizeof(double) * d);
+  double* Hm = (double*)malloc(sizeof(double) * (size_t)d * d);
+  orc_hadamard_matrix(d, Hm);
+  for (int i = 0; i < ntok; ++i) {
+    int t = tok0 + i;
+    for (int j = 0; j < S; ++j) {
+      int code = codes[(size_t)t * S + j];
+      for (int e = 0; e < s; ++e) chat[j * s + e] = orc_h2d(cb[(size_t)code * s + e]);
+    }
+    matvec(Hm, chat, rot, d);
+    double N1 = orc_h2d(scales[(size_t)t * 2 + 0]);
+    double N2 = orc_h2d(scales[(size_t)t * 2 + 1]);
+    const uint16_t* mub = mu_st + (size_t)(t / R) * d;
+    for (int c = 0; c < d; ++c) out[(size_t)i * d + c] = N1 * (N2 * rot[c] + orc_h2d(mub[c]));
+  }
+  free(chat);
+  free(rot);
+  free(Hm);
+}
+
+/* Batched dequant: streams back to back, each with cap_tokens rows of codes /
+ * scales and cap_tokens/R rows of mu; out [n_units][ntok][d]. */
+void orc_dequant(const uint8_t* codes, const uint16_t* scales, const uint16_t* mu_st,
+                 int64_t n_units, int cap_tokens, int tok0, int ntok, int d, int R, int s,
+                 const uint16_t* cb, double* out) {
+  int S = d / s;
+  int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (i = 0; i < n_units; ++i) {
+    orc_dequant_unit(codes + (size_t)i * cap_tokens * S, scales + (size_t)i * cap_tokens * 2,
+                     mu_st + (size_t)i * (cap_tokens / R) * d, tok0, ntok, d, R, s, cb,
+                     out + (size_t)i * ntok * d);
+  }
+}
+
+/* ----------------------------------------------------------- attention --- */
+
+/* Textbook single-query softmax attention, the plain definition the pages'
+ * compressed-cache kernel computes [P3 sec. 4, attention: the score folds the
+ * NSN byproducts in, which is an algebraic rewrite of attending over the
+ * reconstructed cache].
+ *   q   [B][Hq][d]  fp16
+ *   k,v [B][Hkv][T][d] double (reconstructed tokens, then residual tokens)
+ *   out [B][Hq][d]  double
+ * Query head h reads KV head h / (Hq / Hkv).  scores = scale * q.k, softmax
+ * with the maximum subtracted, out = sum_t p_t v_t. */
+void orc_attention(const uint16_t* q, int B, int Hq, int Hkv, int d,
+                   const double* k, const double* v, int T, double scale, double* out) {
+  int G = Hq / Hkv;
+  int64_t bh;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (bh = 0; bh < (int64_t)B * Hq; ++bh) {
+    int b = (int)(bh / Hq), h = (int)(bh % Hq);
+    int hk = h / G;
+    const double* kb = k + ((size_t)b * Hkv + hk) * (size_t)T * d;
+    const double* vb = v + ((size_t)b * Hkv + hk) * (size_t)T * d;
+    double* o = out + ((size_t)b * Hq + h) * d;
+    double* sc = (double*)malloc(sizeof(double) * (T > 0 ? T : 1));
+    double mx = -INFINITY;
+    for (int t = 0; t < T; ++t) {
+      double acc = 0.0;
+      for (int c = 0; c < d; ++c) acc += orc_h2d(q[((size_t)b * Hq + h) * d + c]) * kb[(size_t)t * d + c];
+      sc[t] = scale * acc;
+      if (sc[t] > mx) mx = sc[t];
+    }
+    double l = 0.0;
+    for (int t = 0; t < T; ++t) { sc[t] = exp(sc[t] - mx); l += sc[t]; }
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int t = 0; t < T; ++t) acc += sc[t] * vb[(size_t)t * d + c];
+      o[c] = (T > 0) ? acc / l : 0.0;
+    }
+    free(sc);
+  }
+}
+
+/* -------------------------------------------------------------- k-means --- */
+
+/* Lloyd's k-means on samples [n][s] (fp32 values, taken exactly).
+ * [P3 sec. 3, codebook construction; P2 "Approach"]: the codebook is fit once
+ * with k-means on synthetic standard-normal (torch.randn) data.  The pages give
+ * no initialisation, iteration count or empty-cluster rule; this oracle uses:
+ *   init  = `init` if given, else the first ncw samples;
+ *   each iteration: assign every sample to its nearest centroid (squared
+ *   Euclidean, ties to the lowest index), record the mean squared error per
+ *   element of that assignment in distortion[it], then move each centroid to
+ *   the mean of its members (a centroid with no members stays where it is).
+ * The final centroids are returned in double and rounded to fp16 (RNE). */
+void orc_kmeans(const float* samples, int64_t n, int s, int ncw, int iters,
+                const double* init, double* cent_out, uint16_t* cb_out, double* distortion) {
+  double* c = (double*)malloc(sizeof(double) * (size_t)ncw * s);
+  double* sum = (double*)malloc(sizeof(double) * (size_t)ncw * s);
+  int64_t* cnt = (int64_t*)malloc(sizeof(int64_t) * ncw);
+  int* assign = (int*)malloc(sizeof(int) * (size_t)n);
+  double* dmin = (double*)malloc(sizeof(double) * (size_t)n);
+  for (int k = 0; k < ncw; ++k)
+    for (int i = 0; i < s; ++i)
+      c[(size_t)k * s + i] = init ? init[(size_t)k * s + i] : (double)samples[(size_t)k * s + i];
+  for (int it = 0; it < iters; ++it) {
+    int64_t p;
+#pragma omp parallel for schedule(static)
+    for (p = 0; p < n; ++p) {
+      int best = 0;
+      double bd = INFINITY;
+      for (int k = 0; k < ncw; ++k) {
+        double dist = 0.0;
+        for (int i = 0; i < s; ++i) {
+          double diff = (double)samples[(size_t)p * s + i] - c[(size_t)k * s + i];
+          dist += diff * diff;
+        }
+        if (dist < bd) { bd = dist; best = k; }
+      }
+      assign[p] = best;
+      dmin[p] = bd;
+    }
+    double tot = 0.0;
+    for (int64_t q = 0; q < n; ++q) tot += dmin[q];
+    if (distortion) distortion[it] = tot / ((double)n * s);
+    memset(sum, 0, sizeof(double) * (size_t)ncw * s);
+    memset(cnt, 0, sizeof(int64_t) * ncw);
+    for (int64_t q = 0; q < n; ++q) {
+      int k = assign[q];
+      cnt[k] += 1;
+      for (int i = 0; i < s; ++i) sum[(size_t)k * s + i] += (double)samples[(size_t)q * s + i];
+    }
+    for (int k = 0; k < ncw; ++k)
+      if (cnt[k] > 0)
+        for (int i = 0; i < s; ++i) c[(size_t)k * s + i] = sum[(size_t)k * s + i] / (double)cnt[k];
+  }
+  for (size_t e = 0; e < (size_t)ncw * s; ++e) {
+    if (cent_out) cent_out[e] = c[e];
+    if (cb_out) cb_out[e] = orc_d2h(c[e]);
+  }
+  free(c); free(sum); free(cnt); free(assign); free(dmin);
+}
+
+/* Number of OpenMP threads the batched routines use. */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

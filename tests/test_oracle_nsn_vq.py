@@ -1,0 +1,127 @@
+"""Pins of the oracle's NSN, VQ and encode pipeline against what the pages and
+the mathematics fix: the NSN invariants (norm sqrt(d) after each normalise,
+zero channel means after the shift, exact inverse), brute-force argmin by an
+independent formulation, and the Hadamard/NSN wiring of the encoder."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_bit_amd import synth
+
+D = 128
+
+
+def _block(seed, R=64, d=D, outlier=10.0):
+    return synth.kv_unit(seed, R, d, outlier).numpy()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_nsn_invariants(seed):
+    x = _block(seed)
+    o = oracle.nsn_block(x)
+    R, d = x.shape
+    xd = x.astype(np.float64)
+    # step 1: each token has norm sqrt(d) and x = n1 * y
+    assert np.allclose(np.linalg.norm(o["y"], axis=1), np.sqrt(d), rtol=1e-12)
+    assert np.allclose(o["n1"][:, None] * o["y"], xd, rtol=1e-12, atol=0)
+    # step 2: channel means of z vanish
+    assert np.max(np.abs(o["z"].sum(axis=0))) < 1e-11 * np.sqrt(d) * R
+    assert np.allclose(o["y"].mean(axis=0), o["mu"], atol=1e-14)
+    # step 3: second normalisation, norm sqrt(d)
+    assert np.allclose(np.linalg.norm(o["w"], axis=1), np.sqrt(d), rtol=1e-12)
+    # exact inverse before quantisation: x = n1 * (n2 * w + mu)
+    rec = o["n1"][:, None] * (o["n2"][:, None] * o["w"] + o["mu"][None, :])
+    assert np.allclose(rec, xd, rtol=1e-12, atol=1e-12 * np.abs(xd).max())
+
+
+def test_nsn_scale_invariance_and_degenerate_tokens():
+    x = _block(7)
+    o = oracle.nsn_block(x)
+    # scaling the whole block by a power of two is exact in fp16 and only moves n1
+    x4 = (x.astype(np.float32) * 4).astype(np.float16)
+    o4 = oracle.nsn_block(x4)
+    assert np.allclose(o4["n1"], 4 * o["n1"], rtol=1e-15)
+    for k in ("y", "mu", "w", "n2"):
+        assert np.allclose(o4[k], o[k], rtol=1e-13, atol=1e-13)
+    # zero token: n1 = 0, y = 0; constant block: n2 = 0, w = 0
+    xz = x.copy(); xz[3] = 0
+    oz = oracle.nsn_block(xz)
+    assert oz["n1"][3] == 0 and np.all(oz["y"][3] == 0)
+    xc = np.tile(x[:1], (x.shape[0], 1))
+    oc = oracle.nsn_block(xc)
+    assert np.all(oc["n2"] < 1e-14) and np.all(np.abs(oc["w"]) < 1e-6)
+
+
+def _brute_argmin(v, cbd):
+    # independent formulation: broadcast squared distances, first minimum
+    dist = ((v[:, None, :] - cbd[None, :, :]) ** 2).sum(-1)
+    return np.argmin(dist, axis=1), np.sort(dist, axis=1)
+
+
+def test_vq_matches_brute_force_and_ties(oracle_codebooks):
+    rng = np.random.default_rng(3)
+    for bits, s in ((2, 4), (1, 8)):
+        cb = oracle_codebooks[bits]
+        cbd = oracle.f16_to_f64(cb)
+        v = rng.standard_normal((500, s)) * 1.3
+        ref, srt = _brute_argmin(v, cbd)
+        for i in range(v.shape[0]):
+            code, d1, gap = oracle.vq(v[i], cb)
+            assert code == ref[i]
+            assert d1 == pytest.approx(srt[i, 0], rel=1e-12, abs=1e-15)
+            assert gap == pytest.approx((srt[i, 1] - srt[i, 0]) / srt[i, 0], rel=1e-9)
+    # duplicate codewords: ties go to the lowest index; zero distance gives gap inf
+    cb = oracle_codebooks[2].copy()
+    cb[200] = cb[17]
+    code, d1, gap = oracle.vq(oracle.f16_to_f64(cb[17]), cb)
+    assert code == 17 and d1 == 0.0 and gap == 0.0
+    cb2 = oracle_codebooks[2]
+    code, d1, gap = oracle.vq(oracle.f16_to_f64(cb2[42]), cb2)
+    assert code == 42 and d1 == 0.0 and gap == np.inf
+
+
+@pytest.mark.parametrize("bits,R,L", [(2, 64, 512), (1, 128, 300), (2, 128, 128), (2, 64, 1)])
+def test_encode_wiring(oracle_codebooks, bits, R, L):
+    cb = oracle_codebooks[bits]
+    s = cb.shape[1]
+    x = np.stack([synth.kv_unit(11 + i, L, D).numpy() for i in range(2)])
+    enc = oracle.encode(x, R, cb, with_u=True)
+    r = ((L - 1) % R) + 1
+    assert enc["n_resid"] == r and enc["n_quant"] == L - r
+    nq = L - r
+    # residual: the last r tokens verbatim
+    assert np.array_equal(enc["resid"][:, :r], x.view(np.uint16)[:, nq:])
+    H = oracle.hadamard_matrix(D)
+    cbd = oracle.f16_to_f64(cb)
+    for unit in range(2):
+        for blk in range(nq // R):
+            xb = x[unit, blk * R:(blk + 1) * R]
+            o = oracle.nsn_block(xb)
+            u = enc["u"][unit, blk * R:(blk + 1) * R]
+            assert np.allclose(u, o["w"] @ H.T, atol=1e-12)
+            assert np.array_equal(enc["scales"][unit, blk * R:(blk + 1) * R, 0], oracle.f64_to_f16(o["n1"]))
+            assert np.array_equal(enc["scales"][unit, blk * R:(blk + 1) * R, 1], oracle.f64_to_f16(o["n2"]))
+            assert np.array_equal(enc["mu"][unit, blk], oracle.f64_to_f16(o["mu"]))
+        # codes = brute-force argmin over the sub-vectors of u
+        S = D // s
+        sub = enc["u"][unit].reshape(-1, s)
+        ref, _ = _brute_argmin(sub, cbd)
+        assert np.array_equal(enc["codes"][unit].reshape(-1), ref)
+    assert enc["codes"].shape == (2, nq, D // s)
+
+
+def test_post_transform_stats_standard_normal():
+    """Lemma 1's qualitative content: on Gaussian input, NSN + Hadamard leaves
+    every output channel with mean ~0 and variance ~1."""
+    T = 4096
+    x = synth.uniform_unit(5, (T, D)).numpy()
+    enc = oracle.encode(x[None], 128, np.zeros((256, 4), np.uint16) + 0x3c00, with_u=True)
+    u = enc["u"][0]
+    n = u.shape[0]
+    assert np.all(np.abs(u.mean(0)) <= 5 / np.sqrt(n))
+    assert np.all(np.abs(u.var(0) - 1) <= 5 * np.sqrt(2 / n))
+    # and also on the outlier-heavy K/V generator (per-block centring removes the channel offsets)
+    x2 = synth.kv_unit(9, T, D).numpy()
+    u2 = oracle.encode(x2[None], 128, np.zeros((256, 4), np.uint16), with_u=True)["u"][0]
+    assert np.allclose(np.mean(u2 ** 2), 1.0, rtol=1e-9)
