@@ -127,11 +127,13 @@ void orc_hadamard(const double* w, double* u, int d) {
  *   3. each token is rescaled to norm sqrt(d) again, n2 = ||z|| / sqrt(d),
  *      w = z / n2.
  * A zero token (n1 = 0) gives y = 0.  A token equal to the block mean has
- * z = 0 up to rounding; when its n2 rounds to zero in the stored fp16 format
- * (n2 <= 2^-25) the direction is meaningless and w is set to 0.  The pages do
- * not cover these cases; this is the reading under which reconstruction from
- * the stored values stays exact (x_hat = N1 * MU) and both precisions agree.
+ * z = 0 up to rounding noise; when n2 < 2^-12 the direction of z carries no
+ * information (it is rounding noise in any finite precision), so n2 and w are
+ * set to 0 and the token is reconstructed as N1 * MU, within 2^-12 of its norm.
+ * The pages do not cover these cases; this is the reading under which the
+ * stored values are the same at any working precision.
  * Any output pointer may be NULL. */
+#define NSN_N2_FLOOR (1.0 / 4096.0)
 void orc_nsn_block(const uint16_t* x, int R, int d,
                    double* n1_out, double* y_out, double* mu_out,
                    double* z_out, double* n2_out, double* w_out) {
@@ -165,11 +167,12 @@ void orc_nsn_block(const uint16_t* x, int R, int d,
       ss += zc * zc;
     }
     double n2 = sqrt(ss) / sqrt_d;
+    if (n2 < NSN_N2_FLOOR) n2 = 0.0;
     if (n2_out) n2_out[t] = n2;
     if (w_out) {
       for (int c = 0; c < d; ++c) {
         double zc = y[(size_t)t * d + c] - mu[c];
-        w_out[(size_t)t * d + c] = (orc_d2h(n2) != 0) ? zc / n2 : 0.0;
+        w_out[(size_t)t * d + c] = (n2 > 0.0) ? zc / n2 : 0.0;
       }
     }
     if (y_out) memcpy(y_out + (size_t)t * d, y + (size_t)t * d, sizeof(double) * d);
