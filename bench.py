@@ -1,0 +1,219 @@
+"""Benchmark of the NSNQuant hot path on one MI355X.
+
+One step = prefill encode of a whole layer's K/V context (NSN, Hadamard, VQ,
+residual window) followed by one decode-attention step over the compressed
+cache, on synthetic K/V shaped like the named LLaMA layer.  Inputs are resident
+in HBM before the timed region; input and cache buffers rotate over several
+copies so the 256 MB Infinity Cache cannot serve them.
+
+Prints one JSON line.  `value` is context tokens (batch x context length)
+taken through encode + decode per second.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn tokens/s & HBM GB/s (% roofline) + KV encode tokens/s, 2b/1b"
+HBM_PEAK_GBS = 8000.0
+# Vector ALU: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz (32-bit ops, unpacked)
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+
+
+def encode_bytes_per_vector(bits: int, R: int, d: int = 128) -> float:
+    """HBM bytes the encode must move per head vector: fp16 input, codes,
+    (n1, n2) fp16, and its share of the block mean."""
+    S = d // (4 if bits == 2 else 8)
+    return 2 * d + S + 4 + 2 * d / R
+
+
+def decode_bytes(bits: int, R: int, n_quant: int, n_resid: int, units: int, d: int = 128) -> float:
+    """Algorithmic bytes of one decode step: K and V codes + scalars + means of
+    the compressed tokens, and the fp16 residual tokens, for `units` (b, h)."""
+    S = d // (4 if bits == 2 else 8)
+    per_tok = 2 * (S + 4) + 2 * (2 * d / R)
+    return units * (n_quant * per_tok + n_resid * 2 * 2 * d)
+
+
+def cpu_baseline(w: dict, cb_bits, k, v, q, heads: int):
+    """Time the CPU oracle on `heads` of the layer's KV heads (encode of those
+    heads' K and V, then their decode step); scale to the whole layer."""
+    import numpy as np
+    import oracle
+    from kv_cache_bit_amd import nsnq
+    R = w["R"]
+    G = w["Hq"] // w["Hkv"]
+    kk = k[:, :heads].cpu().contiguous()
+    vv = v[:, :heads].cpu().contiguous()
+    qq = q[:, :heads * G].cpu().contiguous()
+    t0 = time.perf_counter()
+    ek, ev = oracle.encode(kk, R, cb_bits), oracle.encode(vv, R, cb_bits)
+    t1 = time.perf_counter()
+    oracle.reference_decode(qq, ek, ev, ek["n_quant"], ek["n_resid"], R, cb_bits)
+    t2 = time.perf_counter()
+    scale = w["Hkv"] / heads
+    step = (t2 - t0) * scale
+    return dict(step_s=step, encode_s=(t1 - t0) * scale, decode_s=(t2 - t1) * scale,
+                cores=oracle.num_threads(), sample=f"{heads} of {w['Hkv']} KV heads x batch {w['B']}, "
+                f"full context; time scaled x{scale:g}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama2-7b-layer-b1-2bit")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="KV heads in the CPU-baseline sample (0: skip)")
+    ap.add_argument("--codebook-iters", type=int, default=50)
+    ap.add_argument("--no-fp16", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this path has no multi-GPU code).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from kv_cache_bit_amd import nsnq, synth
+
+    nsnq.lib()  # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = dict(synth.WORKLOADS[args.workload])
+    assert w["layers"] == 1, "multi-layer workloads: not in this bench yet"
+    B, Hq, Hkv, L, d, bits, R = w["B"], w["Hq"], w["Hkv"], w["L"], w["d"], w["bits"], w["R"]
+    s = nsnq.sub_dim(bits)
+    p = nsnq.params(bits, R)
+
+    # ---- setup (untimed) ----------------------------------------------------
+    t_cb = time.perf_counter()
+    samples = synth.randn_samples(0, 1 << 20, s).to(dev)
+    _, codebook, dist = nsnq.nsnq_build_codebook(p, samples, args.codebook_iters)
+    torch.cuda.synchronize()
+    t_cb = time.perf_counter() - t_cb
+    k, v = synth.kv_layer(w["config_id"], 0, B, Hkv, L, d, outlier_std=synth.outlier_std_for(args.workload, 0),
+                          device=dev)
+    q = synth.queries(w["config_id"], 0, B, Hq, d, device=dev)
+    set_bytes = 2 * k.numel() * 2
+    nbuf = max(1, min(8, math.ceil(512e6 / set_bytes)))
+    ks = [k] + [k.clone() for _ in range(nbuf - 1)]
+    vs = [v] + [v.clone() for _ in range(nbuf - 1)]
+    r = ((L - 1) % R) + 1
+    nq = L - r
+    caches = [nsnq.KVCache(p, B, Hkv, nq + R, dev) for _ in range(nbuf)]
+    outs = [torch.empty_like(q) for _ in range(nbuf)]
+    # workspace sized for a filled cache
+    caches[0].n_quant, caches[0].n_resid = nq, r
+    ws_bytes = nsnq.nsnq_decode_workspace_bytes(p, caches[0], Hq)
+    caches[0].n_quant = caches[0].n_resid = 0
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        c = caches[i % nbuf]
+        c.n_quant = c.n_resid = 0
+        if ev is not None:
+            ev[0].record(stream)
+        nsnq.nsnq_encode_kv(p, codebook, ks[i % nbuf], vs[i % nbuf], L, c, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        nsnq.nsnq_decode_attention(p, codebook, q, c, out=outs[i % nbuf], ws=wss[i % nbuf], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    ms_per_step = wall * 1e3 / args.steps
+
+    units = B * Hkv
+    n_vec = 2 * units * nq
+    enc_bytes = n_vec * encode_bytes_per_vector(bits, R, d) + 2 * units * r * 2 * d * 2  # + residual copy
+    dec_bytes = decode_bytes(bits, R, nq, r, units, d)
+    enc_s = float(np.mean(enc_ms)) / 1e3
+    dec_s = float(np.mean(dec_ms)) / 1e3
+    cand = n_vec * (d // s) * 256  # argmin candidates per launch
+    enc_gbs = enc_bytes / enc_s / 1e9
+    dec_gbs = dec_bytes / dec_s / 1e9
+    enc_alu_tops = cand / enc_s / 1e12
+
+    # fp16 comparator on the same layer
+    fp16 = None
+    if not args.no_fp16:
+        kf, vf = k[:, :, :L].contiguous(), v[:, :, :L].contiguous()
+        o16 = nsnq.nsnq_fp16_decode_attention(q, kf, vf)
+        for _ in range(5):
+            nsnq.nsnq_fp16_decode_attention(q, kf, vf, out=o16)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n16 = 50
+        e0.record(stream)
+        for _ in range(n16):
+            nsnq.nsnq_fp16_decode_attention(q, kf, vf, out=o16)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t16 = e0.elapsed_time(e1) / n16 / 1e3
+        b16 = units * L * 2 * 2 * d
+        fp16 = dict(us=t16 * 1e6, tokens_per_s=B / t16, gbs=b16 / t16 / 1e9,
+                    compressed_speedup=t16 / dec_s, bytes=b16)
+
+    value = B * L / (ms_per_step / 1e3)
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "context": L,
+                   "head_dim": d, "bits": bits, "residual": R, "encoded_tokens": nq, "residual_tokens": r},
+        "encode": {"us": enc_s * 1e6, "tokens_per_s": B * L / enc_s, "vectors_per_s": n_vec / enc_s,
+                   "hbm_gbs": enc_gbs, "hbm_frac": enc_gbs / HBM_PEAK_GBS,
+                   "argmin_candidates_per_s": cand / enc_s, "bytes": enc_bytes},
+        "decode": {"us": dec_s * 1e6, "tokens_per_s": B / dec_s, "kv_tokens_per_s": units * L / dec_s,
+                   "hbm_gbs": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS, "bytes": dec_bytes},
+        "fp16_decode": fp16,
+        "codebook": {"build_s": t_cb, "iters": args.codebook_iters, "n": 1 << 20,
+                     "final_mse_per_elem": float(dist[-1].item())},
+        "roofline": {"kernel": "encode_kernel", "bound": "alu", "achieved": enc_alu_tops,
+                     "peak": VALU_PEAK_TOPS, "unit": "Tops/s", "frac": enc_alu_tops / VALU_PEAK_TOPS,
+                     "traffic": None,
+                     "note": "achieved = argmin candidate distances per second (one 32-bit compare each)"},
+        "timing": {"step_ms_median": float(np.median(step_ms)), "step_ms_p10": float(np.percentile(step_ms, 10)),
+                   "step_ms_p90": float(np.percentile(step_ms, 90)), "buffer_sets": nbuf},
+    }
+    if args.cpu_heads > 0:
+        cb_bits = codebook.cpu().numpy().view(np.uint16)
+        cb_ = cpu_baseline(w, cb_bits, k, v, q, min(args.cpu_heads, Hkv))
+        res["cpu_baseline"] = {"value": B * L / cb_["step_s"], "unit": "tokens/s", "cores": cb_["cores"],
+                               "kind": "oracle", "sample": cb_["sample"],
+                               "encode_s": cb_["encode_s"], "decode_s": cb_["decode_s"]}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * nsnq.h -- C ABI of libnsnq: NSNQuant KV-cache vector quantisation and
+ * decode attention over the compressed cache, for AMD MI355X (gfx950).
+ *
+ * The method (NSNQuant, "A Double Normalization Approach for Calibration-Free
+ * Low-Bit Vector Quantization of KV Cache"; summarised on the atlas.scime.ai,
+ * gist.science and pith.science pages) encodes each key/value head vector x of
+ * dimension d by
+ *   1. token-wise normalisation to norm sqrt(d), keeping n1 = ||x|| / sqrt(d);
+ *   2. subtracting the channel-wise mean mu of the block of R tokens being
+ *      quantised;
+ *   3. a second token-wise normalisation, keeping n2;
+ *   4. an orthonormal (Sylvester, not randomised) Hadamard rotation;
+ *   5. vector quantisation of each run of s consecutive elements against one
+ *      256-word codebook fit by k-means on seeded standard-normal samples;
+ * while the most recent tokens stay in an fp16 residual window of R tokens.
+ * Attention over the cache folds n1, n2 and mu into the scores and the value
+ * sum (technical summary, sec. 4, "Attention Computation").
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE memory unless stated otherwise, owned by the
+ *    caller, and must stay valid until the work queued on `stream` has run.
+ *    fp16 values are IEEE binary16 bit patterns (uint16_t).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is asynchronous on it; nothing is synchronised.
+ *  - Argument checks run on the host before anything is launched.  On error
+ *    nothing is launched and a status other than NSNQ_OK is returned.  A
+ *    launch failure returns NSNQ_EHIP.  Device faults surface at the caller's
+ *    next synchronisation.  Inputs must be finite (not checked).
+ *  - The library allocates no memory, keeps no global state and prints
+ *    nothing; calls on different streams are independent.
+ *  - Layouts are dense and row-major.  For a cache of `batch` rows,
+ *    `kv_heads` heads and capacity `cap_tokens` (a multiple of R), with
+ *    S = d / s slots per vector (s = 4 at 2 bits, 8 at 1 bit):
+ *      codes  uint8  [batch][kv_heads][cap_tokens][S]
+ *      scales fp16   [batch][kv_heads][cap_tokens][2]   (n1, n2)
+ *      mu     fp16   [batch][kv_heads][cap_tokens / R][d]
+ *      resid  fp16   [batch][kv_heads][R][d]
+ *    Every pointer must be 16-byte aligned.
+ */
+#ifndef NSNQ_H
+#define NSNQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NSNQ_ABI_VERSION 1
+
+typedef int32_t nsnq_status;
+enum {
+  NSNQ_OK = 0,
+  NSNQ_EINVAL = 1,       /* bad argument, shape, counter or alignment */
+  NSNQ_EUNSUPPORTED = 2, /* valid but not implemented (e.g. d != 128) */
+  NSNQ_EHIP = 3,         /* a HIP launch or runtime call failed */
+  NSNQ_EWORKSPACE = 4    /* workspace missing or too small */
+};
+
+/* Format parameters.  head_dim must be 128, bits 1 or 2 (sub-vectors of 8 or 4
+ * elements, one uint8 code each), n_codewords 256, block_tokens (R, the size of
+ * both the residual window and the mean block) 64 or 128. */
+typedef struct {
+  int32_t head_dim;
+  int32_t bits;
+  int32_t n_codewords;
+  int32_t block_tokens;
+} nsnq_params;
+
+/* One of the K or V halves of a cache (layouts above). */
+typedef struct {
+  uint8_t* codes;
+  uint16_t* scales;
+  uint16_t* mu;
+  uint16_t* resid;
+} nsnq_kv;
+
+/* A one-layer compressed cache.  n_quant (a multiple of R) and n_resid
+ * (0..R) are HOST counters, the same for every batch row; the calls below
+ * read and update them. */
+typedef struct {
+  nsnq_kv k, v;
+  int32_t batch;
+  int32_t kv_heads;
+  int32_t cap_tokens;
+  int32_t n_quant;
+  int32_t n_resid;
+} nsnq_cache;
+
+/* ABI version (NSNQ_ABI_VERSION) and a static text for a status. */
+int32_t nsnq_abi_version(void);
+const char* nsnq_status_str(nsnq_status st);
+
+/* Fit the codebook with Lloyd's k-means (technical summary sec. 3, "Codebook
+ * Constructie": k-means on synthetic torch.randn data, once, for any model).
+ *   samples      fp32 [n][s] training vectors, s = 4 (bits 2) or 8 (bits 1);
+ *                n >= n_codewords.
+ *   init         fp32 [256][s] initial centroids, or NULL for the first 256
+ *                samples.
+ *   iters        Lloyd iterations (>= 0).  Each assigns every sample to its
+ *                nearest centroid (squared Euclidean, ties to the lowest
+ *                index) and moves each centroid to the mean of its members; a
+ *                centroid without members stays put.
+ *   centroids    fp32 [256][s] out: final centroids.
+ *   codebook     fp16 [256][s] out: centroids rounded to nearest even.
+ *   distortion   fp32 [iters] out (may be NULL): mean squared error per
+ *                element of iteration i's assignment.
+ *   ws/ws_bytes  device workspace of at least
+ *                nsnq_build_codebook_workspace_bytes() bytes.
+ */
+size_t nsnq_build_codebook_workspace_bytes(const nsnq_params* p);
+nsnq_status nsnq_build_codebook(const nsnq_params* p, const float* samples, int64_t n,
+                                int32_t iters, const float* init, float* centroids,
+                                uint16_t* codebook, float* distortion, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* Prefill encode (technical summary secs. 1-4).  k and v are fp16 streams
+ * indexed [b][h][t][c] at element offsets b*stride_b + h*stride_h +
+ * t*stride_t + c (c contiguous), t < L.  Of the L tokens, the first L - r are
+ * encoded in blocks of R at token positions n_quant.. of the cache, where
+ * r = ((L - 1) mod R) + 1 (0 when L = 0); the last r are copied verbatim into
+ * resid.  Requires cache->n_resid == 0 and n_quant + L - r <= cap_tokens;
+ * afterwards n_quant += L - r and n_resid = r.  codebook: fp16 [256][s]. */
+nsnq_status nsnq_encode_kv(const nsnq_params* p, const uint16_t* codebook, const uint16_t* k,
+                           const uint16_t* v, int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                           int32_t L, nsnq_cache* cache, void* stream);
+
+/* Flush a full residual window (technical summary sec. 4, "Residuals"): the R
+ * residual tokens are encoded as one block at position n_quant, then
+ * n_quant += R and n_resid = 0.  Requires n_resid == R and
+ * n_quant + R <= cap_tokens.  The caller then writes the new token into
+ * resid[.., n_resid, :] and increments n_resid. */
+nsnq_status nsnq_flush_residual(const nsnq_params* p, const uint16_t* codebook, nsnq_cache* cache,
+                                void* stream);
+
+/* Reconstruct quantised tokens [tok0, tok0 + ntok) of the K (which = 0) or V
+ * (which = 1) half: x_hat = N1 * (N2 * H c_hat + MU_block), the inverse of the
+ * encode using only stored values (technical summary sec. 1: the byproducts
+ * rebuild the tensor; sec. 4: dequantisation kernel).  Requires
+ * 0 <= tok0, tok0 + ntok <= n_quant.  out: [batch][kv_heads][ntok][d] as fp32
+ * (out_dtype 0) or fp16 (out_dtype 1). */
+nsnq_status nsnq_dequant(const nsnq_params* p, const uint16_t* codebook, const nsnq_cache* cache,
+                         int32_t which, int32_t tok0, int32_t ntok, int32_t out_dtype, void* out,
+                         void* stream);
+
+/* Decode attention for one query token per batch row over the n_quant
+ * compressed and n_resid fp16 tokens of the cache (technical summary sec. 4,
+ * "Attention Computation"; the figure "Overall structure of attention under
+ * NSNQuant").  q: fp16 [batch][q_heads][d]; query head h reads KV head
+ * h / (q_heads / kv_heads).  softmax over scale * q.k.  num_splits: number of
+ * token ranges per head processed in parallel (0 = choose).  out: fp16
+ * [batch][q_heads][d].  ws/ws_bytes: device workspace of at least
+ * nsnq_decode_workspace_bytes(p, cache, q_heads, num_splits) bytes.
+ * Requires n_quant + n_resid >= 1. */
+size_t nsnq_decode_workspace_bytes(const nsnq_params* p, const nsnq_cache* cache, int32_t q_heads,
+                                   int32_t num_splits);
+nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook, const uint16_t* q,
+                                  int32_t q_heads, const nsnq_cache* cache, float softmax_scale,
+                                  int32_t num_splits, uint16_t* out, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* Comparator: the same decode attention over an uncompressed fp16 cache
+ * k, v [batch][kv_heads][n_tokens][d] (d = 128), used to measure the gain of
+ * the compressed cache.  Workspace from nsnq_fp16_decode_workspace_bytes(). */
+size_t nsnq_fp16_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t n_tokens,
+                                        int32_t num_splits);
+nsnq_status nsnq_fp16_decode_attention(const uint16_t* q, int32_t q_heads, const uint16_t* k,
+                                       const uint16_t* v, int32_t batch, int32_t kv_heads,
+                                       int32_t n_tokens, float softmax_scale, int32_t num_splits,
+                                       uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSNQ_H */

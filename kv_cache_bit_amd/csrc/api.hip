@@ -1,0 +1,371 @@
+// api.hip -- extern "C" entry points of libnsnq: host-side validation, launch
+// configuration and counter bookkeeping.  Every check runs before any HIP
+// call, so a rejected call touches neither the GPU nor the cache.
+
+#include "../../include/nsnq.h"
+#include "nsnq_device.hpp"
+#include "nsnq_launch.hpp"
+
+namespace nsnq {
+hipError_t launch_kmeans_clear(double* acc, int n, hipStream_t stream);
+}
+
+using namespace nsnq;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+nsnq_status check_params(const nsnq_params* p) {
+  if (!p) return NSNQ_EINVAL;
+  if (p->bits != 1 && p->bits != 2) return NSNQ_EINVAL;
+  if (p->n_codewords != 256 || p->head_dim <= 0 || p->block_tokens <= 0) return NSNQ_EINVAL;
+  if (p->head_dim != 128) return NSNQ_EUNSUPPORTED;
+  if (p->block_tokens != 64 && p->block_tokens != 128) return NSNQ_EUNSUPPORTED;
+  return NSNQ_OK;
+}
+
+int sub_of(const nsnq_params* p) { return p->bits == 2 ? 4 : 8; }
+
+nsnq_status check_kv(const nsnq_kv& kv) {
+  if (!kv.codes || !kv.scales || !kv.mu || !kv.resid) return NSNQ_EINVAL;
+  if (!aligned16(kv.codes) || !aligned16(kv.scales) || !aligned16(kv.mu) || !aligned16(kv.resid))
+    return NSNQ_EINVAL;
+  return NSNQ_OK;
+}
+
+nsnq_status check_cache(const nsnq_params* p, const nsnq_cache* c) {
+  if (!c) return NSNQ_EINVAL;
+  if (c->batch <= 0 || c->kv_heads <= 0 || c->cap_tokens <= 0) return NSNQ_EINVAL;
+  if (c->cap_tokens % p->block_tokens != 0) return NSNQ_EINVAL;
+  if (c->n_quant < 0 || c->n_quant % p->block_tokens != 0 || c->n_quant > c->cap_tokens) return NSNQ_EINVAL;
+  if (c->n_resid < 0 || c->n_resid > p->block_tokens) return NSNQ_EINVAL;
+  if ((int64_t)c->batch * c->kv_heads * c->cap_tokens > (int64_t)1 << 40) return NSNQ_EINVAL;
+  nsnq_status s = check_kv(c->k);
+  if (s != NSNQ_OK) return s;
+  return check_kv(c->v);
+}
+
+nsnq_status hip_status(hipError_t e) { return e == hipSuccess ? NSNQ_OK : NSNQ_EHIP; }
+
+// One launch: encode `nblk` blocks per stream from src (strides given) to
+// token n_quant, and copy `rc_r` tokens starting at source token `rc_t0` into
+// the residual window.
+nsnq_status run_encode(const nsnq_params* p, const uint16_t* cb, const uint16_t* k, const uint16_t* v,
+                       int64_t sb, int64_t sh, int64_t st, int nblk, int rc_t0, int rc_r, const nsnq_cache* c,
+                       hipStream_t stream) {
+  if (nblk <= 0 && rc_r <= 0) return NSNQ_OK;
+  EncodeArgs a{};
+  a.src[0] = k;
+  a.src[1] = v;
+  a.sb = sb;
+  a.sh = sh;
+  a.st = st;
+  a.codes[0] = c->k.codes;
+  a.codes[1] = c->v.codes;
+  a.scales[0] = c->k.scales;
+  a.scales[1] = c->v.scales;
+  a.mu[0] = c->k.mu;
+  a.mu[1] = c->v.mu;
+  a.resid[0] = c->k.resid;
+  a.resid[1] = c->v.resid;
+  a.codebook = cb;
+  a.H = c->kv_heads;
+  a.n_units = c->batch * c->kv_heads;
+  a.cap = c->cap_tokens;
+  a.dst_tok0 = c->n_quant;
+  a.nblk = nblk > 0 ? nblk : 0;
+  a.R = p->block_tokens;
+  a.rc_t0 = rc_t0;
+  a.rc_r = rc_r;
+  return hip_status(launch_encode(a, sub_of(p), p->block_tokens, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nsnq_abi_version(void) { return NSNQ_ABI_VERSION; }
+
+const char* nsnq_status_str(nsnq_status st) {
+  switch (st) {
+    case NSNQ_OK: return "ok";
+    case NSNQ_EINVAL: return "invalid argument";
+    case NSNQ_EUNSUPPORTED: return "unsupported parameters";
+    case NSNQ_EHIP: return "HIP runtime error";
+    case NSNQ_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+size_t nsnq_build_codebook_workspace_bytes(const nsnq_params* p) {
+  if (check_params(p) != NSNQ_OK) return 0;
+  return sizeof(double) * ((size_t)kCodewords * sub_of(p) + kCodewords + 1);
+}
+
+nsnq_status nsnq_build_codebook(const nsnq_params* p, const float* samples, int64_t n, int32_t iters,
+                                const float* init, float* centroids, uint16_t* codebook, float* distortion,
+                                void* ws, size_t ws_bytes, void* stream) {
+  nsnq_status s = check_params(p);
+  if (s != NSNQ_OK) return s;
+  if (!samples || !centroids || !codebook || n < p->n_codewords || iters < 0) return NSNQ_EINVAL;
+  if (!aligned16(samples) || !aligned16(centroids) || !aligned16(codebook)) return NSNQ_EINVAL;
+  if (init && !aligned16(init)) return NSNQ_EINVAL;
+  if (!ws || ws_bytes < nsnq_build_codebook_workspace_bytes(p) || !aligned16(ws)) return NSNQ_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int sub = sub_of(p);
+  double* acc = (double*)ws;
+  KmeansArgs a{};
+  a.samples = samples;
+  a.n = n;
+  a.cent = centroids;
+  a.sums = acc;
+  a.counts = acc + kCodewords * sub;
+  a.dsum = acc + kCodewords * sub + kCodewords;
+  a.distortion = distortion;
+  a.codebook = codebook;
+  hipError_t e = launch_kmeans_init(init ? init : samples, centroids, sub, st);
+  if (e == hipSuccess) e = launch_kmeans_clear(acc, kCodewords * sub + kCodewords + 1, st);
+  for (int it = 0; it < iters && e == hipSuccess; ++it) {
+    a.it = it;
+    e = launch_kmeans_iter(a, sub, st);
+  }
+  if (e == hipSuccess) e = launch_kmeans_finish(a, sub, st);
+  return hip_status(e);
+}
+
+nsnq_status nsnq_encode_kv(const nsnq_params* p, const uint16_t* codebook, const uint16_t* k, const uint16_t* v,
+                           int64_t stride_b, int64_t stride_h, int64_t stride_t, int32_t L, nsnq_cache* cache,
+                           void* stream) {
+  nsnq_status s = check_params(p);
+  if (s != NSNQ_OK) return s;
+  s = check_cache(p, cache);
+  if (s != NSNQ_OK) return s;
+  if (!codebook || !aligned16(codebook) || L < 0) return NSNQ_EINVAL;
+  if (L == 0) return NSNQ_OK;
+  if (!k || !v || !aligned16(k) || !aligned16(v)) return NSNQ_EINVAL;
+  // 16-byte aligned token rows: every stride a multiple of 8 elements
+  if (stride_t < p->head_dim || stride_b < 0 || stride_h < 0) return NSNQ_EINVAL;
+  if ((stride_t % 8) || (stride_h % 8) || (stride_b % 8)) return NSNQ_EINVAL;
+  if (cache->n_resid != 0) return NSNQ_EINVAL;
+  const int R = p->block_tokens;
+  const int r = ((L - 1) % R) + 1;
+  const int nq = L - r;
+  if ((int64_t)cache->n_quant + nq > cache->cap_tokens) return NSNQ_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  s = run_encode(p, codebook, k, v, stride_b, stride_h, stride_t, nq / R, nq, r, cache, st);
+  if (s != NSNQ_OK) return s;
+  cache->n_quant += nq;
+  cache->n_resid = r;
+  return NSNQ_OK;
+}
+
+nsnq_status nsnq_flush_residual(const nsnq_params* p, const uint16_t* codebook, nsnq_cache* cache, void* stream) {
+  nsnq_status s = check_params(p);
+  if (s != NSNQ_OK) return s;
+  s = check_cache(p, cache);
+  if (s != NSNQ_OK) return s;
+  if (!codebook || !aligned16(codebook)) return NSNQ_EINVAL;
+  const int R = p->block_tokens;
+  if (cache->n_resid != R) return NSNQ_EINVAL;
+  if ((int64_t)cache->n_quant + R > cache->cap_tokens) return NSNQ_EINVAL;
+  const int64_t st = p->head_dim, sh = (int64_t)R * p->head_dim, sb = sh * cache->kv_heads;
+  s = run_encode(p, codebook, cache->k.resid, cache->v.resid, sb, sh, st, 1, 0, 0, cache, (hipStream_t)stream);
+  if (s != NSNQ_OK) return s;
+  cache->n_quant += R;
+  cache->n_resid = 0;
+  return NSNQ_OK;
+}
+
+nsnq_status nsnq_dequant(const nsnq_params* p, const uint16_t* codebook, const nsnq_cache* cache, int32_t which,
+                         int32_t tok0, int32_t ntok, int32_t out_dtype, void* out, void* stream) {
+  nsnq_status s = check_params(p);
+  if (s != NSNQ_OK) return s;
+  s = check_cache(p, cache);
+  if (s != NSNQ_OK) return s;
+  if (!codebook || !aligned16(codebook)) return NSNQ_EINVAL;
+  if (which != 0 && which != 1) return NSNQ_EINVAL;
+  if (out_dtype != 0 && out_dtype != 1) return NSNQ_EINVAL;
+  if (tok0 < 0 || ntok < 0 || (int64_t)tok0 + ntok > cache->n_quant) return NSNQ_EINVAL;
+  if (ntok == 0) return NSNQ_OK;
+  if (!out || !aligned16(out)) return NSNQ_EINVAL;
+  const nsnq_kv& kv = which == 0 ? cache->k : cache->v;
+  DequantArgs a{};
+  a.codes = kv.codes;
+  a.scales = kv.scales;
+  a.mu = kv.mu;
+  a.codebook = codebook;
+  a.out = out;
+  a.H = cache->kv_heads;
+  a.cap = cache->cap_tokens;
+  a.R = p->block_tokens;
+  a.tok0 = tok0;
+  a.ntok = ntok;
+  a.out_f16 = out_dtype;
+  return hip_status(launch_dequant(a, sub_of(p), cache->batch * cache->kv_heads, (hipStream_t)stream));
+}
+
+namespace {
+
+struct DecodePlan {
+  int gh, split_tokens, nsplit_q, nsplit;
+  size_t lds;
+};
+
+// Query heads per work-group: the largest of 4, 2, 1 dividing G.
+int heads_per_group(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
+
+DecodePlan plan_decode(const nsnq_params* p, const nsnq_cache* c, int q_heads, int num_splits) {
+  DecodePlan pl{};
+  const int G = q_heads / c->kv_heads;
+  const int R = p->block_tokens;
+  pl.gh = heads_per_group(G);
+  const int nblk = c->n_quant / R;
+  const int max_ts = decode_max_split_tokens(sub_of(p), pl.gh, R);
+  const int max_bps = max_ts / R;  // blocks per split
+  int bps;
+  if (nblk == 0) {
+    bps = 1;
+  } else if (num_splits > 0) {
+    bps = (nblk + num_splits - 1) / num_splits;
+  } else {
+    // aim for about 2048 work-groups over the whole grid
+    const int64_t units = (int64_t)c->batch * c->kv_heads * (G / pl.gh);
+    int64_t want = (2048 + units - 1) / units;
+    if (want < 1) want = 1;
+    bps = (int)((nblk + want - 1) / want);
+  }
+  if (bps < 1) bps = 1;
+  if (bps > max_bps) bps = max_bps;
+  pl.split_tokens = bps * R;
+  pl.nsplit_q = nblk == 0 ? 0 : (nblk + bps - 1) / bps;
+  pl.nsplit = pl.nsplit_q + (c->n_resid > 0 ? 1 : 0);
+  pl.lds = decode_lds_bytes(sub_of(p), pl.gh, pl.split_tokens, R);
+  return pl;
+}
+
+}  // namespace
+
+size_t nsnq_decode_workspace_bytes(const nsnq_params* p, const nsnq_cache* cache, int32_t q_heads,
+                                   int32_t num_splits) {
+  if (check_params(p) != NSNQ_OK || !cache || cache->kv_heads <= 0 || q_heads <= 0 ||
+      q_heads % cache->kv_heads != 0 || cache->batch <= 0 || cache->n_quant < 0 || cache->n_resid < 0)
+    return 0;
+  const DecodePlan pl = plan_decode(p, cache, q_heads, num_splits);
+  return sizeof(float) * (size_t)cache->batch * q_heads * (size_t)pl.nsplit * (kDim + 2);
+}
+
+nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook, const uint16_t* q,
+                                  int32_t q_heads, const nsnq_cache* cache, float softmax_scale,
+                                  int32_t num_splits, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  nsnq_status s = check_params(p);
+  if (s != NSNQ_OK) return s;
+  s = check_cache(p, cache);
+  if (s != NSNQ_OK) return s;
+  if (!codebook || !q || !out || !aligned16(codebook) || !aligned16(q) || !aligned16(out)) return NSNQ_EINVAL;
+  if (q_heads <= 0 || q_heads % cache->kv_heads != 0) return NSNQ_EINVAL;
+  const int G = q_heads / cache->kv_heads;
+  if (G > 64 || num_splits < 0) return NSNQ_EINVAL;
+  if (cache->n_quant + cache->n_resid < 1) return NSNQ_EINVAL;
+  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return NSNQ_EINVAL;
+  const size_t need = nsnq_decode_workspace_bytes(p, cache, q_heads, num_splits);
+  if (!ws || !aligned16(ws) || ws_bytes < need) return NSNQ_EWORKSPACE;
+  const DecodePlan pl = plan_decode(p, cache, q_heads, num_splits);
+  DecodeArgs a{};
+  a.q = q;
+  a.kcodes = cache->k.codes;
+  a.kscales = cache->k.scales;
+  a.kmu = cache->k.mu;
+  a.kresid = cache->k.resid;
+  a.vcodes = cache->v.codes;
+  a.vscales = cache->v.scales;
+  a.vmu = cache->v.mu;
+  a.vresid = cache->v.resid;
+  a.codebook = codebook;
+  a.ws = (float*)ws;
+  a.Hq = q_heads;
+  a.Hkv = cache->kv_heads;
+  a.G = G;
+  a.cap = cache->cap_tokens;
+  a.R = p->block_tokens;
+  a.n_quant = cache->n_quant;
+  a.n_resid = cache->n_resid;
+  a.split_tokens = pl.split_tokens;
+  a.nsplit_q = pl.nsplit_q;
+  a.nsplit = pl.nsplit;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_decode(a, sub_of(p), pl.gh, cache->batch, pl.lds, st);
+  if (e != hipSuccess) return NSNQ_EHIP;
+  CombineArgs cb{};
+  cb.ws = (const float*)ws;
+  cb.out = out;
+  cb.Hq = q_heads;
+  cb.nsplit = pl.nsplit;
+  return hip_status(launch_combine(cb, cache->batch, st));
+}
+
+// --------------------------------------------------------------- fp16 ------
+
+namespace {
+int fp16_split_tokens(int G, int T, int num_splits, int units) {
+  int ts;
+  if (num_splits > 0) {
+    ts = (T + num_splits - 1) / num_splits;
+  } else {
+    int64_t want = (2048 + units - 1) / units;
+    if (want < 1) want = 1;
+    ts = (int)((T + want - 1) / want);
+  }
+  ts = (ts + 63) / 64 * 64;
+  if (ts < 64) ts = 64;
+  while (ts > 64 && fp16_decode_lds_bytes(G, ts) > 160 * 1024) ts -= 64;
+  return ts;
+}
+}  // namespace
+
+size_t nsnq_fp16_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t n_tokens, int32_t num_splits) {
+  (void)num_splits;
+  if (batch <= 0 || q_heads <= 0 || n_tokens <= 0) return 0;
+  // worst case over G: one split per 64 tokens
+  const size_t ns = (size_t)(n_tokens + 63) / 64;
+  return sizeof(float) * (size_t)batch * q_heads * ns * (kDim + 2);
+}
+
+nsnq_status nsnq_fp16_decode_attention(const uint16_t* q, int32_t q_heads, const uint16_t* k, const uint16_t* v,
+                                       int32_t batch, int32_t kv_heads, int32_t n_tokens, float softmax_scale,
+                                       int32_t num_splits, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return NSNQ_EINVAL;
+  if (batch <= 0 || kv_heads <= 0 || q_heads <= 0 || q_heads % kv_heads != 0 || n_tokens <= 0 || num_splits < 0)
+    return NSNQ_EINVAL;
+  const int G = q_heads / kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return NSNQ_EUNSUPPORTED;
+  if (!(softmax_scale > 0.f)) return NSNQ_EINVAL;
+  const int ts = fp16_split_tokens(G, n_tokens, num_splits, batch * kv_heads);
+  const int nsplit = (n_tokens + ts - 1) / ts;
+  const size_t need = sizeof(float) * (size_t)batch * q_heads * nsplit * (kDim + 2);
+  if (!ws || !aligned16(ws) || ws_bytes < need) return NSNQ_EWORKSPACE;
+  Fp16DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.ws = (float*)ws;
+  a.Hq = q_heads;
+  a.Hkv = kv_heads;
+  a.G = G;
+  a.T = n_tokens;
+  a.split_tokens = ts;
+  a.nsplit = nsplit;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipStream_t st = (hipStream_t)stream;
+  if (launch_fp16_decode(a, batch, st) != hipSuccess) return NSNQ_EHIP;
+  CombineArgs cb{};
+  cb.ws = (const float*)ws;
+  cb.out = out;
+  cb.Hq = q_heads;
+  cb.nsplit = nsplit;
+  return hip_status(launch_combine(cb, batch, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+// aux.hip -- dequantisation and k-means codebook fitting (gfx950).
+
+#include "nsnq_device.hpp"
+#include "nsnq_launch.hpp"
+
+namespace nsnq {
+
+// ---------------------------------------------------------------------------
+// Dequant: x_hat = N1 * (N2 * H c_hat + MU_block).  Same lane layout as the
+// encoder (one sub-vector per lane, S lanes per token); the Hadamard inverse is
+// the forward transform (H symmetric, orthonormal).  64 tokens per group.
+template <int SUB>
+__global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
+  constexpr int S = kDim / SUB;
+  constexpr int TPR = kWave / S;
+  constexpr int TPB = 64;                // tokens per work-group
+  constexpr int ROWS = TPB / 4 / TPR;
+  __shared__ float cbf[kCodewords * SUB];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = lane % S, tir = lane / S;
+  const int unit = blockIdx.y;
+  for (int i = threadIdx.x; i < kCodewords * SUB; i += 256) cbf[i] = h2f(a.codebook[i]);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const int i = blockIdx.x * TPB + wave * (TPB / 4) + r * TPR + tir;  // output token
+    const bool act = i < a.ntok;
+    const int t = a.tok0 + (act ? i : 0);                               // cache token
+    const int64_t ct = (int64_t)unit * a.cap + t;
+    const uint32_t code = a.codes[ct * S + slot];
+    const uint32_t sc = reinterpret_cast<const uint32_t*>(a.scales)[ct];
+    const float n1 = h2f(sc & 0xffff), n2 = h2f(sc >> 16);
+    float x[SUB];
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) x[e] = cbf[code * SUB + e];
+    fwht128<SUB>(x, lane);
+    const uint16_t* mp = a.mu + ((int64_t)unit * (a.cap / a.R) + t / a.R) * kDim + slot * SUB;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) x[e] = n1 * fmaf(n2, x[e] * kInvSqrtD, h2f(mp[e]));
+    if (act) {
+      const int64_t o = ((int64_t)unit * a.ntok + i) * kDim + slot * SUB;
+      if (a.out_f16) {
+        uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + o;
+#pragma unroll
+        for (int e = 0; e < SUB; ++e) out[e] = f2h(x[e]);
+      } else {
+        float* out = reinterpret_cast<float*>(a.out) + o;
+#pragma unroll
+        for (int e = 0; e < SUB; ++e) out[e] = x[e];
+      }
+    }
+  }
+}
+
+hipError_t launch_dequant(const DequantArgs& a, int sub, int n_units, hipStream_t stream) {
+  dim3 grid((a.ntok + 63) / 64, n_units), block(256);
+  if (sub == 4) hipLaunchKernelGGL(dequant_kernel<4>, grid, block, 0, stream, a);
+  else if (sub == 8) hipLaunchKernelGGL(dequant_kernel<8>, grid, block, 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// k-means (Lloyd).  Iteration = assign (fp32 squared distances in difference
+// form, ties to the lowest index) with per-group LDS accumulation of member
+// sums (fp64), counts and distortion, flushed to global fp64 accumulators;
+// then a one-group update that moves non-empty centroids to their means and
+// clears the accumulators for the next iteration.
+
+template <int SUB>
+__global__ __launch_bounds__(256) void kmeans_assign_kernel(KmeansArgs a) {
+  __shared__ float cent[kCodewords * SUB];
+  __shared__ double lsum[kCodewords * SUB];
+  __shared__ double lcnt[kCodewords];
+  __shared__ double ldist[4];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kCodewords * SUB; i += 256) {
+    cent[i] = a.cent[i];
+    lsum[i] = 0.0;
+  }
+  lcnt[tid] = 0.0;
+  __syncthreads();
+  double dl = 0.0;
+  for (int64_t p = (int64_t)blockIdx.x * 256 + tid; p < a.n; p += (int64_t)gridDim.x * 256) {
+    float x[SUB];
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) x[e] = a.samples[p * SUB + e];
+    float bd = INFINITY;
+    int best = 0;
+    for (int k = 0; k < kCodewords; ++k) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) {
+        const float df = x[e] - cent[k * SUB + e];
+        d = fmaf(df, df, d);
+      }
+      if (d < bd) {
+        bd = d;
+        best = k;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) atomicAdd(&lsum[best * SUB + e], (double)x[e]);
+    atomicAdd(&lcnt[best], 1.0);
+    dl += (double)bd;
+  }
+  // wave sum of the distortion
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) dl += __shfl_xor(dl, m, kWave);
+  if ((tid & 63) == 0) ldist[tid >> 6] = dl;
+  __syncthreads();
+  for (int i = tid; i < kCodewords * SUB; i += 256)
+    if (lsum[i] != 0.0) atomicAdd(&a.sums[i], lsum[i]);
+  if (lcnt[tid] != 0.0) atomicAdd(&a.counts[tid], lcnt[tid]);
+  if (tid == 0) atomicAdd(a.dsum, (ldist[0] + ldist[1]) + (ldist[2] + ldist[3]));
+}
+
+template <int SUB>
+__global__ __launch_bounds__(256) void kmeans_update_kernel(KmeansArgs a) {
+  const int k = threadIdx.x;
+  const double cnt = a.counts[k];
+  if (cnt > 0.0) {
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) a.cent[k * SUB + e] = (float)(a.sums[k * SUB + e] / cnt);
+  }
+#pragma unroll
+  for (int e = 0; e < SUB; ++e) a.sums[k * SUB + e] = 0.0;
+  a.counts[k] = 0.0;
+  __syncthreads();
+  if (k == 0) {
+    if (a.distortion) a.distortion[a.it] = (float)(*a.dsum / ((double)a.n * SUB));
+    *a.dsum = 0.0;
+  }
+}
+
+__global__ void kmeans_clear_kernel(double* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0.0;
+}
+
+__global__ void kmeans_finish_kernel(KmeansArgs a, int total) {
+  for (int i = threadIdx.x; i < total; i += blockDim.x) a.codebook[i] = f2h(a.cent[i]);
+}
+
+hipError_t launch_kmeans_iter(const KmeansArgs& a, int sub, hipStream_t stream) {
+  const int64_t want = (a.n + 255) / 256;
+  const int grid = (int)(want < 2048 ? want : 2048);
+  if (sub == 4) {
+    hipLaunchKernelGGL(kmeans_assign_kernel<4>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(kmeans_update_kernel<4>, dim3(1), dim3(256), 0, stream, a);
+  } else if (sub == 8) {
+    hipLaunchKernelGGL(kmeans_assign_kernel<8>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(kmeans_update_kernel<8>, dim3(1), dim3(256), 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_kmeans_init(const float* src, float* cent, int sub, hipStream_t stream) {
+  hipError_t e = hipMemcpyAsync(cent, src, sizeof(float) * kCodewords * sub, hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_kmeans_clear(double* acc, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(kmeans_clear_kernel, dim3(1), dim3(256), 0, stream, acc, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_kmeans_finish(const KmeansArgs& a, int sub, hipStream_t stream) {
+  hipLaunchKernelGGL(kmeans_finish_kernel, dim3(1), dim3(256), 0, stream, a, kCodewords * sub);
+  return hipGetLastError();
+}
+
+}  // namespace nsnq

@@ -1,0 +1,325 @@
+// encode.hip -- fused NSN + Hadamard + VQ encode of R-token blocks (gfx950).
+//
+// One work-group (4 waves) encodes one block of R tokens of one (batch row,
+// head) stream, K or V.  Each lane holds one sub-vector (s = SUB elements) of
+// one token, so a token occupies S = 128/SUB consecutive lanes and a wave "row"
+// covers 64/S tokens.
+//
+//  1. token-wise normalisation to norm sqrt(d) (n1), kept in registers;
+//  2. channel mean over the block (wave partial sums, LDS across waves);
+//  3. second normalisation (n2), w = z / n2;
+//  4. Walsh-Hadamard transform across the S lanes of a token, scaled by
+//     1/sqrt(d);
+//  5. VQ: squared distances to all 256 codewords as an MFMA GEMM, then a
+//     per-lane argmin on packed (distance | index) keys.
+//
+// Distance GEMM.  Codewords are the rows (M) and sub-vectors the columns (N)
+// of v_mfma_f32_32x32x16_f16 tiles, so each lane receives 16 candidate
+// codewords of ONE sub-vector per tile and the argmin runs in registers.  The
+// K dimension carries, for each sub-vector u and codeword c,
+//     [u_hi, u_lo] . [-2c, -2c]  +  [uu_hi, uu_lo, 1, 1] . [1, 1, b_hi, b_lo]
+// with u = u_hi + u_lo split into two fp16 halves (22 significant bits),
+// uu = ||u||^2 and b = ||c||^2 + eps likewise split, so the accumulator holds
+// D = ||u - c||^2 + eps >= 0 to ~1e-6 absolute.  Positive floats order like
+// their bit patterns; the low 8 mantissa bits are replaced by the codeword
+// index and a v_min3_u32 chain yields the argmin (ties: lowest index).  The
+// truncation costs at most 2^-15 relative, below the 1e-4 near-tie band.
+// At 2 bits (SUB = 4) all terms fit one K = 16 instruction; at 1 bit
+// (SUB = 8) the hi/lo products fill K = 16 and the bias terms go through a
+// second 32x32x8 instruction.
+
+#include "nsnq_device.hpp"
+#include "nsnq_launch.hpp"
+
+namespace nsnq {
+
+// eps keeps the packed distance strictly positive despite rounding when a
+// sub-vector sits on a codeword.
+constexpr float kDistEps = 0.000244140625f;  // 2^-12
+// n2 below this is rounding noise of the shift: treated as zero
+constexpr float kN2Floor = 0.000244140625f;  // 2^-12
+
+__device__ __forceinline__ uint32_t pack_h2(half_t a, half_t b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ half8_t u32x4_to_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  uint4_t v = {a, b, c, d};
+  return __builtin_bit_cast(half8_t, v);
+}
+
+__device__ __forceinline__ uint4_t half8_to_u32x4(half8_t h) { return __builtin_bit_cast(uint4_t, h); }
+
+// Move lanes 0-31 / 32-63 between two registers:
+//   lo_out = [a(lanes 0-31), b(lanes 0-31) moved up]
+//   hi_out = [a(lanes 32-63) moved down, b(lanes 32-63)]
+__device__ __forceinline__ void half_swap(uint32_t a, uint32_t b, uint32_t& lo_out, uint32_t& hi_out, int lane) {
+  uint32_t a_x = __shfl_xor(a, 32, kWave);
+  uint32_t b_x = __shfl_xor(b, 32, kWave);
+  lo_out = lane < 32 ? a : b_x;
+  hi_out = lane < 32 ? a_x : b;
+}
+
+// Work-groups past the encode blocks copy the last r tokens of each stream
+// into the residual window (one group per (b, h), K or V).
+__device__ __forceinline__ void resid_copy(const EncodeArgs& a, int unit, int kv) {
+  const int b = unit / a.H, h = unit % a.H;
+  const uint16_t* src = a.src[kv] + (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)a.rc_t0 * a.st;
+  uint16_t* dst = a.resid[kv] + (int64_t)unit * a.R * kDim;
+  for (int i = threadIdx.x; i < a.rc_r * 16; i += blockDim.x) {  // 16 x 8 halves per row
+    const int t = i >> 4, c = (i & 15) * 8;
+    *reinterpret_cast<uint4*>(dst + (int64_t)t * kDim + c) =
+        *reinterpret_cast<const uint4*>(src + (int64_t)t * a.st + c);
+  }
+}
+
+template <int SUB, int R>
+__global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
+  if ((int)blockIdx.x >= a.nblk * a.n_units) {
+    resid_copy(a, blockIdx.x - a.nblk * a.n_units, blockIdx.y);
+    return;
+  }
+  constexpr int S = kDim / SUB;      // slots = lanes per token
+  constexpr int TPR = kWave / S;     // tokens per wave row
+  constexpr int TPW = R / 4;         // tokens per wave
+  constexpr int ROWS = TPW / TPR;    // rows per wave
+  static_assert(ROWS * TPR * 4 == R, "block split");
+
+  __shared__ float red[4][kDim];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slot = lane % S;
+  const int tir = lane / S;
+
+  const int blk = blockIdx.x % a.nblk;
+  const int unit = blockIdx.x / a.nblk;  // b * H + h
+  const int kv = blockIdx.y;
+  const int b = unit / a.H, h = unit % a.H;
+
+  const uint16_t* src = a.src[kv] + (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)blk * R * a.st;
+  const int64_t tok_base = (int64_t)unit * a.cap + a.dst_tok0 + (int64_t)blk * R;
+
+  // ---- codebook operands (A side), per 32-codeword tile -------------------
+  // lane l holds codeword k = 32 t + (l % 32).
+  half8_t A1[8];
+  half4_t A2[8];
+  {
+    const uint16_t* cb = a.codebook;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int k = 32 * t + (lane & 31);
+      float c[SUB];
+      float nrm = 0.f;
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) {
+        c[e] = h2f(cb[k * SUB + e]);
+        nrm = fmaf(c[e], c[e], nrm);
+      }
+      const float bsum = nrm + kDistEps;
+      const half_t b_hi = (half_t)bsum;
+      const half_t b_lo = (half_t)(bsum - (float)b_hi);
+      half8_t av;
+      if constexpr (SUB == 4) {
+        if (lane < 32) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            av[e] = (half_t)(-2.f * c[e]);
+            av[4 + e] = (half_t)(-2.f * c[e]);
+          }
+        } else {
+          av[0] = (half_t)1.f; av[1] = (half_t)1.f; av[2] = b_hi; av[3] = b_lo;
+          av[4] = (half_t)0.f; av[5] = (half_t)0.f; av[6] = (half_t)0.f; av[7] = (half_t)0.f;
+        }
+        A2[t] = half4_t{(half_t)0.f, (half_t)0.f, (half_t)0.f, (half_t)0.f};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[e] = (half_t)(-2.f * c[e]);
+        A2[t] = half4_t{(half_t)1.f, (half_t)1.f, b_hi, b_lo};
+      }
+      A1[t] = av;
+    }
+  }
+
+  // Load one row (this lane's sub-vector of token `tok`) and normalise it:
+  // y = x / n1 with n1 = ||x|| / sqrt(d).  Pass 2 recomputes this from the
+  // (L2-resident) input instead of keeping R x 128 floats alive.
+  auto load_norm = [&](int tok, float (&y)[SUB], float& n1) {
+    const uint16_t* px = src + (int64_t)tok * a.st + slot * SUB;
+    float v[SUB];
+    if constexpr (SUB == 4) {
+      uint2 raw = *reinterpret_cast<const uint2*>(px);
+      v[0] = h2f(raw.x & 0xffff); v[1] = h2f(raw.x >> 16);
+      v[2] = h2f(raw.y & 0xffff); v[3] = h2f(raw.y >> 16);
+    } else {
+      uint4 raw = *reinterpret_cast<const uint4*>(px);
+      v[0] = h2f(raw.x & 0xffff); v[1] = h2f(raw.x >> 16);
+      v[2] = h2f(raw.y & 0xffff); v[3] = h2f(raw.y >> 16);
+      v[4] = h2f(raw.z & 0xffff); v[5] = h2f(raw.z >> 16);
+      v[6] = h2f(raw.w & 0xffff); v[7] = h2f(raw.w >> 16);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) ss = fmaf(v[e], v[e], ss);
+    ss = group_sum<S>(ss);
+    n1 = sqrtf(ss * (1.0f / kDim));
+    const float inv = n1 > 0.f ? 1.0f / n1 : 0.f;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) y[e] = v[e] * inv;
+  };
+
+  // ---- pass 1: channel sums of y over the block ---------------------------
+  float csum[SUB];
+#pragma unroll
+  for (int e = 0; e < SUB; ++e) csum[e] = 0.f;
+#pragma unroll 4
+  for (int r = 0; r < ROWS; ++r) {
+    float y[SUB], n1;
+    load_norm(wave * TPW + r * TPR + tir, y, n1);
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) csum[e] += y[e];
+  }
+  // combine the TPR lanes holding the same channels, then the 4 waves
+#pragma unroll
+  for (int e = 0; e < SUB; ++e) {
+#pragma unroll
+    for (int m = S; m < kWave; m <<= 1) csum[e] += xshfl(csum[e], m);
+  }
+  if (tir == 0) {
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) red[wave][slot * SUB + e] = csum[e];
+  }
+  __syncthreads();
+  float mu[SUB];
+#pragma unroll
+  for (int e = 0; e < SUB; ++e) {
+    const int c = slot * SUB + e;
+    mu[e] = (red[0][c] + red[1][c] + red[2][c] + red[3][c]) * (1.0f / R);
+  }
+  if (wave == 0 && tir == 0) {
+    uint16_t* pm = a.mu[kv] + ((int64_t)unit * (a.cap / R) + a.dst_tok0 / R + blk) * kDim + slot * SUB;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) pm[e] = f2h(mu[e]);
+  }
+
+  uint8_t* codes = a.codes[kv];
+  uint16_t* scales = a.scales[kv];
+
+  // ---- pass 2: per row: shift, second normalisation, Hadamard, VQ ---------
+#pragma unroll 1
+  for (int r = 0; r < ROWS; ++r) {
+    const int tok = wave * TPW + r * TPR + tir;
+    float u[SUB], n1;
+    load_norm(tok, u, n1);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) {
+      u[e] -= mu[e];
+      ss = fmaf(u[e], u[e], ss);
+    }
+    ss = group_sum<S>(ss);
+    // a token within 2^-12 (relative) of the block mean has no direction left:
+    // store n2 = 0 and quantise w = 0 (reconstructed as n1 * mu)
+    float n2 = sqrtf(ss * (1.0f / kDim));
+    n2 = n2 < kN2Floor ? 0.f : n2;
+    const half_t n2h = (half_t)n2;
+    const float inv2 = n2 > 0.f ? 1.0f / n2 : 0.f;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) u[e] *= inv2;
+    fwht128<SUB>(u, lane);
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) u[e] *= kInvSqrtD;
+
+    if (slot == 0) {
+      const uint32_t pk = pack_h2((half_t)n1, n2h);
+      *reinterpret_cast<uint32_t*>(scales + (tok_base + tok) * 2) = pk;
+    }
+
+    // hi/lo split and squared norm of this lane's sub-vector
+    half_t hi[SUB], lo[SUB];
+    float uu = 0.f;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) {
+      hi[e] = (half_t)u[e];
+      lo[e] = (half_t)(u[e] - (float)hi[e]);
+      uu = fmaf(u[e], u[e], uu);
+    }
+    const half_t uu_hi = (half_t)uu;
+    const half_t uu_lo = (half_t)(uu - (float)uu_hi);
+
+    // B operands of the two 32-column blocks (lanes 0-31 / 32-63 own data)
+    half8_t B0, B1;
+    half4_t Bb0, Bb1;
+    if constexpr (SUB == 4) {
+      const uint32_t P[4] = {pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(lo[0], lo[1]),
+                             pack_h2(lo[2], lo[3])};
+      const uint32_t Q[4] = {pack_h2(uu_hi, uu_lo), pack_h2((half_t)1.f, (half_t)1.f), 0u, 0u};
+      uint32_t b0[4], b1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) half_swap(P[i], Q[i], b0[i], b1[i], lane);
+      B0 = u32x4_to_half8(b0[0], b0[1], b0[2], b0[3]);
+      B1 = u32x4_to_half8(b1[0], b1[1], b1[2], b1[3]);
+      Bb0 = Bb1 = half4_t{(half_t)0.f, (half_t)0.f, (half_t)0.f, (half_t)0.f};
+    } else {
+      const uint32_t P[4] = {pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(hi[4], hi[5]),
+                             pack_h2(hi[6], hi[7])};
+      const uint32_t Q[4] = {pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]), pack_h2(lo[4], lo[5]),
+                             pack_h2(lo[6], lo[7])};
+      uint32_t b0[4], b1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) half_swap(P[i], Q[i], b0[i], b1[i], lane);
+      B0 = u32x4_to_half8(b0[0], b0[1], b0[2], b0[3]);
+      B1 = u32x4_to_half8(b1[0], b1[1], b1[2], b1[3]);
+      const half4_t bias = {uu_hi, uu_lo, (half_t)1.f, (half_t)1.f};
+      const half4_t zero4 = {(half_t)0.f, (half_t)0.f, (half_t)0.f, (half_t)0.f};
+      Bb0 = lane < 32 ? bias : zero4;
+      Bb1 = lane < 32 ? zero4 : bias;
+    }
+
+    uint32_t best0 = 0xffffffffu, best1 = 0xffffffffu;
+    const float16_t zacc = {};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      float16_t acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[t], B0, zacc, 0, 0, 0);
+      float16_t acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[t], B1, zacc, 0, 0, 0);
+      if constexpr (SUB == 8) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2[t], Bb0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2[t], Bb1, acc1, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 16; q += 2) {
+        // accumulator q holds codeword 32t + 8(q/4) + 4(lane/32) + q%4
+        const uint32_t i0 = 32u * t + 8u * (q >> 2) + (q & 3);
+        const uint32_t i1 = 32u * t + 8u * ((q + 1) >> 2) + ((q + 1) & 3);
+        const uint32_t k00 = (__float_as_uint(acc0[q]) & 0xffffff00u) | i0;
+        const uint32_t k01 = (__float_as_uint(acc0[q + 1]) & 0xffffff00u) | i1;
+        const uint32_t k10 = (__float_as_uint(acc1[q]) & 0xffffff00u) | i0;
+        const uint32_t k11 = (__float_as_uint(acc1[q + 1]) & 0xffffff00u) | i1;
+        best0 = min(min(best0, k00), k01);
+        best1 = min(min(best1, k10), k11);
+      }
+    }
+    const uint32_t hbit = (uint32_t)(lane >> 5) << 2;
+    best0 |= hbit;
+    best1 |= hbit;
+    best0 = min(best0, (uint32_t)__shfl_xor(best0, 32, kWave));
+    best1 = min(best1, (uint32_t)__shfl_xor(best1, 32, kWave));
+    // column n of block 0 belongs to lane n, of block 1 to lane 32 + n
+    const uint32_t mine = lane < 32 ? best0 : best1;
+    codes[(tok_base + tok) * S + slot] = (uint8_t)(mine & 0xffu);
+  }
+}
+
+hipError_t launch_encode(const EncodeArgs& a, int sub, int R, hipStream_t stream) {
+  dim3 grid(a.nblk * a.n_units + (a.rc_r > 0 ? a.n_units : 0), 2), block(256);
+  if (grid.x == 0) return hipSuccess;
+  if (sub == 4 && R == 128) hipLaunchKernelGGL((encode_kernel<4, 128>), grid, block, 0, stream, a);
+  else if (sub == 4 && R == 64) hipLaunchKernelGGL((encode_kernel<4, 64>), grid, block, 0, stream, a);
+  else if (sub == 8 && R == 128) hipLaunchKernelGGL((encode_kernel<8, 128>), grid, block, 0, stream, a);
+  else if (sub == 8 && R == 64) hipLaunchKernelGGL((encode_kernel<8, 64>), grid, block, 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+
+}  // namespace nsnq

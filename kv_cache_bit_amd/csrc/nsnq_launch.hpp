@@ -1,0 +1,96 @@
+// nsnq_launch.hpp -- kernel argument blocks and launchers (host <-> device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nsnq {
+
+struct EncodeArgs {
+  const uint16_t* src[2];  // K, V fp16 streams
+  int64_t sb, sh, st;      // element strides (batch, head, token)
+  uint8_t* codes[2];
+  uint16_t* scales[2];
+  uint16_t* mu[2];
+  const uint16_t* codebook;  // fp16 [256][SUB]
+  uint16_t* resid[2];
+  int H;                     // heads
+  int n_units;               // batch * heads
+  int cap;                   // cache capacity (tokens)
+  int dst_tok0;              // first destination token (multiple of R)
+  int nblk;                  // blocks per stream
+  int R;                     // block / window size
+  int rc_t0, rc_r;           // residual copy: first source token and count (0 = none)
+};
+
+struct DequantArgs {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* mu;
+  const uint16_t* codebook;
+  void* out;
+  int H, cap, R, tok0, ntok, out_f16;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;  // [B][Hq][d]
+  const uint8_t* kcodes;
+  const uint16_t* kscales;
+  const uint16_t* kmu;
+  const uint16_t* kresid;
+  const uint8_t* vcodes;
+  const uint16_t* vscales;
+  const uint16_t* vmu;
+  const uint16_t* vresid;
+  const uint16_t* codebook;
+  float* ws;         // partials [B][Hq][nsplit][d + 2]
+  int Hq, Hkv, G;    // G = Hq / Hkv
+  int cap, R;
+  int n_quant, n_resid;
+  int split_tokens;  // compressed tokens per split (multiple of R)
+  int nsplit_q;      // splits over the compressed tokens
+  int nsplit;        // nsplit_q + (n_resid > 0)
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* ws;
+  uint16_t* out;
+  int Hq, nsplit;
+};
+
+struct KmeansArgs {
+  const float* samples;  // [n][SUB]
+  int64_t n;
+  float* cent;           // [256][SUB] current centroids
+  double* sums;          // [256][SUB]
+  double* counts;        // [256]
+  double* dsum;          // [1]
+  float* distortion;     // [iters] or null
+  uint16_t* codebook;    // [256][SUB] fp16 out
+  int it;
+};
+
+struct Fp16DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  float* ws;
+  int Hq, Hkv, G, T;
+  int split_tokens, nsplit;
+  float scale_log2;
+};
+
+hipError_t launch_encode(const EncodeArgs& a, int sub, int R, hipStream_t stream);
+hipError_t launch_dequant(const DequantArgs& a, int sub, int n_units, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int sub, int gh, int B, size_t lds_bytes, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream);
+size_t decode_lds_bytes(int sub, int gh, int split_tokens, int R);
+int decode_max_split_tokens(int sub, int gh, int R);
+hipError_t launch_kmeans_init(const float* src, float* cent, int sub, hipStream_t stream);
+hipError_t launch_kmeans_iter(const KmeansArgs& a, int sub, hipStream_t stream);
+hipError_t launch_kmeans_finish(const KmeansArgs& a, int sub, hipStream_t stream);
+hipError_t launch_fp16_decode(const Fp16DecodeArgs& a, int B, hipStream_t stream);
+size_t fp16_decode_lds_bytes(int G, int split_tokens);
+
+}  // namespace nsnq

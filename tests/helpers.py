@@ -1,0 +1,126 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI,
+pull results back, and compare them with the oracle under the stated bars:
+
+  codes     bit-exact, except where the oracle's best/second distance gap is
+            below 1e-4 relative; such near-tie flips at most 0.01% of codes;
+  scalars   fp16 n1, n2, mu within one fp16 ulp (fp32 vs fp64 rounding);
+  dequant   max |x_hat_gpu - x_hat_oracle| <= 1e-3 * ||x_t||;
+  attention relative L2 error <= 2e-3 per output head.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from kv_cache_bit_amd import nsnq
+
+DEV = "cuda"
+NEAR_TIE = 1e-4
+MAX_TIE_FRAC = 1e-4
+DEQUANT_TOL = 1e-3
+ATTN_TOL = 2e-3
+
+
+def f16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().numpy().view(np.uint16)
+
+
+def cb_tensor(cb_bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(cb_bits).view(np.float16)).to(DEV)
+
+
+def capacity(L: int, R: int, extra_blocks: int = 1) -> int:
+    r = ((L - 1) % R) + 1 if L > 0 else 0
+    nq = L - r
+    return max(R, nq + extra_blocks * R)
+
+
+def gpu_encode(k: torch.Tensor, v: torch.Tensor, bits: int, R: int, cb_bits: np.ndarray, cap: int | None = None):
+    p = nsnq.params(bits, R)
+    B, H, L, d = k.shape
+    cache = nsnq.KVCache(p, B, H, cap or capacity(L, R), DEV)
+    cb = cb_tensor(cb_bits)
+    nsnq.nsnq_encode_kv(p, cb, k.to(DEV), v.to(DEV), L, cache)
+    torch.cuda.synchronize()
+    return p, cb, cache
+
+
+def half_np(cache: nsnq.KVCache, which: int, n_tokens: int | None = None) -> dict:
+    h = cache.k if which == 0 else cache.v
+    nq = cache.n_quant if n_tokens is None else n_tokens
+    R = h.resid.shape[2]
+    return dict(codes=h.codes[:, :, :nq].cpu().numpy(), scales=f16_bits(h.scales[:, :, :nq]),
+                mu=f16_bits(h.mu[:, :, :nq // R]), resid=f16_bits(h.resid))
+
+
+def upload_half(cache: nsnq.KVCache, which: int, enc: dict):
+    """Copy an oracle-encoded half (codes/scales/mu/resid) into a GPU cache."""
+    h = cache.k if which == 0 else cache.v
+    nq = enc["codes"].shape[-2]
+    R = h.resid.shape[2]
+    h.codes[:, :, :nq].copy_(torch.from_numpy(enc["codes"]))
+    h.scales[:, :, :nq].copy_(torch.from_numpy(enc["scales"].view(np.float16)))
+    h.mu[:, :, :nq // R].copy_(torch.from_numpy(enc["mu"].view(np.float16)))
+    h.resid.copy_(torch.from_numpy(enc["resid"].view(np.float16)))
+
+
+def check_codes(g: np.ndarray, o: np.ndarray, gap: np.ndarray, what: str = "codes"):
+    assert g.shape == o.shape, (g.shape, o.shape)
+    mism = g != o
+    n = int(mism.sum())
+    bad = int((mism & (gap >= NEAR_TIE)).sum())
+    assert bad == 0, f"{what}: {bad} mismatches outside the near-tie band (of {n} total, {g.size} codes)"
+    assert n <= max(MAX_TIE_FRAC * g.size, 1), f"{what}: {n} near-tie mismatches of {g.size} codes"
+    return n
+
+
+def check_f16_ulp(g_bits: np.ndarray, o_bits: np.ndarray, what: str, max_flip_frac: float = 1e-2):
+    g = g_bits.view(np.float16).astype(np.float64)
+    o = o_bits.view(np.float16).astype(np.float64)
+    ulp = np.spacing(np.abs(o_bits.view(np.float16))).astype(np.float64)
+    diff = np.abs(g - o)
+    assert np.all(diff <= ulp * 1.0001), f"{what}: max diff {diff.max()} exceeds one fp16 ulp"
+    flips = int((diff > 0).sum())
+    assert flips <= max(max_flip_frac * g.size, 2), f"{what}: {flips} of {g.size} values off by one ulp"
+    return flips
+
+
+def token_norms(x_f16: np.ndarray) -> np.ndarray:
+    return np.linalg.norm(x_f16.astype(np.float64), axis=-1)
+
+
+def check_dequant(g: np.ndarray, o: np.ndarray, norms: np.ndarray, mask: np.ndarray | None = None,
+                  tol: float = DEQUANT_TOL):
+    err = np.abs(g.astype(np.float64) - o).max(axis=-1) / np.maximum(norms, 1e-30)
+    if mask is not None:
+        err = err[mask]
+    assert err.size == 0 or err.max() <= tol, f"dequant: max error {err.max():.3e} of token norm"
+    return float(err.max()) if err.size else 0.0
+
+
+def check_attention(g: np.ndarray, o: np.ndarray, tol: float = ATTN_TOL):
+    g = g.astype(np.float64)
+    rel = np.linalg.norm(g - o, axis=-1) / np.maximum(np.linalg.norm(o, axis=-1), 1e-30)
+    assert rel.max() <= tol, f"attention: max relative L2 error {rel.max():.3e}"
+    return float(rel.max())
+
+
+def oracle_encode_pair(k: torch.Tensor, v: torch.Tensor, R: int, cb_bits: np.ndarray):
+    return oracle.encode(k.cpu(), R, cb_bits), oracle.encode(v.cpu(), R, cb_bits)
+
+
+def compare_encoded(cache: nsnq.KVCache, ek: dict, ev: dict, units=None):
+    """Compare a GPU cache with the oracle's encodings (optionally only the
+    (b, h) pairs in `units`).  Returns per-half code mismatch counts."""
+    out = []
+    for which, e in ((0, ek), (1, ev)):
+        gh = half_np(cache, which)
+        if units is not None:
+            gh = {key: np.stack([val[b, h] for b, h in units]) for key, val in gh.items()}
+        n = check_codes(gh["codes"], e["codes"], e["gap"], "K codes" if which == 0 else "V codes")
+        check_f16_ulp(gh["scales"], e["scales"], "scales")
+        check_f16_ulp(gh["mu"], e["mu"], "mu")
+        assert np.array_equal(gh["resid"][..., :e["n_resid"], :], e["resid"][..., :e["n_resid"], :])
+        out.append(n)
+    return out

@@ -1,0 +1,95 @@
+"""The C-ABI library loads on the CPU host, exports every function that
+include/nsnq.h declares, and rejects bad arguments on the host before any
+HIP call (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nsnq.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(nsnq_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def nsnq():
+    from kv_cache_bit_amd import nsnq as m
+    m.lib()
+    return m
+
+
+def test_exports_every_declared_symbol(nsnq):
+    names = _declared()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(nsnq.lib(), n), n
+    assert nsnq.nsnq_abi_version() == 1
+    assert nsnq.lib().nsnq_status_str(1) == b"invalid argument"
+
+
+def _cache_struct(nsnq, B=1, H=2, cap=256, nq=0, nr=0, ptr=0x1000):
+    kv = nsnq.nsnq_kv(ptr, ptr, ptr, ptr)
+    return nsnq.nsnq_cache(kv, kv, B, H, cap, nq, nr)
+
+
+def test_host_validation_rejects_before_launch(nsnq):
+    L = nsnq.lib()
+    good = nsnq.params(2, 128)
+    c = _cache_struct(nsnq)
+    P = 0x1000  # aligned fake device pointer: never dereferenced on these paths
+    EINVAL, EUNS, EWS = nsnq.NSNQ_EINVAL, nsnq.NSNQ_EUNSUPPORTED, nsnq.NSNQ_EWORKSPACE
+    by = ctypes.byref
+    # bad format parameters
+    assert L.nsnq_encode_kv(by(nsnq.params(3, 128)), P, P, P, 0, 0, 128, 256, by(c), None) == EINVAL
+    assert L.nsnq_encode_kv(by(nsnq.params(2, 128, head_dim=64)), P, P, P, 0, 0, 64, 256, by(c), None) == EUNS
+    assert L.nsnq_encode_kv(by(nsnq.params(2, 96)), P, P, P, 0, 0, 128, 256, by(c), None) == EUNS
+    assert L.nsnq_encode_kv(by(nsnq.params(2, 128, n_codewords=16)), P, P, P, 0, 0, 128, 256, by(c), None) == EINVAL
+    # misaligned or null pointers, bad strides, capacity, residual state
+    assert L.nsnq_encode_kv(by(good), P + 2, P, P, 0, 0, 128, 256, by(c), None) == EINVAL
+    assert L.nsnq_encode_kv(by(good), P, None, P, 0, 0, 128, 256, by(c), None) == EINVAL
+    assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 100, 256, by(c), None) == EINVAL
+    assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 128, 1000, by(c), None) == EINVAL  # 896 > cap 256
+    c_res = _cache_struct(nsnq, nr=5)
+    assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 128, 256, by(c_res), None) == EINVAL
+    c_badcap = _cache_struct(nsnq, cap=200)
+    assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 128, 256, by(c_badcap), None) == EINVAL
+    c_mis = nsnq.nsnq_cache(nsnq.nsnq_kv(P + 4, P, P, P), nsnq.nsnq_kv(P, P, P, P), 1, 2, 256, 0, 0)
+    assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 128, 256, by(c_mis), None) == EINVAL
+    assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 128, 0, by(c), None) == nsnq.NSNQ_OK  # L = 0: no work
+    # flush needs a full window
+    assert L.nsnq_flush_residual(by(good), P, by(_cache_struct(nsnq, nr=100)), None) == EINVAL
+    assert L.nsnq_flush_residual(by(good), P, by(_cache_struct(nsnq, nq=256, nr=128)), None) == EINVAL
+    # dequant range
+    cq = _cache_struct(nsnq, nq=128)
+    assert L.nsnq_dequant(by(good), P, by(cq), 0, 0, 129, 0, P, None) == EINVAL
+    assert L.nsnq_dequant(by(good), P, by(cq), 2, 0, 1, 0, P, None) == EINVAL
+    assert L.nsnq_dequant(by(good), P, by(cq), 0, 0, 0, 0, P, None) == nsnq.NSNQ_OK
+    # decode: empty cache, head grouping, workspace
+    assert L.nsnq_decode_attention(by(good), P, P, 4, by(c), 0.1, 0, P, P, 1 << 20, None) == EINVAL
+    cd = _cache_struct(nsnq, nq=128, nr=3)
+    assert L.nsnq_decode_attention(by(good), P, P, 3, by(cd), 0.1, 0, P, P, 1 << 20, None) == EINVAL
+    need = L.nsnq_decode_workspace_bytes(by(good), by(cd), 4, 0)
+    assert need > 0
+    assert L.nsnq_decode_attention(by(good), P, P, 4, by(cd), 0.1, 0, P, P, need - 4, None) == EWS
+    assert L.nsnq_decode_attention(by(good), P, P, 4, by(cd), 0.1, 0, P, None, need, None) == EWS
+    # codebook fit
+    ws = L.nsnq_build_codebook_workspace_bytes(by(good))
+    assert ws > 0
+    assert L.nsnq_build_codebook(by(good), P, 100, 5, None, P, P, None, P, ws, None) == EINVAL  # n < 256
+    assert L.nsnq_build_codebook(by(good), P, 1000, 5, None, P, P, None, P, ws - 8, None) == EWS
+    # comparator
+    assert L.nsnq_fp16_decode_attention(P, 3, P, P, 1, 1, 10, 0.1, 0, P, P, 1 << 20, None) == EUNS
+    assert L.nsnq_fp16_decode_attention(P, 4, P, P, 1, 1, 0, 0.1, 0, P, P, 1 << 20, None) == EINVAL
+
+
+def test_counters_untouched_on_error(nsnq):
+    c = _cache_struct(nsnq, nq=128, nr=7)
+    good = nsnq.params(2, 128)
+    assert nsnq.lib().nsnq_flush_residual(ctypes.byref(good), 0x1000, ctypes.byref(c), None) == nsnq.NSNQ_EINVAL
+    assert (c.n_quant, c.n_resid) == (128, 7)

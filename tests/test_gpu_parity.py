@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on the same seeded inputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_bit_amd import nsnq, synth
+
+from helpers import (DEV, capacity, check_attention, check_codes, check_dequant, check_f16_ulp,
+                     compare_encoded, f16_bits, gpu_encode, half_np, oracle_encode_pair, token_norms,
+                     upload_half, cb_tensor)
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def _kv(config_id, B, H, L, outlier=10.0):
+    return synth.kv_layer(config_id, 0, B, H, L, D, outlier_std=outlier)
+
+
+# ------------------------------------------------------------------ encode --
+
+@pytest.mark.parametrize("bits,R,B,H,L", [
+    (2, 64, 1, 1, 512),     # the tiny workload
+    (2, 128, 2, 3, 300),    # ragged: 256 encoded, 44 residual
+    (1, 128, 1, 2, 385),
+    (1, 64, 2, 1, 200),
+    (2, 64, 1, 1, 64),      # everything stays in the residual window
+    (2, 128, 1, 2, 1),
+])
+def test_encode_matches_oracle(oracle_codebooks, bits, R, B, H, L):
+    cb = oracle_codebooks[bits]
+    k, v = _kv(100 + bits, B, H, L)
+    p, cbt, cache = gpu_encode(k, v, bits, R, cb)
+    ek, ev = oracle_encode_pair(k, v, R, cb)
+    assert (cache.n_quant, cache.n_resid) == (ek["n_quant"], ek["n_resid"])
+    compare_encoded(cache, ek, ev)
+
+
+def test_encode_degenerate_tokens(oracle_codebooks):
+    """A zero token (n1 = 0) and a block of identical tokens (n2 = 0)."""
+    cb = oracle_codebooks[2]
+    R = 64
+    k, v = _kv(7, 1, 1, 3 * R + 5)
+    k[0, 0, 10] = 0
+    v[0, 0, R:2 * R] = v[0, 0, R]
+    p, cbt, cache = gpu_encode(k, v, 2, R, cb)
+    ek, ev = oracle_encode_pair(k, v, R, cb)
+    compare_encoded(cache, ek, ev)
+    assert np.all(half_np(cache, 1)["scales"][0, 0, R:2 * R, 1] == 0)  # n2 = 0 stored
+    assert np.all(half_np(cache, 0)["scales"][0, 0, 10, 0] == 0)
+
+
+# ----------------------------------------------------------------- dequant --
+
+@pytest.mark.parametrize("bits,R", [(2, 64), (1, 128)])
+def test_dequant_same_cache(oracle_codebooks, bits, R):
+    """GPU reconstruction of the oracle's own cache."""
+    cb = oracle_codebooks[bits]
+    B, H, L = 2, 2, 5 * R + 7
+    k, v = _kv(200 + bits, B, H, L)
+    ek, ev = oracle_encode_pair(k, v, R, cb)
+    p = nsnq.params(bits, R)
+    cache = nsnq.KVCache(p, B, H, capacity(L, R), DEV)
+    upload_half(cache, 0, ek)
+    upload_half(cache, 1, ev)
+    cache.n_quant, cache.n_resid = ek["n_quant"], ek["n_resid"]
+    cbt = cb_tensor(cb)
+    nq = ek["n_quant"]
+    for which, e, x in ((0, ek, k), (1, ev, v)):
+        ref = oracle.dequant(e["codes"], e["scales"], e["mu"], R, cb)
+        norms = token_norms(x[:, :, :nq].numpy())
+        g32 = nsnq.nsnq_dequant(p, cbt, cache, which, 0, nq, torch.float32).cpu().numpy()
+        assert check_dequant(g32, ref, norms) < 1e-5
+        g16 = nsnq.nsnq_dequant(p, cbt, cache, which, 0, nq, torch.float16).cpu().numpy()
+        check_dequant(g16, ref, norms)
+        # a sub-range
+        t0, nt = R + 3, 2 * R
+        gs = nsnq.nsnq_dequant(p, cbt, cache, which, t0, nt, torch.float32).cpu().numpy()
+        assert np.allclose(gs, g32[:, :, t0:t0 + nt], atol=0, rtol=0)
+
+
+@pytest.mark.parametrize("bits,R", [(2, 128), (1, 64)])
+def test_dequant_end_to_end(oracle_codebooks, bits, R):
+    cb = oracle_codebooks[bits]
+    B, H, L = 1, 3, 4 * R + 1
+    k, v = _kv(300 + bits, B, H, L)
+    p, cbt, cache = gpu_encode(k, v, bits, R, cb)
+    ek, ev = oracle_encode_pair(k, v, R, cb)
+    nq = ek["n_quant"]
+    for which, e, x in ((0, ek, k), (1, ev, v)):
+        g = nsnq.nsnq_dequant(p, cbt, cache, which, 0, nq, torch.float32).cpu().numpy()
+        ref = oracle.dequant(e["codes"], e["scales"], e["mu"], R, cb)
+        same = np.all(half_np(cache, which)["codes"] == e["codes"], axis=-1)
+        check_dequant(g, ref, token_norms(x[:, :, :nq].numpy()), mask=same)
+
+
+# --------------------------------------------------------------- attention --
+
+def _decode_ref(q, ek, ev, cb, R):
+    return oracle.reference_decode(q.cpu(), ek, ev, ek["n_quant"], ek["n_resid"], R, cb)
+
+
+@pytest.mark.parametrize("bits,R,B,Hq,Hkv,L", [
+    (2, 64, 1, 1, 1, 512),
+    (2, 128, 2, 4, 4, 700),
+    (1, 128, 1, 8, 2, 1000),   # grouped query heads, G = 4
+    (2, 64, 1, 6, 3, 333),     # G = 2
+    (2, 128, 1, 8, 1, 300),    # G = 8 (two head groups per KV head)
+    (2, 64, 2, 2, 2, 40),      # residual tokens only
+])
+def test_decode_same_cache_and_end_to_end(oracle_codebooks, bits, R, B, Hq, Hkv, L):
+    cb = oracle_codebooks[bits]
+    k, v = _kv(400 + bits, B, Hkv, L)
+    q = synth.queries(400 + bits, 0, B, Hq, D)
+    ek, ev = oracle_encode_pair(k, v, R, cb)
+    ref = _decode_ref(q, ek, ev, cb, R)
+    p = nsnq.params(bits, R)
+    cbt = cb_tensor(cb)
+    # same cache: the oracle's encoding, attended on the GPU
+    cache = nsnq.KVCache(p, B, Hkv, capacity(L, R), DEV)
+    upload_half(cache, 0, ek)
+    upload_half(cache, 1, ev)
+    cache.n_quant, cache.n_resid = ek["n_quant"], ek["n_resid"]
+    qd = q.to(DEV)
+    outs = []
+    for ns in (0, 1, 3):
+        o = nsnq.nsnq_decode_attention(p, cbt, qd, cache, num_splits=ns).float().cpu().numpy()
+        check_attention(o, ref)
+        outs.append(o)
+    for o in outs[1:]:
+        assert np.allclose(o, outs[0], atol=2e-3 * np.abs(outs[0]).max())
+    # end to end: GPU encode, GPU decode
+    _, _, gcache = gpu_encode(k, v, bits, R, cb)
+    o = nsnq.nsnq_decode_attention(p, cbt, qd, gcache).float().cpu().numpy()
+    check_attention(o, ref)
+
+
+def test_flush_then_decode(oracle_codebooks):
+    """Prefill leaves a full window; the next token flushes it, is appended,
+    and attention covers all tokens."""
+    cb = oracle_codebooks[2]
+    R, B, H = 64, 1, 2
+    L = 3 * R
+    k, v = _kv(500, B, H, L + 1)
+    p, cbt, cache = gpu_encode(k[:, :, :L], v[:, :, :L], 2, R, cb, cap=8 * R)
+    assert (cache.n_quant, cache.n_resid) == (2 * R, R)
+    nsnq.nsnq_flush_residual(p, cbt, cache)
+    assert (cache.n_quant, cache.n_resid) == (3 * R, 0)
+    cache.append_token(k[:, :, L].to(DEV), v[:, :, L].to(DEV))
+    torch.cuda.synchronize()
+    ek, ev = oracle_encode_pair(k, v, R, cb)   # L + 1 tokens: 3R encoded, 1 residual
+    assert ek["n_quant"] == 3 * R
+    compare_encoded(cache, ek, ev)
+    q = synth.queries(500, 0, B, H, D)
+    o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), cache).float().cpu().numpy()
+    check_attention(o, _decode_ref(q, ek, ev, cb, R))
+
+
+# ------------------------------------------------------------------ k-means --
+
+@pytest.mark.parametrize("bits", [2, 1])
+def test_kmeans_matches_oracle(bits):
+    s = nsnq.sub_dim(bits)
+    x = synth.randn_samples(900 + bits, 1 << 14, s)
+    p = nsnq.params(bits, 128)
+    xd = x.to(DEV)
+    # one iteration from the same start
+    cent1, cb1, dist1 = nsnq.nsnq_build_codebook(p, xd, 1)
+    ocent1, ocb1, odist1 = oracle.kmeans(x.numpy(), 256, 1)
+    assert dist1.item() == pytest.approx(odist1[0], rel=1e-5)
+    dev = np.abs(cent1.cpu().numpy().astype(np.float64) - ocent1).max(axis=1)
+    assert (dev > 1e-5).sum() <= 4, f"{(dev > 1e-5).sum()} centroids differ"
+    # ten iterations: same distortion curve
+    cent, cbk, dist = nsnq.nsnq_build_codebook(p, xd, 10)
+    _, ocb, odist = oracle.kmeans(x.numpy(), 256, 10)
+    assert np.allclose(dist.cpu().numpy(), odist, rtol=1e-3)
+    assert np.all(np.diff(dist.cpu().numpy()) <= 1e-6)
+    assert np.array_equal(f16_bits(cbk), f16_bits(cent.half()))
+    # explicit init = the oracle's first-iteration centroids
+    init = torch.from_numpy(ocent1.astype(np.float32)).to(DEV)
+    cent2, _, d2 = nsnq.nsnq_build_codebook(p, xd, 1, init=init)
+    _, _, od2 = oracle.kmeans(x.numpy(), 256, 1, init=ocent1.astype(np.float32).astype(np.float64))
+    assert d2.item() == pytest.approx(od2[0], rel=1e-5)
+
+
+# ---------------------------------------------------------- full-size cases --
+
+def test_llama2_layer_2bit_full(oracle_codebooks):
+    """One LLaMA-2-7B-shaped layer: 32 heads, 4096 tokens, 2-bit, R = 128;
+    every code of every head, and the decode step."""
+    cb = oracle_codebooks[2]
+    w = synth.WORKLOADS["llama2-7b-layer-b1-2bit"]
+    B, H, L, R = w["B"], w["Hkv"], w["L"], w["R"]
+    k, v = synth.kv_layer(w["config_id"], 0, B, H, L, D)
+    p, cbt, cache = gpu_encode(k, v, 2, R, cb)
+    assert (cache.n_quant, cache.n_resid) == (3968, 128)
+    ek, ev = oracle_encode_pair(k, v, R, cb)
+    compare_encoded(cache, ek, ev)
+    q = synth.queries(w["config_id"], 0, B, w["Hq"], D)
+    o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), cache).float().cpu().numpy()
+    check_attention(o, _decode_ref(q, ek, ev, cb, R))
+
+
+def test_llama2_layer_1bit_b16_sampled(oracle_codebooks):
+    """Batch 16 at 1 bit: the whole layer is encoded and attended on the GPU in
+    the bench's launch configuration; sampled (b, h) streams are checked."""
+    cb = oracle_codebooks[1]
+    w = synth.WORKLOADS["llama2-7b-layer-b16-1bit"]
+    B, H, L, R = w["B"], w["Hkv"], w["L"], w["R"]
+    k, v = synth.kv_layer(w["config_id"], 0, B, H, L, D, device=DEV)
+    p, cbt, cache = gpu_encode(k, v, 1, R, cb)
+    q = synth.queries(w["config_id"], 0, B, w["Hq"], D, device=DEV)
+    o = nsnq.nsnq_decode_attention(p, cbt, q, cache).float().cpu().numpy()
+    units = [(0, 0), (5, 17), (15, 31)]
+    ks = torch.stack([k[b, h] for b, h in units]).cpu()
+    vs = torch.stack([v[b, h] for b, h in units]).cpu()
+    ek, ev = oracle.encode(ks, R, cb), oracle.encode(vs, R, cb)
+    compare_encoded(cache, ek, ev, units=units)
+    for i, (b, h) in enumerate(units):
+        eki = {key: (val[i:i + 1, None] if isinstance(val, np.ndarray) else val) for key, val in ek.items()}
+        evi = {key: (val[i:i + 1, None] if isinstance(val, np.ndarray) else val) for key, val in ev.items()}
+        ref = oracle.reference_decode(q[b:b + 1, h:h + 1].cpu(), eki, evi, ek["n_quant"], ek["n_resid"], R, cb)
+        check_attention(o[b:b + 1, h:h + 1], ref)
