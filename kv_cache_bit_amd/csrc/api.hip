@@ -229,13 +229,17 @@ DecodePlan plan_decode(const nsnq_params* p, const nsnq_cache* c, int q_heads, i
   } else if (num_splits > 0) {
     bps = (nblk + num_splits - 1) / num_splits;
   } else {
-    // aim for about 2048 work-groups over the whole grid
+    // about 1024 work-groups over the grid, each with at least 256 tokens so
+    // every thread of the group has a token
     const int64_t units = (int64_t)c->batch * c->kv_heads * (G / pl.gh);
-    int64_t want = (2048 + units - 1) / units;
+    int64_t want = (1024 + units - 1) / units;
     if (want < 1) want = 1;
     bps = (int)((nblk + want - 1) / want);
+    const int min_bps = (256 + R - 1) / R;
+    if (bps < min_bps) bps = min_bps;
   }
   if (bps < 1) bps = 1;
+  if (nblk > 0 && (nblk + bps - 1) / bps > kMaxSplits - 1) bps = (nblk + kMaxSplits - 2) / (kMaxSplits - 1);
   if (bps > max_bps) bps = max_bps;
   pl.split_tokens = bps * R;
   pl.nsplit_q = nblk == 0 ? 0 : (nblk + bps - 1) / bps;
@@ -271,6 +275,7 @@ nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook
   const size_t need = nsnq_decode_workspace_bytes(p, cache, q_heads, num_splits);
   if (!ws || !aligned16(ws) || ws_bytes < need) return NSNQ_EWORKSPACE;
   const DecodePlan pl = plan_decode(p, cache, q_heads, num_splits);
+  if (pl.nsplit > kMaxSplits) return NSNQ_EUNSUPPORTED;  // context too long for one combine
   DecodeArgs a{};
   a.q = q;
   a.kcodes = cache->k.codes;
@@ -319,6 +324,7 @@ int fp16_split_tokens(int G, int T, int num_splits, int units) {
   }
   ts = (ts + 63) / 64 * 64;
   if (ts < 64) ts = 64;
+  while ((T + ts - 1) / ts > kMaxSplits) ts += 64;
   while (ts > 64 && fp16_decode_lds_bytes(G, ts) > 160 * 1024) ts -= 64;
   return ts;
 }
@@ -344,6 +350,7 @@ nsnq_status nsnq_fp16_decode_attention(const uint16_t* q, int32_t q_heads, const
   if (!(softmax_scale > 0.f)) return NSNQ_EINVAL;
   const int ts = fp16_split_tokens(G, n_tokens, num_splits, batch * kv_heads);
   const int nsplit = (n_tokens + ts - 1) / ts;
+  if (nsplit > kMaxSplits || fp16_decode_lds_bytes(G, ts) > 160 * 1024) return NSNQ_EUNSUPPORTED;
   const size_t need = sizeof(float) * (size_t)batch * q_heads * nsplit * (kDim + 2);
   if (!ws || !aligned16(ws) || ws_bytes < need) return NSNQ_EWORKSPACE;
   Fp16DecodeArgs a{};

@@ -28,6 +28,8 @@
 // (SUB = 8) the hi/lo products fill K = 16 and the bias terms go through a
 // second 32x32x8 instruction.
 
+#include <type_traits>
+
 #include "nsnq_device.hpp"
 #include "nsnq_launch.hpp"
 
@@ -38,6 +40,13 @@ namespace nsnq {
 constexpr float kDistEps = 0.000244140625f;  // 2^-12
 // n2 below this is rounding noise of the shift: treated as zero
 constexpr float kN2Floor = 0.000244140625f;  // 2^-12
+
+// Packed argmin key: the distance's bits with the low byte replaced by an
+// index.  The in-tile index (< 32) is an inline constant, so this is a single
+// v_and_or_b32; the tile's 32-codeword offset is OR-ed in once per tile.
+__device__ __forceinline__ uint32_t make_key(float dist, uint32_t idx) {
+  return (__float_as_uint(dist) & 0xffffff00u) | idx;
+}
 
 __device__ __forceinline__ uint32_t pack_h2(half_t a, half_t b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
@@ -141,20 +150,18 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     }
   }
 
-  // Load one row (this lane's sub-vector of token `tok`) and normalise it:
+  // One row = this lane's sub-vector of token `tok`: raw fp16 load, then
   // y = x / n1 with n1 = ||x|| / sqrt(d).  Pass 2 recomputes this from the
   // (L2-resident) input instead of keeping R x 128 floats alive.
-  auto load_norm = [&](int tok, float (&y)[SUB], float& n1) {
-    const uint16_t* px = src + (int64_t)tok * a.st + slot * SUB;
+  using raw_t = typename std::conditional<SUB == 4, uint2, uint4>::type;
+  auto load_raw = [&](int tok) -> raw_t {
+    return *reinterpret_cast<const raw_t*>(src + (int64_t)tok * a.st + slot * SUB);
+  };
+  auto norm_raw = [&](const raw_t& raw, float (&y)[SUB], float& n1) {
     float v[SUB];
-    if constexpr (SUB == 4) {
-      uint2 raw = *reinterpret_cast<const uint2*>(px);
-      v[0] = h2f(raw.x & 0xffff); v[1] = h2f(raw.x >> 16);
-      v[2] = h2f(raw.y & 0xffff); v[3] = h2f(raw.y >> 16);
-    } else {
-      uint4 raw = *reinterpret_cast<const uint4*>(px);
-      v[0] = h2f(raw.x & 0xffff); v[1] = h2f(raw.x >> 16);
-      v[2] = h2f(raw.y & 0xffff); v[3] = h2f(raw.y >> 16);
+    v[0] = h2f(raw.x & 0xffff); v[1] = h2f(raw.x >> 16);
+    v[2] = h2f(raw.y & 0xffff); v[3] = h2f(raw.y >> 16);
+    if constexpr (SUB == 8) {
       v[4] = h2f(raw.z & 0xffff); v[5] = h2f(raw.z >> 16);
       v[6] = h2f(raw.w & 0xffff); v[7] = h2f(raw.w >> 16);
     }
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
 #pragma unroll 4
   for (int r = 0; r < ROWS; ++r) {
     float y[SUB], n1;
-    load_norm(wave * TPW + r * TPR + tir, y, n1);
+    norm_raw(load_raw(wave * TPW + r * TPR + tir), y, n1);
 #pragma unroll
     for (int e = 0; e < SUB; ++e) csum[e] += y[e];
   }
@@ -206,11 +213,14 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   uint16_t* scales = a.scales[kv];
 
   // ---- pass 2: per row: shift, second normalisation, Hadamard, VQ ---------
+  raw_t nxt = load_raw(wave * TPW + tir);
 #pragma unroll 1
   for (int r = 0; r < ROWS; ++r) {
     const int tok = wave * TPW + r * TPR + tir;
+    const raw_t cur = nxt;
+    if (r + 1 < ROWS) nxt = load_raw(tok + TPR);  // prefetch the next row
     float u[SUB], n1;
-    load_norm(tok, u, n1);
+    norm_raw(cur, u, n1);
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) {
@@ -286,18 +296,18 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
         acc0 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2[t], Bb0, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2[t], Bb1, acc1, 0, 0, 0);
       }
+      // accumulator q holds codeword 32t + 8(q/4) + 4(lane/32) + q%4
+      uint32_t tb0 = min(make_key(acc0[0], 0u), make_key(acc0[1], 1u));
+      uint32_t tb1 = min(make_key(acc1[0], 0u), make_key(acc1[1], 1u));
 #pragma unroll
-      for (int q = 0; q < 16; q += 2) {
-        // accumulator q holds codeword 32t + 8(q/4) + 4(lane/32) + q%4
-        const uint32_t i0 = 32u * t + 8u * (q >> 2) + (q & 3);
-        const uint32_t i1 = 32u * t + 8u * ((q + 1) >> 2) + ((q + 1) & 3);
-        const uint32_t k00 = (__float_as_uint(acc0[q]) & 0xffffff00u) | i0;
-        const uint32_t k01 = (__float_as_uint(acc0[q + 1]) & 0xffffff00u) | i1;
-        const uint32_t k10 = (__float_as_uint(acc1[q]) & 0xffffff00u) | i0;
-        const uint32_t k11 = (__float_as_uint(acc1[q + 1]) & 0xffffff00u) | i1;
-        best0 = min(min(best0, k00), k01);
-        best1 = min(min(best1, k10), k11);
+      for (int q = 2; q < 16; q += 2) {
+        const uint32_t i0 = 8u * (q >> 2) + (q & 3);
+        const uint32_t i1 = 8u * ((q + 1) >> 2) + ((q + 1) & 3);
+        tb0 = min(min(tb0, make_key(acc0[q], i0)), make_key(acc0[q + 1], i1));
+        tb1 = min(min(tb1, make_key(acc1[q], i0)), make_key(acc1[q + 1], i1));
       }
+      best0 = min(best0, tb0 | (32u * t));
+      best1 = min(best1, tb1 | (32u * t));
     }
     const uint32_t hbit = (uint32_t)(lane >> 5) << 2;
     best0 |= hbit;

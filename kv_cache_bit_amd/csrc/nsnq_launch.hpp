@@ -86,6 +86,7 @@ hipError_t launch_dequant(const DequantArgs& a, int sub, int n_units, hipStream_
 hipError_t launch_decode(const DecodeArgs& a, int sub, int gh, int B, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream);
 size_t decode_lds_bytes(int sub, int gh, int split_tokens, int R);
+constexpr int kMaxSplits = 1024;  // partials one combine can merge
 int decode_max_split_tokens(int sub, int gh, int R);
 hipError_t launch_kmeans_init(const float* src, float* cent, int sub, hipStream_t stream);
 hipError_t launch_kmeans_iter(const KmeansArgs& a, int sub, hipStream_t stream);
