@@ -229,13 +229,13 @@ DecodePlan plan_decode(const nsnq_params* p, const nsnq_cache* c, int q_heads, i
   } else if (num_splits > 0) {
     bps = (nblk + num_splits - 1) / num_splits;
   } else {
-    // about 1024 work-groups over the grid, each with at least 256 tokens so
-    // every thread of the group has a token
+    // about 1024 work-groups over the grid, each with at least 512 tokens so
+    // each of its 4 waves streams at least two 64-token chunks
     const int64_t units = (int64_t)c->batch * c->kv_heads * (G / pl.gh);
     int64_t want = (1024 + units - 1) / units;
     if (want < 1) want = 1;
     bps = (int)((nblk + want - 1) / want);
-    const int min_bps = (256 + R - 1) / R;
+    const int min_bps = (512 + R - 1) / R;
     if (bps < min_bps) bps = min_bps;
   }
   if (bps < 1) bps = 1;

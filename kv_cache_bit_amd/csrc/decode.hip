@@ -7,13 +7,9 @@
 // s-element slice).  For the values,
 //   sum_t p_t v_hat_t = H^T( sum_j sum_c Hist_j[c] C[c] ) + sum_b beta_b MU_b,
 //   Hist_j[c] = sum_{t: c_tj = c} p_t N1_t N2_t,   beta_b = sum_{t in b} p_t N1_t.
-// So a work-group streams only codes and fp16 scalars from HBM: pass 1 gathers
-// LUT entries (LDS) into scores; pass 2 forms sum_t w_t c_hat_t in the Hadamard
-// domain by gathering codewords from LDS (each lane owns 16 channels and a
-// strided subset of tokens).  That is the codeword histogram Hist_j[c] applied
-// to the codebook without materialising it: LDS float atomics serialise on
-// gfx950.  The inverse Hadamard runs once per split.  Residual fp16 tokens get
-// a split of their own.
+// A split streams only packed codes and fp16 scalars from HBM; the codebook
+// product and the inverse Hadamard run once per split.  Residual fp16 tokens
+// get a split of their own.
 
 #include "nsnq_device.hpp"
 #include "nsnq_launch.hpp"
@@ -23,44 +19,27 @@ namespace nsnq {
 
 constexpr int kLutStride = 257;  // odd row stride: finish-step reads hit distinct banks
 
-struct DecodeSmem {
-  // offsets in floats
-  int qf, qr, cbf, lut, sc, qmu, beta, om, red, vred, total;
-};
+// ---------------------------------------------------------------------------
+// Compressed-token split: single streaming pass with online softmax.
+//
+// The work-group builds the query LUTs once; then each wave streams its own
+// 64-token chunks (chunks w, w + 4, ... of the split) with the next chunk's
+// codes and scalars already in flight:
+//   scores  lane = token: s_t = N1 (N2 sum_j LUT_j[c_tj] + q . MU_b)
+//   softmax running max / sum per head; the value accumulators are rescaled
+//           when the max moves
+//   values  lane (sq, tg) owns 16 Hadamard-domain channels (slots 4 sq..4 sq+3
+//           at 2 bits, 2 sq, 2 sq + 1 at 1 bit) and tokens 8 tg .. 8 tg + 7 of
+//           the chunk: acc += w_t C[c_tj] with w_t = p_t N1_t N2_t, codewords
+//           gathered from the fp16 codebook in LDS;
+//   means   the block-mean term sum_t p_t N1_t MU_b is accumulated per chunk
+//           (2 channels per lane).
+// At the end the waves merge through LDS, the Hadamard-domain sum goes through
+// one inverse transform, and the split's (m, l, o) partial is written.
 
-// Blocks of R tokens one split may span (mean-term registers per wave: 4).
+constexpr int kChunk = 64;
+// Blocks of R tokens one split may span.
 constexpr int kMaxSplitBlocks = 16;
-
-__host__ __device__ inline DecodeSmem decode_smem(int sub, int gh, int split_tokens, int R) {
-  const int S = kDim / sub;
-  const int nb = split_tokens / R;
-  DecodeSmem s;
-  int o = 0;
-  s.qf = o; o += gh * kDim;
-  s.qr = o; o += gh * kDim;
-  s.cbf = o; o += kCodewords * sub;
-  s.lut = o; o += gh * S * kLutStride;
-  s.sc = o; o += gh * split_tokens;
-  s.qmu = o; o += gh * nb;
-  s.beta = o; o += gh * nb;
-  s.om = o; o += gh * kDim;
-  s.red = o; o += 2 * 4 * gh;
-  s.vred = o; o += 4 * gh * kDim;
-  s.total = o;
-  return s;
-}
-
-size_t decode_lds_bytes(int sub, int gh, int split_tokens, int R) {
-  return (size_t)decode_smem(sub, gh, split_tokens, R).total * sizeof(float);
-}
-
-int decode_max_split_tokens(int sub, int gh, int R) {
-  const size_t cap = 160 * 1024;
-  int best = 0;
-  for (int ts = R; ts <= kMaxSplitBlocks * R; ts += R)
-    if (decode_lds_bytes(sub, gh, ts, R) <= cap) best = ts;
-  return best;
-}
 
 // Block-wide reduction of GH values per thread (max or sum); red is 4*GH floats.
 template <int GH, bool MAX>
@@ -80,6 +59,37 @@ __device__ __forceinline__ void block_reduce(float (&v)[GH], float* red, int lan
   __syncthreads();
 }
 
+
+struct DecodeSmem {
+  // offsets in floats
+  int qf, qr, cbh, lut, wbuf, total;
+};
+
+__host__ __device__ inline DecodeSmem decode_smem(int sub, int gh, int split_tokens, int R) {
+  (void)split_tokens;
+  (void)R;
+  const int S = kDim / sub;
+  DecodeSmem s;
+  int o = 0;
+  s.qf = o; o += gh * kDim;
+  s.qr = o; o += gh * kDim;
+  s.cbh = o; o += kCodewords * sub / 2;      // fp16 codebook
+  s.lut = o; o += gh * S * kLutStride;       // LUTs; reused for the wave merge
+  s.wbuf = o; o += 4 * gh * kChunk;          // per-wave chunk weights
+  s.total = o;
+  return s;
+}
+
+size_t decode_lds_bytes(int sub, int gh, int split_tokens, int R) {
+  return (size_t)decode_smem(sub, gh, split_tokens, R).total * sizeof(float);
+}
+
+int decode_max_split_tokens(int sub, int gh, int R) {
+  (void)sub;
+  (void)gh;
+  return kMaxSplitBlocks * R;
+}
+
 template <int S>
 __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&cw)[S / 4]) {
 #pragma unroll
@@ -92,9 +102,10 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&cw)[S / 
 // Residual split: fp16 keys and values, one query token per head.
 template <int GH>
 __device__ __forceinline__ void decode_residual(const DecodeArgs& a, float* qf, float* sc, float* ov, float* red,
-                                                float* ws_base, int64_t ws_head, int64_t unit, int TS) {
+                                                float* ws_base, int64_t ws_head, int64_t unit) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nt = a.n_resid;
+  constexpr int TS = 128;
   const uint16_t* kr = a.kresid + unit * a.R * kDim;
   const uint16_t* vr = a.vresid + unit * a.R * kDim;
   __syncthreads();
@@ -175,19 +186,14 @@ __device__ __forceinline__ void decode_residual(const DecodeArgs& a, float* qf, 
 template <int SUB, int GH>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int S = kDim / SUB;
-  constexpr int CW = S / 4;  // 32-bit words of codes per token
+  constexpr int CW = S / 4;      // 32-bit words of codes per token
+  constexpr int SPT = 16 / SUB;  // value slots per lane
   extern __shared__ float smem[];
-  const int TS = a.split_tokens;
-  const DecodeSmem L = decode_smem(SUB, GH, TS, a.R);
+  const DecodeSmem L = decode_smem(SUB, GH, a.split_tokens, a.R);
   float* qf = smem + L.qf;
   float* qr = smem + L.qr;
-  float* cbf = smem + L.cbf;
+  uint16_t* cbh = reinterpret_cast<uint16_t*>(smem + L.cbh);
   float* lut = smem + L.lut;
-  float* sc = smem + L.sc;
-  float* qmu = smem + L.qmu;
-  float* beta = smem + L.beta;
-  float* om = smem + L.om;
-  float* red = smem + L.red;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x;
@@ -207,70 +213,63 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 
   if (split >= a.nsplit_q) {
-    decode_residual<GH>(a, qf, sc, lut, red, ws_base, ws_head, unit, TS);
+    float* red = lut + 4 * GH * kDim;
+    decode_residual<GH>(a, qf, lut + 4 * GH * kDim + 8 * GH, lut, red, ws_base, ws_head, unit);
     return;
   }
 
-  // ---------------- compressed tokens ----------------
-  const int t0 = split * TS;
-  const int ntok = min(TS, a.n_quant - t0);
-  const int nb = ntok / a.R;
+  const int t0 = split * a.split_tokens;
+  const int ntok = min(a.split_tokens, a.n_quant - t0);
+  const int nchunk = ntok / kChunk;
   const uint8_t* kc = a.kcodes + (unit * a.cap + t0) * S;
   const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.kscales) + unit * a.cap + t0;
   const uint8_t* vc = a.vcodes + (unit * a.cap + t0) * S;
   const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.vscales) + unit * a.cap + t0;
-  const int iters = (ntok + 255) / 256;
+  const uint16_t* kmu = a.kmu + (unit * nbmu + t0 / a.R) * kDim;
+  const uint16_t* vmu = a.vmu + (unit * nbmu + t0 / a.R) * kDim;
 
-  // issue the first token loads and the block means before the LUT work
-  uint32_t kcw[CW], ksc = 0, vsc = 0;
-  if (tid < ntok) {
-    load_codes<S>(kc + (int64_t)tid * S, kcw);
-    ksc = ks[tid];
-    vsc = vs[tid];
-  }
-  uint32_t kmu_r[kMaxSplitBlocks / 4], vmu_r[kMaxSplitBlocks / 4];
+  const int sq = lane & 7, tg = lane >> 3;
+  // one chunk's loads for this lane
+  struct ChunkRegs {
+    uint32_t kcw[CW];
+    uint32_t ksc, vsc, kmu2, vmu2;
+    uint32_t vcw[8];
+  };
+  auto load_chunk = [&](int ch, ChunkRegs& r) {
+    const int tl = ch * kChunk + lane;  // this lane's token for scores
+    load_codes<S>(kc + (int64_t)tl * S, r.kcw);
+    r.ksc = ks[tl];
+    r.vsc = vs[tl];
+    const int bl = (ch * kChunk) / a.R;
+    r.kmu2 = *reinterpret_cast<const uint32_t*>(kmu + (int64_t)bl * kDim + 2 * lane);
+    r.vmu2 = *reinterpret_cast<const uint32_t*>(vmu + (int64_t)bl * kDim + 2 * lane);
 #pragma unroll
-  for (int i = 0; i < kMaxSplitBlocks / 4; ++i) {
-    const int bl = wave + 4 * i;
-    kmu_r[i] = vmu_r[i] = 0;
-    if (bl < nb) {
-      const int64_t row = (unit * nbmu + t0 / a.R + bl) * kDim + 2 * lane;
-      kmu_r[i] = *reinterpret_cast<const uint32_t*>(a.kmu + row);
-      vmu_r[i] = *reinterpret_cast<const uint32_t*>(a.vmu + row);
+    for (int i = 0; i < 8; ++i) {
+      const uint8_t* p = vc + (int64_t)(ch * kChunk + 8 * tg + i) * S + sq * SPT;
+      if constexpr (SPT == 4) r.vcw[i] = *reinterpret_cast<const uint32_t*>(p);
+      else r.vcw[i] = *reinterpret_cast<const uint16_t*>(p);
     }
-  }
-  for (int i = tid; i < kCodewords * SUB; i += 256) cbf[i] = h2f(a.codebook[i]);
-  for (int i = tid; i < GH * kDim; i += 256) om[i] = 0.f;
-  __syncthreads();
+  };
+  ChunkRegs cur;
+  int ch = wave;
+  if (ch < nchunk) load_chunk(ch, cur);
 
-  // rotate the queries (one wave per head); q . MU_b per block
+  for (int i = tid; i < kCodewords * SUB; i += 256) cbh[i] = a.codebook[i];
+  __syncthreads();
+  // rotate the queries (one wave per head)
   if (wave < GH) {
     float x[2] = {qf[wave * kDim + 2 * lane], qf[wave * kDim + 2 * lane + 1]};
     fwht128<2>(x, lane);
     qr[wave * kDim + 2 * lane] = x[0] * kInvSqrtD;
     qr[wave * kDim + 2 * lane + 1] = x[1] * kInvSqrtD;
   }
-#pragma unroll
-  for (int i = 0; i < kMaxSplitBlocks / 4; ++i) {
-    const int bl = wave + 4 * i;
-    if (bl < nb) {
-      const float m0 = h2f(kmu_r[i] & 0xffff), m1 = h2f(kmu_r[i] >> 16);
-#pragma unroll
-      for (int g = 0; g < GH; ++g) {
-        float d = fmaf(qf[g * kDim + 2 * lane], m0, qf[g * kDim + 2 * lane + 1] * m1);
-        d = group_sum<kWave>(d);
-        if (lane == 0) qmu[g * nb + bl] = d;
-      }
-    }
-  }
   __syncthreads();
-
   // LUT_j[c] = (Hq)_j . C[c]; thread = codeword
   {
     const int c = tid;
     float cv[SUB];
 #pragma unroll
-    for (int e = 0; e < SUB; ++e) cv[e] = cbf[c * SUB + e];
+    for (int e = 0; e < SUB; ++e) cv[e] = h2f(cbh[c * SUB + e]);
 #pragma unroll
     for (int g = 0; g < GH; ++g) {
 #pragma unroll 8
@@ -284,104 +283,88 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // pass 1: scores from K codes
-  float m[GH];
+  float m[GH], l[GH], acc[GH][16], om0[GH], om1[GH];
+  float q0[GH], q1[GH];
 #pragma unroll
-  for (int g = 0; g < GH; ++g) m[g] = -INFINITY;
-  for (int it = 0; it < iters; ++it) {
-    const int t = it * 256 + tid;
-    if (t < ntok) {
-      if (it > 0) {
-        load_codes<S>(kc + (int64_t)t * S, kcw);
-        ksc = ks[t];
-      }
-      const float n1 = h2f(ksc & 0xffff), n2 = h2f(ksc >> 16);
-      const int bl = t / a.R;
-#pragma unroll
-      for (int g = 0; g < GH; ++g) {
-        const float* lg = lut + g * S * kLutStride;
-        float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < S; j += 2) {
-          acc0 += lg[j * kLutStride + ((kcw[j >> 2] >> (8 * (j & 3))) & 0xffu)];
-          acc1 += lg[(j + 1) * kLutStride + ((kcw[(j + 1) >> 2] >> (8 * ((j + 1) & 3))) & 0xffu)];
-        }
-        const float sv = a.scale_log2 * n1 * fmaf(n2, acc0 + acc1, qmu[g * nb + bl]);
-        sc[g * TS + t] = sv;
-        m[g] = fmaxf(m[g], sv);
-      }
-    }
-  }
-  block_reduce<GH, true>(m, red, lane, wave);
-
-  // softmax weights times the V scales: w_t = p_t N1_t N2_t, beta_b += p_t N1_t
-  for (int i = tid; i < GH * nb; i += 256) beta[i] = 0.f;
-  float l[GH];
-#pragma unroll
-  for (int g = 0; g < GH; ++g) l[g] = 0.f;
-  __syncthreads();
-  for (int it = 0; it < iters; ++it) {
-    const int t = it * 256 + tid;
-    float pn1[GH];
-#pragma unroll
-    for (int g = 0; g < GH; ++g) pn1[g] = 0.f;
-    if (t < ntok) {
-      if (it > 0) vsc = vs[t];
-      const float n1 = h2f(vsc & 0xffff), n2 = h2f(vsc >> 16);
-#pragma unroll
-      for (int g = 0; g < GH; ++g) {
-        const float pr = exp2f(sc[g * TS + t] - m[g]);
-        l[g] += pr;
-        pn1[g] = pr * n1;
-        sc[g * TS + t] = pr * n1 * n2;
-      }
-    }
-    // a wave's 64 tokens lie in one mean block (64 divides R, splits are R-aligned)
-    const int bl = (it * 256 + wave * 64) / a.R;
-#pragma unroll
-    for (int g = 0; g < GH; ++g) {
-      const float sum = group_sum<kWave>(pn1[g]);
-      if (lane == 0 && bl < nb) atomicAdd(beta + g * nb + bl, sum);
-    }
-  }
-  block_reduce<GH, false>(l, red, lane, wave);  // also publishes w_t in sc
-
-  // pass 2: o_hat = sum_t w_t c_hat_t.  Lane (sq, tg) owns 16 channels (4 slots
-  // at 2 bits, 2 at 1 bit) and tokens tg, tg + 32, ...
-  constexpr int SPT = 16 / SUB;  // slots per thread
-  const int sq = tid & 7, tg = tid >> 3;
-  float acc[GH][16];
-#pragma unroll
-  for (int g = 0; g < GH; ++g)
+  for (int g = 0; g < GH; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+    om0[g] = om1[g] = 0.f;
+    q0[g] = qf[g * kDim + 2 * lane];
+    q1[g] = qf[g * kDim + 2 * lane + 1];
 #pragma unroll
     for (int c = 0; c < 16; ++c) acc[g][c] = 0.f;
-  const uint8_t* vrow = vc + sq * SPT;
-  for (int t = tg; t < ntok; t += 32) {
-    uint32_t cw;
-    if constexpr (SPT == 4) cw = *reinterpret_cast<const uint32_t*>(vrow + (int64_t)t * S);
-    else cw = *reinterpret_cast<const uint16_t*>(vrow + (int64_t)t * S);
-    float wg[GH];
+  }
+  float* wb = smem + L.wbuf + wave * GH * kChunk;
+
+  for (; ch < nchunk; ch += 4) {
+    ChunkRegs nxt;
+    if (ch + 4 < nchunk) load_chunk(ch + 4, nxt);
+    const float kn1 = h2f(cur.ksc & 0xffff), kn2 = h2f(cur.ksc >> 16);
+    const float vn1 = h2f(cur.vsc & 0xffff), vn2 = h2f(cur.vsc >> 16);
+    const float km0 = h2f(cur.kmu2 & 0xffff), km1 = h2f(cur.kmu2 >> 16);
+    const float vm0 = h2f(cur.vmu2 & 0xffff), vm1 = h2f(cur.vmu2 >> 16);
 #pragma unroll
-    for (int g = 0; g < GH; ++g) wg[g] = sc[g * TS + t];
+    for (int g = 0; g < GH; ++g) {
+      // score of this lane's token
+      const float* lg = lut + g * S * kLutStride;
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int si = 0; si < SPT; ++si) {
-      const uint32_t code = (cw >> (8 * si)) & 0xffu;
-      const float4* cp = reinterpret_cast<const float4*>(cbf + code * SUB);
+      for (int j = 0; j < S; j += 2) {
+        s0 += lg[j * kLutStride + ((cur.kcw[j >> 2] >> (8 * (j & 3))) & 0xffu)];
+        s1 += lg[(j + 1) * kLutStride + ((cur.kcw[(j + 1) >> 2] >> (8 * ((j + 1) & 3))) & 0xffu)];
+      }
+      const float qmu = group_sum<kWave>(fmaf(q0[g], km0, q1[g] * km1));
+      const float sv = a.scale_log2 * kn1 * fmaf(kn2, s0 + s1, qmu);
+      // online softmax over the chunk
+      const float mn = fmaxf(m[g], group_max<kWave>(sv));
+      const float alpha = exp2f(m[g] - mn);
+      const float pr = exp2f(sv - mn);
+      m[g] = mn;
+      l[g] = fmaf(l[g], alpha, group_sum<kWave>(pr));
+      const float pn1 = group_sum<kWave>(pr * vn1);
+      om0[g] = fmaf(om0[g], alpha, pn1 * vm0);
+      om1[g] = fmaf(om1[g], alpha, pn1 * vm1);
 #pragma unroll
-      for (int hh = 0; hh < SUB / 4; ++hh) {
-        const float4 c4 = cp[hh];
+      for (int c = 0; c < 16; ++c) acc[g][c] *= alpha;
+      wb[g * kChunk + lane] = pr * vn1 * vn2;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // values: tokens 8 tg .. 8 tg + 7 of the chunk, this lane's 16 channels
 #pragma unroll
-        for (int g = 0; g < GH; ++g) {
-          float* ag = &acc[g][si * SUB + 4 * hh];
-          ag[0] = fmaf(wg[g], c4.x, ag[0]);
-          ag[1] = fmaf(wg[g], c4.y, ag[1]);
-          ag[2] = fmaf(wg[g], c4.z, ag[2]);
-          ag[3] = fmaf(wg[g], c4.w, ag[3]);
+    for (int i = 0; i < 8; ++i) {
+      float wg[GH];
+#pragma unroll
+      for (int g = 0; g < GH; ++g) wg[g] = wb[g * kChunk + 8 * tg + i];
+#pragma unroll
+      for (int si = 0; si < SPT; ++si) {
+        const uint32_t code = (cur.vcw[i] >> (8 * si)) & 0xffu;
+        const uint16_t* cp = cbh + code * SUB;
+#pragma unroll
+        for (int hh = 0; hh < SUB / 4; ++hh) {
+          const uint2 c4 = *reinterpret_cast<const uint2*>(cp + 4 * hh);
+          const float c0 = h2f(c4.x & 0xffff), c1 = h2f(c4.x >> 16);
+          const float c2 = h2f(c4.y & 0xffff), c3 = h2f(c4.y >> 16);
+#pragma unroll
+          for (int g = 0; g < GH; ++g) {
+            float* ag = &acc[g][si * SUB + 4 * hh];
+            ag[0] = fmaf(wg[g], c0, ag[0]);
+            ag[1] = fmaf(wg[g], c1, ag[1]);
+            ag[2] = fmaf(wg[g], c2, ag[2]);
+            ag[3] = fmaf(wg[g], c3, ag[3]);
+          }
         }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    cur = nxt;
   }
-  // reduce over the 8 token groups of the wave (lane bits 3..5), then the waves
+
+  // token-group reduction inside the wave (lane bits 3..5)
 #pragma unroll
   for (int g = 0; g < GH; ++g)
 #pragma unroll
@@ -392,45 +375,48 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       v += xshfl(v, 32);
       acc[g][c] = v;
     }
-  float* vred = smem + L.vred;
-  if (lane < 8) {
-#pragma unroll
-    for (int g = 0; g < GH; ++g)
-#pragma unroll
-      for (int c = 0; c < 16; ++c) vred[(wave * GH + g) * kDim + sq * 16 + c] = acc[g][c];
-  }
+  // merge the 4 waves through LDS (the LUT space is free now)
   __syncthreads();
-  for (int o = tid; o < GH * kDim; o += 256) {
-    const int g = o / kDim, c = o % kDim;
-    qr[o] = (vred[(0 * GH + g) * kDim + c] + vred[(1 * GH + g) * kDim + c]) +
-            (vred[(2 * GH + g) * kDim + c] + vred[(3 * GH + g) * kDim + c]);
-  }
-  // mean terms: sum_b beta_b MU_b, from the V means this wave prefetched
+  float* mrg = lut;  // [4 waves][GH][2 + 128 + 128]: m, l, acc, mean term
+  constexpr int MS = 2 + 2 * kDim;
 #pragma unroll
-  for (int i = 0; i < kMaxSplitBlocks / 4; ++i) {
-    const int bl = wave + 4 * i;
-    if (bl < nb) {
-      const float m0 = h2f(vmu_r[i] & 0xffff), m1 = h2f(vmu_r[i] >> 16);
-#pragma unroll
-      for (int g = 0; g < GH; ++g) {
-        const float be = beta[g * nb + bl];
-        atomicAdd(om + g * kDim + 2 * lane, be * m0);
-        atomicAdd(om + g * kDim + 2 * lane + 1, be * m1);
-      }
+  for (int g = 0; g < GH; ++g) {
+    float* r = mrg + (wave * GH + g) * MS;
+    if (lane == 0) {
+      r[0] = m[g];
+      r[1] = l[g];
     }
+    if (lane < 8) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) r[2 + sq * 16 + c] = acc[g][c];
+    }
+    r[2 + kDim + 2 * lane] = om0[g];
+    r[2 + kDim + 2 * lane + 1] = om1[g];
   }
   __syncthreads();
-  // inverse Hadamard of o_hat (one wave per head) plus the mean terms
   if (wave < GH) {
     const int g = wave;
-    float x[2] = {qr[g * kDim + 2 * lane], qr[g * kDim + 2 * lane + 1]};
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg[(w * GH + g) * MS]);
+    float lsum = 0.f, x[2] = {0.f, 0.f}, om[2] = {0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* r = mrg + (w * GH + g) * MS;
+      const float f = r[0] == -INFINITY ? 0.f : exp2f(r[0] - M);
+      lsum = fmaf(f, r[1], lsum);
+      x[0] = fmaf(f, r[2 + 2 * lane], x[0]);
+      x[1] = fmaf(f, r[2 + 2 * lane + 1], x[1]);
+      om[0] = fmaf(f, r[2 + kDim + 2 * lane], om[0]);
+      om[1] = fmaf(f, r[2 + kDim + 2 * lane + 1], om[1]);
+    }
     fwht128<2>(x, lane);
     float* wo = ws_base + g * ws_head;
-    wo[2 * lane] = fmaf(x[0], kInvSqrtD, om[g * kDim + 2 * lane]);
-    wo[2 * lane + 1] = fmaf(x[1], kInvSqrtD, om[g * kDim + 2 * lane + 1]);
+    wo[2 * lane] = fmaf(x[0], kInvSqrtD, om[0]);
+    wo[2 * lane + 1] = fmaf(x[1], kInvSqrtD, om[1]);
     if (lane == 0) {
-      wo[kDim] = m[g];
-      wo[kDim + 1] = l[g];
+      wo[kDim] = M;
+      wo[kDim + 1] = lsum;
     }
   }
 }
