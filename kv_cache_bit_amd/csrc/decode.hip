@@ -370,9 +370,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       float v = acc[g][c];
-      v += xshfl(v, 8);
-      v += xshfl(v, 16);
-      v += xshfl(v, 32);
+      v += xlane<8>(v);
+      v += xlane<16>(v);
+      v += xlane<32>(v);
       acc[g][c] = v;
     }
   // merge the 4 waves through LDS (the LUT space is free now)

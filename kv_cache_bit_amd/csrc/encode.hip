@@ -41,11 +41,11 @@ constexpr float kDistEps = 0.000244140625f;  // 2^-12
 // n2 below this is rounding noise of the shift: treated as zero
 constexpr float kN2Floor = 0.000244140625f;  // 2^-12
 
-// Packed argmin key: the distance's bits with the low byte replaced by an
-// index.  The in-tile index (< 32) is an inline constant, so this is a single
-// v_and_or_b32; the tile's 32-codeword offset is OR-ed in once per tile.
-__device__ __forceinline__ uint32_t make_key(float dist, uint32_t idx) {
-  return (__float_as_uint(dist) & 0xffffff00u) | idx;
+// Packed argmin key: the distance's bits with the low byte replaced by the
+// codeword index.  With the mask in a VGPR and the index in an SGPR this is a
+// single v_and_or_b32 (constant-bus limit: one scalar operand).
+__device__ __forceinline__ uint32_t make_key(float dist, uint32_t vmask, uint32_t idx) {
+  return (__float_as_uint(dist) & vmask) | idx;
 }
 
 __device__ __forceinline__ uint32_t pack_h2(half_t a, half_t b) {
@@ -59,14 +59,13 @@ __device__ __forceinline__ half8_t u32x4_to_half8(uint32_t a, uint32_t b, uint32
 
 __device__ __forceinline__ uint4_t half8_to_u32x4(half8_t h) { return __builtin_bit_cast(uint4_t, h); }
 
-// Move lanes 0-31 / 32-63 between two registers:
+// Move lanes 0-31 / 32-63 between two registers (one v_permlane32_swap):
 //   lo_out = [a(lanes 0-31), b(lanes 0-31) moved up]
 //   hi_out = [a(lanes 32-63) moved down, b(lanes 32-63)]
-__device__ __forceinline__ void half_swap(uint32_t a, uint32_t b, uint32_t& lo_out, uint32_t& hi_out, int lane) {
-  uint32_t a_x = __shfl_xor(a, 32, kWave);
-  uint32_t b_x = __shfl_xor(b, 32, kWave);
-  lo_out = lane < 32 ? a : b_x;
-  hi_out = lane < 32 ? a_x : b;
+__device__ __forceinline__ void half_swap(uint32_t a, uint32_t b, uint32_t& lo_out, uint32_t& hi_out, int) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  lo_out = r[0];
+  hi_out = r[1];
 }
 
 // Work-groups past the encode blocks copy the last r tokens of each stream
@@ -168,9 +167,10 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) ss = fmaf(v[e], v[e], ss);
-    ss = group_sum<S>(ss);
-    n1 = sqrtf(ss * (1.0f / kDim));
-    const float inv = n1 > 0.f ? 1.0f / n1 : 0.f;
+    ss = group_sum<S>(ss) * (1.0f / kDim);
+    const float rs = __builtin_amdgcn_rsqf(ss);  // 1 / n1
+    const float inv = ss > 0.f ? rs : 0.f;
+    n1 = ss * inv;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) y[e] = v[e] * inv;
   };
@@ -189,8 +189,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   // combine the TPR lanes holding the same channels, then the 4 waves
 #pragma unroll
   for (int e = 0; e < SUB; ++e) {
-#pragma unroll
-    for (int m = S; m < kWave; m <<= 1) csum[e] += xshfl(csum[e], m);
+    if constexpr (S <= 16) csum[e] += xlane<16>(csum[e]);
+    csum[e] += xlane<32>(csum[e]);
   }
   if (tir == 0) {
 #pragma unroll
@@ -227,13 +227,13 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
       u[e] -= mu[e];
       ss = fmaf(u[e], u[e], ss);
     }
-    ss = group_sum<S>(ss);
+    ss = group_sum<S>(ss) * (1.0f / kDim);
     // a token within 2^-12 (relative) of the block mean has no direction left:
     // store n2 = 0 and quantise w = 0 (reconstructed as n1 * mu)
-    float n2 = sqrtf(ss * (1.0f / kDim));
-    n2 = n2 < kN2Floor ? 0.f : n2;
-    const half_t n2h = (half_t)n2;
-    const float inv2 = n2 > 0.f ? 1.0f / n2 : 0.f;
+    const float rs2 = __builtin_amdgcn_rsqf(ss);
+    const bool live = ss >= kN2Floor * kN2Floor;
+    const float inv2 = live ? rs2 : 0.f;
+    const half_t n2h = (half_t)(ss * inv2);
 #pragma unroll
     for (int e = 0; e < SUB; ++e) u[e] *= inv2;
     fwht128<SUB>(u, lane);
@@ -286,6 +286,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
       Bb1 = lane < 32 ? zero4 : bias;
     }
 
+    uint32_t vmask;  // 0xffffff00 in a VGPR (opaque so it is not folded into a literal)
+    asm("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(0xffffff00u));
     uint32_t best0 = 0xffffffffu, best1 = 0xffffffffu;
     const float16_t zacc = {};
 #pragma unroll
@@ -296,26 +298,23 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
         acc0 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2[t], Bb0, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2[t], Bb1, acc1, 0, 0, 0);
       }
-      // accumulator q holds codeword 32t + 8(q/4) + 4(lane/32) + q%4
-      uint32_t tb0 = min(make_key(acc0[0], 0u), make_key(acc0[1], 1u));
-      uint32_t tb1 = min(make_key(acc1[0], 0u), make_key(acc1[1], 1u));
 #pragma unroll
-      for (int q = 2; q < 16; q += 2) {
-        const uint32_t i0 = 8u * (q >> 2) + (q & 3);
-        const uint32_t i1 = 8u * ((q + 1) >> 2) + ((q + 1) & 3);
-        tb0 = min(min(tb0, make_key(acc0[q], i0)), make_key(acc0[q + 1], i1));
-        tb1 = min(min(tb1, make_key(acc1[q], i0)), make_key(acc1[q + 1], i1));
+      for (int q = 0; q < 16; q += 2) {
+        // accumulator q holds codeword 32t + 8(q/4) + 4(lane/32) + q%4
+        const uint32_t i0 = 32u * t + 8u * (q >> 2) + (q & 3);
+        const uint32_t i1 = 32u * t + 8u * ((q + 1) >> 2) + ((q + 1) & 3);
+        best0 = min(min(best0, make_key(acc0[q], vmask, i0)), make_key(acc0[q + 1], vmask, i1));
+        best1 = min(min(best1, make_key(acc1[q], vmask, i0)), make_key(acc1[q + 1], vmask, i1));
       }
-      best0 = min(best0, tb0 | (32u * t));
-      best1 = min(best1, tb1 | (32u * t));
     }
     const uint32_t hbit = (uint32_t)(lane >> 5) << 2;
     best0 |= hbit;
     best1 |= hbit;
-    best0 = min(best0, (uint32_t)__shfl_xor(best0, 32, kWave));
-    best1 = min(best1, (uint32_t)__shfl_xor(best1, 32, kWave));
-    // column n of block 0 belongs to lane n, of block 1 to lane 32 + n
-    const uint32_t mine = lane < 32 ? best0 : best1;
+    // column n of block 0 belongs to lane n, of block 1 to lane 32 + n: one
+    // swap brings each column's other half next to it
+    uint32_t klo, khi;
+    half_swap(best0, best1, klo, khi, lane);  // klo = [b0 low, b1 low], khi = [b0 high, b1 high]
+    const uint32_t mine = min(klo, khi);
     codes[(tok_base + tok) * S + slot] = (uint8_t)(mine & 0xffu);
   }
 }

@@ -21,30 +21,64 @@ typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float h2f(uint16_t bits) { return (float)__builtin_bit_cast(half_t, bits); }
 __device__ __forceinline__ uint16_t f2h(float x) { return __builtin_bit_cast(uint16_t, (half_t)x); }
 
-// Butterfly partner exchange inside a wave.
+// Value held by lane (lane ^ M).  DPP for M = 1, 2, 8 (quad permutes and the
+// row rotation by 8 are exactly these XORs within a 16-lane row), the LDS
+// swizzle unit for 4 and 16, v_permlane32_swap for 32.
+template <int M>
+__device__ __forceinline__ float xlane(float v) {
+  const int iv = __builtin_bit_cast(int, v);
+  if constexpr (M == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, false));
+  else if constexpr (M == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, false));
+  else if constexpr (M == 4) return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x101F));
+  else if constexpr (M == 8) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, false));
+  else if constexpr (M == 16) return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x401F));
+  else {
+    static_assert(M == 32, "lane xor");
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)iv, (unsigned)iv, false, false);
+    const unsigned lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    return __builtin_bit_cast(float, lane < 32 ? r[1] : r[0]);
+  }
+}
+
+// Runtime-mask butterfly partner (any lane xor), through the LDS crossbar.
 __device__ __forceinline__ float xshfl(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
-// Sum over the `width` lanes that share lane / width (width a power of two).
+// Sum / max over the WIDTH lanes that share lane / WIDTH (WIDTH a power of two).
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < WIDTH; m <<= 1) v += xshfl(v, m);
+  if constexpr (WIDTH >= 2) v += xlane<1>(v);
+  if constexpr (WIDTH >= 4) v += xlane<2>(v);
+  if constexpr (WIDTH >= 8) v += xlane<4>(v);
+  if constexpr (WIDTH >= 16) v += xlane<8>(v);
+  if constexpr (WIDTH >= 32) v += xlane<16>(v);
+  if constexpr (WIDTH >= 64) v += xlane<32>(v);
   return v;
 }
 
 template <int WIDTH>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int m = 1; m < WIDTH; m <<= 1) v = fmaxf(v, xshfl(v, m));
+  if constexpr (WIDTH >= 2) v = fmaxf(v, xlane<1>(v));
+  if constexpr (WIDTH >= 4) v = fmaxf(v, xlane<2>(v));
+  if constexpr (WIDTH >= 8) v = fmaxf(v, xlane<4>(v));
+  if constexpr (WIDTH >= 16) v = fmaxf(v, xlane<8>(v));
+  if constexpr (WIDTH >= 32) v = fmaxf(v, xlane<16>(v));
+  if constexpr (WIDTH >= 64) v = fmaxf(v, xlane<32>(v));
   return v;
 }
 
 // Unnormalised Sylvester-order Walsh-Hadamard transform of a 128-vector held
 // E consecutive elements per lane, in 128/E consecutive lanes (element
 // c = lane_in_group * E + e).  Result u_c = sum_j (-1)^popcount(c & j) x_j.
+// Cross-lane stage with partner p: lower lane x + p, upper lane p - x.
+template <int M, int E>
+__device__ __forceinline__ void fwht_stage(float (&x)[E], int lane) {
+  const float sgn = (lane & M) ? -1.f : 1.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = fmaf(x[e], sgn, xlane<M>(x[e]));
+}
+
 template <int E>
 __device__ __forceinline__ void fwht128(float (&x)[E], int lane) {
-  // in-lane stages: element bits
 #pragma unroll
   for (int h = 1; h < E; h <<= 1) {
 #pragma unroll
@@ -56,17 +90,13 @@ __device__ __forceinline__ void fwht128(float (&x)[E], int lane) {
       }
     }
   }
-  // cross-lane stages: lane bits
   constexpr int LANES = kDim / E;
-#pragma unroll
-  for (int m = 1; m < LANES; m <<= 1) {
-    const bool upper = (lane & m) != 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float p = xshfl(x[e], m);
-      x[e] = upper ? (p - x[e]) : (x[e] + p);
-    }
-  }
+  if constexpr (LANES >= 2) fwht_stage<1>(x, lane);
+  if constexpr (LANES >= 4) fwht_stage<2>(x, lane);
+  if constexpr (LANES >= 8) fwht_stage<4>(x, lane);
+  if constexpr (LANES >= 16) fwht_stage<8>(x, lane);
+  if constexpr (LANES >= 32) fwht_stage<16>(x, lane);
+  if constexpr (LANES >= 64) fwht_stage<32>(x, lane);
 }
 
 // 1/sqrt(128)
