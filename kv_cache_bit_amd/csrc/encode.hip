@@ -109,45 +109,46 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   const int64_t tok_base = (int64_t)unit * a.cap + a.dst_tok0 + (int64_t)blk * R;
 
   // ---- codebook operands (A side), per 32-codeword tile -------------------
-  // lane l holds codeword k = 32 t + (l % 32).
-  half8_t A1[8];
-  half4_t A2[8];
-  {
+  // Built once per group into LDS (lane l of tile t holds codeword
+  // 32 t + (l % 32)) and re-read per row, which keeps ~40 VGPRs free.
+  __shared__ half8_t sA1[8][kWave];
+  __shared__ half4_t sA2[8][kWave];
+  for (int i = threadIdx.x; i < 8 * kWave; i += 256) {
+    const int t = i / kWave, l = i % kWave;
+    const int k = 32 * t + (l & 31);
     const uint16_t* cb = a.codebook;
+    float c[SUB];
+    float nrm = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int k = 32 * t + (lane & 31);
-      float c[SUB];
-      float nrm = 0.f;
-#pragma unroll
-      for (int e = 0; e < SUB; ++e) {
-        c[e] = h2f(cb[k * SUB + e]);
-        nrm = fmaf(c[e], c[e], nrm);
-      }
-      const float bsum = nrm + kDistEps;
-      const half_t b_hi = (half_t)bsum;
-      const half_t b_lo = (half_t)(bsum - (float)b_hi);
-      half8_t av;
-      if constexpr (SUB == 4) {
-        if (lane < 32) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            av[e] = (half_t)(-2.f * c[e]);
-            av[4 + e] = (half_t)(-2.f * c[e]);
-          }
-        } else {
-          av[0] = (half_t)1.f; av[1] = (half_t)1.f; av[2] = b_hi; av[3] = b_lo;
-          av[4] = (half_t)0.f; av[5] = (half_t)0.f; av[6] = (half_t)0.f; av[7] = (half_t)0.f;
-        }
-        A2[t] = half4_t{(half_t)0.f, (half_t)0.f, (half_t)0.f, (half_t)0.f};
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) av[e] = (half_t)(-2.f * c[e]);
-        A2[t] = half4_t{(half_t)1.f, (half_t)1.f, b_hi, b_lo};
-      }
-      A1[t] = av;
+    for (int e = 0; e < SUB; ++e) {
+      c[e] = h2f(cb[k * SUB + e]);
+      nrm = fmaf(c[e], c[e], nrm);
     }
+    const float bsum = nrm + kDistEps;
+    const half_t b_hi = (half_t)bsum;
+    const half_t b_lo = (half_t)(bsum - (float)b_hi);
+    half8_t av;
+    half4_t a2 = {(half_t)0.f, (half_t)0.f, (half_t)0.f, (half_t)0.f};
+    if constexpr (SUB == 4) {
+      if (l < 32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          av[e] = (half_t)(-2.f * c[e]);
+          av[4 + e] = (half_t)(-2.f * c[e]);
+        }
+      } else {
+        av[0] = (half_t)1.f; av[1] = (half_t)1.f; av[2] = b_hi; av[3] = b_lo;
+        av[4] = (half_t)0.f; av[5] = (half_t)0.f; av[6] = (half_t)0.f; av[7] = (half_t)0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) av[e] = (half_t)(-2.f * c[e]);
+      a2 = half4_t{(half_t)1.f, (half_t)1.f, b_hi, b_lo};
+    }
+    sA1[t][l] = av;
+    sA2[t][l] = a2;
   }
+  // (visible after the first __syncthreads below)
 
   // One row = this lane's sub-vector of token `tok`: raw fp16 load, then
   // y = x / n1 with n1 = ||x|| / sqrt(d).  Pass 2 recomputes this from the
@@ -292,11 +293,13 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     const float16_t zacc = {};
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      float16_t acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[t], B0, zacc, 0, 0, 0);
-      float16_t acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[t], B1, zacc, 0, 0, 0);
+      const half8_t A1t = sA1[t][lane];
+      float16_t acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1t, B0, zacc, 0, 0, 0);
+      float16_t acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1t, B1, zacc, 0, 0, 0);
       if constexpr (SUB == 8) {
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2[t], Bb0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2[t], Bb1, acc1, 0, 0, 0);
+        const half4_t A2t = sA2[t][lane];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2t, Bb0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2t, Bb1, acc1, 0, 0, 0);
       }
 #pragma unroll
       for (int q = 0; q < 16; q += 2) {
