@@ -43,6 +43,92 @@ def decode_bytes(bits: int, R: int, n_quant: int, n_resid: int, units: int, d: i
     return units * (n_quant * per_tok + n_resid * 2 * 2 * d)
 
 
+def measure_layer(nsnq, synth, workload: str, reps: int, dev):
+    """Encode and decode timing of one layer of `workload` (no CPU baseline):
+    mean HIP-event times over `reps` calls on rotating buffers."""
+    import numpy as np
+    import torch
+    w = synth.WORKLOADS[workload]
+    B, Hq, Hkv, L, d, bits, R = w["B"], w["Hq"], w["Hkv"], w["L"], w["d"], w["bits"], w["R"]
+    p = nsnq.params(bits, R)
+    s = nsnq.sub_dim(bits)
+    _, cb, _ = nsnq.nsnq_build_codebook(p, synth.randn_samples(0, 1 << 18, s).to(dev), 20)
+    k, v = synth.kv_layer(w["config_id"], 0, B, Hkv, L, d, device=dev)
+    q = synth.queries(w["config_id"], 0, B, Hq, d, device=dev)
+    nbuf = max(1, min(4, math.ceil(512e6 / (4 * k.numel()))))
+    ks = [k] + [k.clone() for _ in range(nbuf - 1)]
+    vs = [v] + [v.clone() for _ in range(nbuf - 1)]
+    r = ((L - 1) % R) + 1
+    nq = L - r
+    caches = [nsnq.KVCache(p, B, Hkv, nq + R, dev) for _ in range(nbuf)]
+    for i in range(nbuf):
+        nsnq.nsnq_encode_kv(p, cb, ks[i], vs[i], L, caches[i])
+    ws = torch.empty(nsnq.nsnq_decode_workspace_bytes(p, caches[0], Hq), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def enc(i):
+        c = caches[i % nbuf]
+        c.n_quant = c.n_resid = 0
+        nsnq.nsnq_encode_kv(p, cb, ks[i % nbuf], vs[i % nbuf], L, c, stream=stream)
+
+    def dec(i):
+        nsnq.nsnq_decode_attention(p, cb, q, caches[i % nbuf], out=out, ws=ws, stream=stream)
+
+    res = {}
+    for name, f in (("encode", enc), ("decode", dec)):
+        for i in range(3):
+            f(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            f(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / reps / 1e3
+    units = B * Hkv
+    n_vec = 2 * units * nq
+    enc_b = n_vec * encode_bytes_per_vector(bits, R, d) + 2 * units * r * 2 * d * 2
+    dec_b = decode_bytes(bits, R, nq, r, units, d)
+    del ks, vs, caches
+    return {"workload": workload, "bits": bits, "batch": B, "context": L,
+            "encode": {"us": res["encode"] * 1e6, "tokens_per_s": B * L / res["encode"],
+                       "hbm_gbs": enc_b / res["encode"] / 1e9,
+                       "hbm_frac": enc_b / res["encode"] / 1e9 / HBM_PEAK_GBS},
+            "decode": {"us": res["decode"] * 1e6, "tokens_per_s": B / res["decode"],
+                       "hbm_gbs": dec_b / res["decode"] / 1e9,
+                       "hbm_frac": dec_b / res["decode"] / 1e9 / HBM_PEAK_GBS, "bytes": dec_b}}
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """Plain device-to-device copy of `nbytes`, for scaling FETCH_SIZE /
+    WRITE_SIZE counters to bytes."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def encode_traffic(kernel_file: str):
+    """HBM bytes per encode launch from the committed rocprofv3 counter
+    summary, or None when the kernel source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "encode_kernel_llama2-7b-layer-b1-2bit_traffic.json")
+    try:
+        rec = json.load(open(path))
+        src = open(kernel_file, "rb").read()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def cpu_baseline(w: dict, cb_bits, k, v, q, heads: int):
     """Time the CPU oracle on `heads` of the layer's KV heads (encode of those
     heads' K and V, then their decode step); scale to the whole layer."""
@@ -75,7 +161,12 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=4, help="KV heads in the CPU-baseline sample (0: skip)")
     ap.add_argument("--codebook-iters", type=int, default=50)
     ap.add_argument("--no-fp16", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 1-bit layer measurement")
+    ap.add_argument("--copy-bytes", type=int, default=0, help="only run a device copy of this size")
     args = ap.parse_args()
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes, max(args.steps, 1))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(this path has no multi-GPU code).", file=sys.stderr)
@@ -201,11 +292,15 @@ def main():
                      "final_mse_per_elem": float(dist[-1].item())},
         "roofline": {"kernel": "encode_kernel", "bound": "alu", "achieved": enc_alu_tops,
                      "peak": VALU_PEAK_TOPS, "unit": "Tops/s", "frac": enc_alu_tops / VALU_PEAK_TOPS,
-                     "traffic": None,
+                     "traffic": encode_traffic(os.path.join(ROOT, "kv_cache_bit_amd", "csrc", "encode.hip")),
                      "note": "achieved = argmin candidate distances per second (one 32-bit compare each)"},
         "timing": {"step_ms_median": float(np.median(step_ms)), "step_ms_p10": float(np.percentile(step_ms, 10)),
                    "step_ms_p90": float(np.percentile(step_ms, 90)), "buffer_sets": nbuf},
     }
+    if not args.no_extra and args.workload != "llama2-7b-layer-b16-1bit":
+        del ks, vs, caches
+        torch.cuda.empty_cache()
+        res["one_bit"] = measure_layer(nsnq, synth, "llama2-7b-layer-b16-1bit", 10, dev)
     if args.cpu_heads > 0:
         cb_bits = codebook.cpu().numpy().view(np.uint16)
         cb_ = cpu_baseline(w, cb_bits, k, v, q, min(args.cpu_heads, Hkv))

@@ -151,12 +151,17 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   // (visible after the first __syncthreads below)
 
   // One row = this lane's sub-vector of token `tok`: raw fp16 load, then
-  // y = x / n1 with n1 = ||x|| / sqrt(d).  Pass 2 recomputes this from the
-  // (L2-resident) input instead of keeping R x 128 floats alive.
+  // y = x / n1 with n1 = ||x|| / sqrt(d).  Pass 1 reads the block from HBM
+  // once and keeps the raw fp16 rows in LDS; pass 2 recomputes y from there
+  // instead of keeping R x 128 floats in registers.
   using raw_t = typename std::conditional<SUB == 4, uint2, uint4>::type;
+  __shared__ raw_t xs[R * S];  // [token][slot], R x 256 bytes
   auto load_raw = [&](int tok) -> raw_t {
-    return *reinterpret_cast<const raw_t*>(src + (int64_t)tok * a.st + slot * SUB);
+    const raw_t v = *reinterpret_cast<const raw_t*>(src + (int64_t)tok * a.st + slot * SUB);
+    xs[tok * S + slot] = v;
+    return v;
   };
+  auto lds_raw = [&](int tok) -> raw_t { return xs[tok * S + slot]; };
   auto norm_raw = [&](const raw_t& raw, float (&y)[SUB], float& n1) {
     float v[SUB];
     v[0] = h2f(raw.x & 0xffff); v[1] = h2f(raw.x >> 16);
@@ -214,14 +219,11 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   uint16_t* scales = a.scales[kv];
 
   // ---- pass 2: per row: shift, second normalisation, Hadamard, VQ ---------
-  raw_t nxt = load_raw(wave * TPW + tir);
 #pragma unroll 1
   for (int r = 0; r < ROWS; ++r) {
     const int tok = wave * TPW + r * TPR + tir;
-    const raw_t cur = nxt;
-    if (r + 1 < ROWS) nxt = load_raw(tok + TPR);  // prefetch the next row
     float u[SUB], n1;
-    norm_raw(cur, u, n1);
+    norm_raw(lds_raw(tok), u, n1);
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) {
