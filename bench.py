@@ -101,6 +101,96 @@ def measure_layer(nsnq, synth, workload: str, reps: int, dev):
                        "hbm_frac": dec_b / res["decode"] / 1e9 / HBM_PEAK_GBS, "bytes": dec_b}}
 
 
+def decode_step_bench(nsnq, synth, workload: str, steps: int, dev, distinct_layers: int = 2):
+    """Whole-model decode step (every layer's decode attention, one new token
+    per sequence) on a multi-layer workload, against the fp16-cache comparator
+    at the largest batch whose fp16 cache fits the same HBM budget.
+
+    Setup encodes `distinct_layers` layers from the generator and copies their
+    compressed caches to the remaining layers, so every layer has its own
+    buffers (no cache reuse across layers) without generating hundreds of GB
+    of fp16 input.  The fp16 side holds two layers' caches and alternates
+    between them across the layer loop (each is far larger than the 256 MB
+    Infinity Cache)."""
+    import numpy as np
+    import torch
+    w = synth.WORKLOADS[workload]
+    NL, B, Hq, Hkv, L, d, bits, R = (w["layers"], w["B"], w["Hq"], w["Hkv"], w["L"], w["d"], w["bits"], w["R"])
+    p = nsnq.params(bits, R)
+    s = nsnq.sub_dim(bits)
+    _, cb, _ = nsnq.nsnq_build_codebook(p, synth.randn_samples(0, 1 << 20, s).to(dev), 50)
+    r = ((L - 1) % R) + 1
+    nq = L - r
+    caches, qs = [], []
+    for layer in range(NL):
+        c = nsnq.KVCache(p, B, Hkv, nq + R, dev)
+        if layer < distinct_layers:
+            k, v = synth.kv_layer(w["config_id"], layer, B, Hkv, L, d,
+                                  outlier_std=synth.outlier_std_for(workload, layer), device=dev)
+            nsnq.nsnq_encode_kv(p, cb, k, v, L, c)
+            del k, v
+        else:
+            src = caches[layer % distinct_layers]
+            for dst_h, src_h in ((c.k, src.k), (c.v, src.v)):
+                for name in ("codes", "scales", "mu", "resid"):
+                    getattr(dst_h, name).copy_(getattr(src_h, name))
+            c.n_quant, c.n_resid = src.n_quant, src.n_resid
+        caches.append(c)
+        qs.append(synth.queries(w["config_id"], layer, B, Hq, d, device=dev))
+    torch.cuda.synchronize()
+    ws = torch.empty(nsnq.nsnq_decode_workspace_bytes(p, caches[0], Hq), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(q) for q in qs]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for layer in range(NL):
+            nsnq.nsnq_decode_attention(p, cb, qs[layer], caches[layer], out=outs[layer], ws=ws, stream=stream)
+
+    def timed(f, n):
+        for _ in range(2):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n / 1e3
+
+    t_c = timed(step, steps)
+    cache_bytes = sum(c.nbytes() for c in caches)
+    dec_b = NL * decode_bytes(bits, R, nq, r, B * Hkv, d)
+    del caches
+    torch.cuda.empty_cache()
+    # fp16 comparator: largest batch whose fp16 K/V for all layers fits the budget
+    free, total = torch.cuda.mem_get_info()
+    budget = free - 8e9
+    per_seq = NL * 2 * Hkv * L * d * 2
+    B16 = int(max(1, min(B, budget // per_seq)))
+    kf = [torch.randn(B16, Hkv, L, d, device=dev, dtype=torch.float16) for _ in range(2)]
+    vf = [torch.randn(B16, Hkv, L, d, device=dev, dtype=torch.float16) for _ in range(2)]
+    q16 = qs[0][:B16].contiguous()
+    ws16 = torch.empty(nsnq.nsnq_fp16_decode_workspace_bytes(B16, Hq, L), dtype=torch.uint8, device=dev)
+    o16 = torch.empty_like(q16)
+
+    def step16():
+        for layer in range(NL):
+            nsnq.nsnq_fp16_decode_attention(q16, kf[layer % 2], vf[layer % 2], out=o16, ws=ws16, stream=stream)
+
+    t_16 = timed(step16, steps)
+    b16 = NL * B16 * Hkv * L * 2 * 2 * d
+    return {"metric": "decode-attn tokens/s", "workload": workload, "layers": NL, "batch": B, "context": L,
+            "bits": bits, "step_ms": t_c * 1e3, "tokens_per_s": B / t_c,
+            "hbm_gbs": dec_b / t_c / 1e9, "hbm_frac": dec_b / t_c / 1e9 / HBM_PEAK_GBS,
+            "compressed_cache_gb": cache_bytes / 1e9,
+            "fp16": {"batch": B16, "step_ms": t_16 * 1e3, "tokens_per_s": B16 / t_16,
+                     "hbm_gbs": b16 / t_16 / 1e9, "cache_gb": per_seq * B16 / 1e9,
+                     "budget_gb": budget / 1e9},
+            "gain_tokens_per_s": (B / t_c) / (B16 / t_16),
+            "setup": f"{distinct_layers} distinct layers encoded, caches copied to the other {NL - distinct_layers}"}
+
+
 def copy_calibration(nbytes: int, reps: int):
     """Plain device-to-device copy of `nbytes`, for scaling FETCH_SIZE /
     WRITE_SIZE counters to bytes."""
@@ -181,7 +271,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = dict(synth.WORKLOADS[args.workload])
-    assert w["layers"] == 1, "multi-layer workloads: not in this bench yet"
+    if w["layers"] > 1:
+        print(json.dumps(decode_step_bench(nsnq, synth, args.workload, max(args.steps // 5, 3), dev)), flush=True)
+        return
     B, Hq, Hkv, L, d, bits, R = w["B"], w["Hq"], w["Hkv"], w["L"], w["d"], w["bits"], w["R"]
     s = nsnq.sub_dim(bits)
     p = nsnq.params(bits, R)

@@ -226,3 +226,41 @@ def test_llama2_layer_1bit_b16_sampled(oracle_codebooks):
         evi = {key: (val[i:i + 1, None] if isinstance(val, np.ndarray) else val) for key, val in ev.items()}
         ref = oracle.reference_decode(q[b:b + 1, h:h + 1].cpu(), eki, evi, ek["n_quant"], ek["n_resid"], R, cb)
         check_attention(o[b:b + 1, h:h + 1], ref)
+
+
+def _sampled_layer_check(cb, w, layer, units, outlier):
+    """Encode and attend one whole layer on the GPU (the bench's launch
+    configuration), then check sampled (b, kv-head) streams and their query
+    heads against the oracle."""
+    B, Hq, Hkv, L, R, bits = w["B"], w["Hq"], w["Hkv"], w["L"], w["R"], w["bits"]
+    G = Hq // Hkv
+    k, v = synth.kv_layer(w["config_id"], layer, B, Hkv, L, D, outlier_std=outlier, device=DEV)
+    p, cbt, cache = gpu_encode(k, v, bits, R, cb)
+    q = synth.queries(w["config_id"], layer, B, Hq, D, device=DEV)
+    o = nsnq.nsnq_decode_attention(p, cbt, q, cache).float().cpu().numpy()
+    ks = torch.stack([k[b, h] for b, h in units]).cpu()
+    vs = torch.stack([v[b, h] for b, h in units]).cpu()
+    del k, v
+    ek, ev = oracle.encode(ks, R, cb), oracle.encode(vs, R, cb)
+    compare_encoded(cache, ek, ev, units=units)
+    for i, (b, h) in enumerate(units):
+        eki = {key: (val[i:i + 1, None] if isinstance(val, np.ndarray) else val) for key, val in ek.items()}
+        evi = {key: (val[i:i + 1, None] if isinstance(val, np.ndarray) else val) for key, val in ev.items()}
+        qh = q[b:b + 1, h * G:(h + 1) * G].cpu()
+        ref = oracle.reference_decode(qh, eki, evi, ek["n_quant"], ek["n_resid"], R, cb)
+        check_attention(o[b:b + 1, h * G:(h + 1) * G], ref)
+
+
+def test_llama31_gqa_32k_layer0_sampled(oracle_codebooks):
+    """LLaMA-3.1-8B shape, layer 0 (30x outlier channels): batch 4, 32768
+    tokens, 32 query heads over 8 KV heads (G = 4)."""
+    w = synth.WORKLOADS["llama3.1-8b-gqa-b4-32k-2bit"]
+    _sampled_layer_check(oracle_codebooks[2], w, 0, [(0, 0), (3, 7)],
+                         synth.outlier_std_for("llama3.1-8b-gqa-b4-32k-2bit", 0))
+
+
+def test_llama2_b256_layer_sampled(oracle_codebooks):
+    """Batch-256 LLaMA-2-7B layer (the batch-scaling workload): the whole
+    layer on the GPU, sampled streams against the oracle."""
+    w = synth.WORKLOADS["llama2-7b-b256-2bit"]
+    _sampled_layer_check(oracle_codebooks[2], w, 5, [(0, 0), (131, 16), (255, 31)], 10.0)
