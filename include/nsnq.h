@@ -10,7 +10,8 @@
  *   2. subtracting the channel-wise mean mu of the block of R tokens being
  *      quantised;
  *   3. a second token-wise normalisation, keeping n2;
- *   4. an orthonormal (Sylvester, not randomised) Hadamard rotation;
+ *   4. an orthonormal Hadamard rotation (Sylvester order; optionally
+ *      randomised by a sign vector, see nsnq_params);
  *   5. vector quantisation of each run of s consecutive elements against one
  *      256-word codebook fit by k-means on seeded standard-normal samples;
  * while the most recent tokens stay in an fp16 residual window of R tokens.
@@ -48,7 +49,7 @@
 extern "C" {
 #endif
 
-#define NSNQ_ABI_VERSION 1
+#define NSNQ_ABI_VERSION 2
 
 typedef int32_t nsnq_status;
 enum {
@@ -59,14 +60,33 @@ enum {
   NSNQ_EWORKSPACE = 4    /* workspace missing or too small */
 };
 
+/* Format flags. */
+enum {
+  /* Scale adjustment "Strategy 3" (technical summary sec. 3, Scale
+   * Adjustment): the quantised head vector c_hat is scaled by
+   * alpha = |u|^2 / (u . c_hat) so that its component along the Hadamard-
+   * domain vector u is preserved (the error is orthogonal to u).  alpha is
+   * folded into the stored n2, so dequantisation and attention are unchanged. */
+  NSNQ_SCALE_ADJUST = 1
+};
+
 /* Format parameters.  head_dim must be 128, bits 1 or 2 (sub-vectors of 8 or 4
  * elements, one uint8 code each), n_codewords 256, block_tokens (R, the size of
- * both the residual window and the mean block) 64 or 128. */
+ * both the residual window and the mean block) 64 or 128.
+ *   flags           NSNQ_* flags above (0 = the plain pipeline).
+ *   hadamard_signs  NULL for the plain (Sylvester) Hadamard transform, or a
+ *                   device array of head_dim int8 values +1/-1: the randomised
+ *                   Hadamard transform u = H diag(signs) w (technical summary
+ *                   sec. 2).  Encode, dequant and attention of one cache must
+ *                   use the same signs. */
 typedef struct {
   int32_t head_dim;
   int32_t bits;
   int32_t n_codewords;
   int32_t block_tokens;
+  int32_t flags;
+  int32_t reserved; /* must be 0 */
+  const int8_t* hadamard_signs;
 } nsnq_params;
 
 /* One of the K or V halves of a cache (layouts above). */
@@ -94,7 +114,7 @@ int32_t nsnq_abi_version(void);
 const char* nsnq_status_str(nsnq_status st);
 
 /* Fit the codebook with Lloyd's k-means (technical summary sec. 3, "Codebook
- * Constructie": k-means on synthetic torch.randn data, once, for any model).
+ * Construction": k-means on synthetic torch.randn data, once, for any model).
  *   samples      fp32 [n][s] training vectors, s = 4 (bits 2) or 8 (bits 1);
  *                n >= n_codewords.
  *   init         fp32 [256][s] initial centroids, or NULL for the first 256
@@ -136,7 +156,8 @@ nsnq_status nsnq_flush_residual(const nsnq_params* p, const uint16_t* codebook, 
                                 void* stream);
 
 /* Reconstruct quantised tokens [tok0, tok0 + ntok) of the K (which = 0) or V
- * (which = 1) half: x_hat = N1 * (N2 * H c_hat + MU_block), the inverse of the
+ * (which = 1) half: x_hat = N1 * (N2 * D H c_hat + MU_block), D = diag(signs)
+ * (identity without signs), the inverse of the
  * encode using only stored values (technical summary sec. 1: the byproducts
  * rebuild the tensor; sec. 4: dequantisation kernel).  Requires
  * 0 <= tok0, tok0 + ntok <= n_quant.  out: [batch][kv_heads][ntok][d] as fp32

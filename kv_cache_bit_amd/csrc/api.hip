@@ -22,6 +22,7 @@ nsnq_status check_params(const nsnq_params* p) {
   if (p->n_codewords != 256 || p->head_dim <= 0 || p->block_tokens <= 0) return NSNQ_EINVAL;
   if (p->head_dim != 128) return NSNQ_EUNSUPPORTED;
   if (p->block_tokens != 64 && p->block_tokens != 128) return NSNQ_EUNSUPPORTED;
+  if ((p->flags & ~NSNQ_SCALE_ADJUST) != 0 || p->reserved != 0) return NSNQ_EINVAL;
   return NSNQ_OK;
 }
 
@@ -78,6 +79,8 @@ nsnq_status run_encode(const nsnq_params* p, const uint16_t* cb, const uint16_t*
   a.R = p->block_tokens;
   a.rc_t0 = rc_t0;
   a.rc_r = rc_r;
+  a.signs = p->hadamard_signs;
+  a.scale_adjust = (p->flags & NSNQ_SCALE_ADJUST) ? 1 : 0;
   return hip_status(launch_encode(a, sub_of(p), p->block_tokens, stream));
 }
 
@@ -202,6 +205,7 @@ nsnq_status nsnq_dequant(const nsnq_params* p, const uint16_t* codebook, const n
   a.tok0 = tok0;
   a.ntok = ntok;
   a.out_f16 = out_dtype;
+  a.signs = p->hadamard_signs;
   return hip_status(launch_dequant(a, sub_of(p), cache->batch * cache->kv_heads, (hipStream_t)stream));
 }
 
@@ -299,6 +303,7 @@ nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook
   a.nsplit_q = pl.nsplit_q;
   a.nsplit = pl.nsplit;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.signs = p->hadamard_signs;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = launch_decode(a, sub_of(p), pl.gh, cache->batch, pl.lds, st);
   if (e != hipSuccess) return NSNQ_EHIP;

@@ -6,7 +6,7 @@
 namespace nsnq {
 
 // ---------------------------------------------------------------------------
-// Dequant: x_hat = N1 * (N2 * H c_hat + MU_block).  Same lane layout as the
+// Dequant: x_hat = N1 * (N2 * D H c_hat + MU_block), D = diag(signs).  Same lane layout as the
 // encoder (one sub-vector per lane, S lanes per token); the Hadamard inverse is
 // the forward transform (H symmetric, orthonormal).  64 tokens per group.
 template <int SUB>
@@ -36,7 +36,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
     fwht128<SUB>(x, lane);
     const uint16_t* mp = a.mu + ((int64_t)unit * (a.cap / a.R) + t / a.R) * kDim + slot * SUB;
 #pragma unroll
-    for (int e = 0; e < SUB; ++e) x[e] = n1 * fmaf(n2, x[e] * kInvSqrtD, h2f(mp[e]));
+    for (int e = 0; e < SUB; ++e) {
+      const float sg = a.signs ? (float)a.signs[slot * SUB + e] : 1.f;
+      x[e] = n1 * fmaf(n2, x[e] * (kInvSqrtD * sg), h2f(mp[e]));
+    }
     if (act) {
       const int64_t o = ((int64_t)unit * a.ntok + i) * kDim + slot * SUB;
       if (a.out_f16) {

@@ -256,9 +256,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
   for (int i = tid; i < kCodewords * SUB; i += 256) cbh[i] = a.codebook[i];
   __syncthreads();
-  // rotate the queries (one wave per head)
+  // rotate the queries (one wave per head): q' = H D q
+  const float sg0 = a.signs ? (float)a.signs[2 * lane] : 1.f;
+  const float sg1 = a.signs ? (float)a.signs[2 * lane + 1] : 1.f;
   if (wave < GH) {
-    float x[2] = {qf[wave * kDim + 2 * lane], qf[wave * kDim + 2 * lane + 1]};
+    float x[2] = {qf[wave * kDim + 2 * lane] * sg0, qf[wave * kDim + 2 * lane + 1] * sg1};
     fwht128<2>(x, lane);
     qr[wave * kDim + 2 * lane] = x[0] * kInvSqrtD;
     qr[wave * kDim + 2 * lane + 1] = x[1] * kInvSqrtD;
@@ -412,8 +414,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
     fwht128<2>(x, lane);
     float* wo = ws_base + g * ws_head;
-    wo[2 * lane] = fmaf(x[0], kInvSqrtD, om[0]);
-    wo[2 * lane + 1] = fmaf(x[1], kInvSqrtD, om[1]);
+    wo[2 * lane] = fmaf(x[0], kInvSqrtD * sg0, om[0]);
+    wo[2 * lane + 1] = fmaf(x[1], kInvSqrtD * sg1, om[1]);
     if (lane == 0) {
       wo[kDim] = M;
       wo[kDim + 1] = lsum;

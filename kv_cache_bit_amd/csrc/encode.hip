@@ -217,6 +217,10 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
 
   uint8_t* codes = a.codes[kv];
   uint16_t* scales = a.scales[kv];
+  // randomised Hadamard: u = H diag(s) w
+  float sgn[SUB];
+#pragma unroll
+  for (int e = 0; e < SUB; ++e) sgn[e] = a.signs ? (float)a.signs[slot * SUB + e] : 1.f;
 
   // ---- pass 2: per row: shift, second normalisation, Hadamard, VQ ---------
 #pragma unroll 1
@@ -236,17 +240,12 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     const float rs2 = __builtin_amdgcn_rsqf(ss);
     const bool live = ss >= kN2Floor * kN2Floor;
     const float inv2 = live ? rs2 : 0.f;
-    const half_t n2h = (half_t)(ss * inv2);
+    const float n2 = ss * inv2;
 #pragma unroll
-    for (int e = 0; e < SUB; ++e) u[e] *= inv2;
+    for (int e = 0; e < SUB; ++e) u[e] *= inv2 * sgn[e];
     fwht128<SUB>(u, lane);
 #pragma unroll
     for (int e = 0; e < SUB; ++e) u[e] *= kInvSqrtD;
-
-    if (slot == 0) {
-      const uint32_t pk = pack_h2((half_t)n1, n2h);
-      *reinterpret_cast<uint32_t*>(scales + (tok_base + tok) * 2) = pk;
-    }
 
     // hi/lo split and squared norm of this lane's sub-vector
     half_t hi[SUB], lo[SUB];
@@ -320,7 +319,25 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     uint32_t klo, khi;
     half_swap(best0, best1, klo, khi, lane);  // klo = [b0 low, b1 low], khi = [b0 high, b1 high]
     const uint32_t mine = min(klo, khi);
-    codes[(tok_base + tok) * S + slot] = (uint8_t)(mine & 0xffu);
+    const uint32_t code = mine & 0xffu;
+    codes[(tok_base + tok) * S + slot] = (uint8_t)code;
+    // Strategy-3 scale: alpha = |u|^2 / (u . c_hat), folded into n2
+    float n2s = n2;
+    if (a.scale_adjust) {
+      // the codeword from the MFMA operand tiles: lanes < 32 of tile code/32
+      // hold -2 c (exact in fp16)
+      const half8_t cw = sA1[code >> 5][code & 31];
+      float uc = 0.f;
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) uc = fmaf(u[e], -0.5f * (float)cw[e], uc);
+      uc = group_sum<S>(uc);
+      const float utot = group_sum<S>(uu);
+      if (uc > 0.f) n2s = n2 * (utot / uc);
+    }
+    if (slot == 0) {
+      const uint32_t pk = pack_h2((half_t)n1, (half_t)n2s);
+      *reinterpret_cast<uint32_t*>(scales + (tok_base + tok) * 2) = pk;
+    }
   }
 }
 

@@ -21,6 +21,8 @@ struct EncodeArgs {
   int nblk;                  // blocks per stream
   int R;                     // block / window size
   int rc_t0, rc_r;           // residual copy: first source token and count (0 = none)
+  const int8_t* signs;       // randomised-Hadamard signs [128] or null
+  int scale_adjust;          // fold alpha = |u|^2 / (u . c_hat) into n2
 };
 
 struct DequantArgs {
@@ -30,6 +32,7 @@ struct DequantArgs {
   const uint16_t* codebook;
   void* out;
   int H, cap, R, tok0, ntok, out_f16;
+  const int8_t* signs;
 };
 
 struct DecodeArgs {
@@ -51,6 +54,7 @@ struct DecodeArgs {
   int nsplit_q;      // splits over the compressed tokens
   int nsplit;        // nsplit_q + (n_resid > 0)
   float scale_log2;  // softmax scale * log2(e)
+  const int8_t* signs;  // randomised-Hadamard signs [128] or null
 };
 
 struct CombineArgs {

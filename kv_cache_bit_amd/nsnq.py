@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnsnq.so")
 
 NSNQ_OK, NSNQ_EINVAL, NSNQ_EUNSUPPORTED, NSNQ_EHIP, NSNQ_EWORKSPACE = range(5)
+NSNQ_SCALE_ADJUST = 1
 
 i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 P = ctypes.c_void_p
@@ -25,7 +26,8 @@ size_t = ctypes.c_size_t
 
 
 class nsnq_params(ctypes.Structure):
-    _fields_ = [("head_dim", i32), ("bits", i32), ("n_codewords", i32), ("block_tokens", i32)]
+    _fields_ = [("head_dim", i32), ("bits", i32), ("n_codewords", i32), ("block_tokens", i32),
+                ("flags", i32), ("reserved", i32), ("hadamard_signs", P)]
 
 
 class nsnq_kv(ctypes.Structure):
@@ -100,8 +102,15 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
-def params(bits: int, block_tokens: int, head_dim: int = 128, n_codewords: int = 256) -> nsnq_params:
-    return nsnq_params(head_dim, bits, n_codewords, block_tokens)
+def params(bits: int, block_tokens: int, head_dim: int = 128, n_codewords: int = 256, flags: int = 0,
+           signs: torch.Tensor | None = None) -> nsnq_params:
+    """Format parameters.  `signs`: device int8 [head_dim] of +-1 for the
+    randomised Hadamard transform (kept referenced by the returned struct)."""
+    p = nsnq_params(head_dim, bits, n_codewords, block_tokens, flags, 0, _ptr(signs))
+    if signs is not None:
+        assert signs.dtype == torch.int8 and signs.is_contiguous() and signs.numel() == head_dim
+        p._signs_ref = signs
+    return p
 
 
 def sub_dim(bits: int) -> int:

@@ -109,3 +109,9 @@ def outlier_std_for(workload: str, layer: int) -> float:
     if workload.startswith("llama3.1") and layer < 2:
         return 30.0
     return 10.0
+
+
+def hadamard_signs(seed: int, d: int = 128) -> torch.Tensor:
+    """+-1 int8 [d] for the randomised Hadamard transform (fair coin per channel)."""
+    g = _gen(seed, "cpu")
+    return (torch.randint(0, 2, (d,), generator=g, dtype=torch.int8) * 2 - 1).to(torch.int8)

@@ -48,8 +48,8 @@ def lib():
             "orc_nsn_block": (None, [P, i32, i32, P, P, P, P, P, P]),
             "orc_vq": (i32, [P, i32, P, i32, P, P]),
             "orc_resid_count": (i32, [i32, i32]),
-            "orc_encode": (i32, [P, i64, i32, i32, i32, i32, P, i32, P, P, P, P, P, P]),
-            "orc_dequant": (None, [P, P, P, i64, i32, i32, i32, i32, i32, i32, P, P]),
+            "orc_encode": (i32, [P, i64, i32, i32, i32, i32, P, i32, P, i32, P, P, P, P, P, P]),
+            "orc_dequant": (None, [P, P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P]),
             "orc_attention": (None, [P, i32, i32, i32, i32, P, P, i32, f64, P]),
             "orc_kmeans": (None, [P, i64, i32, i32, i32, P, P, P, P]),
             "orc_num_threads": (i32, []),
@@ -129,8 +129,18 @@ def resid_count(L: int, R: int) -> int:
     return lib().orc_resid_count(L, R)
 
 
-def encode(x, R: int, codebook, with_u: bool = False) -> dict:
+def _signs(signs):
+    if signs is None:
+        return None
+    if hasattr(signs, "detach"):
+        signs = signs.detach().cpu().numpy()
+    return np.ascontiguousarray(signs, dtype=np.float64)
+
+
+def encode(x, R: int, codebook, with_u: bool = False, signs=None, scale_adjust: bool = False) -> dict:
     """Encode streams x fp16 [..., L, d] (leading dims are independent units).
+    signs: +-1 [d] for the randomised Hadamard transform (None: plain);
+    scale_adjust: Strategy-3 scale folded into n2.
 
     Returns codes [..., nq, S] uint8, scales [..., nq, 2] (fp16 bits),
     mu [..., nq/R, d] (fp16 bits), resid [..., R, d] (fp16 bits, rows >= r
@@ -149,8 +159,10 @@ def encode(x, R: int, codebook, with_u: bool = False) -> dict:
     resid = np.zeros((n_units, R, d), np.uint16)
     gap = np.zeros((n_units, nq, S), np.float64)
     u = np.zeros((n_units, nq, d), np.float64) if with_u else None
-    lib().orc_encode(_p(xb), n_units, L, d, R, s, _p(cb), ncw, _p(codes), _p(scales), _p(mu),
-                     _p(resid), _p(gap), _p(u) if with_u else None)
+    sg = _signs(signs)
+    lib().orc_encode(_p(xb), n_units, L, d, R, s, _p(cb), ncw, _p(sg) if sg is not None else None,
+                     int(scale_adjust), _p(codes), _p(scales), _p(mu), _p(resid), _p(gap),
+                     _p(u) if with_u else None)
     out = dict(codes=codes.reshape(*lead, nq, S), scales=scales.reshape(*lead, nq, 2),
                mu=mu.reshape(*lead, nq // R, d), resid=resid.reshape(*lead, R, d),
                gap=gap.reshape(*lead, nq, S), n_quant=nq, n_resid=r)
@@ -159,7 +171,8 @@ def encode(x, R: int, codebook, with_u: bool = False) -> dict:
     return out
 
 
-def dequant(codes, scales, mu, R: int, codebook, tok0: int = 0, ntok: int | None = None) -> np.ndarray:
+def dequant(codes, scales, mu, R: int, codebook, tok0: int = 0, ntok: int | None = None,
+            signs=None) -> np.ndarray:
     """Reconstruct tokens [tok0, tok0+ntok) of streams with codes [..., cap, S],
     scales [..., cap, 2] (fp16 bits), mu [..., cap/R, d] (fp16 bits)."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
@@ -174,7 +187,9 @@ def dequant(codes, scales, mu, R: int, codebook, tok0: int = 0, ntok: int | None
     if ntok is None:
         ntok = cap - tok0
     out = np.empty((n_units, ntok, d), np.float64)
-    lib().orc_dequant(_p(codes), _p(scales), _p(mu), n_units, cap, tok0, ntok, d, R, s, _p(cb), _p(out))
+    sg = _signs(signs)
+    lib().orc_dequant(_p(codes), _p(scales), _p(mu), n_units, cap, tok0, ntok, d, R, s, _p(cb),
+                      _p(sg) if sg is not None else None, _p(out))
     return out.reshape(*lead, ntok, d)
 
 
@@ -211,7 +226,7 @@ def num_threads() -> int:
 
 
 def reference_decode(q, k_cache: dict, v_cache: dict, n_quant: int, n_resid: int,
-                     R: int, codebook, scale: float | None = None) -> np.ndarray:
+                     R: int, codebook, scale: float | None = None, signs=None) -> np.ndarray:
     """Attention over a compressed cache, by its plain definition: reconstruct
     the n_quant quantised tokens, append the n_resid fp16 residual tokens, and
     run textbook softmax attention.  Caches are dicts with codes [B,H,cap,S],
@@ -222,8 +237,10 @@ def reference_decode(q, k_cache: dict, v_cache: dict, n_quant: int, n_resid: int
         scale = 1.0 / np.sqrt(d)
     parts_k, parts_v = [], []
     if n_quant > 0:
-        parts_k.append(dequant(k_cache["codes"], k_cache["scales"], k_cache["mu"], R, codebook, 0, n_quant))
-        parts_v.append(dequant(v_cache["codes"], v_cache["scales"], v_cache["mu"], R, codebook, 0, n_quant))
+        parts_k.append(dequant(k_cache["codes"], k_cache["scales"], k_cache["mu"], R, codebook, 0, n_quant,
+                               signs=signs))
+        parts_v.append(dequant(v_cache["codes"], v_cache["scales"], v_cache["mu"], R, codebook, 0, n_quant,
+                               signs=signs))
     if n_resid > 0:
         parts_k.append(f16_to_f64(as_f16_bits(k_cache["resid"])[..., :n_resid, :]))
         parts_v.append(f16_to_f64(as_f16_bits(v_cache["resid"])[..., :n_resid, :]))

@@ -242,9 +242,15 @@ int orc_resid_count(int L, int R) {
  *   gap    [nq][d/s]  relative best/second gap (may be NULL)
  *   u_out  [nq][d]    Hadamard output, before VQ (may be NULL)
  * and resid [R][d] fp16: the last r tokens, verbatim (rows >= r untouched).
+ * signs: NULL for the plain Hadamard transform, or d values +1/-1 for the
+ * randomised transform u = H diag(signs) w ([P3 sec. 2]).
+ * scale_adjust: scale adjustment "Strategy 3" ([P3 sec. 3]): the quantised
+ * vector c_hat (all slots' codewords) is scaled by alpha = |u|^2 / (u . c_hat)
+ * so that its component along u equals u; alpha multiplies the stored n2
+ * (alpha = 1 when u . c_hat <= 0).
  * Returns nq. */
 int orc_encode_unit(const uint16_t* x, int L, int d, int R, int s,
-                    const uint16_t* cb, int ncw,
+                    const uint16_t* cb, int ncw, const double* signs, int scale_adjust,
                     uint8_t* codes, uint16_t* scales, uint16_t* mu_st,
                     uint16_t* resid, double* gap, double* u_out) {
   int r = orc_resid_count(L, R);
@@ -257,6 +263,7 @@ int orc_encode_unit(const uint16_t* x, int L, int d, int R, int s,
   double* u = (double*)malloc(sizeof(double) * d);
   double* Hm = (double*)malloc(sizeof(double) * (size_t)d * d);
   double* cbd = (double*)malloc(sizeof(double) * (size_t)ncw * s);
+  double* ws = (double*)malloc(sizeof(double) * d);
   orc_hadamard_matrix(d, Hm);
   for (size_t e = 0; e < (size_t)ncw * s; ++e) cbd[e] = orc_h2d(cb[e]);
   for (int blk = 0; blk < nq / R; ++blk) {
@@ -265,21 +272,29 @@ int orc_encode_unit(const uint16_t* x, int L, int d, int R, int s,
     for (int c = 0; c < d; ++c) mu_st[(size_t)blk * d + c] = orc_d2h(mu[c]);
     for (int t = 0; t < R; ++t) {
       size_t tok = (size_t)blk * R + t;
-      scales[tok * 2 + 0] = orc_d2h(n1[t]);
-      scales[tok * 2 + 1] = orc_d2h(n2[t]);
-      matvec(Hm, w + (size_t)t * d, u, d);
+      for (int c = 0; c < d; ++c) ws[c] = w[(size_t)t * d + c] * (signs ? signs[c] : 1.0);
+      matvec(Hm, ws, u, d);
       if (u_out) memcpy(u_out + tok * d, u, sizeof(double) * d);
+      double uu = 0.0, uc = 0.0;
       for (int j = 0; j < S; ++j) {
         double g;
         int code = vq_dbl(u + (size_t)j * s, s, cbd, ncw, NULL, &g);
         codes[tok * S + j] = (uint8_t)code;
         if (gap) gap[tok * S + j] = g;
+        for (int e = 0; e < s; ++e) {
+          uu += u[j * s + e] * u[j * s + e];
+          uc += u[j * s + e] * cbd[(size_t)code * s + e];
+        }
       }
+      double alpha = 1.0;
+      if (scale_adjust && uc > 0.0) alpha = uu / uc;
+      scales[tok * 2 + 0] = orc_d2h(n1[t]);
+      scales[tok * 2 + 1] = orc_d2h(n2[t] * alpha);
     }
   }
   for (int t = 0; t < r; ++t)
     memcpy(resid + (size_t)t * d, x + (size_t)(nq + t) * d, sizeof(uint16_t) * d);
-  free(n1); free(n2); free(mu); free(w); free(u); free(Hm); free(cbd);
+  free(n1); free(n2); free(mu); free(w); free(u); free(Hm); free(cbd); free(ws);
   return nq;
 }
 
@@ -288,7 +303,7 @@ int orc_encode_unit(const uint16_t* x, int L, int d, int R, int s,
  * (codes/scales/gap/u sized for nq = L - r tokens per unit, mu for nq/R
  * blocks, resid for R rows).  OpenMP over units only. */
 int orc_encode(const uint16_t* x, int64_t n_units, int L, int d, int R, int s,
-               const uint16_t* cb, int ncw,
+               const uint16_t* cb, int ncw, const double* signs, int scale_adjust,
                uint8_t* codes, uint16_t* scales, uint16_t* mu_st, uint16_t* resid,
                double* gap, double* u_out) {
   int r = orc_resid_count(L, R);
@@ -297,7 +312,7 @@ int orc_encode(const uint16_t* x, int64_t n_units, int L, int d, int R, int s,
   int64_t i;
 #pragma omp parallel for schedule(dynamic, 1)
   for (i = 0; i < n_units; ++i) {
-    orc_encode_unit(x + (size_t)i * L * d, L, d, R, s, cb, ncw,
+    orc_encode_unit(x + (size_t)i * L * d, L, d, R, s, cb, ncw, signs, scale_adjust,
                     codes + (size_t)i * nq * S, scales + (size_t)i * nq * 2,
                     mu_st + (size_t)i * (nq / R) * d, resid + (size_t)i * R * d,
                     gap ? gap + (size_t)i * nq * S : NULL,
@@ -311,10 +326,11 @@ int orc_encode(const uint16_t* x, int64_t n_units, int L, int d, int R, int s,
 /* Reconstruct tokens [tok0, tok0 + ntok) of one stream from stored values only:
  *   x_hat = N1 * (N2 * H^T c_hat + MU_block),  c_hat = concat_j C[code_j]
  * [P3 sec. 1: the byproducts (s1, o, s2) rebuild the tensor; sec. 4: dequant
- * kernel].  H^T = H for the Sylvester matrix. */
+ * kernel].  H^T = H for the Sylvester matrix; with signs, the inverse of
+ * u = H diag(signs) w is w = diag(signs) H u. */
 void orc_dequant_unit(const uint8_t* codes, const uint16_t* scales, const uint16_t* mu_st,
                       int tok0, int ntok, int d, int R, int s,
-                      const uint16_t* cb, double* out) {
+                      const uint16_t* cb, const double* signs, double* out) {
   int S = d / s;
   double* chat = (double*)malloc(sizeof(double) * d);
   double* rot = (double*)malloc(sizeof(double) * d);
@@ -330,7 +346,8 @@ void orc_dequant_unit(const uint8_t* codes, const uint16_t* scales, const uint16
     double N1 = orc_h2d(scales[(size_t)t * 2 + 0]);
     double N2 = orc_h2d(scales[(size_t)t * 2 + 1]);
     const uint16_t* mub = mu_st + (size_t)(t / R) * d;
-    for (int c = 0; c < d; ++c) out[(size_t)i * d + c] = N1 * (N2 * rot[c] + orc_h2d(mub[c]));
+    for (int c = 0; c < d; ++c)
+      out[(size_t)i * d + c] = N1 * (N2 * (signs ? signs[c] : 1.0) * rot[c] + orc_h2d(mub[c]));
   }
   free(chat);
   free(rot);
@@ -341,13 +358,13 @@ void orc_dequant_unit(const uint8_t* codes, const uint16_t* scales, const uint16
  * scales and cap_tokens/R rows of mu; out [n_units][ntok][d]. */
 void orc_dequant(const uint8_t* codes, const uint16_t* scales, const uint16_t* mu_st,
                  int64_t n_units, int cap_tokens, int tok0, int ntok, int d, int R, int s,
-                 const uint16_t* cb, double* out) {
+                 const uint16_t* cb, const double* signs, double* out) {
   int S = d / s;
   int64_t i;
 #pragma omp parallel for schedule(dynamic, 1)
   for (i = 0; i < n_units; ++i) {
     orc_dequant_unit(codes + (size_t)i * cap_tokens * S, scales + (size_t)i * cap_tokens * 2,
-                     mu_st + (size_t)i * (cap_tokens / R) * d, tok0, ntok, d, R, s, cb,
+                     mu_st + (size_t)i * (cap_tokens / R) * d, tok0, ntok, d, R, s, cb, signs,
                      out + (size_t)i * ntok * d);
   }
 }

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(nsnq):
     assert len(names) == 11
     for n in names:
         assert hasattr(nsnq.lib(), n), n
-    assert nsnq.nsnq_abi_version() == 1
+    assert nsnq.nsnq_abi_version() == 2
     assert nsnq.lib().nsnq_status_str(1) == b"invalid argument"
 
 
@@ -50,6 +50,14 @@ def test_host_validation_rejects_before_launch(nsnq):
     assert L.nsnq_encode_kv(by(nsnq.params(2, 128, head_dim=64)), P, P, P, 0, 0, 64, 256, by(c), None) == EUNS
     assert L.nsnq_encode_kv(by(nsnq.params(2, 96)), P, P, P, 0, 0, 128, 256, by(c), None) == EUNS
     assert L.nsnq_encode_kv(by(nsnq.params(2, 128, n_codewords=16)), P, P, P, 0, 0, 128, 256, by(c), None) == EINVAL
+    # unknown flags, nonzero reserved field
+    bad_flags = nsnq.params(2, 128, flags=4)
+    assert L.nsnq_encode_kv(by(bad_flags), P, P, P, 0, 0, 128, 256, by(c), None) == EINVAL
+    bad_res = nsnq.params(2, 128)
+    bad_res.reserved = 1
+    assert L.nsnq_encode_kv(by(bad_res), P, P, P, 0, 0, 128, 256, by(c), None) == EINVAL
+    adj = nsnq.params(2, 128, flags=nsnq.NSNQ_SCALE_ADJUST)
+    assert L.nsnq_encode_kv(by(adj), P, P, P, 0, 0, 128, 0, by(c), None) == nsnq.NSNQ_OK
     # misaligned or null pointers, bad strides, capacity, residual state
     assert L.nsnq_encode_kv(by(good), P + 2, P, P, 0, 0, 128, 256, by(c), None) == EINVAL
     assert L.nsnq_encode_kv(by(good), P, None, P, 0, 0, 128, 256, by(c), None) == EINVAL

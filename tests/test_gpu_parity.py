@@ -161,6 +161,43 @@ def test_flush_then_decode(oracle_codebooks):
     check_attention(o, _decode_ref(q, ek, ev, cb, R))
 
 
+# ------------------------------------------- randomised Hadamard, Strategy 3 --
+
+@pytest.mark.parametrize("bits,R,use_signs,adjust", [
+    (2, 64, True, False),
+    (2, 128, False, True),
+    (2, 128, True, True),
+    (1, 128, True, True),
+])
+def test_rht_and_scale_adjust(oracle_codebooks, bits, R, use_signs, adjust):
+    """Encode, dequant and decode with a sign vector and/or Strategy 3."""
+    cb = oracle_codebooks[bits]
+    B, Hq, Hkv, L = 2, 4, 2, 5 * R + 9
+    k, v = _kv(600 + bits, B, Hkv, L)
+    q = synth.queries(600 + bits, 0, B, Hq, D)
+    signs = synth.hadamard_signs(60 + bits) if use_signs else None
+    flags = nsnq.NSNQ_SCALE_ADJUST if adjust else 0
+    p, cbt, cache = gpu_encode(k, v, bits, R, cb, flags=flags, signs=signs)
+    ek, ev = oracle_encode_pair(k, v, R, cb, signs=signs, scale_adjust=adjust)
+    compare_encoded(cache, ek, ev, scale_adjust=adjust)
+    nq = ek["n_quant"]
+    for which, e, x in ((0, ek, k), (1, ev, v)):
+        g = nsnq.nsnq_dequant(p, cbt, cache, which, 0, nq, torch.float32).cpu().numpy()
+        ref = oracle.dequant(e["codes"], e["scales"], e["mu"], R, cb, signs=signs)
+        same = np.all(half_np(cache, which)["codes"] == e["codes"], axis=-1)
+        check_dequant(g, ref, token_norms(x[:, :, :nq].numpy()), mask=same)
+    ref = oracle.reference_decode(q, ek, ev, nq, ek["n_resid"], R, cb, signs=signs)
+    o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), cache).float().cpu().numpy()
+    check_attention(o, ref)
+    # the oracle's own cache attended on the GPU
+    oc = nsnq.KVCache(p, B, Hkv, capacity(L, R), DEV)
+    upload_half(oc, 0, ek)
+    upload_half(oc, 1, ev)
+    oc.n_quant, oc.n_resid = nq, ek["n_resid"]
+    o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), oc, num_splits=3).float().cpu().numpy()
+    check_attention(o, ref)
+
+
 # ------------------------------------------------------------------ k-means --
 
 @pytest.mark.parametrize("bits", [2, 1])
