@@ -212,18 +212,28 @@ nsnq_status nsnq_dequant(const nsnq_params* p, const uint16_t* codebook, const n
 namespace {
 
 struct DecodePlan {
+  bool mfma;  // matrix-core kernel (grouped heads) instead of LUT scoring
   int gh, split_tokens, nsplit_q, nsplit;
   size_t lds;
 };
 
-// Query heads per work-group: the largest of 4, 2, 1 dividing G.
+// Query heads per work-group.  Matrix-core kernel: G itself for G = 2, 4, 8,
+// 16, else 16 when G is a multiple of 16.  LUT kernel (G = 1 and the rest):
+// the largest of 4, 2, 1 dividing G.
+int mfma_heads_per_group(int G) {
+  if (G == 2 || G == 4 || G == 8 || G == 16) return G;
+  if (G > 16 && G % 16 == 0) return 16;
+  return 0;
+}
 int heads_per_group(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
 
 DecodePlan plan_decode(const nsnq_params* p, const nsnq_cache* c, int q_heads, int num_splits) {
   DecodePlan pl{};
   const int G = q_heads / c->kv_heads;
   const int R = p->block_tokens;
-  pl.gh = heads_per_group(G);
+  const int gq = mfma_heads_per_group(G);
+  pl.mfma = gq > 0;
+  pl.gh = pl.mfma ? gq : heads_per_group(G);
   const int nblk = c->n_quant / R;
   const int max_ts = decode_max_split_tokens(sub_of(p), pl.gh, R);
   const int max_bps = max_ts / R;  // blocks per split
@@ -248,7 +258,7 @@ DecodePlan plan_decode(const nsnq_params* p, const nsnq_cache* c, int q_heads, i
   pl.split_tokens = bps * R;
   pl.nsplit_q = nblk == 0 ? 0 : (nblk + bps - 1) / bps;
   pl.nsplit = pl.nsplit_q + (c->n_resid > 0 ? 1 : 0);
-  pl.lds = decode_lds_bytes(sub_of(p), pl.gh, pl.split_tokens, R);
+  pl.lds = pl.mfma ? decode_mfma_lds_bytes(sub_of(p), pl.gh) : decode_lds_bytes(sub_of(p), pl.gh, pl.split_tokens, R);
   return pl;
 }
 
@@ -305,7 +315,8 @@ nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.signs = p->hadamard_signs;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_decode(a, sub_of(p), pl.gh, cache->batch, pl.lds, st);
+  hipError_t e = pl.mfma ? launch_decode_mfma(a, sub_of(p), pl.gh, cache->batch, st)
+                         : launch_decode(a, sub_of(p), pl.gh, cache->batch, pl.lds, st);
   if (e != hipSuccess) return NSNQ_EHIP;
   CombineArgs cb{};
   cb.ws = (const float*)ws;

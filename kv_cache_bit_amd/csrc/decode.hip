@@ -13,6 +13,7 @@
 
 #include "nsnq_device.hpp"
 #include "nsnq_launch.hpp"
+#include "decode_common.hpp"
 
 namespace nsnq {
 
@@ -38,27 +39,6 @@ constexpr int kLutStride = 257;  // odd row stride: finish-step reads hit distin
 // one inverse transform, and the split's (m, l, o) partial is written.
 
 constexpr int kChunk = 64;
-// Blocks of R tokens one split may span.
-constexpr int kMaxSplitBlocks = 16;
-
-// Block-wide reduction of GH values per thread (max or sum); red is 4*GH floats.
-template <int GH, bool MAX>
-__device__ __forceinline__ void block_reduce(float (&v)[GH], float* red, int lane, int wave) {
-#pragma unroll
-  for (int g = 0; g < GH; ++g) v[g] = MAX ? group_max<kWave>(v[g]) : group_sum<kWave>(v[g]);
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < GH; ++g) red[wave * GH + g] = v[g];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < GH; ++g) {
-    float r0 = red[g], r1 = red[GH + g], r2 = red[2 * GH + g], r3 = red[3 * GH + g];
-    v[g] = MAX ? fmaxf(fmaxf(r0, r1), fmaxf(r2, r3)) : (r0 + r1) + (r2 + r3);
-  }
-  __syncthreads();
-}
-
 
 struct DecodeSmem {
   // offsets in floats
@@ -96,90 +76,6 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&cw)[S / 
   for (int i = 0; i < S / 16; ++i) {
     const uint4 v4 = *reinterpret_cast<const uint4*>(p + 16 * i);
     cw[4 * i] = v4.x; cw[4 * i + 1] = v4.y; cw[4 * i + 2] = v4.z; cw[4 * i + 3] = v4.w;
-  }
-}
-
-// Residual split: fp16 keys and values, one query token per head.
-template <int GH>
-__device__ __forceinline__ void decode_residual(const DecodeArgs& a, float* qf, float* sc, float* ov, float* red,
-                                                float* ws_base, int64_t ws_head, int64_t unit) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nt = a.n_resid;
-  constexpr int TS = 128;
-  const uint16_t* kr = a.kresid + unit * a.R * kDim;
-  const uint16_t* vr = a.vresid + unit * a.R * kDim;
-  __syncthreads();
-  // scores: one thread per token, the whole key row in flight at once
-  if (tid < nt) {
-    const uint4* row = reinterpret_cast<const uint4*>(kr + (int64_t)tid * kDim);
-    uint4 kv[16];
-#pragma unroll
-    for (int ch = 0; ch < 16; ++ch) kv[ch] = row[ch];
-    float acc[GH];
-#pragma unroll
-    for (int g = 0; g < GH; ++g) acc[g] = 0.f;
-#pragma unroll
-    for (int ch = 0; ch < 16; ++ch) {
-      const uint32_t w4[4] = {kv[ch].x, kv[ch].y, kv[ch].z, kv[ch].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float k0 = h2f(w4[i] & 0xffff), k1 = h2f(w4[i] >> 16);
-        const int c = ch * 8 + 2 * i;
-#pragma unroll
-        for (int g = 0; g < GH; ++g) acc[g] = fmaf(qf[g * kDim + c], k0, fmaf(qf[g * kDim + c + 1], k1, acc[g]));
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < GH; ++g) sc[g * TS + tid] = acc[g] * a.scale_log2;
-  }
-  __syncthreads();
-  float m[GH], l[GH];
-#pragma unroll
-  for (int g = 0; g < GH; ++g) m[g] = -INFINITY;
-  for (int t = tid; t < nt; t += 256)
-#pragma unroll
-    for (int g = 0; g < GH; ++g) m[g] = fmaxf(m[g], sc[g * TS + t]);
-  block_reduce<GH, true>(m, red, lane, wave);
-#pragma unroll
-  for (int g = 0; g < GH; ++g) l[g] = 0.f;
-  for (int t = tid; t < nt; t += 256)
-#pragma unroll
-    for (int g = 0; g < GH; ++g) {
-      const float pr = exp2f(sc[g * TS + t] - m[g]);
-      sc[g * TS + t] = pr;
-      l[g] += pr;
-    }
-  block_reduce<GH, false>(l, red, lane, wave);
-  // values: wave per token row, lanes own channels (2 lane, 2 lane + 1)
-  float o0[GH], o1[GH];
-#pragma unroll
-  for (int g = 0; g < GH; ++g) o0[g] = o1[g] = 0.f;
-#pragma unroll 8
-  for (int t = wave; t < nt; t += 4) {
-    const uint32_t vv = *reinterpret_cast<const uint32_t*>(vr + (int64_t)t * kDim + 2 * lane);
-    const float v0 = h2f(vv & 0xffff), v1 = h2f(vv >> 16);
-#pragma unroll
-    for (int g = 0; g < GH; ++g) {
-      const float pr = sc[g * TS + t];
-      o0[g] = fmaf(pr, v0, o0[g]);
-      o1[g] = fmaf(pr, v1, o1[g]);
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < GH; ++g) {
-    ov[(wave * GH + g) * kDim + 2 * lane] = o0[g];
-    ov[(wave * GH + g) * kDim + 2 * lane + 1] = o1[g];
-  }
-  __syncthreads();
-  for (int o = tid; o < GH * kDim; o += 256) {
-    const int g = o / kDim, c = o % kDim;
-    const float sum = (ov[(0 * GH + g) * kDim + c] + ov[(1 * GH + g) * kDim + c]) +
-                      (ov[(2 * GH + g) * kDim + c] + ov[(3 * GH + g) * kDim + c]);
-    ws_base[g * ws_head + c] = sum;
-    if (c == 0) {
-      ws_base[g * ws_head + kDim] = m[g];
-      ws_base[g * ws_head + kDim + 1] = l[g];
-    }
   }
 }
 

@@ -88,6 +88,8 @@ struct Fp16DecodeArgs {
 hipError_t launch_encode(const EncodeArgs& a, int sub, int R, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, int sub, int n_units, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int sub, int gh, int B, size_t lds_bytes, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int sub, int gq, int B, hipStream_t stream);
+size_t decode_mfma_lds_bytes(int sub, int gq);
 hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream);
 size_t decode_lds_bytes(int sub, int gh, int split_tokens, int R);
 constexpr int kMaxSplits = 1024;  // partials one combine can merge

@@ -112,6 +112,10 @@ def _decode_ref(q, ek, ev, cb, R):
     (2, 64, 1, 6, 3, 333),     # G = 2
     (2, 128, 1, 8, 1, 300),    # G = 8 (two head groups per KV head)
     (2, 64, 2, 2, 2, 40),      # residual tokens only
+    (2, 128, 1, 16, 1, 300),   # G = 16: one matrix-core column per head
+    (1, 64, 1, 32, 1, 200),    # G = 32: two 16-head groups
+    (2, 64, 1, 12, 2, 333),    # G = 6: LUT kernel, 3 groups of 2
+    (1, 128, 2, 8, 4, 129),    # G = 2, one residual token
 ])
 def test_decode_same_cache_and_end_to_end(oracle_codebooks, bits, R, B, Hq, Hkv, L):
     cb = oracle_codebooks[bits]
