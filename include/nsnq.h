@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define NSNQ_ABI_VERSION 2
+#define NSNQ_ABI_VERSION 3
 
 typedef int32_t nsnq_status;
 enum {
@@ -97,9 +97,20 @@ typedef struct {
   uint16_t* resid;
 } nsnq_kv;
 
-/* A one-layer compressed cache.  n_quant (a multiple of R) and n_resid
- * (0..R) are HOST counters, the same for every batch row; the calls below
- * read and update them. */
+/* A one-layer compressed cache.
+ *
+ * Uniform cache (seq_quant = seq_resid = NULL): n_quant (a multiple of R) and
+ * n_resid (0..R) are HOST counters, the same for every batch row; the calls
+ * below read and update them.
+ *
+ * Ragged cache (both non-NULL): seq_quant and seq_resid are DEVICE int32
+ * arrays [batch] holding each row's own counters (same rules per row); the
+ * kernels read and update them.  Rows are independent sequences of different
+ * lengths (serving batches).  The host then keeps bounds, maintained by the
+ * calls: max_len >= every row's n_quant + n_resid, and from it
+ * n_quant = R * floor(max_len / R) and n_resid = min(R, max_len), which size
+ * launches and workspaces (a loose bound costs only idle work-groups).
+ * max_len is unused for uniform caches. */
 typedef struct {
   nsnq_kv k, v;
   int32_t batch;
@@ -107,6 +118,9 @@ typedef struct {
   int32_t cap_tokens;
   int32_t n_quant;
   int32_t n_resid;
+  int32_t max_len;
+  int32_t* seq_quant;
+  int32_t* seq_resid;
 } nsnq_cache;
 
 /* ABI version (NSNQ_ABI_VERSION) and a static text for a status. */
@@ -147,13 +161,37 @@ nsnq_status nsnq_encode_kv(const nsnq_params* p, const uint16_t* codebook, const
                            const uint16_t* v, int64_t stride_b, int64_t stride_h, int64_t stride_t,
                            int32_t L, nsnq_cache* cache, void* stream);
 
+/* Ragged prefill: row b encodes the first lengths[b] tokens of its streams
+ * exactly as nsnq_encode_kv does for L = lengths[b] (device int32 array
+ * [batch], 0 <= lengths[b] <= max_len), writing seq_quant[b] and
+ * seq_resid[b].  Requires a ragged cache with n_quant == n_resid == max_len
+ * == 0 (empty; the device counters are overwritten) and
+ * R * floor(max_len / R) <= cap_tokens.  Afterwards the host bounds are those
+ * of max_len.  Uniform caches: EINVAL. */
+nsnq_status nsnq_encode_kv_ragged(const nsnq_params* p, const uint16_t* codebook, const uint16_t* k,
+                                  const uint16_t* v, int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                                  const int32_t* lengths, int32_t max_len, nsnq_cache* cache, void* stream);
+
 /* Flush a full residual window (technical summary sec. 4, "Residuals"): the R
  * residual tokens are encoded as one block at position n_quant, then
- * n_quant += R and n_resid = 0.  Requires n_resid == R and
- * n_quant + R <= cap_tokens.  The caller then writes the new token into
- * resid[.., n_resid, :] and increments n_resid. */
+ * n_quant += R and n_resid = 0.  Uniform cache: requires n_resid == R and
+ * n_quant + R <= cap_tokens; the caller then writes the new token into
+ * resid[.., n_resid, :] and increments n_resid (or calls nsnq_append_kv).
+ * Ragged cache: every row whose seq_resid is R is flushed, the others are
+ * left alone (nothing is launched when the bound n_resid is below R); the
+ * bounds do not change. */
 nsnq_status nsnq_flush_residual(const nsnq_params* p, const uint16_t* codebook, nsnq_cache* cache,
                                 void* stream);
+
+/* Append one token per row (the decode step's new key and value): k_new and
+ * v_new fp16 [batch][kv_heads][d].  A row whose residual window is full is
+ * first flushed as by nsnq_flush_residual, then the token is written at its
+ * window position and its n_resid incremented.  Works on uniform caches
+ * (host counters; requires n_quant + R <= cap_tokens when n_resid == R) and
+ * ragged caches (device counters, per row; max_len grows by one and requires
+ * R * floor((max_len + 1) / R) <= cap_tokens). */
+nsnq_status nsnq_append_kv(const nsnq_params* p, const uint16_t* codebook, const uint16_t* k_new,
+                           const uint16_t* v_new, nsnq_cache* cache, void* stream);
 
 /* Reconstruct quantised tokens [tok0, tok0 + ntok) of the K (which = 0) or V
  * (which = 1) half: x_hat = N1 * (N2 * D H c_hat + MU_block), D = diag(signs)
@@ -161,7 +199,8 @@ nsnq_status nsnq_flush_residual(const nsnq_params* p, const uint16_t* codebook, 
  * encode using only stored values (technical summary sec. 1: the byproducts
  * rebuild the tensor; sec. 4: dequantisation kernel).  Requires
  * 0 <= tok0, tok0 + ntok <= n_quant.  out: [batch][kv_heads][ntok][d] as fp32
- * (out_dtype 0) or fp16 (out_dtype 1). */
+ * (out_dtype 0) or fp16 (out_dtype 1).  Ragged cache: tokens at or past a
+ * row's seq_quant are written as zeros. */
 nsnq_status nsnq_dequant(const nsnq_params* p, const uint16_t* codebook, const nsnq_cache* cache,
                          int32_t which, int32_t tok0, int32_t ntok, int32_t out_dtype, void* out,
                          void* stream);
@@ -174,7 +213,8 @@ nsnq_status nsnq_dequant(const nsnq_params* p, const uint16_t* codebook, const n
  * token ranges per head processed in parallel (0 = choose).  out: fp16
  * [batch][q_heads][d].  ws/ws_bytes: device workspace of at least
  * nsnq_decode_workspace_bytes(p, cache, q_heads, num_splits) bytes.
- * Requires n_quant + n_resid >= 1. */
+ * Requires n_quant + n_resid >= 1 (ragged cache: per row, else that row's
+ * output is zero). */
 size_t nsnq_decode_workspace_bytes(const nsnq_params* p, const nsnq_cache* cache, int32_t q_heads,
                                    int32_t num_splits);
 nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook, const uint16_t* q,

@@ -42,6 +42,9 @@ nsnq_status check_cache(const nsnq_params* p, const nsnq_cache* c) {
   if (c->n_quant < 0 || c->n_quant % p->block_tokens != 0 || c->n_quant > c->cap_tokens) return NSNQ_EINVAL;
   if (c->n_resid < 0 || c->n_resid > p->block_tokens) return NSNQ_EINVAL;
   if ((int64_t)c->batch * c->kv_heads * c->cap_tokens > (int64_t)1 << 40) return NSNQ_EINVAL;
+  if ((c->seq_quant == nullptr) != (c->seq_resid == nullptr)) return NSNQ_EINVAL;
+  if (c->seq_quant && ((((uintptr_t)c->seq_quant) & 3u) || (((uintptr_t)c->seq_resid) & 3u))) return NSNQ_EINVAL;
+  if (c->seq_quant && c->max_len < 0) return NSNQ_EINVAL;
   nsnq_status s = check_kv(c->k);
   if (s != NSNQ_OK) return s;
   return check_kv(c->v);
@@ -82,6 +85,48 @@ nsnq_status run_encode(const nsnq_params* p, const uint16_t* cb, const uint16_t*
   a.signs = p->hadamard_signs;
   a.scale_adjust = (p->flags & NSNQ_SCALE_ADJUST) ? 1 : 0;
   return hip_status(launch_encode(a, sub_of(p), p->block_tokens, stream));
+}
+
+bool is_ragged(const nsnq_cache* c) { return c->seq_quant != nullptr; }
+
+// Host bounds of a ragged cache from its length bound.
+int64_t ragged_quant_bound(int64_t max_len, int R) { return max_len / R * R; }
+void set_ragged_bounds(nsnq_cache* c, int max_len, int R) {
+  c->max_len = max_len;
+  c->n_quant = (int32_t)ragged_quant_bound(max_len, R);
+  c->n_resid = max_len < R ? max_len : R;
+}
+
+// Ragged flush: one launch over every row's window; rows that are not full
+// exit at once.
+nsnq_status run_ragged_flush(const nsnq_params* p, const uint16_t* cb, const nsnq_cache* c, hipStream_t stream) {
+  const int R = p->block_tokens;
+  const int64_t st = p->head_dim, sh = (int64_t)R * p->head_dim, sb = sh * c->kv_heads;
+  EncodeArgs a{};
+  a.src[0] = c->k.resid;
+  a.src[1] = c->v.resid;
+  a.sb = sb;
+  a.sh = sh;
+  a.st = st;
+  a.codes[0] = c->k.codes;
+  a.codes[1] = c->v.codes;
+  a.scales[0] = c->k.scales;
+  a.scales[1] = c->v.scales;
+  a.mu[0] = c->k.mu;
+  a.mu[1] = c->v.mu;
+  a.resid[0] = c->k.resid;
+  a.resid[1] = c->v.resid;
+  a.codebook = cb;
+  a.H = c->kv_heads;
+  a.n_units = c->batch * c->kv_heads;
+  a.cap = c->cap_tokens;
+  a.nblk = 1;
+  a.R = R;
+  a.signs = p->hadamard_signs;
+  a.scale_adjust = (p->flags & NSNQ_SCALE_ADJUST) ? 1 : 0;
+  a.fl_quant = c->seq_quant;
+  a.fl_resid = c->seq_resid;
+  return hip_status(launch_encode(a, sub_of(p), R, stream));
 }
 
 }  // namespace
@@ -150,7 +195,7 @@ nsnq_status nsnq_encode_kv(const nsnq_params* p, const uint16_t* codebook, const
   // 16-byte aligned token rows: every stride a multiple of 8 elements
   if (stride_t < p->head_dim || stride_b < 0 || stride_h < 0) return NSNQ_EINVAL;
   if ((stride_t % 8) || (stride_h % 8) || (stride_b % 8)) return NSNQ_EINVAL;
-  if (cache->n_resid != 0) return NSNQ_EINVAL;
+  if (cache->n_resid != 0 || is_ragged(cache)) return NSNQ_EINVAL;
   const int R = p->block_tokens;
   const int r = ((L - 1) % R) + 1;
   const int nq = L - r;
@@ -163,6 +208,54 @@ nsnq_status nsnq_encode_kv(const nsnq_params* p, const uint16_t* codebook, const
   return NSNQ_OK;
 }
 
+nsnq_status nsnq_encode_kv_ragged(const nsnq_params* p, const uint16_t* codebook, const uint16_t* k,
+                                  const uint16_t* v, int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                                  const int32_t* lengths, int32_t max_len, nsnq_cache* cache, void* stream) {
+  nsnq_status s = check_params(p);
+  if (s != NSNQ_OK) return s;
+  s = check_cache(p, cache);
+  if (s != NSNQ_OK) return s;
+  if (!is_ragged(cache) || cache->n_quant != 0 || cache->n_resid != 0 || cache->max_len != 0) return NSNQ_EINVAL;
+  if (!codebook || !aligned16(codebook) || !lengths || (((uintptr_t)lengths) & 3u) || max_len < 0)
+    return NSNQ_EINVAL;
+  if (!k || !v || !aligned16(k) || !aligned16(v)) return NSNQ_EINVAL;
+  if (stride_t < p->head_dim || stride_b < 0 || stride_h < 0) return NSNQ_EINVAL;
+  if ((stride_t % 8) || (stride_h % 8) || (stride_b % 8)) return NSNQ_EINVAL;
+  const int R = p->block_tokens;
+  const int nq_max = max_len > 0 ? max_len - (((max_len - 1) % R) + 1) : 0;  // largest row n_quant
+  if (ragged_quant_bound(max_len, R) > cache->cap_tokens) return NSNQ_EINVAL;
+  EncodeArgs a{};
+  a.src[0] = k;
+  a.src[1] = v;
+  a.sb = stride_b;
+  a.sh = stride_h;
+  a.st = stride_t;
+  a.codes[0] = cache->k.codes;
+  a.codes[1] = cache->v.codes;
+  a.scales[0] = cache->k.scales;
+  a.scales[1] = cache->v.scales;
+  a.mu[0] = cache->k.mu;
+  a.mu[1] = cache->v.mu;
+  a.resid[0] = cache->k.resid;
+  a.resid[1] = cache->v.resid;
+  a.codebook = codebook;
+  a.H = cache->kv_heads;
+  a.n_units = cache->batch * cache->kv_heads;
+  a.cap = cache->cap_tokens;
+  a.nblk = nq_max / R;
+  a.R = R;
+  a.signs = p->hadamard_signs;
+  a.scale_adjust = (p->flags & NSNQ_SCALE_ADJUST) ? 1 : 0;
+  a.lens = lengths;
+  a.lens_max = max_len;
+  a.out_quant = cache->seq_quant;
+  a.out_resid = cache->seq_resid;
+  s = hip_status(launch_encode(a, sub_of(p), R, (hipStream_t)stream));
+  if (s != NSNQ_OK) return s;
+  set_ragged_bounds(cache, max_len, R);
+  return NSNQ_OK;
+}
+
 nsnq_status nsnq_flush_residual(const nsnq_params* p, const uint16_t* codebook, nsnq_cache* cache, void* stream) {
   nsnq_status s = check_params(p);
   if (s != NSNQ_OK) return s;
@@ -170,6 +263,19 @@ nsnq_status nsnq_flush_residual(const nsnq_params* p, const uint16_t* codebook, 
   if (s != NSNQ_OK) return s;
   if (!codebook || !aligned16(codebook)) return NSNQ_EINVAL;
   const int R = p->block_tokens;
+  if (is_ragged(cache)) {
+    if (cache->n_resid < R) return NSNQ_OK;  // no row can be full
+    if (ragged_quant_bound(cache->max_len, R) > cache->cap_tokens) return NSNQ_EINVAL;
+    s = run_ragged_flush(p, codebook, cache, (hipStream_t)stream);
+    if (s != NSNQ_OK) return s;
+    AppendArgs a{};  // counters only
+    a.H = cache->kv_heads;
+    a.R = R;
+    a.cap = cache->cap_tokens;
+    a.seq_quant = cache->seq_quant;
+    a.seq_resid = cache->seq_resid;
+    return hip_status(launch_append(a, cache->batch, (hipStream_t)stream));  // lengths, so bounds, unchanged
+  }
   if (cache->n_resid != R) return NSNQ_EINVAL;
   if ((int64_t)cache->n_quant + R > cache->cap_tokens) return NSNQ_EINVAL;
   const int64_t st = p->head_dim, sh = (int64_t)R * p->head_dim, sb = sh * cache->kv_heads;
@@ -177,6 +283,56 @@ nsnq_status nsnq_flush_residual(const nsnq_params* p, const uint16_t* codebook, 
   if (s != NSNQ_OK) return s;
   cache->n_quant += R;
   cache->n_resid = 0;
+  return NSNQ_OK;
+}
+
+nsnq_status nsnq_append_kv(const nsnq_params* p, const uint16_t* codebook, const uint16_t* k_new,
+                           const uint16_t* v_new, nsnq_cache* cache, void* stream) {
+  nsnq_status s = check_params(p);
+  if (s != NSNQ_OK) return s;
+  s = check_cache(p, cache);
+  if (s != NSNQ_OK) return s;
+  if (!codebook || !aligned16(codebook) || !k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))
+    return NSNQ_EINVAL;
+  const int R = p->block_tokens;
+  const bool may_flush = cache->n_resid == R;
+  if (is_ragged(cache)) {
+    if (ragged_quant_bound((int64_t)cache->max_len + 1, R) > cache->cap_tokens) return NSNQ_EINVAL;
+  } else if (may_flush && (int64_t)cache->n_quant + R > cache->cap_tokens) {
+    return NSNQ_EINVAL;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.kresid = cache->k.resid;
+  a.vresid = cache->v.resid;
+  a.H = cache->kv_heads;
+  a.R = R;
+  a.cap = cache->cap_tokens;
+  if (is_ragged(cache)) {
+    if (may_flush) {
+      s = run_ragged_flush(p, codebook, cache, st);
+      if (s != NSNQ_OK) return s;
+    }
+    a.seq_quant = cache->seq_quant;
+    a.seq_resid = cache->seq_resid;
+    s = hip_status(launch_append(a, cache->batch, st));
+    if (s != NSNQ_OK) return s;
+    set_ragged_bounds(cache, cache->max_len + 1, R);
+    return NSNQ_OK;
+  }
+  if (may_flush) {
+    const int64_t tst = p->head_dim, sh = (int64_t)R * p->head_dim, sb = sh * cache->kv_heads;
+    s = run_encode(p, codebook, cache->k.resid, cache->v.resid, sb, sh, tst, 1, 0, 0, cache, st);
+    if (s != NSNQ_OK) return s;
+    cache->n_quant += R;
+    cache->n_resid = 0;
+  }
+  a.pos = cache->n_resid;
+  s = hip_status(launch_append(a, cache->batch, st));
+  if (s != NSNQ_OK) return s;
+  cache->n_resid += 1;
   return NSNQ_OK;
 }
 
@@ -206,6 +362,7 @@ nsnq_status nsnq_dequant(const nsnq_params* p, const uint16_t* codebook, const n
   a.ntok = ntok;
   a.out_f16 = out_dtype;
   a.signs = p->hadamard_signs;
+  a.seq_quant = cache->seq_quant;
   return hip_status(launch_dequant(a, sub_of(p), cache->batch * cache->kv_heads, (hipStream_t)stream));
 }
 
@@ -314,6 +471,8 @@ nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook
   a.nsplit = pl.nsplit;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.signs = p->hadamard_signs;
+  a.seq_quant = cache->seq_quant;
+  a.seq_resid = cache->seq_resid;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = pl.mfma ? launch_decode_mfma(a, sub_of(p), pl.gh, cache->batch, st)
                          : launch_decode(a, sub_of(p), pl.gh, cache->batch, pl.lds, st);

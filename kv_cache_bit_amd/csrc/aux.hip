@@ -25,6 +25,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   for (int r = 0; r < ROWS; ++r) {
     const int i = blockIdx.x * TPB + wave * (TPB / 4) + r * TPR + tir;  // output token
     const bool act = i < a.ntok;
+    const bool live = !a.seq_quant || a.tok0 + i < a.seq_quant[unit / a.H];  // ragged: past the row's end -> 0
     const int t = a.tok0 + (act ? i : 0);                               // cache token
     const int64_t ct = (int64_t)unit * a.cap + t;
     const uint32_t code = a.codes[ct * S + slot];
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 #pragma unroll
     for (int e = 0; e < SUB; ++e) {
       const float sg = a.signs ? (float)a.signs[slot * SUB + e] : 1.f;
-      x[e] = n1 * fmaf(n2, x[e] * (kInvSqrtD * sg), h2f(mp[e]));
+      x[e] = live ? n1 * fmaf(n2, x[e] * (kInvSqrtD * sg), h2f(mp[e])) : 0.f;
     }
     if (act) {
       const int64_t o = ((int64_t)unit * a.ntok + i) * kDim + slot * SUB;

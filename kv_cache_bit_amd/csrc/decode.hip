@@ -110,12 +110,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
   if (split >= a.nsplit_q) {
     float* red = lut + 4 * GH * kDim;
-    decode_residual<GH>(a, qf, lut + 4 * GH * kDim + 8 * GH, lut, red, ws_base, ws_head, unit);
+    decode_residual<GH>(a, row_resid(a, b), qf, lut + 4 * GH * kDim + 8 * GH, lut, red, ws_base, ws_head, unit);
     return;
   }
 
   const int t0 = split * a.split_tokens;
-  const int ntok = min(a.split_tokens, a.n_quant - t0);
+  const int ntok = max(0, min(a.split_tokens, row_quant(a, b) - t0));  // 0: empty partial
   const int nchunk = ntok / kChunk;
   const uint8_t* kc = a.kcodes + (unit * a.cap + t0) * S;
   const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.kscales) + unit * a.cap + t0;
@@ -339,6 +339,10 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   if ((c & 63) == 0) red[c >> 6] = M;
   __syncthreads();
   M = fmaxf(red[0], red[1]);
+  if (M == -INFINITY) {  // a row without tokens (ragged cache): zero output
+    a.out[(int64_t)bh * kDim + c] = 0;
+    return;
+  }
   float num = 0.f, den = 0.f;
   int i = 0;
   for (; i + 8 <= a.nsplit; i += 8) {

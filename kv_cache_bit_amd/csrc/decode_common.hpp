@@ -31,10 +31,9 @@ __device__ __forceinline__ void block_reduce(float (&v)[GH], float* red, int lan
 
 // Residual split: fp16 keys and values, one query token per head.
 template <int GH>
-__device__ __forceinline__ void decode_residual(const DecodeArgs& a, float* qf, float* sc, float* ov, float* red,
-                                                float* ws_base, int64_t ws_head, int64_t unit) {
+__device__ __forceinline__ void decode_residual(const DecodeArgs& a, int nt, float* qf, float* sc, float* ov,
+                                                float* red, float* ws_base, int64_t ws_head, int64_t unit) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nt = a.n_resid;
   constexpr int TS = 128;
   const uint16_t* kr = a.kresid + unit * a.R * kDim;
   const uint16_t* vr = a.vresid + unit * a.R * kDim;

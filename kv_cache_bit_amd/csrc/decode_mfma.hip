@@ -138,12 +138,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   float* qf = smem + L::qf;
   for (int i = tid; i < GQ * kDim; i += 256) qf[i] = h2f(a.q[((int64_t)b * a.Hq + h0) * kDim + i]);
   if (split >= a.nsplit_q) {
-    decode_residual<GQ>(a, qf, smem + L::rsc, smem + L::rov, smem + L::rred, ws_base, ws_head, unit);
+    decode_residual<GQ>(a, row_resid(a, b), qf, smem + L::rsc, smem + L::rov, smem + L::rred, ws_base, ws_head,
+                        unit);
     return;
   }
 
   const int t0 = split * a.split_tokens;
-  const int ntok = min(a.split_tokens, a.n_quant - t0);
+  const int ntok = max(0, min(a.split_tokens, row_quant(a, b) - t0));  // 0: empty partial
   const int nchunk = ntok / kMChunk;
   const int nblk = ntok / a.R;
   const uint8_t* kc = a.kcodes + (unit * a.cap + t0) * S;

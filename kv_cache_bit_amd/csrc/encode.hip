@@ -68,13 +68,29 @@ __device__ __forceinline__ void half_swap(uint32_t a, uint32_t b, uint32_t& lo_o
   hi_out = r[1];
 }
 
+// Split of a stream of L tokens: the last r = ((L - 1) mod R) + 1 stay in the
+// residual window (r = 0 when L = 0).
+__device__ __forceinline__ int resid_of(int L, int R) { return L > 0 ? ((L - 1) % R) + 1 : 0; }
+
 // Work-groups past the encode blocks copy the last r tokens of each stream
-// into the residual window (one group per (b, h), K or V).
+// into the residual window (one group per (b, h), K or V).  Ragged prefill:
+// r and the first copied token follow the row's length, and the group of
+// (h = 0, K) writes the row's counters.
 __device__ __forceinline__ void resid_copy(const EncodeArgs& a, int unit, int kv) {
   const int b = unit / a.H, h = unit % a.H;
-  const uint16_t* src = a.src[kv] + (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)a.rc_t0 * a.st;
+  int t0 = a.rc_t0, r = a.rc_r;
+  if (a.lens) {
+    const int L = min(max(a.lens[b], 0), a.lens_max);
+    r = resid_of(L, a.R);
+    t0 = L - r;
+    if (h == 0 && kv == 0 && threadIdx.x == 0) {
+      a.out_quant[b] = t0;
+      a.out_resid[b] = r;
+    }
+  }
+  const uint16_t* src = a.src[kv] + (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t0 * a.st;
   uint16_t* dst = a.resid[kv] + (int64_t)unit * a.R * kDim;
-  for (int i = threadIdx.x; i < a.rc_r * 16; i += blockDim.x) {  // 16 x 8 halves per row
+  for (int i = threadIdx.x; i < r * 16; i += blockDim.x) {  // 16 x 8 halves per row
     const int t = i >> 4, c = (i & 15) * 8;
     *reinterpret_cast<uint4*>(dst + (int64_t)t * kDim + c) =
         *reinterpret_cast<const uint4*>(src + (int64_t)t * a.st + c);
@@ -104,9 +120,17 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   const int unit = blockIdx.x / a.nblk;  // b * H + h
   const int kv = blockIdx.y;
   const int b = unit / a.H, h = unit % a.H;
+  int dst0 = a.dst_tok0;  // first destination token of this launch's blocks
+  if (a.lens) {           // ragged prefill: this row encodes L - r tokens
+    const int L = min(max(a.lens[b], 0), a.lens_max);
+    if (blk * R >= L - resid_of(L, R)) return;
+  } else if (a.fl_resid) {  // ragged flush: only full windows, each at its row's n_quant
+    dst0 = a.fl_quant[b];
+    if (a.fl_resid[b] != R || dst0 < 0 || dst0 % R != 0 || dst0 + R > a.cap) return;
+  }
 
   const uint16_t* src = a.src[kv] + (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)blk * R * a.st;
-  const int64_t tok_base = (int64_t)unit * a.cap + a.dst_tok0 + (int64_t)blk * R;
+  const int64_t tok_base = (int64_t)unit * a.cap + dst0 + (int64_t)blk * R;
 
   // ---- codebook operands (A side), per 32-codeword tile -------------------
   // Built once per group into LDS (lane l of tile t holds codeword
@@ -210,7 +234,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     mu[e] = (red[0][c] + red[1][c] + red[2][c] + red[3][c]) * (1.0f / R);
   }
   if (wave == 0 && tir == 0) {
-    uint16_t* pm = a.mu[kv] + ((int64_t)unit * (a.cap / R) + a.dst_tok0 / R + blk) * kDim + slot * SUB;
+    uint16_t* pm = a.mu[kv] + ((int64_t)unit * (a.cap / R) + dst0 / R + blk) * kDim + slot * SUB;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) pm[e] = f2h(mu[e]);
   }
@@ -341,8 +365,58 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   }
 }
 
+// Append one token per row into the residual window (after any flush of the
+// same step has run).  One group per row: every head's K and V row, then the
+// row's counters.  Without a token (k_new null, ragged only) it just moves the
+// counters of the rows that a flush has encoded.
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int b = blockIdx.x;
+  int pos = a.pos;
+  bool flushed = false;
+  if (a.seq_resid) {
+    pos = a.seq_resid[b];
+    if (pos < 0 || pos > a.R) return;  // not a valid window position: the row is left as it is
+    if (pos == a.R) {
+      const int nq = a.seq_quant[b];
+      if (nq < 0 || nq % a.R != 0 || nq + a.R > a.cap) return;  // no room: the row is left as it is
+      flushed = true;
+      pos = 0;
+    }
+  }
+  if (!a.k_new) {
+    if (a.seq_resid && flushed) {
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        a.seq_quant[b] += a.R;
+        a.seq_resid[b] = 0;
+      }
+    }
+    return;
+  }
+  for (int i = threadIdx.x; i < 2 * a.H * 16; i += blockDim.x) {  // 16 x 8 halves per row
+    const int kv = i / (a.H * 16), h = (i / 16) % a.H, c = (i % 16) * 8;
+    const int64_t unit = (int64_t)b * a.H + h;
+    const uint16_t* src = (kv ? a.v_new : a.k_new) + unit * kDim + c;
+    uint16_t* dst = (kv ? a.vresid : a.kresid) + (unit * a.R + pos) * kDim + c;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
+  if (a.seq_resid) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      if (flushed) a.seq_quant[b] += a.R;
+      a.seq_resid[b] = pos + 1;
+    }
+  }
+}
+
+hipError_t launch_append(const AppendArgs& a, int B, hipStream_t stream) {
+  hipLaunchKernelGGL(append_kernel, dim3(B), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_encode(const EncodeArgs& a, int sub, int R, hipStream_t stream) {
-  dim3 grid(a.nblk * a.n_units + (a.rc_r > 0 ? a.n_units : 0), 2), block(256);
+  const bool rcopy = a.rc_r > 0 || a.lens != nullptr;
+  dim3 grid(a.nblk * a.n_units + (rcopy ? a.n_units : 0), 2), block(256);
   if (grid.x == 0) return hipSuccess;
   if (sub == 4 && R == 128) hipLaunchKernelGGL((encode_kernel<4, 128>), grid, block, 0, stream, a);
   else if (sub == 4 && R == 64) hipLaunchKernelGGL((encode_kernel<4, 64>), grid, block, 0, stream, a);

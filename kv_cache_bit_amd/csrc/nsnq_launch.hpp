@@ -23,6 +23,28 @@ struct EncodeArgs {
   int rc_t0, rc_r;           // residual copy: first source token and count (0 = none)
   const int8_t* signs;       // randomised-Hadamard signs [128] or null
   int scale_adjust;          // fold alpha = |u|^2 / (u . c_hat) into n2
+  // ragged prefill: per-row stream lengths (device [B]); the block / residual
+  // split of each row follows its own length, and the row counters are
+  // written to out_quant / out_resid.  Null for uniform launches.
+  const int32_t* lens;
+  int lens_max;  // lengths are clamped to [0, lens_max]
+  int32_t* out_quant;
+  int32_t* out_resid;
+  // ragged flush: only rows with fl_resid[b] == R are encoded, at token
+  // fl_quant[b].  Null otherwise.
+  const int32_t* fl_quant;
+  const int32_t* fl_resid;
+};
+
+struct AppendArgs {
+  const uint16_t* k_new;  // [B][H][d]
+  const uint16_t* v_new;
+  uint16_t* kresid;
+  uint16_t* vresid;
+  int H, R, cap;
+  int pos;                // uniform: window position to write
+  int32_t* seq_quant;     // ragged: per-row counters (null for uniform)
+  int32_t* seq_resid;
 };
 
 struct DequantArgs {
@@ -33,6 +55,7 @@ struct DequantArgs {
   void* out;
   int H, cap, R, tok0, ntok, out_f16;
   const int8_t* signs;
+  const int32_t* seq_quant;  // ragged: tokens >= seq_quant[b] come out as 0
 };
 
 struct DecodeArgs {
@@ -55,7 +78,19 @@ struct DecodeArgs {
   int nsplit;        // nsplit_q + (n_resid > 0)
   float scale_log2;  // softmax scale * log2(e)
   const int8_t* signs;  // randomised-Hadamard signs [128] or null
+  const int32_t* seq_quant;  // ragged: per-row counters (null: n_quant / n_resid)
+  const int32_t* seq_resid;
 };
+
+// Per-row token counts of a decode launch.
+// Per-row token counts of a decode launch (ragged counters are clamped to the
+// host bounds the launch was sized for).
+__device__ __forceinline__ int row_quant(const DecodeArgs& a, int b) {
+  return a.seq_quant ? max(0, min(a.seq_quant[b], a.n_quant)) : a.n_quant;
+}
+__device__ __forceinline__ int row_resid(const DecodeArgs& a, int b) {
+  return a.seq_resid ? max(0, min(a.seq_resid[b], a.n_resid)) : a.n_resid;
+}
 
 struct CombineArgs {
   const float* ws;
@@ -86,6 +121,7 @@ struct Fp16DecodeArgs {
 };
 
 hipError_t launch_encode(const EncodeArgs& a, int sub, int R, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, int B, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, int sub, int n_units, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int sub, int gh, int B, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int sub, int gq, int B, hipStream_t stream);

@@ -36,7 +36,8 @@ class nsnq_kv(ctypes.Structure):
 
 class nsnq_cache(ctypes.Structure):
     _fields_ = [("k", nsnq_kv), ("v", nsnq_kv), ("batch", i32), ("kv_heads", i32),
-                ("cap_tokens", i32), ("n_quant", i32), ("n_resid", i32)]
+                ("cap_tokens", i32), ("n_quant", i32), ("n_resid", i32), ("max_len", i32),
+                ("seq_quant", P), ("seq_resid", P)]
 
 
 _PP, _PC = ctypes.POINTER(nsnq_params), ctypes.POINTER(nsnq_cache)
@@ -47,7 +48,9 @@ _SIGNATURES = {
     "nsnq_build_codebook_workspace_bytes": (size_t, [_PP]),
     "nsnq_build_codebook": (i32, [_PP, P, i64, i32, P, P, P, P, P, size_t, P]),
     "nsnq_encode_kv": (i32, [_PP, P, P, P, i64, i64, i64, i32, _PC, P]),
+    "nsnq_encode_kv_ragged": (i32, [_PP, P, P, P, i64, i64, i64, P, i32, _PC, P]),
     "nsnq_flush_residual": (i32, [_PP, P, _PC, P]),
+    "nsnq_append_kv": (i32, [_PP, P, P, P, _PC, P]),
     "nsnq_dequant": (i32, [_PP, P, _PC, i32, i32, i32, i32, P, P]),
     "nsnq_decode_workspace_bytes": (size_t, [_PP, _PC, i32, i32]),
     "nsnq_decode_attention": (i32, [_PP, P, P, i32, _PC, f32, i32, P, P, size_t, P]),
@@ -159,14 +162,40 @@ def nsnq_encode_kv(p: nsnq_params, codebook, k, v, L: int, cache: "KVCache", str
     c = cache.c_struct()
     _check(lib().nsnq_encode_kv(ctypes.byref(p), _ptr(codebook), _ptr(k), _ptr(v), sb, sh, st, L,
                                 ctypes.byref(c), _stream(stream)), "nsnq_encode_kv")
-    cache.n_quant, cache.n_resid = c.n_quant, c.n_resid
+    cache.n_quant, cache.n_resid, cache.max_len = c.n_quant, c.n_resid, c.max_len
+
+
+def nsnq_encode_kv_ragged(p: nsnq_params, codebook, k, v, lengths: torch.Tensor, max_len: int,
+                          cache: "KVCache", stream=None):
+    """Ragged prefill: row b encodes its first lengths[b] tokens (lengths: device
+    int32 [B]); the cache must be ragged and empty."""
+    assert k.dtype == torch.float16 and v.dtype == torch.float16
+    assert k.stride() == v.stride() and k.shape == v.shape and k.stride(3) == 1
+    assert lengths.dtype == torch.int32 and lengths.is_contiguous() and lengths.numel() == cache.batch
+    sb, sh, st, _ = k.stride()
+    c = cache.c_struct()
+    _check(lib().nsnq_encode_kv_ragged(ctypes.byref(p), _ptr(codebook), _ptr(k), _ptr(v), sb, sh, st,
+                                       _ptr(lengths), max_len, ctypes.byref(c), _stream(stream)),
+           "nsnq_encode_kv_ragged")
+    cache.n_quant, cache.n_resid, cache.max_len = c.n_quant, c.n_resid, c.max_len
+
+
+def nsnq_append_kv(p: nsnq_params, codebook, k_new, v_new, cache: "KVCache", stream=None):
+    """Append one token per row (k_new, v_new fp16 [B, H, d]), flushing full windows first."""
+    assert k_new.dtype == torch.float16 and v_new.dtype == torch.float16
+    assert k_new.is_contiguous() and v_new.is_contiguous()
+    assert tuple(k_new.shape) == (cache.batch, cache.kv_heads, p.head_dim) and k_new.shape == v_new.shape
+    c = cache.c_struct()
+    _check(lib().nsnq_append_kv(ctypes.byref(p), _ptr(codebook), _ptr(k_new), _ptr(v_new), ctypes.byref(c),
+                                _stream(stream)), "nsnq_append_kv")
+    cache.n_quant, cache.n_resid, cache.max_len = c.n_quant, c.n_resid, c.max_len
 
 
 def nsnq_flush_residual(p: nsnq_params, codebook, cache: "KVCache", stream=None):
     c = cache.c_struct()
     _check(lib().nsnq_flush_residual(ctypes.byref(p), _ptr(codebook), ctypes.byref(c), _stream(stream)),
            "nsnq_flush_residual")
-    cache.n_quant, cache.n_resid = c.n_quant, c.n_resid
+    cache.n_quant, cache.n_resid, cache.max_len = c.n_quant, c.n_resid, c.max_len
 
 
 def nsnq_dequant(p: nsnq_params, codebook, cache: "KVCache", which: int, tok0: int, ntok: int,
@@ -240,9 +269,12 @@ class KVHalf:
 
 class KVCache:
     """Caller-owned buffers of one layer's compressed cache plus the two host
-    counters (n_quant, n_resid) the library reads and updates."""
+    counters (n_quant, n_resid) the library reads and updates.  A ragged cache
+    also owns per-row device counters seq_quant / seq_resid (int32 [B]); its
+    host counters are then upper bounds."""
 
-    def __init__(self, p: nsnq_params, batch: int, kv_heads: int, cap_tokens: int, device="cuda"):
+    def __init__(self, p: nsnq_params, batch: int, kv_heads: int, cap_tokens: int, device="cuda",
+                 ragged: bool = False):
         R, d = p.block_tokens, p.head_dim
         S = d // sub_dim(p.bits)
         assert cap_tokens % R == 0
@@ -250,6 +282,9 @@ class KVCache:
         self.device = torch.device(device)
         self.n_quant = 0
         self.n_resid = 0
+        self.max_len = 0
+        self.seq_quant = torch.zeros(batch, dtype=torch.int32, device=device) if ragged else None
+        self.seq_resid = torch.zeros(batch, dtype=torch.int32, device=device) if ragged else None
 
         def half():
             return KVHalf(
@@ -265,15 +300,7 @@ class KVCache:
         def kv(h: KVHalf):
             return nsnq_kv(h.codes.data_ptr(), h.scales.data_ptr(), h.mu.data_ptr(), h.resid.data_ptr())
         return nsnq_cache(kv(self.k), kv(self.v), self.batch, self.kv_heads, self.cap_tokens,
-                          self.n_quant, self.n_resid)
-
-    def append_token(self, k_new: torch.Tensor, v_new: torch.Tensor):
-        """Write one new token per (batch row, head) into the residual window
-        (the caller flushes first when it is full)."""
-        assert self.n_resid < self.k.resid.shape[2], "residual window full: flush first"
-        self.k.resid[:, :, self.n_resid].copy_(k_new)
-        self.v.resid[:, :, self.n_resid].copy_(v_new)
-        self.n_resid += 1
+                          self.n_quant, self.n_resid, self.max_len, _ptr(self.seq_quant), _ptr(self.seq_resid))
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for h in (self.k, self.v)

@@ -26,16 +26,16 @@ def nsnq():
 
 def test_exports_every_declared_symbol(nsnq):
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(nsnq.lib(), n), n
-    assert nsnq.nsnq_abi_version() == 2
+    assert nsnq.nsnq_abi_version() == 3
     assert nsnq.lib().nsnq_status_str(1) == b"invalid argument"
 
 
-def _cache_struct(nsnq, B=1, H=2, cap=256, nq=0, nr=0, ptr=0x1000):
+def _cache_struct(nsnq, B=1, H=2, cap=256, nq=0, nr=0, ptr=0x1000, sq=None, sr=None, ml=0):
     kv = nsnq.nsnq_kv(ptr, ptr, ptr, ptr)
-    return nsnq.nsnq_cache(kv, kv, B, H, cap, nq, nr)
+    return nsnq.nsnq_cache(kv, kv, B, H, cap, nq, nr, ml, sq, sr)
 
 
 def test_host_validation_rejects_before_launch(nsnq):
@@ -67,7 +67,7 @@ def test_host_validation_rejects_before_launch(nsnq):
     assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 128, 256, by(c_res), None) == EINVAL
     c_badcap = _cache_struct(nsnq, cap=200)
     assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 128, 256, by(c_badcap), None) == EINVAL
-    c_mis = nsnq.nsnq_cache(nsnq.nsnq_kv(P + 4, P, P, P), nsnq.nsnq_kv(P, P, P, P), 1, 2, 256, 0, 0)
+    c_mis = nsnq.nsnq_cache(nsnq.nsnq_kv(P + 4, P, P, P), nsnq.nsnq_kv(P, P, P, P), 1, 2, 256, 0, 0, 0, None, None)
     assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 128, 256, by(c_mis), None) == EINVAL
     assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 128, 0, by(c), None) == nsnq.NSNQ_OK  # L = 0: no work
     # flush needs a full window
@@ -91,6 +91,25 @@ def test_host_validation_rejects_before_launch(nsnq):
     assert ws > 0
     assert L.nsnq_build_codebook(by(good), P, 100, 5, None, P, P, None, P, ws, None) == EINVAL  # n < 256
     assert L.nsnq_build_codebook(by(good), P, 1000, 5, None, P, P, None, P, ws - 8, None) == EWS
+    # ragged caches: both counter arrays or neither, aligned; the uniform
+    # prefill refuses them and the ragged prefill needs one that is empty
+    assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 128, 256, by(_cache_struct(nsnq, sq=P)), None) == EINVAL
+    assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 128, 256,
+                            by(_cache_struct(nsnq, sq=P + 2, sr=P)), None) == EINVAL
+    cr = _cache_struct(nsnq, sq=P, sr=P + 64)
+    assert L.nsnq_encode_kv(by(good), P, P, P, 0, 0, 128, 256, by(cr), None) == EINVAL
+    assert L.nsnq_encode_kv_ragged(by(good), P, P, P, 0, 0, 128, P, 1000, by(cr), None) == EINVAL  # > cap
+    assert L.nsnq_encode_kv_ragged(by(good), P, P, P, 0, 0, 128, P, 10, by(c), None) == EINVAL   # uniform
+    assert L.nsnq_encode_kv_ragged(by(good), P, P, P, 0, 0, 128, P, 10,
+                                   by(_cache_struct(nsnq, nq=128, sq=P, sr=P + 64)), None) == EINVAL  # not empty
+    assert L.nsnq_encode_kv_ragged(by(good), P, P, P, 0, 0, 128, P + 1, 10, by(cr), None) == EINVAL  # misaligned
+    # append: a full window needs room for its flush
+    assert L.nsnq_append_kv(by(good), P, P, P, by(_cache_struct(nsnq, nq=256, nr=128)), None) == EINVAL
+    assert L.nsnq_append_kv(by(good), P, P + 8, P, by(c), None) == EINVAL
+    assert L.nsnq_append_kv(by(good), P, P, P, by(_cache_struct(nsnq, nq=256, nr=127, ml=383, sq=P, sr=P + 64)),
+                            None) == EINVAL  # a 384-token row may need 384 quantised slots > cap 256
+    cr_nofull = _cache_struct(nsnq, nq=128, nr=5, ml=133, sq=P, sr=P + 64)
+    assert L.nsnq_flush_residual(by(good), P, by(cr_nofull), None) == nsnq.NSNQ_OK  # no row can be full
     # comparator
     assert L.nsnq_fp16_decode_attention(P, 3, P, P, 1, 1, 10, 0.1, 0, P, P, 1 << 20, None) == EUNS
     assert L.nsnq_fp16_decode_attention(P, 4, P, P, 1, 1, 0, 0.1, 0, P, P, 1 << 20, None) == EINVAL

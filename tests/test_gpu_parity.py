@@ -9,7 +9,7 @@ import torch
 import oracle
 from kv_cache_bit_amd import nsnq, synth
 
-from helpers import (DEV, capacity, check_attention, check_codes, check_dequant, check_f16_ulp,
+from helpers import (DEV, capacity, check_attention, check_codes, check_dequant, check_f16_ulp, check_tie_rate,
                      compare_encoded, f16_bits, gpu_encode, half_np, oracle_encode_pair, token_norms,
                      upload_half, cb_tensor)
 
@@ -155,7 +155,7 @@ def test_flush_then_decode(oracle_codebooks):
     assert (cache.n_quant, cache.n_resid) == (2 * R, R)
     nsnq.nsnq_flush_residual(p, cbt, cache)
     assert (cache.n_quant, cache.n_resid) == (3 * R, 0)
-    cache.append_token(k[:, :, L].to(DEV), v[:, :, L].to(DEV))
+    nsnq.nsnq_append_kv(p, cbt, k[:, :, L].contiguous().to(DEV), v[:, :, L].contiguous().to(DEV), cache)
     torch.cuda.synchronize()
     ek, ev = oracle_encode_pair(k, v, R, cb)   # L + 1 tokens: 3R encoded, 1 residual
     assert ek["n_quant"] == 3 * R
@@ -200,6 +200,105 @@ def test_rht_and_scale_adjust(oracle_codebooks, bits, R, use_signs, adjust):
     oc.n_quant, oc.n_resid = nq, ek["n_resid"]
     o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), oc, num_splits=3).float().cpu().numpy()
     check_attention(o, ref)
+
+
+# ------------------------------------------------------------ ragged rows --
+
+def _row_state(cache: nsnq.KVCache, which: int, b: int, nq: int, r: int) -> dict:
+    h = cache.k if which == 0 else cache.v
+    R = h.resid.shape[2]
+    return dict(codes=h.codes[b:b + 1, :, :nq].cpu().numpy(), scales=f16_bits(h.scales[b:b + 1, :, :nq]),
+                mu=f16_bits(h.mu[b:b + 1, :, :nq // R]), resid=f16_bits(h.resid[b:b + 1]))
+
+
+def _check_row(cache, b, ek, ev):
+    """Row b against the oracle; returns (near-tie flips, codes compared)."""
+    nq, r = ek["n_quant"], ek["n_resid"]
+    flips = total = 0
+    for which, e in ((0, ek), (1, ev)):
+        g = _row_state(cache, which, b, nq, r)
+        flips += check_codes(g["codes"], e["codes"], e["gap"], pooled=True)
+        total += g["codes"].size
+        check_f16_ulp(g["scales"], e["scales"], "scales")
+        check_f16_ulp(g["mu"], e["mu"], "mu")
+        assert np.array_equal(g["resid"][..., :r, :], e["resid"][..., :r, :])
+    return flips, total
+
+
+@pytest.mark.parametrize("bits,R,Hq,Hkv", [(2, 64, 2, 2), (1, 128, 8, 2), (2, 128, 4, 1)])
+def test_ragged_prefill_append_decode(oracle_codebooks, bits, R, Hq, Hkv):
+    """Rows of different lengths (one empty): prefill, decode, then appends that
+    flush each row's window at its own step, and decode again; every row must
+    match the oracle's encoding of its own prefix."""
+    cb = oracle_codebooks[bits]
+    lengths = [0, 1, R, R + 1, 3 * R + 7, 5 * R]
+    B, T = len(lengths), R + 3
+    Lmax = max(lengths)
+    k, v = _kv(700 + bits, B, Hkv, Lmax + T)
+    q = synth.queries(700 + bits, 0, B, Hq, D)
+    p = nsnq.params(bits, R)
+    cbt = cb_tensor(cb)
+    cache = nsnq.KVCache(p, B, Hkv, capacity(Lmax + T, R), DEV, ragged=True)
+    lens = torch.tensor(lengths, dtype=torch.int32, device=DEV)
+    nsnq.nsnq_encode_kv_ragged(p, cbt, k.to(DEV), v.to(DEV), lens, Lmax, cache)
+    torch.cuda.synchronize()
+
+    def check_all(cur_len):
+        sq, sr = cache.seq_quant.cpu().tolist(), cache.seq_resid.cpu().tolist()
+        refs = []
+        flips = total = 0
+        for b, Lb in enumerate(cur_len):
+            ek = oracle.encode(k[b:b + 1, :, :Lb], R, cb)
+            ev = oracle.encode(v[b:b + 1, :, :Lb], R, cb)
+            assert (sq[b], sr[b]) == (ek["n_quant"], ek["n_resid"]), (b, Lb)
+            assert sq[b] <= cache.n_quant and sr[b] <= cache.n_resid
+            f, t = _check_row(cache, b, ek, ev)
+            flips, total = flips + f, total + t
+            refs.append((ek, ev))
+        check_tie_rate(flips, total)
+        out = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), cache).float().cpu().numpy()
+        for b, (ek, ev) in enumerate(refs):
+            if ek["n_quant"] + ek["n_resid"] == 0:
+                assert np.all(out[b] == 0)
+                continue
+            ref = oracle.reference_decode(q[b:b + 1], ek, ev, ek["n_quant"], ek["n_resid"], R, cb)
+            check_attention(out[b:b + 1], ref)
+        return refs
+
+    check_all(lengths)
+    # dequant over the bound range: rows past their own end read as zeros
+    if cache.n_quant > 0:
+        g = nsnq.nsnq_dequant(p, cbt, cache, 0, 0, cache.n_quant, torch.float32).cpu().numpy()
+        for b, Lb in enumerate(lengths):
+            nqb = cache.seq_quant[b].item()
+            assert np.all(g[b, :, nqb:] == 0)
+            if nqb:
+                e = oracle.encode(k[b:b + 1, :, :Lb], R, cb)
+                ref = oracle.dequant(e["codes"], e["scales"], e["mu"], R, cb)
+                same = np.all(_row_state(cache, 0, b, nqb, 0)["codes"] == e["codes"], axis=-1)
+                check_dequant(g[b:b + 1, :, :nqb], ref, token_norms(k[b:b + 1, :, :nqb].numpy()), mask=same)
+    for i in range(T):
+        idx = torch.tensor([Lb + i for Lb in lengths])
+        kn = k[torch.arange(B), :, idx].contiguous().to(DEV)
+        vn = v[torch.arange(B), :, idx].contiguous().to(DEV)
+        nsnq.nsnq_append_kv(p, cbt, kn, vn, cache)
+    torch.cuda.synchronize()
+    check_all([Lb + T for Lb in lengths])
+
+
+def test_uniform_append_flushes_full_window(oracle_codebooks):
+    cb = oracle_codebooks[2]
+    R, B, H = 64, 2, 2
+    L = 3 * R
+    k, v = _kv(800, B, H, L + 2)
+    p, cbt, cache = gpu_encode(k[:, :, :L], v[:, :, :L], 2, R, cb, cap=8 * R)
+    assert (cache.n_quant, cache.n_resid) == (2 * R, R)
+    for t in (L, L + 1):
+        nsnq.nsnq_append_kv(p, cbt, k[:, :, t].contiguous().to(DEV), v[:, :, t].contiguous().to(DEV), cache)
+    torch.cuda.synchronize()
+    assert (cache.n_quant, cache.n_resid) == (3 * R, 2)
+    ek, ev = oracle_encode_pair(k, v, R, cb)
+    compare_encoded(cache, ek, ev)
 
 
 # ------------------------------------------------------------------ k-means --
