@@ -37,6 +37,18 @@
  *      scales fp16   [batch][kv_heads][cap_tokens][2]   (n1, n2)
  *      mu     fp16   [batch][kv_heads][cap_tokens / R][d]
  *      resid  fp16   [batch][kv_heads][R][d]
+ *    With NSNQ_DOUBLE_QUANT, scales and mu instead hold one byte record per
+ *    block of R tokens, [batch][kv_heads][cap_tokens / R][record]:
+ *      scales record, 16 * ceil((2R + R/2 + 4) / 16) bytes:
+ *        [0, 2R)           N2 fp16 per token of the block
+ *        [2R, 2R + R/2)    s1 4-bit codes (token t: byte t/2, low nibble
+ *                          for even t)
+ *        then              S1, Z1 fp16 (step and zero of the codes), zeros
+ *      mu record, 80 bytes:
+ *        [0, 64)           mean 4-bit codes (channel c: byte c/2, low nibble
+ *                          for even c)
+ *        [64, 80)          (S, Z) fp16 of the channel groups 0-31, ..., 96-127
+ *    nsnq_buffer_bytes() gives every buffer's size.
  *    Every pointer must be 16-byte aligned.
  */
 #ifndef NSNQ_H
@@ -49,7 +61,7 @@
 extern "C" {
 #endif
 
-#define NSNQ_ABI_VERSION 3
+#define NSNQ_ABI_VERSION 4
 
 typedef int32_t nsnq_status;
 enum {
@@ -67,7 +79,16 @@ enum {
    * alpha = |u|^2 / (u . c_hat) so that its component along the Hadamard-
    * domain vector u is preserved (the error is orthogonal to u).  alpha is
    * folded into the stored n2, so dequantisation and attention are unchanged. */
-  NSNQ_SCALE_ADJUST = 1
+  NSNQ_SCALE_ADJUST = 1,
+  /* Double quantisation (technical summary sec. 3, DQ; machine review,
+   * implementation details: groups of 32 channels for the mean, of R tokens
+   * for s1, 4-bit round-to-nearest).  Each group stores Z = fp16(min) and
+   * S = fp16((max - min) / 15); a value v is coded q = clamp(rint((v - Z) / S),
+   * 0, 15) (q = 0 when S = 0) and read back as Z + S q.  The encoder divides
+   * tokens by the read-back s1 and subtracts the read-back mean, so the stored
+   * values reconstruct the vector up to the VQ error.  n2 stays fp16.  Changes
+   * the scales / mu layout (above). */
+  NSNQ_DOUBLE_QUANT = 2
 };
 
 /* Format parameters.  head_dim must be 128, bits 1 or 2 (sub-vectors of 8 or 4
@@ -126,6 +147,12 @@ typedef struct {
 /* ABI version (NSNQ_ABI_VERSION) and a static text for a status. */
 int32_t nsnq_abi_version(void);
 const char* nsnq_status_str(nsnq_status st);
+
+/* Sizes in bytes of the four buffers of ONE (batch row, KV head) unit of a
+ * cache of capacity cap_tokens (a multiple of R) in format p: codes, scales,
+ * mu (K or V alike) and resid.  Multiply by batch * kv_heads.  Host only. */
+nsnq_status nsnq_buffer_bytes(const nsnq_params* p, int32_t cap_tokens, size_t* codes, size_t* scales,
+                              size_t* mu, size_t* resid);
 
 /* Fit the codebook with Lloyd's k-means (technical summary sec. 3, "Codebook
  * Construction": k-means on synthetic torch.randn data, once, for any model).

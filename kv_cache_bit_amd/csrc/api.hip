@@ -22,7 +22,7 @@ nsnq_status check_params(const nsnq_params* p) {
   if (p->n_codewords != 256 || p->head_dim <= 0 || p->block_tokens <= 0) return NSNQ_EINVAL;
   if (p->head_dim != 128) return NSNQ_EUNSUPPORTED;
   if (p->block_tokens != 64 && p->block_tokens != 128) return NSNQ_EUNSUPPORTED;
-  if ((p->flags & ~NSNQ_SCALE_ADJUST) != 0 || p->reserved != 0) return NSNQ_EINVAL;
+  if ((p->flags & ~(NSNQ_SCALE_ADJUST | NSNQ_DOUBLE_QUANT)) != 0 || p->reserved != 0) return NSNQ_EINVAL;
   return NSNQ_OK;
 }
 
@@ -84,6 +84,7 @@ nsnq_status run_encode(const nsnq_params* p, const uint16_t* cb, const uint16_t*
   a.rc_r = rc_r;
   a.signs = p->hadamard_signs;
   a.scale_adjust = (p->flags & NSNQ_SCALE_ADJUST) ? 1 : 0;
+  a.dq = (p->flags & NSNQ_DOUBLE_QUANT) ? 1 : 0;
   return hip_status(launch_encode(a, sub_of(p), p->block_tokens, stream));
 }
 
@@ -124,6 +125,7 @@ nsnq_status run_ragged_flush(const nsnq_params* p, const uint16_t* cb, const nsn
   a.R = R;
   a.signs = p->hadamard_signs;
   a.scale_adjust = (p->flags & NSNQ_SCALE_ADJUST) ? 1 : 0;
+  a.dq = (p->flags & NSNQ_DOUBLE_QUANT) ? 1 : 0;
   a.fl_quant = c->seq_quant;
   a.fl_resid = c->seq_resid;
   return hip_status(launch_encode(a, sub_of(p), R, stream));
@@ -144,6 +146,25 @@ const char* nsnq_status_str(nsnq_status st) {
     case NSNQ_EWORKSPACE: return "workspace missing or too small";
     default: return "unknown status";
   }
+}
+
+nsnq_status nsnq_buffer_bytes(const nsnq_params* p, int32_t cap_tokens, size_t* codes, size_t* scales, size_t* mu,
+                              size_t* resid) {
+  nsnq_status s = check_params(p);
+  if (s != NSNQ_OK) return s;
+  const int R = p->block_tokens;
+  if (cap_tokens < 0 || cap_tokens % R != 0 || !codes || !scales || !mu || !resid) return NSNQ_EINVAL;
+  const size_t nb = (size_t)(cap_tokens / R);
+  *codes = (size_t)cap_tokens * (p->head_dim / sub_of(p));
+  if (p->flags & NSNQ_DOUBLE_QUANT) {
+    *scales = nb * (size_t)(((2 * R + R / 2 + 4) + 15) / 16 * 16);
+    *mu = nb * 80;
+  } else {
+    *scales = (size_t)cap_tokens * 4;
+    *mu = nb * (size_t)p->head_dim * 2;
+  }
+  *resid = (size_t)R * p->head_dim * 2;
+  return NSNQ_OK;
 }
 
 size_t nsnq_build_codebook_workspace_bytes(const nsnq_params* p) {
@@ -246,6 +267,7 @@ nsnq_status nsnq_encode_kv_ragged(const nsnq_params* p, const uint16_t* codebook
   a.R = R;
   a.signs = p->hadamard_signs;
   a.scale_adjust = (p->flags & NSNQ_SCALE_ADJUST) ? 1 : 0;
+  a.dq = (p->flags & NSNQ_DOUBLE_QUANT) ? 1 : 0;
   a.lens = lengths;
   a.lens_max = max_len;
   a.out_quant = cache->seq_quant;
@@ -363,6 +385,7 @@ nsnq_status nsnq_dequant(const nsnq_params* p, const uint16_t* codebook, const n
   a.out_f16 = out_dtype;
   a.signs = p->hadamard_signs;
   a.seq_quant = cache->seq_quant;
+  a.dq = (p->flags & NSNQ_DOUBLE_QUANT) ? 1 : 0;
   return hip_status(launch_dequant(a, sub_of(p), cache->batch * cache->kv_heads, (hipStream_t)stream));
 }
 
@@ -473,6 +496,7 @@ nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook
   a.signs = p->hadamard_signs;
   a.seq_quant = cache->seq_quant;
   a.seq_resid = cache->seq_resid;
+  a.dq = (p->flags & NSNQ_DOUBLE_QUANT) ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = pl.mfma ? launch_decode_mfma(a, sub_of(p), pl.gh, cache->batch, st)
                          : launch_decode(a, sub_of(p), pl.gh, cache->batch, pl.lds, st);

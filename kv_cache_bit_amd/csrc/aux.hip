@@ -28,18 +28,33 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
     const bool live = !a.seq_quant || a.tok0 + i < a.seq_quant[unit / a.H];  // ragged: past the row's end -> 0
     const int t = a.tok0 + (act ? i : 0);                               // cache token
     const int64_t ct = (int64_t)unit * a.cap + t;
+    const int64_t blk = (int64_t)unit * (a.cap / a.R) + t / a.R;
     const uint32_t code = a.codes[ct * S + slot];
-    const uint32_t sc = reinterpret_cast<const uint32_t*>(a.scales)[ct];
-    const float n1 = h2f(sc & 0xffff), n2 = h2f(sc >> 16);
+    float n1, n2, mv[SUB];
+    if (a.dq) {
+      const uint8_t* rec = reinterpret_cast<const uint8_t*>(a.scales) + blk * dq_record_bytes(a.R);
+      const uint32_t tq = dq_token(rec, a.R, t % a.R);
+      n1 = dq_value(dq_s1_params(rec, a.R), tq >> 16);
+      n2 = h2f(tq & 0xffff);
+      const uint8_t* mrec = reinterpret_cast<const uint8_t*>(a.mu) + blk * kDqMuRecord;
+#pragma unroll
+      for (int e = 0; e < SUB; e += 2) dq_mu_pair(mrec, (slot * SUB + e) / 2, mv[e], mv[e + 1]);
+    } else {
+      const uint32_t sc = reinterpret_cast<const uint32_t*>(a.scales)[ct];
+      n1 = h2f(sc & 0xffff);
+      n2 = h2f(sc >> 16);
+      const uint16_t* mp = a.mu + blk * kDim + slot * SUB;
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) mv[e] = h2f(mp[e]);
+    }
     float x[SUB];
 #pragma unroll
     for (int e = 0; e < SUB; ++e) x[e] = cbf[code * SUB + e];
     fwht128<SUB>(x, lane);
-    const uint16_t* mp = a.mu + ((int64_t)unit * (a.cap / a.R) + t / a.R) * kDim + slot * SUB;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) {
       const float sg = a.signs ? (float)a.signs[slot * SUB + e] : 1.f;
-      x[e] = live ? n1 * fmaf(n2, x[e] * (kInvSqrtD * sg), h2f(mp[e])) : 0.f;
+      x[e] = live ? n1 * fmaf(n2, x[e] * (kInvSqrtD * sg), mv[e]) : 0.f;
     }
     if (act) {
       const int64_t o = ((int64_t)unit * a.ntok + i) * kDim + slot * SUB;

@@ -79,7 +79,7 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&cw)[S / 
   }
 }
 
-template <int SUB, int GH>
+template <int SUB, int GH, bool DQ>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int S = kDim / SUB;
   constexpr int CW = S / 4;      // 32-bit words of codes per token
@@ -123,22 +123,44 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.vscales) + unit * a.cap + t0;
   const uint16_t* kmu = a.kmu + (unit * nbmu + t0 / a.R) * kDim;
   const uint16_t* vmu = a.vmu + (unit * nbmu + t0 / a.R) * kDim;
+  const int64_t blk0 = unit * nbmu + t0 / a.R;  // first block of the split (record index)
 
   const int sq = lane & 7, tg = lane >> 3;
   // one chunk's loads for this lane
   struct ChunkRegs {
     uint32_t kcw[CW];
-    uint32_t ksc, vsc, kmu2, vmu2;
+    uint32_t ksc, vsc;    // (n1, n2) fp16 pairs, or (q1 << 16 | n2) double-quantised
+    uint32_t kpar, vpar;  // double-quantised: the block's (S1, Z1)
+    // block means of channels 2 lane, 2 lane + 1: an fp16 pair, or two fp32
+    // read-back values when double-quantised
+    uint32_t km[DQ ? 2 : 1], vm[DQ ? 2 : 1];
     uint32_t vcw[8];
   };
   auto load_chunk = [&](int ch, ChunkRegs& r) {
     const int tl = ch * kChunk + lane;  // this lane's token for scores
     load_codes<S>(kc + (int64_t)tl * S, r.kcw);
-    r.ksc = ks[tl];
-    r.vsc = vs[tl];
     const int bl = (ch * kChunk) / a.R;
-    r.kmu2 = *reinterpret_cast<const uint32_t*>(kmu + (int64_t)bl * kDim + 2 * lane);
-    r.vmu2 = *reinterpret_cast<const uint32_t*>(vmu + (int64_t)bl * kDim + 2 * lane);
+    if constexpr (DQ) {
+      const int SRB = dq_record_bytes(a.R), tb = tl % a.R;
+      const uint8_t* kr = reinterpret_cast<const uint8_t*>(a.kscales) + (blk0 + bl) * SRB;
+      const uint8_t* vr = reinterpret_cast<const uint8_t*>(a.vscales) + (blk0 + bl) * SRB;
+      r.ksc = dq_token(kr, a.R, tb);
+      r.vsc = dq_token(vr, a.R, tb);
+      r.kpar = dq_s1_params(kr, a.R);
+      r.vpar = dq_s1_params(vr, a.R);
+      float m0, m1;
+      dq_mu_pair(reinterpret_cast<const uint8_t*>(a.kmu) + (blk0 + bl) * kDqMuRecord, lane, m0, m1);
+      r.km[0] = __float_as_uint(m0);
+      r.km[DQ ? 1 : 0] = __float_as_uint(m1);
+      dq_mu_pair(reinterpret_cast<const uint8_t*>(a.vmu) + (blk0 + bl) * kDqMuRecord, lane, m0, m1);
+      r.vm[0] = __float_as_uint(m0);
+      r.vm[DQ ? 1 : 0] = __float_as_uint(m1);
+    } else {
+      r.ksc = ks[tl];
+      r.vsc = vs[tl];
+      r.km[0] = *reinterpret_cast<const uint32_t*>(kmu + (int64_t)bl * kDim + 2 * lane);
+      r.vm[0] = *reinterpret_cast<const uint32_t*>(vmu + (int64_t)bl * kDim + 2 * lane);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint8_t* p = vc + (int64_t)(ch * kChunk + 8 * tg + i) * S + sq * SPT;
@@ -198,10 +220,26 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   for (; ch < nchunk; ch += 4) {
     ChunkRegs nxt;
     if (ch + 4 < nchunk) load_chunk(ch + 4, nxt);
-    const float kn1 = h2f(cur.ksc & 0xffff), kn2 = h2f(cur.ksc >> 16);
-    const float vn1 = h2f(cur.vsc & 0xffff), vn2 = h2f(cur.vsc >> 16);
-    const float km0 = h2f(cur.kmu2 & 0xffff), km1 = h2f(cur.kmu2 >> 16);
-    const float vm0 = h2f(cur.vmu2 & 0xffff), vm1 = h2f(cur.vmu2 >> 16);
+    float kn1, kn2, vn1, vn2, km0, km1, vm0, vm1;
+    if constexpr (DQ) {
+      kn1 = dq_value(cur.kpar, cur.ksc >> 16);
+      kn2 = h2f(cur.ksc & 0xffff);
+      vn1 = dq_value(cur.vpar, cur.vsc >> 16);
+      vn2 = h2f(cur.vsc & 0xffff);
+      km0 = __uint_as_float(cur.km[0]);
+      km1 = __uint_as_float(cur.km[DQ ? 1 : 0]);
+      vm0 = __uint_as_float(cur.vm[0]);
+      vm1 = __uint_as_float(cur.vm[DQ ? 1 : 0]);
+    } else {
+      kn1 = h2f(cur.ksc & 0xffff);
+      kn2 = h2f(cur.ksc >> 16);
+      vn1 = h2f(cur.vsc & 0xffff);
+      vn2 = h2f(cur.vsc >> 16);
+      km0 = h2f(cur.km[0] & 0xffff);
+      km1 = h2f(cur.km[0] >> 16);
+      vm0 = h2f(cur.vm[0] & 0xffff);
+      vm1 = h2f(cur.vm[0] >> 16);
+    }
 #pragma unroll
     for (int g = 0; g < GH; ++g) {
       // score of this lane's token
@@ -364,18 +402,23 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   a.out[(int64_t)bh * kDim + c] = f2h(num / den);
 }
 
-template <int SUB, int GH>
-static hipError_t launch_decode_t(const DecodeArgs& a, int B, size_t lds, hipStream_t stream) {
+template <int SUB, int GH, bool DQ>
+static hipError_t launch_decode_dq(const DecodeArgs& a, int B, size_t lds, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_split_kernel<SUB, GH>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_split_kernel<SUB, GH, DQ>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid(a.nsplit, B * a.Hkv * (a.G / GH)), block(256);
-  hipLaunchKernelGGL((decode_split_kernel<SUB, GH>), grid, block, lds, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<SUB, GH, DQ>), grid, block, lds, stream, a);
   return hipGetLastError();
+}
+
+template <int SUB, int GH>
+static hipError_t launch_decode_t(const DecodeArgs& a, int B, size_t lds, hipStream_t stream) {
+  return a.dq ? launch_decode_dq<SUB, GH, true>(a, B, lds, stream) : launch_decode_dq<SUB, GH, false>(a, B, lds, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int sub, int gh, int B, size_t lds, hipStream_t stream) {

@@ -89,9 +89,9 @@ struct MfmaSmem {
   static constexpr int qf = cbh + kCodewords * SUB / 2;  // [GQ][128] queries
   static constexpr int qr = qf + GQ * kDim;              // [GQ][128] H D q / sqrt(d)
   static constexpr int qmu = qr + GQ * kDim;             // [kMaxSplitBlocks][GQ] q . KMU_b
-  static constexpr int kmu = qmu + kMaxSplitBlocks * GQ;  // [kMaxSplitBlocks][128] fp16 K block means
+  static constexpr int kmu = qmu + kMaxSplitBlocks * GQ;  // [kMaxSplitBlocks][128] fp32 K block means
   static constexpr int VSTW = kMChunk * S / 4 + 4 * kMChunk;  // per wave: V codes, 4 per-token factors
-  static constexpr int vst = kmu + kMaxSplitBlocks * kDim / 2;
+  static constexpr int vst = kmu + kMaxSplitBlocks * kDim;
   static constexpr int main_end = vst + 4 * VSTW;
   // merge of the four waves
   static constexpr int mrg = 0;  // [4][GQ][2 + 128]
@@ -104,8 +104,8 @@ struct MfmaSmem {
   // persistent
   static constexpr int bc = cmax3(main_end, mrg_end, res_end);  // [kMaxChunks][GQ] beta
   static constexpr int mc = bc + kMaxChunks * GQ;                // [kMaxChunks][GQ] max
-  static constexpr int vmu = mc + kMaxChunks * GQ;               // [kMaxSplitBlocks][128] fp16 V block means
-  static constexpr int total = vmu + kMaxSplitBlocks * kDim / 2;
+  static constexpr int vmu = mc + kMaxChunks * GQ;               // [kMaxSplitBlocks][128] fp32 V block means
+  static constexpr int total = vmu + kMaxSplitBlocks * kDim;
 };
 
 // Channel held by accumulator row `row` (0..15) of value tile `tile` (0..7).
@@ -117,7 +117,7 @@ __device__ __forceinline__ int value_channel(int tile, int row) {
 
 }  // namespace
 
-template <int SUB, int GQ>
+template <int SUB, int GQ, bool DQ>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   using L = MfmaSmem<SUB, GQ>;
   constexpr int S = kDim / SUB;
@@ -153,6 +153,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.vscales) + unit * a.cap + t0;
   const uint16_t* kmu = a.kmu + (unit * nbmu + t0 / a.R) * kDim;
   const uint16_t* vmu = a.vmu + (unit * nbmu + t0 / a.R) * kDim;
+  const int64_t blk0 = unit * nbmu + t0 / a.R;  // first block of the split (record index)
 
   // One chunk's global loads for this lane: the K codes its score tiles need
   // (token 16 tau + m16, the 8 (2 bits) or 4 (1 bit) code bytes starting at
@@ -161,7 +162,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KCW = SUB == 4 ? 2 : 1;
   struct Ld {
     uint32_t kc[4][KCW];
-    uint32_t ksc, vsc;
+    uint32_t ksc, vsc;    // (n1, n2) fp16 pairs, or (q1 << 16 | n2) double-quantised
+    uint32_t kpar, vpar;  // double-quantised: the chunk's block (S1, Z1)
     uint4_t vcode[S / 16];
   };
   auto load = [&](int ch, Ld& r) {
@@ -177,8 +179,20 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         r.kc[tau][0] = *reinterpret_cast<const uint32_t*>(p);
       }
     }
-    r.ksc = ks[base + lane];
-    r.vsc = vs[base + lane];
+    if constexpr (DQ) {
+      const int SRB = dq_record_bytes(a.R);
+      const int64_t rb = blk0 + (int)(base / a.R);
+      const int tb = (int)((base + lane) % a.R);
+      const uint8_t* kr = reinterpret_cast<const uint8_t*>(a.kscales) + rb * SRB;
+      const uint8_t* vr = reinterpret_cast<const uint8_t*>(a.vscales) + rb * SRB;
+      r.ksc = dq_token(kr, a.R, tb);
+      r.vsc = dq_token(vr, a.R, tb);
+      r.kpar = dq_s1_params(kr, a.R);
+      r.vpar = dq_s1_params(vr, a.R);
+    } else {
+      r.ksc = ks[base + lane];
+      r.vsc = vs[base + lane];
+    }
 #pragma unroll
     for (int i = 0; i < S / 16; ++i) r.vcode[i] = *reinterpret_cast<const uint4_t*>(vc + (base + lane) * S + 16 * i);
   };
@@ -189,19 +203,29 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   // ---- per-split set-up: codebook, rotated queries, q . KMU_b -------------
   uint32_t* cb32 = reinterpret_cast<uint32_t*>(smem + L::cbh);
   for (int i = tid; i < kCodewords * SUB / 2; i += 256) cb32[i] = reinterpret_cast<const uint32_t*>(a.codebook)[i];
-  // the split's block means (at most 16 x 256 B each for K and V), all loads in flight together
+  // the split's block means as fp32 (at most 16 blocks x 128 channels for K
+  // and V), all loads in flight together
   {
-    uint32_t* kmul = reinterpret_cast<uint32_t*>(smem + L::kmu);
-    uint32_t* vmul = reinterpret_cast<uint32_t*>(smem + L::vmu);
-    const uint32_t* ksrc = reinterpret_cast<const uint32_t*>(kmu);
-    const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(vmu);
-    const int nw = nblk * kDim / 2;
-    uint32_t kt[4], vt[4];
+    float2* kmul = reinterpret_cast<float2*>(smem + L::kmu);
+    float2* vmul = reinterpret_cast<float2*>(smem + L::vmu);
+    const int nw = nblk * kDim / 2;  // channel pairs
+    float2 kt[4], vt[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = tid + 256 * j;
-      kt[j] = i < nw ? ksrc[i] : 0u;
-      vt[j] = i < nw ? vsrc[i] : 0u;
+      kt[j] = vt[j] = float2{0.f, 0.f};
+      if (i < nw) {
+        if constexpr (DQ) {
+          const int bl = i / (kDim / 2), cp = i % (kDim / 2);
+          dq_mu_pair(reinterpret_cast<const uint8_t*>(a.kmu) + (blk0 + bl) * kDqMuRecord, cp, kt[j].x, kt[j].y);
+          dq_mu_pair(reinterpret_cast<const uint8_t*>(a.vmu) + (blk0 + bl) * kDqMuRecord, cp, vt[j].x, vt[j].y);
+        } else {
+          const uint32_t k2 = reinterpret_cast<const uint32_t*>(kmu)[i];
+          const uint32_t v2 = reinterpret_cast<const uint32_t*>(vmu)[i];
+          kt[j] = float2{h2f(k2 & 0xffff), h2f(k2 >> 16)};
+          vt[j] = float2{h2f(v2 & 0xffff), h2f(v2 >> 16)};
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -222,21 +246,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   float* qmu = smem + L::qmu;
   for (int i = tid; i < nblk * GQ; i += 256) {
     const int bl = i / GQ, g = i % GQ;
-    const uint4* mp = reinterpret_cast<const uint4*>(smem + L::kmu) + bl * (kDim / 8);
+    const float4* mp = reinterpret_cast<const float4*>(smem + L::kmu) + bl * (kDim / 4);
     const float4* qg = reinterpret_cast<const float4*>(qf + g * kDim);
     float s0 = 0.f, s1 = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < kDim / 8; ++c) {
-      const uint4 m8 = mp[c];
-      const float4 qa = qg[2 * c], qb = qg[2 * c + 1];
-      s0 = fmaf(qa.x, h2f(m8.x & 0xffff), s0);
-      s1 = fmaf(qa.y, h2f(m8.x >> 16), s1);
-      s0 = fmaf(qa.z, h2f(m8.y & 0xffff), s0);
-      s1 = fmaf(qa.w, h2f(m8.y >> 16), s1);
-      s0 = fmaf(qb.x, h2f(m8.z & 0xffff), s0);
-      s1 = fmaf(qb.y, h2f(m8.z >> 16), s1);
-      s0 = fmaf(qb.z, h2f(m8.w & 0xffff), s0);
-      s1 = fmaf(qb.w, h2f(m8.w >> 16), s1);
+#pragma unroll 8
+    for (int c = 0; c < kDim / 4; ++c) {
+      const float4 m4 = mp[c], q4 = qg[c];
+      s0 = fmaf(q4.x, m4.x, s0);
+      s1 = fmaf(q4.y, m4.y, s1);
+      s0 = fmaf(q4.z, m4.z, s0);
+      s1 = fmaf(q4.w, m4.w, s1);
     }
     qmu[i] = s0 + s1;
   }
@@ -276,8 +295,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < S / 16; ++i) *reinterpret_cast<uint4_t*>(vcl + lane * S + 16 * i) = cur.vcode[i];
     {
-      const float kn1 = h2f(cur.ksc & 0xffff), kn2 = h2f(cur.ksc >> 16);
-      const float vn1 = h2f(cur.vsc & 0xffff), vn2 = h2f(cur.vsc >> 16);
+      float kn1, kn2, vn1, vn2;
+      if constexpr (DQ) {
+        kn1 = dq_value(cur.kpar, cur.ksc >> 16);
+        kn2 = h2f(cur.ksc & 0xffff);
+        vn1 = dq_value(cur.vpar, cur.vsc >> 16);
+        vn2 = h2f(cur.vsc & 0xffff);
+      } else {
+        kn1 = h2f(cur.ksc & 0xffff);
+        kn2 = h2f(cur.ksc >> 16);
+        vn1 = h2f(cur.vsc & 0xffff);
+        vn2 = h2f(cur.vsc >> 16);
+      }
       const float kas = a.scale_log2 * kn1;
       fka[lane] = kas * kn2;
       fkb[lane] = kas;
@@ -448,13 +477,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
     fwht128<2>(x, lane);
     // sum over chunks of 2^(m_c - M) beta_c MU_b(c), channels 2 lane, 2 lane + 1
-    const uint32_t* vmul = reinterpret_cast<const uint32_t*>(smem + L::vmu);
+    const float2* vmul = reinterpret_cast<const float2*>(smem + L::vmu);
     float om0 = 0.f, om1 = 0.f;
     for (int ci = 0; ci < nchunk; ++ci) {
       const float f = exp2f(mc[ci * GQ + g] - M) * bc[ci * GQ + g];
-      const uint32_t mu2 = vmul[((ci * kMChunk) / a.R) * (kDim / 2) + lane];
-      om0 = fmaf(f, h2f(mu2 & 0xffff), om0);
-      om1 = fmaf(f, h2f(mu2 >> 16), om1);
+      const float2 mu2 = vmul[((ci * kMChunk) / a.R) * (kDim / 2) + lane];
+      om0 = fmaf(f, mu2.x, om0);
+      om1 = fmaf(f, mu2.y, om1);
     }
     float* wo = ws_base + g * ws_head;
     wo[2 * lane] = fmaf(x[0], kInvSqrtD * sg0, om0);
@@ -478,19 +507,24 @@ size_t decode_mfma_lds_bytes(int sub, int gq) {
   return (size_t)w * sizeof(float);
 }
 
-template <int SUB, int GQ>
-static hipError_t launch_mfma_t(const DecodeArgs& a, int B, hipStream_t stream) {
+template <int SUB, int GQ, bool DQ>
+static hipError_t launch_mfma_dq(const DecodeArgs& a, int B, hipStream_t stream) {
   const size_t lds = (size_t)MfmaSmem<SUB, GQ>::total * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<SUB, GQ>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<SUB, GQ, DQ>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid(a.nsplit, B * a.Hkv * (a.G / GQ)), block(256);
-  hipLaunchKernelGGL((decode_mfma_kernel<SUB, GQ>), grid, block, lds, stream, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<SUB, GQ, DQ>), grid, block, lds, stream, a);
   return hipGetLastError();
+}
+
+template <int SUB, int GQ>
+static hipError_t launch_mfma_t(const DecodeArgs& a, int B, hipStream_t stream) {
+  return a.dq ? launch_mfma_dq<SUB, GQ, true>(a, B, stream) : launch_mfma_dq<SUB, GQ, false>(a, B, stream);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int sub, int gq, int B, hipStream_t stream) {

@@ -97,7 +97,20 @@ __device__ __forceinline__ void resid_copy(const EncodeArgs& a, int unit, int kv
   }
 }
 
-template <int SUB, int R>
+// Double-quantised format: bytes of one block's scales record (n2 fp16 per
+// token, s1 4-bit codes, their (S, Z) pair, padding to 16) and mean record
+// (4-bit codes of the 128 channels, (S, Z) per 32-channel group).
+template <int R>
+constexpr int dq_scales_bytes() { return ((2 * R + R / 2 + 4) + 15) / 16 * 16; }
+constexpr int kDqMuBytes = 80;
+
+// 4-bit round-to-nearest code of v in a group with fp16 zero Z and step S.
+__device__ __forceinline__ float rtn4_code(float v, float Z, float S) {
+  if (!(S > 0.f)) return 0.f;
+  return fminf(fmaxf(rintf((v - Z) / S), 0.f), 15.f);
+}
+
+template <int SUB, int R, bool DQ>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   if ((int)blockIdx.x >= a.nblk * a.n_units) {
     resid_copy(a, blockIdx.x - a.nblk * a.n_units, blockIdx.y);
@@ -206,15 +219,70 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   };
 
   // ---- pass 1: channel sums of y over the block ---------------------------
+  // Double-quantised format: s1 is first coded in 4 bits over the block and
+  // tokens are divided by the stored value n1_hat (so the reconstruction from
+  // stored values only carries the VQ error).
+  constexpr int SR = dq_scales_bytes<R>();
+  __shared__ float n1s[DQ ? R : 1];   // s1 per token
+  __shared__ float n1hs[DQ ? R : 1];  // n1_hat per token
+  uint8_t* srec = reinterpret_cast<uint8_t*>(a.scales[kv]) + ((int64_t)unit * (a.cap / R) + dst0 / R + blk) * SR;
+  uint8_t* mrec = reinterpret_cast<uint8_t*>(a.mu[kv]) + ((int64_t)unit * (a.cap / R) + dst0 / R + blk) * kDqMuBytes;
   float csum[SUB];
 #pragma unroll
   for (int e = 0; e < SUB; ++e) csum[e] = 0.f;
+  if constexpr (DQ) {
 #pragma unroll 4
-  for (int r = 0; r < ROWS; ++r) {
-    float y[SUB], n1;
-    norm_raw(load_raw(wave * TPW + r * TPR + tir), y, n1);
+    for (int r = 0; r < ROWS; ++r) {
+      const int tok = wave * TPW + r * TPR + tir;
+      float y[SUB], n1;
+      norm_raw(load_raw(tok), y, n1);
+      if (slot == 0) n1s[tok] = n1;
+    }
+    __syncthreads();
+    float lo = INFINITY, hi = -INFINITY;
+    for (int i = lane; i < R; i += kWave) {
+      lo = fminf(lo, n1s[i]);
+      hi = fmaxf(hi, n1s[i]);
+    }
+    lo = -group_max<kWave>(-lo);
+    hi = group_max<kWave>(hi);
+    const half_t Z1h = (half_t)lo, S1h = (half_t)((hi - lo) / 15.f);
+    const float Z1 = (float)Z1h, S1 = (float)S1h;
+    if (wave == 0) {
+      for (int i = lane; i < R / 2; i += kWave) {
+        const int q0 = (int)rtn4_code(n1s[2 * i], Z1, S1), q1 = (int)rtn4_code(n1s[2 * i + 1], Z1, S1);
+        srec[2 * R + i] = (uint8_t)(q0 | (q1 << 4));
+      }
+      if (lane == 0) {
+        *reinterpret_cast<uint32_t*>(srec + 2 * R + R / 2) = pack_h2(S1h, Z1h);
+        for (int i = 2 * R + R / 2 + 4; i < SR; ++i) srec[i] = 0;
+      }
+    }
+#pragma unroll 4
+    for (int r = 0; r < ROWS; ++r) {
+      const int tok = wave * TPW + r * TPR + tir;
+      const float nh = fmaf(S1, rtn4_code(n1s[tok], Z1, S1), Z1);
+      const float inv = nh > 0.f ? 1.f / nh : 0.f;
+      const raw_t raw = lds_raw(tok);
+      float v[SUB];
+      v[0] = h2f(raw.x & 0xffff); v[1] = h2f(raw.x >> 16);
+      v[2] = h2f(raw.y & 0xffff); v[3] = h2f(raw.y >> 16);
+      if constexpr (SUB == 8) {
+        v[4] = h2f(raw.z & 0xffff); v[5] = h2f(raw.z >> 16);
+        v[6] = h2f(raw.w & 0xffff); v[7] = h2f(raw.w >> 16);
+      }
 #pragma unroll
-    for (int e = 0; e < SUB; ++e) csum[e] += y[e];
+      for (int e = 0; e < SUB; ++e) csum[e] += v[e] * inv;
+      if (slot == 0) n1hs[tok] = nh;
+    }
+  } else {
+#pragma unroll 4
+    for (int r = 0; r < ROWS; ++r) {
+      float y[SUB], n1;
+      norm_raw(load_raw(wave * TPW + r * TPR + tir), y, n1);
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) csum[e] += y[e];
+    }
   }
   // combine the TPR lanes holding the same channels, then the 4 waves
 #pragma unroll
@@ -233,7 +301,33 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     const int c = slot * SUB + e;
     mu[e] = (red[0][c] + red[1][c] + red[2][c] + red[3][c]) * (1.0f / R);
   }
-  if (wave == 0 && tir == 0) {
+  if constexpr (DQ) {
+    // 4-bit codes of the mean in groups of 32 channels (32 / SUB slots); the
+    // pass below shifts by the stored mean mu_hat
+    constexpr int GL = 32 / SUB;
+    float lo = mu[0], hi = mu[0];
+#pragma unroll
+    for (int e = 1; e < SUB; ++e) {
+      lo = fminf(lo, mu[e]);
+      hi = fmaxf(hi, mu[e]);
+    }
+    lo = -group_max<GL>(-lo);
+    hi = group_max<GL>(hi);
+    const half_t Zh = (half_t)lo, Sh = (half_t)((hi - lo) / 15.f);
+    const float Zm = (float)Zh, Sm = (float)Sh;
+    int qm[SUB];
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) {
+      const float q = rtn4_code(mu[e], Zm, Sm);
+      qm[e] = (int)q;
+      mu[e] = fmaf(Sm, q, Zm);
+    }
+    if (wave == 0 && tir == 0) {
+#pragma unroll
+      for (int e = 0; e < SUB; e += 2) mrec[(slot * SUB + e) / 2] = (uint8_t)(qm[e] | (qm[e + 1] << 4));
+      if (slot % GL == 0) *reinterpret_cast<uint32_t*>(mrec + 64 + 4 * (slot / GL)) = pack_h2(Sh, Zh);
+    }
+  } else if (wave == 0 && tir == 0) {
     uint16_t* pm = a.mu[kv] + ((int64_t)unit * (a.cap / R) + dst0 / R + blk) * kDim + slot * SUB;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) pm[e] = f2h(mu[e]);
@@ -251,7 +345,19 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   for (int r = 0; r < ROWS; ++r) {
     const int tok = wave * TPW + r * TPR + tir;
     float u[SUB], n1;
-    norm_raw(lds_raw(tok), u, n1);
+    if constexpr (DQ) {
+      n1 = n1hs[tok];
+      const float inv = n1 > 0.f ? 1.f / n1 : 0.f;
+      const raw_t raw = lds_raw(tok);
+      u[0] = h2f(raw.x & 0xffff) * inv; u[1] = h2f(raw.x >> 16) * inv;
+      u[2] = h2f(raw.y & 0xffff) * inv; u[3] = h2f(raw.y >> 16) * inv;
+      if constexpr (SUB == 8) {
+        u[4] = h2f(raw.z & 0xffff) * inv; u[5] = h2f(raw.z >> 16) * inv;
+        u[6] = h2f(raw.w & 0xffff) * inv; u[7] = h2f(raw.w >> 16) * inv;
+      }
+    } else {
+      norm_raw(lds_raw(tok), u, n1);
+    }
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) {
@@ -359,8 +465,12 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
       if (uc > 0.f) n2s = n2 * (utot / uc);
     }
     if (slot == 0) {
-      const uint32_t pk = pack_h2((half_t)n1, (half_t)n2s);
-      *reinterpret_cast<uint32_t*>(scales + (tok_base + tok) * 2) = pk;
+      if constexpr (DQ) {
+        *reinterpret_cast<half_t*>(srec + 2 * tok) = (half_t)n2s;
+      } else {
+        const uint32_t pk = pack_h2((half_t)n1, (half_t)n2s);
+        *reinterpret_cast<uint32_t*>(scales + (tok_base + tok) * 2) = pk;
+      }
     }
   }
 }
@@ -418,11 +528,19 @@ hipError_t launch_encode(const EncodeArgs& a, int sub, int R, hipStream_t stream
   const bool rcopy = a.rc_r > 0 || a.lens != nullptr;
   dim3 grid(a.nblk * a.n_units + (rcopy ? a.n_units : 0), 2), block(256);
   if (grid.x == 0) return hipSuccess;
-  if (sub == 4 && R == 128) hipLaunchKernelGGL((encode_kernel<4, 128>), grid, block, 0, stream, a);
-  else if (sub == 4 && R == 64) hipLaunchKernelGGL((encode_kernel<4, 64>), grid, block, 0, stream, a);
-  else if (sub == 8 && R == 128) hipLaunchKernelGGL((encode_kernel<8, 128>), grid, block, 0, stream, a);
-  else if (sub == 8 && R == 64) hipLaunchKernelGGL((encode_kernel<8, 64>), grid, block, 0, stream, a);
-  else return hipErrorInvalidValue;
+  if (a.dq) {
+    if (sub == 4 && R == 128) hipLaunchKernelGGL((encode_kernel<4, 128, true>), grid, block, 0, stream, a);
+    else if (sub == 4 && R == 64) hipLaunchKernelGGL((encode_kernel<4, 64, true>), grid, block, 0, stream, a);
+    else if (sub == 8 && R == 128) hipLaunchKernelGGL((encode_kernel<8, 128, true>), grid, block, 0, stream, a);
+    else if (sub == 8 && R == 64) hipLaunchKernelGGL((encode_kernel<8, 64, true>), grid, block, 0, stream, a);
+    else return hipErrorInvalidValue;
+  } else {
+    if (sub == 4 && R == 128) hipLaunchKernelGGL((encode_kernel<4, 128, false>), grid, block, 0, stream, a);
+    else if (sub == 4 && R == 64) hipLaunchKernelGGL((encode_kernel<4, 64, false>), grid, block, 0, stream, a);
+    else if (sub == 8 && R == 128) hipLaunchKernelGGL((encode_kernel<8, 128, false>), grid, block, 0, stream, a);
+    else if (sub == 8 && R == 64) hipLaunchKernelGGL((encode_kernel<8, 64, false>), grid, block, 0, stream, a);
+    else return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ struct EncodeArgs {
   int rc_t0, rc_r;           // residual copy: first source token and count (0 = none)
   const int8_t* signs;       // randomised-Hadamard signs [128] or null
   int scale_adjust;          // fold alpha = |u|^2 / (u . c_hat) into n2
+  int dq;                    // double-quantised scales / mean records
   // ragged prefill: per-row stream lengths (device [B]); the block / residual
   // split of each row follows its own length, and the row counters are
   // written to out_quant / out_resid.  Null for uniform launches.
@@ -56,7 +57,36 @@ struct DequantArgs {
   int H, cap, R, tok0, ntok, out_f16;
   const int8_t* signs;
   const int32_t* seq_quant;  // ragged: tokens >= seq_quant[b] come out as 0
+  int dq;                    // double-quantised scales / mean records
 };
+
+// ---- double-quantised records (byte layout in nsnq.h) ----------------------
+__host__ __device__ constexpr int dq_record_bytes(int R) { return ((2 * R + R / 2 + 4) + 15) / 16 * 16; }
+constexpr int kDqMuRecord = 80;
+
+// (s1 code of token tb, n2 bits) of a scales record, as q << 16 | n2.
+__device__ __forceinline__ uint32_t dq_token(const uint8_t* rec, int R, int tb) {
+  const uint32_t n2 = *reinterpret_cast<const uint16_t*>(rec + 2 * tb);
+  const uint32_t q = (rec[2 * R + tb / 2] >> (4 * (tb & 1))) & 15u;
+  return n2 | (q << 16);
+}
+// (S1, Z1) fp16 pair of a scales record.
+__device__ __forceinline__ uint32_t dq_s1_params(const uint8_t* rec, int R) {
+  return *reinterpret_cast<const uint32_t*>(rec + 2 * R + R / 2);
+}
+// Read-back value Z + S q of an (S, Z) fp16 pair.
+__device__ __forceinline__ float dq_value(uint32_t sz, uint32_t q) {
+  const float S = (float)__builtin_bit_cast(_Float16, (uint16_t)(sz & 0xffff));
+  const float Z = (float)__builtin_bit_cast(_Float16, (uint16_t)(sz >> 16));
+  return fmaf(S, (float)q, Z);
+}
+// Mean of channels 2j and 2j + 1 (j < 64) from a mean record.
+__device__ __forceinline__ void dq_mu_pair(const uint8_t* rec, int j, float& m0, float& m1) {
+  const uint32_t b = rec[j];
+  const uint32_t sz = *reinterpret_cast<const uint32_t*>(rec + 64 + 4 * (j / 16));
+  m0 = dq_value(sz, b & 15u);
+  m1 = dq_value(sz, b >> 4);
+}
 
 struct DecodeArgs {
   const uint16_t* q;  // [B][Hq][d]
@@ -80,6 +110,7 @@ struct DecodeArgs {
   const int8_t* signs;  // randomised-Hadamard signs [128] or null
   const int32_t* seq_quant;  // ragged: per-row counters (null: n_quant / n_resid)
   const int32_t* seq_resid;
+  int dq;                    // double-quantised scales / mean records
 };
 
 // Per-row token counts of a decode launch.

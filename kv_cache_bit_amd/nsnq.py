@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libnsnq.so")
 
 NSNQ_OK, NSNQ_EINVAL, NSNQ_EUNSUPPORTED, NSNQ_EHIP, NSNQ_EWORKSPACE = range(5)
 NSNQ_SCALE_ADJUST = 1
+NSNQ_DOUBLE_QUANT = 2
 
 i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 P = ctypes.c_void_p
@@ -45,6 +46,7 @@ _PP, _PC = ctypes.POINTER(nsnq_params), ctypes.POINTER(nsnq_cache)
 _SIGNATURES = {
     "nsnq_abi_version": (i32, []),
     "nsnq_status_str": (ctypes.c_char_p, [i32]),
+    "nsnq_buffer_bytes": (i32, [_PP, i32, P, P, P, P]),
     "nsnq_build_codebook_workspace_bytes": (size_t, [_PP]),
     "nsnq_build_codebook": (i32, [_PP, P, i64, i32, P, P, P, P, P, size_t, P]),
     "nsnq_encode_kv": (i32, [_PP, P, P, P, i64, i64, i64, i32, _PC, P]),
@@ -125,6 +127,14 @@ def sub_dim(bits: int) -> int:
 
 def nsnq_abi_version() -> int:
     return lib().nsnq_abi_version()
+
+
+def nsnq_buffer_bytes(p: nsnq_params, cap_tokens: int) -> tuple[int, int, int, int]:
+    """Bytes of (codes, scales, mu, resid) per (batch row, KV head) unit."""
+    out = [ctypes.c_size_t() for _ in range(4)]
+    _check(lib().nsnq_buffer_bytes(ctypes.byref(p), cap_tokens, *[ctypes.byref(o) for o in out]),
+           "nsnq_buffer_bytes")
+    return tuple(o.value for o in out)
 
 
 def nsnq_build_codebook_workspace_bytes(p: nsnq_params) -> int:
@@ -262,8 +272,8 @@ def nsnq_fp16_decode_attention(q, k, v, softmax_scale: float | None = None, num_
 @dataclass
 class KVHalf:
     codes: torch.Tensor   # uint8 [B, H, cap, S]
-    scales: torch.Tensor  # fp16 [B, H, cap, 2]
-    mu: torch.Tensor      # fp16 [B, H, cap/R, d]
+    scales: torch.Tensor  # fp16 [B, H, cap, 2]; double-quantised: uint8 [B, H, cap/R, record bytes]
+    mu: torch.Tensor      # fp16 [B, H, cap/R, d]; double-quantised: uint8 [B, H, cap/R, 80]
     resid: torch.Tensor   # fp16 [B, H, R, d]
 
 
@@ -286,11 +296,20 @@ class KVCache:
         self.seq_quant = torch.zeros(batch, dtype=torch.int32, device=device) if ragged else None
         self.seq_resid = torch.zeros(batch, dtype=torch.int32, device=device) if ragged else None
 
+        self.dq = bool(p.flags & NSNQ_DOUBLE_QUANT)
+        _, sc_bytes, mu_bytes, _ = nsnq_buffer_bytes(p, cap_tokens)
+        nb = cap_tokens // R
+
         def half():
+            if self.dq:
+                scales = torch.zeros(batch, kv_heads, nb, sc_bytes // max(nb, 1), dtype=torch.uint8, device=device)
+                mu = torch.zeros(batch, kv_heads, nb, mu_bytes // max(nb, 1), dtype=torch.uint8, device=device)
+            else:
+                scales = torch.zeros(batch, kv_heads, cap_tokens, 2, dtype=torch.float16, device=device)
+                mu = torch.zeros(batch, kv_heads, nb, d, dtype=torch.float16, device=device)
             return KVHalf(
                 codes=torch.zeros(batch, kv_heads, cap_tokens, S, dtype=torch.uint8, device=device),
-                scales=torch.zeros(batch, kv_heads, cap_tokens, 2, dtype=torch.float16, device=device),
-                mu=torch.zeros(batch, kv_heads, cap_tokens // R, d, dtype=torch.float16, device=device),
+                scales=scales, mu=mu,
                 resid=torch.zeros(batch, kv_heads, R, d, dtype=torch.float16, device=device))
 
         self.k = half()

@@ -53,6 +53,10 @@ def lib():
             "orc_attention": (None, [P, i32, i32, i32, i32, P, P, i32, f64, P]),
             "orc_kmeans": (None, [P, i64, i32, i32, i32, P, P, P, P]),
             "orc_num_threads": (i32, []),
+            "orc_rtn4": (None, [P, i32, P, P, P, P, P]),
+            "orc_dq_scales_bytes": (i32, [i32]),
+            "orc_encode_dq": (i32, [P, i64, i32, i32, i32, i32, P, i32, P, i32, P, P, P, P, P, P, P, P, P]),
+            "orc_dequant_dq": (None, [P, P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(_lib, name)
@@ -137,10 +141,32 @@ def _signs(signs):
     return np.ascontiguousarray(signs, dtype=np.float64)
 
 
-def encode(x, R: int, codebook, with_u: bool = False, signs=None, scale_adjust: bool = False) -> dict:
+DQ_MU_BYTES = 80
+
+
+def dq_scales_bytes(R: int) -> int:
+    """Bytes of one block's scales record in the double-quantised format."""
+    return lib().orc_dq_scales_bytes(R)
+
+
+def rtn4(v) -> dict:
+    """4-bit round-to-nearest of one group: Z, S (fp16 bits), q, v_hat, margin."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    Z, S = ctypes.c_uint16(), ctypes.c_uint16()
+    q = np.empty(v.size, np.uint8)
+    vh = np.empty(v.size, np.float64)
+    m = np.empty(v.size, np.float64)
+    lib().orc_rtn4(_p(v), v.size, ctypes.byref(Z), ctypes.byref(S), _p(q), _p(vh), _p(m))
+    return dict(Z=Z.value, S=S.value, q=q, vhat=vh, margin=m)
+
+
+def encode(x, R: int, codebook, with_u: bool = False, signs=None, scale_adjust: bool = False,
+           dq: bool = False) -> dict:
     """Encode streams x fp16 [..., L, d] (leading dims are independent units).
     signs: +-1 [d] for the randomised Hadamard transform (None: plain);
-    scale_adjust: Strategy-3 scale folded into n2.
+    scale_adjust: Strategy-3 scale folded into n2; dq: double-quantised format
+    (scales [..., nq/R, dq_scales_bytes(R)] and mu [..., nq/R, 80] uint8
+    records, plus n1hat / m1 per token and mmu per block channel).
 
     Returns codes [..., nq, S] uint8, scales [..., nq, 2] (fp16 bits),
     mu [..., nq/R, d] (fp16 bits), resid [..., R, d] (fp16 bits, rows >= r
@@ -160,6 +186,23 @@ def encode(x, R: int, codebook, with_u: bool = False, signs=None, scale_adjust: 
     gap = np.zeros((n_units, nq, S), np.float64)
     u = np.zeros((n_units, nq, d), np.float64) if with_u else None
     sg = _signs(signs)
+    if dq:
+        SR = dq_scales_bytes(R)
+        scales = np.zeros((n_units, nq // R, SR), np.uint8)
+        mu = np.zeros((n_units, nq // R, DQ_MU_BYTES), np.uint8)
+        n1hat = np.zeros((n_units, nq), np.float64)
+        m1 = np.zeros((n_units, nq), np.float64)
+        mmu = np.zeros((n_units, nq // R, d), np.float64)
+        lib().orc_encode_dq(_p(xb), n_units, L, d, R, s, _p(cb), ncw, _p(sg) if sg is not None else None,
+                            int(scale_adjust), _p(codes), _p(scales), _p(mu), _p(resid), _p(gap),
+                            _p(u) if with_u else None, _p(n1hat), _p(m1), _p(mmu))
+        out = dict(codes=codes.reshape(*lead, nq, S), scales=scales.reshape(*lead, nq // R, SR),
+                   mu=mu.reshape(*lead, nq // R, DQ_MU_BYTES), resid=resid.reshape(*lead, R, d),
+                   gap=gap.reshape(*lead, nq, S), n1hat=n1hat.reshape(*lead, nq), m1=m1.reshape(*lead, nq),
+                   mmu=mmu.reshape(*lead, nq // R, d), n_quant=nq, n_resid=r, dq=True)
+        if with_u:
+            out["u"] = u.reshape(*lead, nq, d)
+        return out
     lib().orc_encode(_p(xb), n_units, L, d, R, s, _p(cb), ncw, _p(sg) if sg is not None else None,
                      int(scale_adjust), _p(codes), _p(scales), _p(mu), _p(resid), _p(gap),
                      _p(u) if with_u else None)
@@ -172,9 +215,26 @@ def encode(x, R: int, codebook, with_u: bool = False, signs=None, scale_adjust: 
 
 
 def dequant(codes, scales, mu, R: int, codebook, tok0: int = 0, ntok: int | None = None,
-            signs=None) -> np.ndarray:
+            signs=None, dq: bool = False) -> np.ndarray:
     """Reconstruct tokens [tok0, tok0+ntok) of streams with codes [..., cap, S],
-    scales [..., cap, 2] (fp16 bits), mu [..., cap/R, d] (fp16 bits)."""
+    scales [..., cap, 2] (fp16 bits), mu [..., cap/R, d] (fp16 bits); with
+    dq, scales and mu are the uint8 records of the double-quantised format."""
+    if dq:
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.uint8)
+        mu = np.ascontiguousarray(mu, dtype=np.uint8)
+        cb = as_f16_bits(codebook)
+        *lead, cap, S = codes.shape
+        s = cb.shape[1]
+        d = S * s
+        n_units = int(np.prod(lead)) if lead else 1
+        if ntok is None:
+            ntok = cap - tok0
+        out = np.empty((n_units, ntok, d), np.float64)
+        sg = _signs(signs)
+        lib().orc_dequant_dq(_p(codes), _p(scales), _p(mu), n_units, cap, tok0, ntok, d, R, s, _p(cb),
+                             _p(sg) if sg is not None else None, _p(out))
+        return out.reshape(*lead, ntok, d)
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = as_f16_bits(scales)
     mu = as_f16_bits(mu)
@@ -237,10 +297,11 @@ def reference_decode(q, k_cache: dict, v_cache: dict, n_quant: int, n_resid: int
         scale = 1.0 / np.sqrt(d)
     parts_k, parts_v = [], []
     if n_quant > 0:
+        dq = bool(k_cache.get("dq", False))
         parts_k.append(dequant(k_cache["codes"], k_cache["scales"], k_cache["mu"], R, codebook, 0, n_quant,
-                               signs=signs))
+                               signs=signs, dq=dq))
         parts_v.append(dequant(v_cache["codes"], v_cache["scales"], v_cache["mu"], R, codebook, 0, n_quant,
-                               signs=signs))
+                               signs=signs, dq=dq))
     if n_resid > 0:
         parts_k.append(f16_to_f64(as_f16_bits(k_cache["resid"])[..., :n_resid, :]))
         parts_v.append(f16_to_f64(as_f16_bits(v_cache["resid"])[..., :n_resid, :]))

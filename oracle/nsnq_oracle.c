@@ -321,6 +321,228 @@ int orc_encode(const uint16_t* x, int64_t n_units, int L, int d, int R, int s,
   return nq;
 }
 
+/* --------------------------------------------- double quantisation --- */
+
+/* Double quantisation [P3 sec. 3, DQ: the NSN parameters (the mean o and the
+ * scale s1) are stored in 4 bits; P4 implementation details: groups of 32
+ * channels for o, of the residual size R for s1, round-to-nearest].  Reading
+ * taken here: asymmetric min/max round-to-nearest per group,
+ *   Z = fp16(min v), S = fp16((max v - min v) / 15),
+ *   q_i = clamp(rint((v_i - Z) / S), 0, 15)   (S = 0: q_i = 0),
+ *   v_hat_i = Z + S q_i,
+ * and the stored (quantised) values are the ones the NSN forward pass uses:
+ * tokens are divided by n1_hat and shifted by mu_hat, so the reconstruction
+ * n1_hat (N2 H c_hat + mu_hat) differs from x only by the VQ error.  n2 stays
+ * fp16.  margin_i = | frac((v_i - Z) / S) - 1/2 | is how far the rounding
+ * decision is from a tie (in steps; 1/2 when S = 0). */
+void orc_rtn4(const double* v, int n, uint16_t* Zb, uint16_t* Sb, uint8_t* q, double* vhat, double* margin) {
+  double lo = v[0], hi = v[0];
+  for (int i = 1; i < n; ++i) {
+    if (v[i] < lo) lo = v[i];
+    if (v[i] > hi) hi = v[i];
+  }
+  uint16_t zb = orc_d2h(lo), sb = orc_d2h((hi - lo) / 15.0);
+  double Z = orc_h2d(zb), S = orc_h2d(sb);
+  for (int i = 0; i < n; ++i) {
+    double t = S > 0.0 ? (v[i] - Z) / S : 0.0;
+    double k = rint(t);
+    if (k < 0.0) k = 0.0;
+    if (k > 15.0) k = 15.0;
+    q[i] = (uint8_t)k;
+    vhat[i] = Z + S * k;
+    if (margin) margin[i] = S > 0.0 ? fabs(t - floor(t) - 0.5) : 0.5;
+  }
+  *Zb = zb;
+  *Sb = sb;
+}
+
+/* Byte layout of one block of R tokens (per stream) in the double-quantised
+ * format:
+ *   scales record, orc_dq_scales_bytes(R) bytes:
+ *     [0, 2R)            n2 fp16 per token
+ *     [2R, 2R + R/2)     q1 nibbles (token t: byte t/2, low nibble for even t)
+ *     next 4 bytes       S1, Z1 (fp16)
+ *     zero padding to a multiple of 16
+ *   mean record, 80 bytes:
+ *     [0, 64)            mu nibbles (channel c: byte c/2, low nibble for even c)
+ *     [64, 80)           (S, Z) fp16 pairs of the four 32-channel groups */
+int orc_dq_scales_bytes(int R) { return ((2 * R + R / 2 + 4) + 15) / 16 * 16; }
+#define ORC_DQ_MU_BYTES 80
+
+static void put_h(uint8_t* p, uint16_t h) { p[0] = (uint8_t)(h & 0xff); p[1] = (uint8_t)(h >> 8); }
+static uint16_t get_h(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+static int get_nib(const uint8_t* p, int i) { return (p[i / 2] >> (4 * (i & 1))) & 15; }
+
+/* Encode one stream in the double-quantised format (same split, NSN, Hadamard,
+ * VQ and options as orc_encode_unit).  scales_rec: [nq/R][orc_dq_scales_bytes]
+ * bytes, mu_rec: [nq/R][80] bytes.  Optional outputs per quantised token:
+ * n1hat, m1 (margin of its q1); per block and channel: mmu (margin of its mu
+ * code).  Returns nq. */
+int orc_encode_unit_dq(const uint16_t* x, int L, int d, int R, int s,
+                       const uint16_t* cb, int ncw, const double* signs, int scale_adjust,
+                       uint8_t* codes, uint8_t* scales_rec, uint8_t* mu_rec, uint16_t* resid,
+                       double* gap, double* u_out, double* n1hat_out, double* m1_out, double* mmu_out) {
+  int r = orc_resid_count(L, R);
+  int nq = L - r;
+  int S = d / s;
+  int SR = orc_dq_scales_bytes(R);
+  double sqrt_d = sqrt((double)d);
+  double* n1 = (double*)malloc(sizeof(double) * R);
+  double* n1h = (double*)malloc(sizeof(double) * R);
+  double* m1 = (double*)malloc(sizeof(double) * R);
+  uint8_t* q1 = (uint8_t*)malloc(R);
+  double* y = (double*)malloc(sizeof(double) * (size_t)R * d);
+  double* mu = (double*)malloc(sizeof(double) * d);
+  double* muh = (double*)malloc(sizeof(double) * d);
+  double* mm = (double*)malloc(sizeof(double) * d);
+  uint8_t* qm = (uint8_t*)malloc(d);
+  double* w = (double*)malloc(sizeof(double) * d);
+  double* u = (double*)malloc(sizeof(double) * d);
+  double* Hm = (double*)malloc(sizeof(double) * (size_t)d * d);
+  double* cbd = (double*)malloc(sizeof(double) * (size_t)ncw * s);
+  orc_hadamard_matrix(d, Hm);
+  for (size_t e = 0; e < (size_t)ncw * s; ++e) cbd[e] = orc_h2d(cb[e]);
+  for (int blk = 0; blk < nq / R; ++blk) {
+    const uint16_t* xb = x + (size_t)blk * R * d;
+    uint8_t* sr = scales_rec + (size_t)blk * SR;
+    uint8_t* mr = mu_rec + (size_t)blk * ORC_DQ_MU_BYTES;
+    memset(sr, 0, SR);
+    memset(mr, 0, ORC_DQ_MU_BYTES);
+    /* s1 per token, then its 4-bit group over the block */
+    for (int t = 0; t < R; ++t) {
+      double ss = 0.0;
+      for (int c = 0; c < d; ++c) {
+        double v = orc_h2d(xb[(size_t)t * d + c]);
+        ss += v * v;
+      }
+      n1[t] = sqrt(ss) / sqrt_d;
+    }
+    uint16_t Z1, S1;
+    orc_rtn4(n1, R, &Z1, &S1, q1, n1h, m1);
+    for (int t = 0; t < R; ++t) sr[2 * R + t / 2] |= (uint8_t)(q1[t] << (4 * (t & 1)));
+    put_h(sr + 2 * R + R / 2, S1);
+    put_h(sr + 2 * R + R / 2 + 2, Z1);
+    /* first normalisation by the stored s1, block mean, its 4-bit groups */
+    for (int t = 0; t < R; ++t)
+      for (int c = 0; c < d; ++c) {
+        double v = orc_h2d(xb[(size_t)t * d + c]);
+        y[(size_t)t * d + c] = n1h[t] > 0.0 ? v / n1h[t] : 0.0;
+      }
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int t = 0; t < R; ++t) acc += y[(size_t)t * d + c];
+      mu[c] = acc / (double)R;
+    }
+    for (int g = 0; g < d / 32; ++g) {
+      uint16_t Zm, Sm;
+      orc_rtn4(mu + 32 * g, 32, &Zm, &Sm, qm + 32 * g, muh + 32 * g, mm + 32 * g);
+      put_h(mr + 64 + 4 * g, Sm);
+      put_h(mr + 64 + 4 * g + 2, Zm);
+    }
+    for (int c = 0; c < d; ++c) mr[c / 2] |= (uint8_t)(qm[c] << (4 * (c & 1)));
+    if (mmu_out) memcpy(mmu_out + (size_t)blk * d, mm, sizeof(double) * d);
+    /* shift by the stored mean, second normalisation, Hadamard, VQ */
+    for (int t = 0; t < R; ++t) {
+      size_t tok = (size_t)blk * R + t;
+      double ss = 0.0;
+      for (int c = 0; c < d; ++c) {
+        double zc = y[(size_t)t * d + c] - muh[c];
+        ss += zc * zc;
+      }
+      double n2 = sqrt(ss) / sqrt_d;
+      if (n2 < NSN_N2_FLOOR) n2 = 0.0;
+      for (int c = 0; c < d; ++c) {
+        double zc = y[(size_t)t * d + c] - muh[c];
+        w[c] = (n2 > 0.0 ? zc / n2 : 0.0) * (signs ? signs[c] : 1.0);
+      }
+      matvec(Hm, w, u, d);
+      if (u_out) memcpy(u_out + tok * d, u, sizeof(double) * d);
+      double uu = 0.0, uc = 0.0;
+      for (int j = 0; j < S; ++j) {
+        double g;
+        int code = vq_dbl(u + (size_t)j * s, s, cbd, ncw, NULL, &g);
+        codes[tok * S + j] = (uint8_t)code;
+        if (gap) gap[tok * S + j] = g;
+        for (int e = 0; e < s; ++e) {
+          uu += u[j * s + e] * u[j * s + e];
+          uc += u[j * s + e] * cbd[(size_t)code * s + e];
+        }
+      }
+      double alpha = (scale_adjust && uc > 0.0) ? uu / uc : 1.0;
+      put_h(sr + 2 * t, orc_d2h(n2 * alpha));
+      if (n1hat_out) n1hat_out[tok] = n1h[t];
+      if (m1_out) m1_out[tok] = m1[t];
+    }
+  }
+  for (int t = 0; t < r; ++t)
+    memcpy(resid + (size_t)t * d, x + (size_t)(nq + t) * d, sizeof(uint16_t) * d);
+  free(n1); free(n1h); free(m1); free(q1); free(y); free(mu); free(muh); free(mm); free(qm);
+  free(w); free(u); free(Hm); free(cbd);
+  return nq;
+}
+
+int orc_encode_dq(const uint16_t* x, int64_t n_units, int L, int d, int R, int s,
+                  const uint16_t* cb, int ncw, const double* signs, int scale_adjust,
+                  uint8_t* codes, uint8_t* scales_rec, uint8_t* mu_rec, uint16_t* resid,
+                  double* gap, double* u_out, double* n1hat, double* m1, double* mmu) {
+  int r = orc_resid_count(L, R);
+  int nq = L - r;
+  int S = d / s;
+  int SR = orc_dq_scales_bytes(R);
+  int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (i = 0; i < n_units; ++i) {
+    orc_encode_unit_dq(x + (size_t)i * L * d, L, d, R, s, cb, ncw, signs, scale_adjust,
+                       codes + (size_t)i * nq * S, scales_rec + (size_t)i * (nq / R) * SR,
+                       mu_rec + (size_t)i * (nq / R) * ORC_DQ_MU_BYTES, resid + (size_t)i * R * d,
+                       gap ? gap + (size_t)i * nq * S : NULL, u_out ? u_out + (size_t)i * nq * d : NULL,
+                       n1hat ? n1hat + (size_t)i * nq : NULL, m1 ? m1 + (size_t)i * nq : NULL,
+                       mmu ? mmu + (size_t)i * (nq / R) * d : NULL);
+  }
+  return nq;
+}
+
+/* Reconstruct tokens [tok0, tok0 + ntok) of streams in the double-quantised
+ * format (cap_tokens / R records each):
+ *   x_hat = n1_hat (N2 diag(signs) H c_hat + mu_hat). */
+void orc_dequant_dq(const uint8_t* codes, const uint8_t* scales_rec, const uint8_t* mu_rec,
+                    int64_t n_units, int cap_tokens, int tok0, int ntok, int d, int R, int s,
+                    const uint16_t* cb, const double* signs, double* out) {
+  int S = d / s;
+  int SR = orc_dq_scales_bytes(R);
+  int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (i = 0; i < n_units; ++i) {
+    double* chat = (double*)malloc(sizeof(double) * d);
+    double* rot = (double*)malloc(sizeof(double) * d);
+    double* Hm = (double*)malloc(sizeof(double) * (size_t)d * d);
+    orc_hadamard_matrix(d, Hm);
+    const uint8_t* cu = codes + (size_t)i * cap_tokens * S;
+    for (int k = 0; k < ntok; ++k) {
+      int t = tok0 + k;
+      const uint8_t* sr = scales_rec + ((size_t)i * (cap_tokens / R) + t / R) * SR;
+      const uint8_t* mr = mu_rec + ((size_t)i * (cap_tokens / R) + t / R) * ORC_DQ_MU_BYTES;
+      int tb = t % R;
+      double n1h = orc_h2d(get_h(sr + 2 * R + R / 2 + 2)) +
+                   orc_h2d(get_h(sr + 2 * R + R / 2)) * get_nib(sr + 2 * R, tb);
+      double N2 = orc_h2d(get_h(sr + 2 * tb));
+      for (int j = 0; j < S; ++j) {
+        int code = cu[(size_t)t * S + j];
+        for (int e = 0; e < s; ++e) chat[j * s + e] = orc_h2d(cb[(size_t)code * s + e]);
+      }
+      matvec(Hm, chat, rot, d);
+      for (int c = 0; c < d; ++c) {
+        int g = c / 32;
+        double muh = orc_h2d(get_h(mr + 64 + 4 * g + 2)) + orc_h2d(get_h(mr + 64 + 4 * g)) * get_nib(mr, c);
+        out[((size_t)i * ntok + k) * d + c] = n1h * (N2 * (signs ? signs[c] : 1.0) * rot[c] + muh);
+      }
+    }
+    free(chat);
+    free(rot);
+    free(Hm);
+  }
+}
+
 /* ------------------------------------------------------------- dequant --- */
 
 /* Reconstruct tokens [tok0, tok0 + ntok) of one stream from stored values only:

@@ -51,6 +51,9 @@ def half_np(cache: nsnq.KVCache, which: int, n_tokens: int | None = None) -> dic
     h = cache.k if which == 0 else cache.v
     nq = cache.n_quant if n_tokens is None else n_tokens
     R = h.resid.shape[2]
+    if getattr(cache, "dq", False):
+        return dict(codes=h.codes[:, :, :nq].cpu().numpy(), scales=h.scales[:, :, :nq // R].cpu().numpy(),
+                    mu=h.mu[:, :, :nq // R].cpu().numpy(), resid=f16_bits(h.resid))
     return dict(codes=h.codes[:, :, :nq].cpu().numpy(), scales=f16_bits(h.scales[:, :, :nq]),
                 mu=f16_bits(h.mu[:, :, :nq // R]), resid=f16_bits(h.resid))
 
@@ -61,8 +64,12 @@ def upload_half(cache: nsnq.KVCache, which: int, enc: dict):
     nq = enc["codes"].shape[-2]
     R = h.resid.shape[2]
     h.codes[:, :, :nq].copy_(torch.from_numpy(enc["codes"]))
-    h.scales[:, :, :nq].copy_(torch.from_numpy(enc["scales"].view(np.float16)))
-    h.mu[:, :, :nq // R].copy_(torch.from_numpy(enc["mu"].view(np.float16)))
+    if enc.get("dq", False):
+        h.scales[:, :, :nq // R].copy_(torch.from_numpy(enc["scales"]))
+        h.mu[:, :, :nq // R].copy_(torch.from_numpy(enc["mu"]))
+    else:
+        h.scales[:, :, :nq].copy_(torch.from_numpy(enc["scales"].view(np.float16)))
+        h.mu[:, :, :nq // R].copy_(torch.from_numpy(enc["mu"].view(np.float16)))
     h.resid.copy_(torch.from_numpy(enc["resid"].view(np.float16)))
 
 
@@ -142,3 +149,62 @@ def compare_encoded(cache: nsnq.KVCache, ek: dict, ev: dict, units=None, scale_a
         assert np.array_equal(gh["resid"][..., :e["n_resid"], :], e["resid"][..., :e["n_resid"], :])
         out.append(n)
     return out
+
+
+# ---------------------------------------------------- double quantisation --
+
+DQ_MARGIN = 0.02  # 4-bit decisions this close (in steps) to a rounding tie may differ (fp32 vs fp64)
+
+
+def _dq_fields(sc: np.ndarray, mu: np.ndarray, R: int):
+    """Parse double-quantised records [..., nb, bytes] into (n2 bits [..., nb, R],
+    q1 [..., nb, R], s1 (S, Z) bits [..., nb, 2], qm [..., nb, 128], mu (S, Z)
+    bits [..., nb, 4, 2])."""
+    n2 = np.ascontiguousarray(sc[..., :2 * R]).view(np.uint16)
+    nib = sc[..., 2 * R:2 * R + R // 2]
+    q1 = np.stack([nib & 15, nib >> 4], axis=-1).reshape(*nib.shape[:-1], R)
+    sz = np.ascontiguousarray(sc[..., 2 * R + R // 2:2 * R + R // 2 + 4]).view(np.uint16)
+    qm = np.stack([mu[..., :64] & 15, mu[..., :64] >> 4], axis=-1).reshape(*mu.shape[:-1], 128)
+    msz = np.ascontiguousarray(mu[..., 64:80]).view(np.uint16).reshape(*mu.shape[:-1], 4, 2)
+    return n2, q1, sz, qm, msz
+
+
+def compare_encoded_dq(cache: nsnq.KVCache, ek: dict, ev: dict, R: int, scale_adjust: bool = False):
+    """Double-quantised caches against the oracle.  Per block: the fp16 (S, Z)
+    pairs within one ulp; the 4-bit codes equal except for decisions within
+    DQ_MARGIN of a tie; a block whose 4-bit decisions all agree is then held to
+    the plain bars (codes with the near-tie rule, n2 within one ulp).  Blocks
+    with a differing decision (expected rarely) are at most 2% of blocks.
+    Returns the list of per-half boolean block masks (True = compared fully)."""
+    masks = []
+    for which, e in ((0, ek), (1, ev)):
+        gh = half_np(cache, which)
+        gn2, gq1, gsz, gqm, gmsz = _dq_fields(gh["scales"], gh["mu"], R)
+        on2, oq1, osz, oqm, omsz = _dq_fields(e["scales"], e["mu"], R)
+        nb = gq1.shape[-2]
+        # (S, Z) pairs within one fp16 ulp
+        check_f16_ulp(gsz, osz, "s1 (S, Z)", max_flip_frac=0.05)
+        check_f16_ulp(gmsz, omsz, "mean (S, Z)", max_flip_frac=0.05)
+        m1 = e["m1"].reshape(oq1.shape)
+        mmu = e["mmu"].reshape(oqm.shape)
+        same_par = np.all(gsz == osz, axis=-1) & np.all(gmsz == omsz, axis=(-1, -2))
+        d1 = (gq1 != oq1)
+        dm = (gqm != oqm)
+        # with equal (S, Z), differing codes only near a tie
+        assert not np.any(d1 & same_par[..., None] & (m1 >= DQ_MARGIN)), "s1 code differs away from a tie"
+        assert not np.any(dm & same_par[..., None] & (mmu >= DQ_MARGIN)), "mean code differs away from a tie"
+        full = same_par & ~np.any(d1, axis=-1) & ~np.any(dm, axis=-1)
+        assert (~full).sum() <= max(0.02 * full.size, 1), f"{(~full).sum()} of {full.size} blocks differ in 4-bit decisions"
+        S = gh["codes"].shape[-1]
+        cg = gh["codes"].reshape(*gh["codes"].shape[:-2], nb, R, S)
+        co = e["codes"].reshape(cg.shape)
+        gap = e["gap"].reshape(cg.shape)
+        n = check_codes(cg[full], co[full], gap[full], "codes (double-quantised)")
+        if scale_adjust:
+            same = np.all(cg[full] == co[full], axis=-1)
+            check_f16_ulp(gn2[full][same], on2[full][same], "n2")
+        else:
+            check_f16_ulp(gn2[full], on2[full], "n2")
+        assert np.array_equal(gh["resid"][..., :e["n_resid"], :], e["resid"][..., :e["n_resid"], :])
+        masks.append(full)
+    return masks

@@ -26,10 +26,10 @@ def nsnq():
 
 def test_exports_every_declared_symbol(nsnq):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(nsnq.lib(), n), n
-    assert nsnq.nsnq_abi_version() == 3
+    assert nsnq.nsnq_abi_version() == 4
     assert nsnq.lib().nsnq_status_str(1) == b"invalid argument"
 
 
@@ -120,3 +120,21 @@ def test_counters_untouched_on_error(nsnq):
     good = nsnq.params(2, 128)
     assert nsnq.lib().nsnq_flush_residual(ctypes.byref(good), 0x1000, ctypes.byref(c), None) == nsnq.NSNQ_EINVAL
     assert (c.n_quant, c.n_resid) == (128, 7)
+
+
+def test_buffer_bytes(nsnq):
+    """Plain format: codes S B, scales 4 B per token, mu 256 B per block;
+    double-quantised: one padded scales record and one 80-byte mean record
+    per block."""
+    for bits, S in ((2, 32), (1, 16)):
+        for R in (64, 128):
+            c, sc, mu, rs = nsnq.nsnq_buffer_bytes(nsnq.params(bits, R), 4 * R)
+            assert (c, sc, mu, rs) == (4 * R * S, 4 * R * 4, 4 * 256, R * 256)
+            p = nsnq.params(bits, R, flags=nsnq.NSNQ_DOUBLE_QUANT)
+            c, sc, mu, rs = nsnq.nsnq_buffer_bytes(p, 4 * R)
+            rec = {64: 176, 128: 336}[R]
+            assert (c, sc, mu, rs) == (4 * R * S, 4 * rec, 4 * 80, R * 256)
+    with pytest.raises(nsnq.NsnqError):
+        nsnq.nsnq_buffer_bytes(nsnq.params(2, 128), 100)
+    with pytest.raises(nsnq.NsnqError):
+        nsnq.nsnq_buffer_bytes(nsnq.params(2, 128, flags=8), 128)

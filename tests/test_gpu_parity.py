@@ -10,6 +10,7 @@ import oracle
 from kv_cache_bit_amd import nsnq, synth
 
 from helpers import (DEV, capacity, check_attention, check_codes, check_dequant, check_f16_ulp, check_tie_rate,
+                     compare_encoded_dq,
                      compare_encoded, f16_bits, gpu_encode, half_np, oracle_encode_pair, token_norms,
                      upload_half, cb_tensor)
 
@@ -200,6 +201,51 @@ def test_rht_and_scale_adjust(oracle_codebooks, bits, R, use_signs, adjust):
     oc.n_quant, oc.n_resid = nq, ek["n_resid"]
     o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), oc, num_splits=3).float().cpu().numpy()
     check_attention(o, ref)
+
+
+# ---------------------------------------------------- double quantisation --
+
+@pytest.mark.parametrize("bits,R,Hq,Hkv,adjust", [
+    (2, 64, 2, 2, False),
+    (2, 128, 8, 2, True),    # G = 4: matrix-core decode
+    (1, 128, 2, 2, False),
+    (1, 64, 4, 2, False),    # G = 2
+])
+def test_double_quant_encode_dequant_decode(oracle_codebooks, bits, R, Hq, Hkv, adjust):
+    cb = oracle_codebooks[bits]
+    B, L = 2, 5 * R + 9
+    k, v = _kv(900 + bits, B, Hkv, L + 1)
+    q = synth.queries(900 + bits, 0, B, Hq, D)
+    flags = nsnq.NSNQ_DOUBLE_QUANT | (nsnq.NSNQ_SCALE_ADJUST if adjust else 0)
+    p, cbt, cache = gpu_encode(k[:, :, :L], v[:, :, :L], bits, R, cb, flags=flags)
+    assert cache.dq
+    kw = dict(dq=True, scale_adjust=adjust)
+    ek, ev = oracle.encode(k[:, :, :L], R, cb, **kw), oracle.encode(v[:, :, :L], R, cb, **kw)
+    masks = compare_encoded_dq(cache, ek, ev, R, scale_adjust=adjust)
+    nq = ek["n_quant"]
+    # dequant of the GPU's own records, on blocks and tokens that agree
+    for which, e, x, full in ((0, ek, k, masks[0]), (1, ev, v, masks[1])):
+        g = nsnq.nsnq_dequant(p, cbt, cache, which, 0, nq, torch.float32).cpu().numpy()
+        ref = oracle.dequant(e["codes"], e["scales"], e["mu"], R, cb, dq=True)
+        same = np.all(half_np(cache, which)["codes"] == e["codes"], axis=-1) & np.repeat(full, R, axis=-1)
+        check_dequant(g, ref, token_norms(x[:, :, :nq].numpy()), mask=same)
+    # decode: end to end, and on the oracle's own records
+    ref = oracle.reference_decode(q, ek, ev, nq, ek["n_resid"], R, cb)
+    o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), cache).float().cpu().numpy()
+    check_attention(o, ref)
+    oc = nsnq.KVCache(p, B, Hkv, capacity(L, R), DEV)
+    upload_half(oc, 0, ek)
+    upload_half(oc, 1, ev)
+    oc.n_quant, oc.n_resid = nq, ek["n_resid"]
+    for ns in (0, 3):
+        o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), oc, num_splits=ns).float().cpu().numpy()
+        check_attention(o, ref)
+    # one more token: the full window is flushed in the double-quantised format
+    if ek["n_resid"] == R:
+        nsnq.nsnq_append_kv(p, cbt, k[:, :, L].contiguous().to(DEV), v[:, :, L].contiguous().to(DEV), cache)
+        torch.cuda.synchronize()
+        ek2, ev2 = oracle.encode(k, R, cb, **kw), oracle.encode(v, R, cb, **kw)
+        compare_encoded_dq(cache, ek2, ev2, R, scale_adjust=adjust)
 
 
 # ------------------------------------------------------------ ragged rows --

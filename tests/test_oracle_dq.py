@@ -1,0 +1,130 @@
+"""Pins of the oracle's double-quantised format (technical summary sec. 3, DQ;
+machine review, implementation details: 4-bit round-to-nearest, groups of 32
+channels for the mean and of R tokens for s1): the 4-bit quantiser against an
+independent nearest-level search and exactly representable groups, the record
+layout parsed independently, and the exact inverse that holds because the
+forward pass divides by and subtracts the stored values."""
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from kv_cache_bit_amd import synth
+
+D = 128
+
+
+def _h(bits) -> float:
+    return float(np.array([bits], np.uint16).view(np.float16)[0])
+
+
+def test_rtn4_exact_grid_and_nearest_level():
+    # a group whose levels are exact: Z and S representable, max - min = 15 S
+    Z, S = -1.25, 0.0625
+    k = np.array([0, 15, 3, 7, 7, 12, 1, 15, 0, 9], np.float64)
+    o = oracle.rtn4(Z + S * k)
+    assert _h(o["Z"]) == Z and _h(o["S"]) == S
+    assert np.array_equal(o["q"], k.astype(np.uint8))
+    assert np.array_equal(o["vhat"], Z + S * k)
+    assert np.allclose(o["margin"], 0.5)
+    # random groups: q is the nearest of the 16 levels (independent search),
+    # and the read-back error is at most half a step plus the fp16 rounding
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        v = rng.standard_normal(32) * rng.uniform(0.01, 30) + rng.uniform(-5, 5)
+        o = oracle.rtn4(v)
+        Zv, Sv = _h(o["Z"]), _h(o["S"])
+        levels = Zv + Sv * np.arange(16)
+        near = np.argmin(np.abs(v[:, None] - levels[None, :]), axis=1)
+        ok = o["margin"] > 1e-9  # exact ties may round either way
+        assert np.array_equal(o["q"][ok], near[ok])
+        bound = Sv / 2 + 16 * Sv * 2.0 ** -11 + abs(Zv) * 2.0 ** -11
+        assert np.all(np.abs(v - o["vhat"]) <= bound * (1 + 1e-12))
+    # a constant group has step 0 and every code 0
+    o = oracle.rtn4(np.full(8, 2.5))
+    assert _h(o["S"]) == 0.0 and np.all(o["q"] == 0) and np.all(o["vhat"] == 2.5)
+
+
+def _parse(enc, R):
+    """Independent reading of the byte records (layout in include/nsnq.h)."""
+    sc, mu = enc["scales"][0], enc["mu"][0]
+    nb = sc.shape[0]
+    n2 = sc[:, :2 * R].copy().view(np.float16).astype(np.float64)
+    nib = sc[:, 2 * R:2 * R + R // 2]
+    q1 = np.stack([nib & 15, nib >> 4], axis=-1).reshape(nb, R)
+    sz = sc[:, 2 * R + R // 2:2 * R + R // 2 + 4].copy().view(np.float16).astype(np.float64)
+    n1hat = sz[:, 1:2] + sz[:, 0:1] * q1
+    qm = np.stack([mu[:, :64] & 15, mu[:, :64] >> 4], axis=-1).reshape(nb, D)
+    msz = mu[:, 64:80].copy().view(np.float16).astype(np.float64).reshape(nb, 4, 2)
+    muhat = msz[:, np.arange(D) // 32, 1] + msz[:, np.arange(D) // 32, 0] * qm
+    assert np.all(sc[:, 2 * R + R // 2 + 4:] == 0)
+    return n2.reshape(-1), n1hat.reshape(-1), muhat
+
+
+@pytest.mark.parametrize("bits,R", [(2, 64), (1, 128), (2, 128)])
+def test_dq_records_and_exact_inverse(oracle_codebooks, bits, R):
+    cb = oracle_codebooks[bits]
+    L = 3 * R + 5
+    x = synth.kv_unit(51 + bits, L, D).numpy()
+    enc = oracle.encode(x[None], R, cb, with_u=True, dq=True)
+    nq = enc["n_quant"]
+    assert enc["scales"].shape[-1] == oracle.dq_scales_bytes(R) == 16 * -(-(2 * R + R // 2 + 4) // 16)
+    n2_st, n1hat, muhat = _parse(enc, R)
+    assert np.array_equal(n1hat, enc["n1hat"][0])
+    # the forward pass used the stored values: x = n1_hat (n2 H^T u + mu_hat) exactly,
+    # with n2 = || x / n1_hat - mu_hat || / sqrt(d) (unrounded)
+    Hs = scipy.linalg.hadamard(D).astype(np.float64) / np.sqrt(D)
+    xd = x[:nq].astype(np.float64)
+    mub = np.repeat(muhat, R, axis=0)
+    z = xd / n1hat[:, None] - mub
+    n2 = np.linalg.norm(z, axis=1) / np.sqrt(D)
+    rec = n1hat[:, None] * (n2[:, None] * (enc["u"][0] @ Hs) + mub)
+    assert np.allclose(rec, xd, rtol=0, atol=1e-10 * np.abs(xd).max())
+    assert np.allclose(n2_st, n2, rtol=2.0 ** -11)
+    # 4-bit codes of s1 and of the mean per group: within half a step (+ fp16 slack)
+    n1 = np.linalg.norm(xd, axis=1) / np.sqrt(D)
+    for b in range(nq // R):
+        span = n1[b * R:(b + 1) * R]
+        step = (span.max() - span.min()) / 15
+        assert np.all(np.abs(span - n1hat[b * R:(b + 1) * R]) <= step / 2 + 2e-3 * span.max())
+    # dequant from the records equals the same formula with the codewords
+    xh = oracle.dequant(enc["codes"], enc["scales"], enc["mu"], R, cb, dq=True)[0]
+    chat = oracle.f16_to_f64(cb)[enc["codes"][0].astype(np.int64)].reshape(nq, D)
+    ref = n1hat[:, None] * (n2_st[:, None] * (chat @ Hs) + mub)
+    assert np.allclose(xh, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # same VQ codes as the plain format would pick for these u, and the
+    # reconstruction error is the scaled VQ error
+    pred = n1hat * n2_st * np.linalg.norm(enc["u"][0] - chat, axis=1)
+    assert np.allclose(np.linalg.norm(xd - xh, axis=1), pred, rtol=1e-2)
+
+
+def test_dq_bits_per_element():
+    """Overhead of the stored NSN parameters per element (d = 128): at R = 64
+    the unpadded records cost 0.238 bits (n2 fp16, s1 in 4 bits with its
+    (S, Z) per R tokens, the mean in 4 bits with (S, Z) per 32 channels); the
+    pages quote about 0.23.  The 16-byte padded records used here cost 0.250
+    (R = 64) and 0.203 (R = 128)."""
+    def over(R, padded):
+        sc = oracle.dq_scales_bytes(R) if padded else 2 * R + R // 2 + 4
+        return 8 * (sc + oracle.DQ_MU_BYTES) / (R * D)
+    assert abs(over(64, False) - 0.2383) < 1e-3
+    assert abs(over(64, True) - 0.25) < 1e-12
+    assert abs(over(128, True) - 0.203125) < 1e-12
+
+
+def test_dq_degenerate_blocks(oracle_codebooks):
+    """A block of identical tokens (zero mean step after the shift) and a zero
+    token: finite, and reconstructed from the records."""
+    cb = oracle_codebooks[2]
+    R = 64
+    x = synth.kv_unit(61, 3 * R + 1, D).numpy()
+    x[R:2 * R] = x[R]
+    x[5] = 0
+    enc = oracle.encode(x[None], R, cb, dq=True)
+    xh = oracle.dequant(enc["codes"], enc["scales"], enc["mu"], R, cb, dq=True)[0]
+    assert np.all(np.isfinite(xh))
+    assert np.all(xh[5] == 0)
+    # the constant block reconstructs to its token up to the 4-bit mean and VQ of the remainder
+    blk = x[R:2 * R].astype(np.float64)
+    err = np.linalg.norm(xh[R:2 * R] - blk, axis=1) / np.linalg.norm(blk, axis=1)
+    assert err.max() < 0.5
