@@ -177,6 +177,25 @@ nsnq_status nsnq_build_codebook(const nsnq_params* p, const float* samples, int6
                                 uint16_t* codebook, float* distortion, void* ws,
                                 size_t ws_bytes, void* stream);
 
+/* Refine a codebook for the cosine distance (technical summary sec. 3,
+ * Codebook Construction: after the k-means start, the codebook is tuned on
+ * synthetic standard-normal data to minimise the cosine distance between
+ * original and quantised vectors).  Reading: full-batch gradient descent with
+ * a fixed step on  loss = mean over x of (1 - cos(x, x_hat)), where x runs over
+ * the training head vectors and x_hat concatenates the nearest codewords
+ * (squared Euclidean, ties to the lowest index) of x's sub-vectors; each step
+ * assigns, then moves every codeword by -lr * d loss / d codeword with the
+ * assignment held fixed.
+ *   samples      fp32 [n][head_dim] training head vectors (n >= 1).
+ *   centroids    fp32 [256][s] in: the start (the k-means centroids);
+ *                out: the refined centroids.
+ *   codebook     fp16 [256][s] out: the refined centroids rounded to nearest even.
+ *   loss         fp32 [iters] out (may be NULL): step i's loss, before its move.
+ *   ws/ws_bytes  as for nsnq_build_codebook (same size). */
+nsnq_status nsnq_finetune_codebook(const nsnq_params* p, const float* samples, int64_t n, int32_t iters, float lr,
+                                   float* centroids, uint16_t* codebook, float* loss, void* ws, size_t ws_bytes,
+                                   void* stream);
+
 /* Prefill encode (technical summary secs. 1-4).  k and v are fp16 streams
  * indexed [b][h][t][c] at element offsets b*stride_b + h*stride_h +
  * t*stride_t + c (c contiguous), t < L.  Of the L tokens, the first L - r are

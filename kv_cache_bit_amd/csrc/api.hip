@@ -203,6 +203,36 @@ nsnq_status nsnq_build_codebook(const nsnq_params* p, const float* samples, int6
   return hip_status(e);
 }
 
+nsnq_status nsnq_finetune_codebook(const nsnq_params* p, const float* samples, int64_t n, int32_t iters, float lr,
+                                   float* centroids, uint16_t* codebook, float* loss, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  nsnq_status s = check_params(p);
+  if (s != NSNQ_OK) return s;
+  if (!samples || !centroids || !codebook || n < 1 || iters < 0 || !(lr >= 0.f) || lr > 1e30f) return NSNQ_EINVAL;
+  if (!aligned16(samples) || !aligned16(centroids) || !aligned16(codebook)) return NSNQ_EINVAL;
+  if (!ws || ws_bytes < nsnq_build_codebook_workspace_bytes(p) || !aligned16(ws)) return NSNQ_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int sub = sub_of(p);
+  double* acc = (double*)ws;
+  KmeansArgs a{};
+  a.samples = samples;
+  a.n = n;
+  a.cent = centroids;
+  a.sums = acc;
+  a.counts = acc + kCodewords * sub;
+  a.dsum = acc + kCodewords * sub + kCodewords;
+  a.distortion = loss;
+  a.codebook = codebook;
+  a.lr = lr;
+  hipError_t e = launch_kmeans_clear(acc, kCodewords * sub + kCodewords + 1, st);
+  for (int it = 0; it < iters && e == hipSuccess; ++it) {
+    a.it = it;
+    e = launch_finetune_iter(a, sub, st);
+  }
+  if (e == hipSuccess) e = launch_kmeans_finish(a, sub, st);
+  return hip_status(e);
+}
+
 nsnq_status nsnq_encode_kv(const nsnq_params* p, const uint16_t* codebook, const uint16_t* k, const uint16_t* v,
                            int64_t stride_b, int64_t stride_h, int64_t stride_t, int32_t L, nsnq_cache* cache,
                            void* stream) {

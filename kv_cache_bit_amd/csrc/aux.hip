@@ -175,6 +175,114 @@ hipError_t launch_kmeans_iter(const KmeansArgs& a, int sub, hipStream_t stream) 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Cosine refinement of the codebook: full-batch gradient descent on the mean
+// of 1 - cos(x, x_hat) over head vectors x [n][128], x_hat the concatenation of
+// the nearest codewords of x's sub-vectors.  One group of S lanes per vector,
+// one sub-vector per lane; the gradient d(1 - cos)/d x_hat of each sub-vector
+// goes to its codeword through fp64 LDS sums, flushed to the global sums.
+
+template <int SUB>
+__global__ __launch_bounds__(256) void finetune_grad_kernel(KmeansArgs a) {
+  constexpr int S = kDim / SUB;
+  constexpr int VPW = kWave / S;  // vectors per wave
+  __shared__ float cent[kCodewords * SUB];
+  __shared__ double lsum[kCodewords * SUB];
+  __shared__ double ldist[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slot = lane % S;
+  for (int i = tid; i < kCodewords * SUB; i += 256) {
+    cent[i] = a.cent[i];
+    lsum[i] = 0.0;
+  }
+  __syncthreads();
+  double dl = 0.0;
+  const int64_t nvec = a.n;  // head vectors
+  const int64_t stride = (int64_t)gridDim.x * 4 * VPW;
+  for (int64_t v0 = ((int64_t)blockIdx.x * 4 + wave) * VPW; v0 < nvec; v0 += stride) {
+    const int64_t v = v0 + lane / S;
+    const bool act = v < nvec;
+    float x[SUB];
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) x[e] = act ? a.samples[v * kDim + slot * SUB + e] : 0.f;
+    float bd = INFINITY;
+    int best = 0;
+    for (int k = 0; k < kCodewords; ++k) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) {
+        const float df = x[e] - cent[k * SUB + e];
+        d = fmaf(df, df, d);
+      }
+      if (d < bd) {
+        bd = d;
+        best = k;
+      }
+    }
+    float xh[SUB], ax = 0.f, xx = 0.f, hh = 0.f;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) {
+      xh[e] = cent[best * SUB + e];
+      ax = fmaf(x[e], xh[e], ax);
+      xx = fmaf(x[e], x[e], xx);
+      hh = fmaf(xh[e], xh[e], hh);
+    }
+    ax = group_sum<S>(ax);
+    xx = group_sum<S>(xx);
+    hh = group_sum<S>(hh);
+    if (act) {
+      if (xx > 0.f && hh > 0.f) {
+        const float nx = sqrtf(xx), nh = sqrtf(hh);
+        const float cosv = ax / (nx * nh);
+        const float gx = 1.f / (nx * nh), gh = cosv / hh;
+#pragma unroll
+        for (int e = 0; e < SUB; ++e) atomicAdd(&lsum[best * SUB + e], (double)(gh * xh[e] - gx * x[e]));
+        if (slot == 0) dl += 1.0 - (double)cosv;
+      } else if (slot == 0) {
+        dl += 1.0;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) dl += __shfl_xor(dl, m, kWave);
+  if (lane == 0) ldist[wave] = dl;
+  __syncthreads();
+  for (int i = tid; i < kCodewords * SUB; i += 256)
+    if (lsum[i] != 0.0) atomicAdd(&a.sums[i], lsum[i]);
+  if (tid == 0) atomicAdd(a.dsum, (ldist[0] + ldist[1]) + (ldist[2] + ldist[3]));
+}
+
+template <int SUB>
+__global__ __launch_bounds__(256) void finetune_update_kernel(KmeansArgs a) {
+  const int k = threadIdx.x;
+#pragma unroll
+  for (int e = 0; e < SUB; ++e) {
+    a.cent[k * SUB + e] = (float)((double)a.cent[k * SUB + e] - a.lr * (a.sums[k * SUB + e] / (double)a.n));
+    a.sums[k * SUB + e] = 0.0;
+  }
+  __syncthreads();
+  if (k == 0) {
+    if (a.distortion) a.distortion[a.it] = (float)(*a.dsum / (double)a.n);
+    *a.dsum = 0.0;
+  }
+}
+
+hipError_t launch_finetune_iter(const KmeansArgs& a, int sub, hipStream_t stream) {
+  const int vpb = 4 * (kWave / (kDim / sub));
+  const int64_t want = (a.n + vpb - 1) / vpb;
+  const int grid = (int)(want < 2048 ? want : 2048);
+  if (sub == 4) {
+    hipLaunchKernelGGL(finetune_grad_kernel<4>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(finetune_update_kernel<4>, dim3(1), dim3(256), 0, stream, a);
+  } else if (sub == 8) {
+    hipLaunchKernelGGL(finetune_grad_kernel<8>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(finetune_update_kernel<8>, dim3(1), dim3(256), 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_kmeans_init(const float* src, float* cent, int sub, hipStream_t stream) {
   hipError_t e = hipMemcpyAsync(cent, src, sizeof(float) * kCodewords * sub, hipMemcpyDeviceToDevice, stream);
   if (e != hipSuccess) return e;

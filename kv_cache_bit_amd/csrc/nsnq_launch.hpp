@@ -139,6 +139,7 @@ struct KmeansArgs {
   float* distortion;     // [iters] or null
   uint16_t* codebook;    // [256][SUB] fp16 out
   int it;
+  double lr;             // cosine refinement: gradient step
 };
 
 struct Fp16DecodeArgs {
@@ -164,6 +165,7 @@ int decode_max_split_tokens(int sub, int gh, int R);
 hipError_t launch_kmeans_init(const float* src, float* cent, int sub, hipStream_t stream);
 hipError_t launch_kmeans_iter(const KmeansArgs& a, int sub, hipStream_t stream);
 hipError_t launch_kmeans_finish(const KmeansArgs& a, int sub, hipStream_t stream);
+hipError_t launch_finetune_iter(const KmeansArgs& a, int sub, hipStream_t stream);
 hipError_t launch_fp16_decode(const Fp16DecodeArgs& a, int B, hipStream_t stream);
 size_t fp16_decode_lds_bytes(int G, int split_tokens);
 

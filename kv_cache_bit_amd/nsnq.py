@@ -49,6 +49,7 @@ _SIGNATURES = {
     "nsnq_buffer_bytes": (i32, [_PP, i32, P, P, P, P]),
     "nsnq_build_codebook_workspace_bytes": (size_t, [_PP]),
     "nsnq_build_codebook": (i32, [_PP, P, i64, i32, P, P, P, P, P, size_t, P]),
+    "nsnq_finetune_codebook": (i32, [_PP, P, i64, i32, f32, P, P, P, P, size_t, P]),
     "nsnq_encode_kv": (i32, [_PP, P, P, P, i64, i64, i64, i32, _PC, P]),
     "nsnq_encode_kv_ragged": (i32, [_PP, P, P, P, i64, i64, i64, P, i32, _PC, P]),
     "nsnq_flush_residual": (i32, [_PP, P, _PC, P]),
@@ -162,6 +163,27 @@ def nsnq_build_codebook(p: nsnq_params, samples: torch.Tensor, iters: int, init=
                                      ws.numel() * ws.element_size(), _stream(stream)),
            "nsnq_build_codebook")
     return centroids, codebook, distortion
+
+
+def nsnq_finetune_codebook(p: nsnq_params, samples: torch.Tensor, iters: int, lr: float, centroids: torch.Tensor,
+                           codebook=None, loss=None, ws=None, stream=None):
+    """Cosine refinement of `centroids` (fp32 [256, s], updated in place) on
+    head vectors samples fp32 [n, 128].  Returns (centroids, codebook fp16, loss fp32 [iters])."""
+    s = sub_dim(p.bits)
+    dev = samples.device
+    assert samples.dtype == torch.float32 and samples.is_contiguous() and samples.shape[1] == p.head_dim
+    assert centroids.dtype == torch.float32 and centroids.is_contiguous() and tuple(centroids.shape) == (256, s)
+    if codebook is None:
+        codebook = torch.empty(256, s, dtype=torch.float16, device=dev)
+    if loss is None and iters > 0:
+        loss = torch.empty(iters, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(nsnq_build_codebook_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    _check(lib().nsnq_finetune_codebook(ctypes.byref(p), _ptr(samples), samples.shape[0], iters, float(lr),
+                                        _ptr(centroids), _ptr(codebook), _ptr(loss), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)),
+           "nsnq_finetune_codebook")
+    return centroids, codebook, loss
 
 
 def nsnq_encode_kv(p: nsnq_params, codebook, k, v, L: int, cache: "KVCache", stream=None):

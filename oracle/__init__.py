@@ -54,6 +54,8 @@ def lib():
             "orc_kmeans": (None, [P, i64, i32, i32, i32, P, P, P, P]),
             "orc_num_threads": (i32, []),
             "orc_rtn4": (None, [P, i32, P, P, P, P, P]),
+            "orc_cos_loss_grad": (f64, [P, i64, i32, i32, P, i32, P]),
+            "orc_finetune": (None, [P, i64, i32, i32, i32, i32, f64, P, P, P]),
             "orc_dq_scales_bytes": (i32, [i32]),
             "orc_encode_dq": (i32, [P, i64, i32, i32, i32, i32, P, i32, P, i32, P, P, P, P, P, P, P, P, P]),
             "orc_dequant_dq": (None, [P, P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P]),
@@ -279,6 +281,29 @@ def kmeans(samples, ncw: int, iters: int, init: np.ndarray | None = None):
     lib().orc_kmeans(_p(x), n, s, ncw, iters, _p(ini) if ini is not None else None,
                      _p(cent), _p(cb), _p(dist))
     return cent, cb, dist[:iters]
+
+
+def cos_loss_grad(x, centroids) -> tuple[float, np.ndarray]:
+    """Cosine objective of the codebook refinement and its gradient, for head
+    vectors x fp32 [n, d] and centroids float64 [ncw, s]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    c = np.ascontiguousarray(centroids, dtype=np.float64)
+    ncw, s = c.shape
+    g = np.empty_like(c)
+    loss = lib().orc_cos_loss_grad(_p(x), x.shape[0], x.shape[1], s, _p(c), ncw, _p(g))
+    return loss, g
+
+
+def finetune(x, centroids, iters: int, lr: float):
+    """Gradient descent on the cosine objective; returns (centroids float64,
+    codebook fp16 bits, loss per step)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    c = np.array(centroids, dtype=np.float64, copy=True, order="C")
+    ncw, s = c.shape
+    cb = np.empty((ncw, s), np.uint16)
+    loss = np.empty(max(iters, 1), np.float64)
+    lib().orc_finetune(_p(x), x.shape[0], x.shape[1], s, ncw, iters, float(lr), _p(c), _p(cb), _p(loss))
+    return c, cb, loss[:iters]
 
 
 def num_threads() -> int:

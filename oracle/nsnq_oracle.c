@@ -692,6 +692,83 @@ void orc_kmeans(const float* samples, int64_t n, int s, int ncw, int iters,
   free(c); free(sum); free(cnt); free(assign); free(dmin);
 }
 
+/* ------------------------------------------------ cosine fine-tune --- */
+
+/* Loss and gradient of the cosine objective of the codebook refinement
+ * [P3 sec. 3, codebook construction: after k-means on torch.randn data the
+ * codebook is refined to minimise the cosine distance between the original and
+ * the quantised vectors].  Training vectors x [n][d] (fp32, taken exactly) are
+ * head vectors of S = d / s sub-vectors; each sub-vector is assigned to its
+ * nearest codeword (squared Euclidean, ties to the lowest index) and x_hat is
+ * the concatenation of the assigned codewords.  Returns
+ *   loss = mean over x of (1 - cos(x, x_hat)),
+ * and grad [ncw][s] = d loss / d codebook with the assignment held fixed:
+ *   d(1 - cos)/d x_hat = -( x / (|x| |x_hat|) - cos x_hat / |x_hat|^2 ),
+ * added to the codeword each sub-vector is assigned to, then divided by n.
+ * A vector with x = 0 or x_hat = 0 contributes 1 to the loss and nothing to
+ * the gradient. */
+double orc_cos_loss_grad(const float* x, int64_t n, int d, int s, const double* c, int ncw, double* grad) {
+  int S = d / s;
+  memset(grad, 0, sizeof(double) * (size_t)ncw * s);
+  double loss = 0.0;
+  int* code = (int*)malloc(sizeof(int) * S);
+  double* xh = (double*)malloc(sizeof(double) * d);
+  for (int64_t p = 0; p < n; ++p) {
+    const float* xp = x + (size_t)p * d;
+    for (int j = 0; j < S; ++j) {
+      int best = 0;
+      double bd = INFINITY;
+      for (int k = 0; k < ncw; ++k) {
+        double dist = 0.0;
+        for (int e = 0; e < s; ++e) {
+          double diff = (double)xp[j * s + e] - c[(size_t)k * s + e];
+          dist += diff * diff;
+        }
+        if (dist < bd) { bd = dist; best = k; }
+      }
+      code[j] = best;
+      for (int e = 0; e < s; ++e) xh[j * s + e] = c[(size_t)best * s + e];
+    }
+    double a = 0.0, xx = 0.0, hh = 0.0;
+    for (int i = 0; i < d; ++i) {
+      a += (double)xp[i] * xh[i];
+      xx += (double)xp[i] * xp[i];
+      hh += xh[i] * xh[i];
+    }
+    if (xx <= 0.0 || hh <= 0.0) {
+      loss += 1.0;
+      continue;
+    }
+    double nx = sqrt(xx), nh = sqrt(hh), cosv = a / (nx * nh);
+    loss += 1.0 - cosv;
+    for (int j = 0; j < S; ++j)
+      for (int e = 0; e < s; ++e) {
+        int i = j * s + e;
+        grad[(size_t)code[j] * s + e] += -((double)xp[i] / (nx * nh) - cosv * xh[i] / hh);
+      }
+  }
+  for (size_t e = 0; e < (size_t)ncw * s; ++e) grad[e] /= (double)n;
+  free(code);
+  free(xh);
+  return loss / (double)n;
+}
+
+/* Full-batch gradient descent with a fixed step lr, `iters` steps from
+ * cent_io (in: the k-means centroids; out: refined).  loss[it] is the loss of
+ * step it's assignment, before the step.  cb_out: fp16 (RNE) of the result. */
+void orc_finetune(const float* x, int64_t n, int d, int s, int ncw, int iters, double lr,
+                  double* cent_io, uint16_t* cb_out, double* loss) {
+  double* grad = (double*)malloc(sizeof(double) * (size_t)ncw * s);
+  for (int it = 0; it < iters; ++it) {
+    double l = orc_cos_loss_grad(x, n, d, s, cent_io, ncw, grad);
+    if (loss) loss[it] = l;
+    for (size_t e = 0; e < (size_t)ncw * s; ++e) cent_io[e] -= lr * grad[e];
+  }
+  if (cb_out)
+    for (size_t e = 0; e < (size_t)ncw * s; ++e) cb_out[e] = orc_d2h(cent_io[e]);
+  free(grad);
+}
+
 /* Number of OpenMP threads the batched routines use. */
 int orc_num_threads(void) {
 #ifdef _OPENMP

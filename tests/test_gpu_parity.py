@@ -374,6 +374,27 @@ def test_kmeans_matches_oracle(bits):
     assert d2.item() == pytest.approx(od2[0], rel=1e-5)
 
 
+@pytest.mark.parametrize("bits", [2, 1])
+def test_cosine_finetune_matches_oracle(bits):
+    """Same start (the oracle's k-means centroids in fp32), same training head
+    vectors: the loss curve and the refined centroids agree (assignments are
+    fp32 argmins on the GPU, so a near-tie may move one vector's gradient)."""
+    s = nsnq.sub_dim(bits)
+    ocent, _, _ = oracle.kmeans(synth.randn_samples(bits, 1 << 13, s).numpy(), 256, 6)
+    start = ocent.astype(np.float32)
+    x = synth.randn_samples(950 + bits, 4096, D)
+    p = nsnq.params(bits, 128)
+    cent = torch.from_numpy(start.copy()).to(DEV)
+    iters, lr = 6, 64.0
+    cent, cbk, loss = nsnq.nsnq_finetune_codebook(p, x.to(DEV), iters, lr, cent)
+    oc, ocb, oloss = oracle.finetune(x.numpy(), start.astype(np.float64), iters, lr)
+    assert np.allclose(loss.cpu().numpy(), oloss, rtol=2e-5, atol=0)
+    assert np.all(np.diff(oloss) < 0)
+    dev = np.abs(cent.cpu().numpy().astype(np.float64) - oc).max()
+    assert dev < 1e-4, dev
+    assert np.array_equal(f16_bits(cbk), f16_bits(cent.half()))
+
+
 # ---------------------------------------------------------- full-size cases --
 
 def test_llama2_layer_2bit_full(oracle_codebooks):
