@@ -268,6 +268,32 @@ nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook
                                   int32_t num_splits, uint16_t* out, void* ws, size_t ws_bytes,
                                   void* stream);
 
+/* Keys quantised before RoPE (technical summary sec. 4, Attention
+ * Computation: NSN is applied to keys before the rotary embedding).  Token t
+ * of a row (compressed tokens first, then the residual window) sits at
+ * position pos0 + t; its reconstructed key is rotated in the rotate-half
+ * convention, pairs (c, c + 64) for c < 64:
+ *   k'[c]      = k[c] cos[pos][c] - k[c + 64] sin[pos][c]
+ *   k'[c + 64] = k[c + 64] cos[pos][c] + k[c] sin[pos][c]
+ * with the caller's tables cos, sin: device fp32 [max_pos][64] (any
+ * frequencies, e.g. theta_c = base^(-2c/128), or scaled ones).  q is the
+ * already-rotated query.  Requires pos0 >= 0 and pos0 + (tokens of the
+ * longest row, or max_len for a ragged cache) <= max_pos. */
+typedef struct {
+  const float* cos;
+  const float* sin;
+  int32_t max_pos;
+  int32_t pos0;
+} nsnq_rope;
+
+/* Decode attention as nsnq_decode_attention, with the keys of the cache
+ * stored before RoPE (nsnq_rope above).  Values are unchanged.  Workspace:
+ * nsnq_decode_workspace_bytes (it covers both calls). */
+nsnq_status nsnq_decode_attention_prerope(const nsnq_params* p, const uint16_t* codebook, const uint16_t* q,
+                                          int32_t q_heads, const nsnq_cache* cache, float softmax_scale,
+                                          const nsnq_rope* rope, int32_t num_splits, uint16_t* out, void* ws,
+                                          size_t ws_bytes, void* stream);
+
 /* Comparator: the same decode attention over an uncompressed fp16 cache
  * k, v [batch][kv_heads][n_tokens][d] (d = 128), used to measure the gain of
  * the compressed cache.  Workspace from nsnq_fp16_decode_workspace_bytes(). */

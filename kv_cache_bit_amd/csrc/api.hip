@@ -437,11 +437,12 @@ int mfma_heads_per_group(int G) {
 }
 int heads_per_group(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
 
-DecodePlan plan_decode(const nsnq_params* p, const nsnq_cache* c, int q_heads, int num_splits) {
+DecodePlan plan_decode(const nsnq_params* p, const nsnq_cache* c, int q_heads, int num_splits,
+                       bool lut_only = false) {
   DecodePlan pl{};
   const int G = q_heads / c->kv_heads;
   const int R = p->block_tokens;
-  const int gq = mfma_heads_per_group(G);
+  const int gq = lut_only ? 0 : mfma_heads_per_group(G);
   pl.mfma = gq > 0;
   pl.gh = pl.mfma ? gq : heads_per_group(G);
   const int nblk = c->n_quant / R;
@@ -479,13 +480,39 @@ size_t nsnq_decode_workspace_bytes(const nsnq_params* p, const nsnq_cache* cache
   if (check_params(p) != NSNQ_OK || !cache || cache->kv_heads <= 0 || q_heads <= 0 ||
       q_heads % cache->kv_heads != 0 || cache->batch <= 0 || cache->n_quant < 0 || cache->n_resid < 0)
     return 0;
+  // enough for both kernels' plans (the pre-RoPE call always uses the LUT kernel)
   const DecodePlan pl = plan_decode(p, cache, q_heads, num_splits);
-  return sizeof(float) * (size_t)cache->batch * q_heads * (size_t)pl.nsplit * (kDim + 2);
+  const DecodePlan pr = plan_decode(p, cache, q_heads, num_splits, true);
+  const int ns = pl.nsplit > pr.nsplit ? pl.nsplit : pr.nsplit;
+  return sizeof(float) * (size_t)cache->batch * q_heads * (size_t)ns * (kDim + 2);
+}
+
+namespace {
+nsnq_status run_decode(const nsnq_params* p, const uint16_t* codebook, const uint16_t* q, int32_t q_heads,
+                       const nsnq_cache* cache, float softmax_scale, const nsnq_rope* rope, int32_t num_splits,
+                       uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 }
 
 nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook, const uint16_t* q,
                                   int32_t q_heads, const nsnq_cache* cache, float softmax_scale,
                                   int32_t num_splits, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  return run_decode(p, codebook, q, q_heads, cache, softmax_scale, nullptr, num_splits, out, ws, ws_bytes, stream);
+}
+
+nsnq_status nsnq_decode_attention_prerope(const nsnq_params* p, const uint16_t* codebook, const uint16_t* q,
+                                          int32_t q_heads, const nsnq_cache* cache, float softmax_scale,
+                                          const nsnq_rope* rope, int32_t num_splits, uint16_t* out, void* ws,
+                                          size_t ws_bytes, void* stream) {
+  if (!rope) return NSNQ_EINVAL;
+  return run_decode(p, codebook, q, q_heads, cache, softmax_scale, rope, num_splits, out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+nsnq_status run_decode(const nsnq_params* p, const uint16_t* codebook, const uint16_t* q, int32_t q_heads,
+                       const nsnq_cache* cache, float softmax_scale, const nsnq_rope* rope, int32_t num_splits,
+                       uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
   nsnq_status s = check_params(p);
   if (s != NSNQ_OK) return s;
   s = check_cache(p, cache);
@@ -498,7 +525,13 @@ nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook
   if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return NSNQ_EINVAL;
   const size_t need = nsnq_decode_workspace_bytes(p, cache, q_heads, num_splits);
   if (!ws || !aligned16(ws) || ws_bytes < need) return NSNQ_EWORKSPACE;
-  const DecodePlan pl = plan_decode(p, cache, q_heads, num_splits);
+  if (rope) {
+    if (!rope->cos || !rope->sin || !aligned16(rope->cos) || !aligned16(rope->sin)) return NSNQ_EINVAL;
+    const int64_t last = (int64_t)rope->pos0 + (is_ragged(cache) ? (int64_t)cache->max_len
+                                                                  : (int64_t)cache->n_quant + cache->n_resid);
+    if (rope->pos0 < 0 || last > rope->max_pos) return NSNQ_EINVAL;
+  }
+  const DecodePlan pl = plan_decode(p, cache, q_heads, num_splits, rope != nullptr);
   if (pl.nsplit > kMaxSplits) return NSNQ_EUNSUPPORTED;  // context too long for one combine
   DecodeArgs a{};
   a.q = q;
@@ -527,6 +560,11 @@ nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook
   a.seq_quant = cache->seq_quant;
   a.seq_resid = cache->seq_resid;
   a.dq = (p->flags & NSNQ_DOUBLE_QUANT) ? 1 : 0;
+  if (rope) {
+    a.rope_cos = rope->cos;
+    a.rope_sin = rope->sin;
+    a.rope_pos0 = rope->pos0;
+  }
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = pl.mfma ? launch_decode_mfma(a, sub_of(p), pl.gh, cache->batch, st)
                          : launch_decode(a, sub_of(p), pl.gh, cache->batch, pl.lds, st);
@@ -538,6 +576,9 @@ nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook
   cb.nsplit = pl.nsplit;
   return hip_status(launch_combine(cb, cache->batch, st));
 }
+}  // namespace
+
+extern "C" {
 
 // --------------------------------------------------------------- fp16 ------
 

@@ -79,7 +79,7 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&cw)[S / 
   }
 }
 
-template <int SUB, int GH, bool DQ>
+template <int SUB, int GH, bool DQ, bool ROPE>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int S = kDim / SUB;
   constexpr int CW = S / 4;      // 32-bit words of codes per token
@@ -184,8 +184,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     qr[wave * kDim + 2 * lane + 1] = x[1] * kInvSqrtD;
   }
   __syncthreads();
-  // LUT_j[c] = (Hq)_j . C[c]; thread = codeword
-  {
+  // LUT_j[c] = (Hq)_j . C[c]; thread = codeword (keys stored before RoPE
+  // need no table: their dot products are formed from dequantised keys)
+  if constexpr (!ROPE) {
     const int c = tid;
     float cv[SUB];
 #pragma unroll
@@ -216,6 +217,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int c = 0; c < 16; ++c) acc[g][c] = 0.f;
   }
   float* wb = smem + L.wbuf + wave * GH * kChunk;
+  // keys stored before RoPE: lane (token group tt, j) dequantises channels
+  // 8 j .. 8 j + 7 of token 4 pass + tt, rotates them and dots them with the
+  // queries; the per-token dot products go through LDS (the LUT space)
+  const int rj = lane & 15, rtt = lane >> 4;
+  float* rsc = lut + wave * GH * kChunk;
+  float rq[ROPE ? GH : 1][8], rsg[8];
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int g = 0; g < GH; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rq[g][e] = qf[g * kDim + 8 * rj + e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rsg[e] = (a.signs ? (float)a.signs[8 * rj + e] : 1.f) * kInvSqrtD;
+  }
 
   for (; ch < nchunk; ch += 4) {
     ChunkRegs nxt;
@@ -240,18 +255,96 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       vm0 = h2f(cur.vm[0] & 0xffff);
       vm1 = h2f(cur.vm[0] >> 16);
     }
+    if constexpr (ROPE) {
+      // the chunk's block mean for channels 8 rj .. 8 rj + 7
+      const int bl = (ch * kChunk) / a.R;
+      float mk[8];
+      if constexpr (DQ) {
+        const uint8_t* mr = reinterpret_cast<const uint8_t*>(a.kmu) + (blk0 + bl) * kDqMuRecord;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) dq_mu_pair(mr, 4 * rj + e / 2, mk[e], mk[e + 1]);
+      } else {
+        const uint4 m8 = *reinterpret_cast<const uint4*>(kmu + (int64_t)bl * kDim + 8 * rj);
+        const uint32_t mw[4] = {m8.x, m8.y, m8.z, m8.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mk[e] = h2f((e & 1) ? (mw[e >> 1] >> 16) : (mw[e >> 1] & 0xffff));
+      }
+#pragma unroll 2
+      for (int pass = 0; pass < kChunk / 4; ++pass) {
+        const int tok = 4 * pass + rtt;
+        const int64_t tc = (int64_t)ch * kChunk + tok;  // token in the split
+        float x[8];
+        if constexpr (SUB == 4) {
+          const uint32_t c2 = *reinterpret_cast<const uint16_t*>(kc + tc * S + 2 * rj);
+          const uint2 w0 = *reinterpret_cast<const uint2*>(cbh + (c2 & 0xffu) * 4);
+          const uint2 w1 = *reinterpret_cast<const uint2*>(cbh + (c2 >> 8) * 4);
+          const uint32_t w[4] = {w0.x, w0.y, w1.x, w1.y};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = h2f((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffff));
+        } else {
+          const uint32_t c1 = kc[tc * S + rj];
+          const uint4 w4 = *reinterpret_cast<const uint4*>(cbh + c1 * 8);
+          const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = h2f((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffff));
+        }
+        fwht128<8>(x, lane);
+        float tn1, tn2;
+        if constexpr (DQ) {
+          const uint8_t* kr = reinterpret_cast<const uint8_t*>(a.kscales) + (blk0 + bl) * dq_record_bytes(a.R);
+          const uint32_t tq = dq_token(kr, a.R, (int)(tc % a.R));
+          tn1 = dq_value(dq_s1_params(kr, a.R), tq >> 16);
+          tn2 = h2f(tq & 0xffff);
+        } else {
+          const uint32_t sc = ks[tc];
+          tn1 = h2f(sc & 0xffff);
+          tn2 = h2f(sc >> 16);
+        }
+        const int64_t pos = (int64_t)a.rope_pos0 + t0 + tc;
+        const float4* cs4 = reinterpret_cast<const float4*>(a.rope_cos + pos * (kDim / 2) + 8 * (rj & 7));
+        const float4* sn4 = reinterpret_cast<const float4*>(a.rope_sin + pos * (kDim / 2) + 8 * (rj & 7));
+        const float4 ca = cs4[0], cb = cs4[1], sa = sn4[0], sb = sn4[1];
+        const float cv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+        const float sv8[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+        // rotate-half pairs (c, c + 64): lanes rj < 8 hold c < 64, the partner is rj ^ 8
+        const float ssg = rj < 8 ? -1.f : 1.f;
+        float r[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float kk = tn1 * fmaf(tn2, x[e] * rsg[e], mk[e]);
+          const float pk = xlane<8>(kk);
+          r[e] = fmaf(kk, cv[e], ssg * pk * sv8[e]);
+        }
+#pragma unroll
+        for (int g = 0; g < GH; ++g) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d = fmaf(r[e], rq[g][e], d);
+          d = group_sum<16>(d);
+          if (rj == 0) rsc[g * kChunk + tok] = d;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 #pragma unroll
     for (int g = 0; g < GH; ++g) {
-      // score of this lane's token
-      const float* lg = lut + g * S * kLutStride;
-      float s0 = 0.f, s1 = 0.f;
+      float sv;
+      if constexpr (ROPE) {
+        sv = a.scale_log2 * rsc[g * kChunk + lane];
+      } else {
+        // score of this lane's token
+        const float* lg = lut + g * S * kLutStride;
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < S; j += 2) {
-        s0 += lg[j * kLutStride + ((cur.kcw[j >> 2] >> (8 * (j & 3))) & 0xffu)];
-        s1 += lg[(j + 1) * kLutStride + ((cur.kcw[(j + 1) >> 2] >> (8 * ((j + 1) & 3))) & 0xffu)];
+        for (int j = 0; j < S; j += 2) {
+          s0 += lg[j * kLutStride + ((cur.kcw[j >> 2] >> (8 * (j & 3))) & 0xffu)];
+          s1 += lg[(j + 1) * kLutStride + ((cur.kcw[(j + 1) >> 2] >> (8 * ((j + 1) & 3))) & 0xffu)];
+        }
+        const float qmu = group_sum<kWave>(fmaf(q0[g], km0, q1[g] * km1));
+        sv = a.scale_log2 * kn1 * fmaf(kn2, s0 + s1, qmu);
       }
-      const float qmu = group_sum<kWave>(fmaf(q0[g], km0, q1[g] * km1));
-      const float sv = a.scale_log2 * kn1 * fmaf(kn2, s0 + s1, qmu);
       // online softmax over the chunk
       const float mn = fmaxf(m[g], group_max<kWave>(sv));
       const float alpha = exp2f(m[g] - mn);
@@ -402,23 +495,27 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   a.out[(int64_t)bh * kDim + c] = f2h(num / den);
 }
 
-template <int SUB, int GH, bool DQ>
+template <int SUB, int GH, bool DQ, bool ROPE>
 static hipError_t launch_decode_dq(const DecodeArgs& a, int B, size_t lds, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_split_kernel<SUB, GH, DQ>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_split_kernel<SUB, GH, DQ, ROPE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid(a.nsplit, B * a.Hkv * (a.G / GH)), block(256);
-  hipLaunchKernelGGL((decode_split_kernel<SUB, GH, DQ>), grid, block, lds, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<SUB, GH, DQ, ROPE>), grid, block, lds, stream, a);
   return hipGetLastError();
 }
 
 template <int SUB, int GH>
 static hipError_t launch_decode_t(const DecodeArgs& a, int B, size_t lds, hipStream_t stream) {
-  return a.dq ? launch_decode_dq<SUB, GH, true>(a, B, lds, stream) : launch_decode_dq<SUB, GH, false>(a, B, lds, stream);
+  if (a.rope_cos)
+    return a.dq ? launch_decode_dq<SUB, GH, true, true>(a, B, lds, stream)
+                : launch_decode_dq<SUB, GH, false, true>(a, B, lds, stream);
+  return a.dq ? launch_decode_dq<SUB, GH, true, false>(a, B, lds, stream)
+              : launch_decode_dq<SUB, GH, false, false>(a, B, lds, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int sub, int gh, int B, size_t lds, hipStream_t stream) {

@@ -47,15 +47,43 @@ __device__ __forceinline__ void decode_residual(const DecodeArgs& a, int nt, flo
     float acc[GH];
 #pragma unroll
     for (int g = 0; g < GH; ++g) acc[g] = 0.f;
+    if (a.rope_cos) {
+      // keys stored before RoPE: rotate the pairs (c, c + 64) by the token's
+      // position (after the n_quant compressed tokens of the row)
+      const int64_t pos = (int64_t)a.rope_pos0 + row_quant(a, (int)(unit / a.Hkv)) + tid;
+      const float4* cs4 = reinterpret_cast<const float4*>(a.rope_cos + pos * (kDim / 2));
+      const float4* sn4 = reinterpret_cast<const float4*>(a.rope_sin + pos * (kDim / 2));
 #pragma unroll
-    for (int ch = 0; ch < 16; ++ch) {
-      const uint32_t w4[4] = {kv[ch].x, kv[ch].y, kv[ch].z, kv[ch].w};
+      for (int ch = 0; ch < 8; ++ch) {
+        const uint32_t lo4[4] = {kv[ch].x, kv[ch].y, kv[ch].z, kv[ch].w};
+        const uint32_t hi4[4] = {kv[ch + 8].x, kv[ch + 8].y, kv[ch + 8].z, kv[ch + 8].w};
+        const float4 ca = cs4[2 * ch], cb = cs4[2 * ch + 1], sa = sn4[2 * ch], sb = sn4[2 * ch + 1];
+        const float cv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+        const float sv[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float k0 = h2f(w4[i] & 0xffff), k1 = h2f(w4[i] >> 16);
-        const int c = ch * 8 + 2 * i;
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t wl = lo4[i >> 1], wh = hi4[i >> 1];
+          const float k0 = h2f((i & 1) ? (wl >> 16) : (wl & 0xffff));
+          const float k1 = h2f((i & 1) ? (wh >> 16) : (wh & 0xffff));
+          const float r0 = fmaf(k0, cv[i], -k1 * sv[i]);
+          const float r1 = fmaf(k1, cv[i], k0 * sv[i]);
+          const int c = ch * 8 + i;
 #pragma unroll
-        for (int g = 0; g < GH; ++g) acc[g] = fmaf(qf[g * kDim + c], k0, fmaf(qf[g * kDim + c + 1], k1, acc[g]));
+          for (int g = 0; g < GH; ++g)
+            acc[g] = fmaf(qf[g * kDim + c], r0, fmaf(qf[g * kDim + c + 64], r1, acc[g]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ch = 0; ch < 16; ++ch) {
+        const uint32_t w4[4] = {kv[ch].x, kv[ch].y, kv[ch].z, kv[ch].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float k0 = h2f(w4[i] & 0xffff), k1 = h2f(w4[i] >> 16);
+          const int c = ch * 8 + 2 * i;
+#pragma unroll
+          for (int g = 0; g < GH; ++g) acc[g] = fmaf(qf[g * kDim + c], k0, fmaf(qf[g * kDim + c + 1], k1, acc[g]));
+        }
       }
     }
 #pragma unroll

@@ -111,6 +111,12 @@ struct DecodeArgs {
   const int32_t* seq_quant;  // ragged: per-row counters (null: n_quant / n_resid)
   const int32_t* seq_resid;
   int dq;                    // double-quantised scales / mean records
+  // keys stored before RoPE: token t of a row sits at position rope_pos0 + t
+  // and is rotated with the tables rope_cos / rope_sin [position][64] (null:
+  // keys are used as stored)
+  const float* rope_cos;
+  const float* rope_sin;
+  int rope_pos0;
 };
 
 // Per-row token counts of a decode launch.

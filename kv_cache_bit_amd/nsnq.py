@@ -31,6 +31,10 @@ class nsnq_params(ctypes.Structure):
                 ("flags", i32), ("reserved", i32), ("hadamard_signs", P)]
 
 
+class nsnq_rope(ctypes.Structure):
+    _fields_ = [("cos", P), ("sin", P), ("max_pos", i32), ("pos0", i32)]
+
+
 class nsnq_kv(ctypes.Structure):
     _fields_ = [("codes", P), ("scales", P), ("mu", P), ("resid", P)]
 
@@ -57,6 +61,8 @@ _SIGNATURES = {
     "nsnq_dequant": (i32, [_PP, P, _PC, i32, i32, i32, i32, P, P]),
     "nsnq_decode_workspace_bytes": (size_t, [_PP, _PC, i32, i32]),
     "nsnq_decode_attention": (i32, [_PP, P, P, i32, _PC, f32, i32, P, P, size_t, P]),
+    "nsnq_decode_attention_prerope": (i32, [_PP, P, P, i32, _PC, f32, ctypes.POINTER(nsnq_rope), i32, P, P,
+                                             size_t, P]),
     "nsnq_fp16_decode_workspace_bytes": (size_t, [i32, i32, i32, i32]),
     "nsnq_fp16_decode_attention": (i32, [P, i32, P, P, i32, i32, i32, f32, i32, P, P, size_t, P]),
 }
@@ -263,6 +269,30 @@ def nsnq_decode_attention(p: nsnq_params, codebook, q, cache: "KVCache", softmax
                                        float(softmax_scale), num_splits, _ptr(out), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream(stream)),
            "nsnq_decode_attention")
+    return out
+
+
+def nsnq_decode_attention_prerope(p: nsnq_params, codebook, q, cache: "KVCache", rope_cos: torch.Tensor,
+                                  rope_sin: torch.Tensor, pos0: int = 0, softmax_scale: float | None = None,
+                                  num_splits: int = 0, out=None, ws=None, stream=None):
+    """Decode step over a cache whose keys were stored before RoPE; rope_cos /
+    rope_sin: device fp32 [max_pos, 64]; q is the rotated query."""
+    B, Hq, d = q.shape
+    assert q.dtype == torch.float16 and q.is_contiguous()
+    assert rope_cos.dtype == torch.float32 and rope_cos.is_contiguous() and rope_cos.shape == rope_sin.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    need = nsnq_decode_workspace_bytes(p, cache, Hq, num_splits)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    c = cache.c_struct()
+    r = nsnq_rope(_ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], pos0)
+    _check(lib().nsnq_decode_attention_prerope(ctypes.byref(p), _ptr(codebook), _ptr(q), Hq, ctypes.byref(c),
+                                               float(softmax_scale), ctypes.byref(r), num_splits, _ptr(out),
+                                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "nsnq_decode_attention_prerope")
     return out
 
 

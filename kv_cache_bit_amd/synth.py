@@ -115,3 +115,12 @@ def hadamard_signs(seed: int, d: int = 128) -> torch.Tensor:
     """+-1 int8 [d] for the randomised Hadamard transform (fair coin per channel)."""
     g = _gen(seed, "cpu")
     return (torch.randint(0, 2, (d,), generator=g, dtype=torch.int8) * 2 - 1).to(torch.int8)
+
+
+def rope_tables(max_pos: int, base: float = 10000.0, d: int = 128):
+    """Rotary-embedding tables cos, sin fp32 [max_pos, d/2] with the standard
+    frequencies theta_c = base^(-2c/d) (angles formed in float64)."""
+    c = torch.arange(d // 2, dtype=torch.float64)
+    theta = base ** (-2.0 * c / d)
+    ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * theta[None, :]
+    return torch.cos(ang).to(torch.float32), torch.sin(ang).to(torch.float32)

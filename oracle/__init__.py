@@ -55,6 +55,7 @@ def lib():
             "orc_num_threads": (i32, []),
             "orc_rtn4": (None, [P, i32, P, P, P, P, P]),
             "orc_cos_loss_grad": (f64, [P, i64, i32, i32, P, i32, P]),
+            "orc_rope": (None, [P, i64, i32, i32, P, P, i32]),
             "orc_finetune": (None, [P, i64, i32, i32, i32, i32, f64, P, P, P]),
             "orc_dq_scales_bytes": (i32, [i32]),
             "orc_encode_dq": (i32, [P, i64, i32, i32, i32, i32, P, i32, P, i32, P, P, P, P, P, P, P, P, P]),
@@ -310,12 +311,28 @@ def num_threads() -> int:
     return lib().orc_num_threads()
 
 
+def rope(k: np.ndarray, cos, sin, pos0: int = 0) -> np.ndarray:
+    """Rotate keys k float64 [..., T, d] (token t at position pos0 + t) with the
+    tables cos, sin fp32 [max_pos, d/2]; returns a new array."""
+    k = np.array(k, dtype=np.float64, copy=True, order="C")
+    *lead, T, d = k.shape
+    n = int(np.prod(lead)) if lead else 1
+    cs = np.ascontiguousarray(cos, dtype=np.float32)
+    sn = np.ascontiguousarray(sin, dtype=np.float32)
+    assert cs.shape == sn.shape and cs.shape[1] == d // 2 and pos0 + T <= cs.shape[0]
+    lib().orc_rope(_p(k), n, T, d, _p(cs), _p(sn), int(pos0))
+    return k
+
+
 def reference_decode(q, k_cache: dict, v_cache: dict, n_quant: int, n_resid: int,
-                     R: int, codebook, scale: float | None = None, signs=None) -> np.ndarray:
+                     R: int, codebook, scale: float | None = None, signs=None, rope_tables=None,
+                     pos0: int = 0) -> np.ndarray:
     """Attention over a compressed cache, by its plain definition: reconstruct
     the n_quant quantised tokens, append the n_resid fp16 residual tokens, and
     run textbook softmax attention.  Caches are dicts with codes [B,H,cap,S],
-    scales, mu (fp16 bits) and resid [B,H,R,d] (fp16 bits)."""
+    scales, mu (fp16 bits) and resid [B,H,R,d] (fp16 bits).  rope_tables =
+    (cos, sin): the keys are stored before RoPE and are rotated to positions
+    pos0 + t before the dot products."""
     qb = as_f16_bits(q)
     d = qb.shape[-1]
     if scale is None:
@@ -332,4 +349,6 @@ def reference_decode(q, k_cache: dict, v_cache: dict, n_quant: int, n_resid: int
         parts_v.append(f16_to_f64(as_f16_bits(v_cache["resid"])[..., :n_resid, :]))
     K = np.concatenate(parts_k, axis=-2)
     V = np.concatenate(parts_v, axis=-2)
+    if rope_tables is not None:
+        K = rope(K, rope_tables[0], rope_tables[1], pos0)
     return attention(qb, K, V, scale)

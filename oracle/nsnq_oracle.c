@@ -591,6 +591,29 @@ void orc_dequant(const uint8_t* codes, const uint16_t* scales, const uint16_t* m
   }
 }
 
+/* ---------------------------------------------------------------- RoPE --- */
+
+/* Rotary position embedding of keys stored before RoPE [P3 sec. 4: NSN is
+ * applied to keys before the rotary embedding]: rotate-half convention, pairs
+ * (c, c + d/2) of token t rotated with the tables at position pos0 + t:
+ *   k'[c]       = k[c] cos[p][c] - k[c + d/2] sin[p][c]
+ *   k'[c + d/2] = k[c + d/2] cos[p][c] + k[c] sin[p][c].
+ * k [n][T][d] in place; cos, sin fp32 [max_pos][d/2] (values taken exactly). */
+void orc_rope(double* k, int64_t n, int T, int d, const float* cs, const float* sn, int pos0) {
+  int h = d / 2;
+  for (int64_t i = 0; i < n; ++i)
+    for (int t = 0; t < T; ++t) {
+      double* kt = k + ((size_t)i * T + t) * d;
+      const float* cr = cs + (size_t)(pos0 + t) * h;
+      const float* sr = sn + (size_t)(pos0 + t) * h;
+      for (int c = 0; c < h; ++c) {
+        double a = kt[c], b = kt[c + h];
+        kt[c] = a * (double)cr[c] - b * (double)sr[c];
+        kt[c + h] = b * (double)cr[c] + a * (double)sr[c];
+      }
+    }
+}
+
 /* ----------------------------------------------------------- attention --- */
 
 /* Textbook single-query softmax attention, the plain definition the pages'

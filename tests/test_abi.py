@@ -26,7 +26,7 @@ def nsnq():
 
 def test_exports_every_declared_symbol(nsnq):
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(nsnq.lib(), n), n
     assert nsnq.nsnq_abi_version() == 4

@@ -248,6 +248,47 @@ def test_double_quant_encode_dequant_decode(oracle_codebooks, bits, R, Hq, Hkv, 
         compare_encoded_dq(cache, ek2, ev2, R, scale_adjust=adjust)
 
 
+# ------------------------------------------------- keys stored before RoPE --
+
+@pytest.mark.parametrize("bits,R,B,Hq,Hkv,L,flags,ragged", [
+    (2, 64, 2, 2, 2, 333, 0, False),
+    (2, 128, 1, 8, 2, 700, 0, False),                          # G = 4 (pre-RoPE always uses the LUT kernel)
+    (1, 128, 2, 4, 4, 300, 0, False),
+    (2, 64, 1, 2, 1, 200, 2, False),                           # double-quantised records
+    (2, 64, 2, 4, 2, 40, 0, False),                            # residual tokens only
+    (2, 64, 3, 2, 1, 0, 0, True),                              # ragged rows
+])
+def test_prerope_decode(oracle_codebooks, bits, R, B, Hq, Hkv, L, flags, ragged):
+    cb = oracle_codebooks[bits]
+    pos0 = 7
+    lengths = [R + 3, 3 * R + 1, 1] if ragged else [L] * B
+    Lmax = max(lengths)
+    cos, sin = synth.rope_tables(pos0 + Lmax + 1, 10000.0 if bits == 2 else 500000.0, D)
+    k, v = _kv(1000 + bits, B, Hkv, Lmax)
+    q = synth.queries(1000 + bits, 0, B, Hq, D)
+    p = nsnq.params(bits, R, flags=flags)
+    cbt = cb_tensor(cb)
+    dq = bool(flags & nsnq.NSNQ_DOUBLE_QUANT)
+    if ragged:
+        cache = nsnq.KVCache(p, B, Hkv, capacity(Lmax, R), DEV, ragged=True)
+        nsnq.nsnq_encode_kv_ragged(p, cbt, k.to(DEV), v.to(DEV), torch.tensor(lengths, dtype=torch.int32,
+                                   device=DEV), Lmax, cache)
+    else:
+        _, _, cache = gpu_encode(k, v, bits, R, cb, flags=flags)
+    out = nsnq.nsnq_decode_attention_prerope(p, cbt, q.to(DEV), cache, cos.to(DEV), sin.to(DEV), pos0)
+    out = out.float().cpu().numpy()
+    for b, Lb in enumerate(lengths):
+        ek = oracle.encode(k[b:b + 1, :, :Lb], R, cb, dq=dq)
+        ev = oracle.encode(v[b:b + 1, :, :Lb], R, cb, dq=dq)
+        ref = oracle.reference_decode(q[b:b + 1], ek, ev, ek["n_quant"], ek["n_resid"], R, cb,
+                                      rope_tables=(cos, sin), pos0=pos0)
+        check_attention(out[b:b + 1], ref)
+    # the rotation matters: the plain decode of the same cache differs
+    if not ragged and L > R:
+        plain = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), cache).float().cpu().numpy()
+        assert not np.allclose(plain, out, rtol=1e-2)
+
+
 # ------------------------------------------------------------ ragged rows --
 
 def _row_state(cache: nsnq.KVCache, which: int, b: int, nq: int, r: int) -> dict:
