@@ -101,6 +101,90 @@ def measure_layer(nsnq, synth, workload: str, reps: int, dev):
                        "hbm_frac": dec_b / res["decode"] / 1e9 / HBM_PEAK_GBS, "bytes": dec_b}}
 
 
+def decode_bytes_dq(bits: int, R: int, n_quant: int, n_resid: int, units: int, d: int = 128) -> float:
+    """Algorithmic decode bytes with double-quantised records: codes, the padded
+    scales record and the 80-byte mean record per block, fp16 residual."""
+    S = d // (4 if bits == 2 else 8)
+    rec = ((2 * R + R // 2 + 4) + 15) // 16 * 16
+    per_tok = 2 * (S + (rec + 80) / R)
+    return units * (n_quant * per_tok + n_resid * 2 * 2 * d)
+
+
+def measure_options(nsnq, synth, w: dict, k, v, q, codebook, dev, reps: int = 20):
+    """The format options on one layer, each against the same inputs: double
+    quantisation, randomised Hadamard + Strategy 3, decode over keys stored
+    before RoPE, and the cosine refinement of the codebook."""
+    import torch
+    B, Hq, Hkv, L, d, bits, R = w["B"], w["Hq"], w["Hkv"], w["L"], w["d"], w["bits"], w["R"]
+    r = ((L - 1) % R) + 1
+    nq = L - r
+    units = B * Hkv
+    stream = torch.cuda.current_stream()
+
+    def timed(f, n=reps):
+        for _ in range(3):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n / 1e3
+
+    def layer(p):
+        cache = nsnq.KVCache(p, B, Hkv, nq + R, dev)
+        ws = torch.empty(max(16, nsnq.nsnq_decode_workspace_bytes(p, cache, Hq)), dtype=torch.uint8, device=dev)
+
+        def enc():
+            cache.n_quant = cache.n_resid = 0
+            nsnq.nsnq_encode_kv(p, codebook, k, v, L, cache, stream=stream)
+        t_enc = timed(enc)
+        cache.n_quant, cache.n_resid = nq, r
+        ws = torch.empty(max(16, nsnq.nsnq_decode_workspace_bytes(p, cache, Hq)), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        t_dec = timed(lambda: nsnq.nsnq_decode_attention(p, codebook, q, cache, out=out, ws=ws, stream=stream))
+        return cache, ws, out, t_enc, t_dec
+
+    res = {}
+    p = nsnq.params(bits, R, flags=nsnq.NSNQ_DOUBLE_QUANT)
+    _, _, _, te, td = layer(p)
+    db = decode_bytes_dq(bits, R, nq, r, units, d)
+    res["double_quant"] = {"encode_us": te * 1e6, "decode_us": td * 1e6, "decode_bytes": db,
+                           "decode_hbm_frac": db / td / 1e9 / HBM_PEAK_GBS,
+                           "bytes_vs_plain": db / decode_bytes(bits, R, nq, r, units, d)}
+    signs = synth.hadamard_signs(1, d).to(dev)
+    p = nsnq.params(bits, R, flags=nsnq.NSNQ_SCALE_ADJUST, signs=signs)
+    _, _, _, te, td = layer(p)
+    res["rht_scale_adjust"] = {"encode_us": te * 1e6, "decode_us": td * 1e6}
+    p = nsnq.params(bits, R)
+    cache, ws, out, _, td_plain = layer(p)
+    cos, sin = synth.rope_tables(L + 1, 10000.0, d)
+    cos, sin = cos.to(dev), sin.to(dev)
+    tr = timed(lambda: nsnq.nsnq_decode_attention_prerope(p, codebook, q, cache, cos, sin, 0, out=out, ws=ws,
+                                                          stream=stream))
+    res["prerope_decode"] = {"us": tr * 1e6, "vs_post_rope": tr / td_plain,
+                             "hbm_frac": decode_bytes(bits, R, nq, r, units, d) / tr / 1e9 / HBM_PEAK_GBS}
+    # cosine refinement from the k-means centroids: 20 steps on 2^16 head vectors
+    s = nsnq.sub_dim(bits)
+    cent, _, _ = nsnq.nsnq_build_codebook(p, synth.randn_samples(0, 1 << 18, s).to(dev), 20)
+    x = synth.randn_samples(5, 1 << 16, d).to(dev)
+    xt = synth.randn_samples(6, 1 << 14, d).to(dev)
+    c0 = cent.clone()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    cent, _, loss = nsnq.nsnq_finetune_codebook(p, x, 20, 64.0, cent)
+    torch.cuda.synchronize()
+    tf = time.perf_counter() - t0
+    _, _, l0 = nsnq.nsnq_finetune_codebook(p, xt, 1, 0.0, c0.clone())
+    _, _, l1 = nsnq.nsnq_finetune_codebook(p, xt, 1, 0.0, cent.clone())
+    res["cosine_finetune"] = {"s": tf, "iters": 20, "n": 1 << 16, "lr": 64.0,
+                              "train_loss": [float(loss[0]), float(loss[-1])],
+                              "held_out_loss": [float(l0[0]), float(l1[0])]}
+    return res
+
+
 def decode_step_bench(nsnq, synth, workload: str, steps: int, dev, distinct_layers: int = 2):
     """Whole-model decode step (every layer's decode attention, one new token
     per sequence) on a multi-layer workload, against the fp16-cache comparator
@@ -389,6 +473,8 @@ def main():
         "timing": {"step_ms_median": float(np.median(step_ms)), "step_ms_p10": float(np.percentile(step_ms, 10)),
                    "step_ms_p90": float(np.percentile(step_ms, 90)), "buffer_sets": nbuf},
     }
+    if not args.no_extra:
+        res["options"] = measure_options(nsnq, synth, w, k, v, q, codebook, dev)
     if not args.no_extra and args.workload != "llama2-7b-layer-b16-1bit":
         del ks, vs, caches
         torch.cuda.empty_cache()
