@@ -110,19 +110,24 @@ __device__ __forceinline__ float rtn4_code(float v, float Z, float S) {
   return fminf(fmaxf(rintf((v - Z) / S), 0.f), 15.f);
 }
 
+// Waves per encode work-group: 8 x 64 lanes share one block's LDS staging,
+// which lets 4 waves per SIMD stay resident (the 48 KB of LDS per group would
+// otherwise cap a 4-wave group at 3).
+constexpr int kEncWaves = 8;
+
 template <int SUB, int R, bool DQ>
-__global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeArgs a) {
   if ((int)blockIdx.x >= a.nblk * a.n_units) {
     resid_copy(a, blockIdx.x - a.nblk * a.n_units, blockIdx.y);
     return;
   }
   constexpr int S = kDim / SUB;      // slots = lanes per token
   constexpr int TPR = kWave / S;     // tokens per wave row
-  constexpr int TPW = R / 4;         // tokens per wave
+  constexpr int TPW = R / kEncWaves;  // tokens per wave
   constexpr int ROWS = TPW / TPR;    // rows per wave
-  static_assert(ROWS * TPR * 4 == R, "block split");
+  static_assert(ROWS * TPR * kEncWaves == R, "block split");
 
-  __shared__ float red[4][kDim];
+  __shared__ float red[kEncWaves][kDim];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   // 32 t + (l % 32)) and re-read per row, which keeps ~40 VGPRs free.
   __shared__ half8_t sA1[8][kWave];
   __shared__ half4_t sA2[8][kWave];
-  for (int i = threadIdx.x; i < 8 * kWave; i += 256) {
+  for (int i = threadIdx.x; i < 8 * kWave; i += blockDim.x) {
     const int t = i / kWave, l = i % kWave;
     const int k = 32 * t + (l & 31);
     const uint16_t* cb = a.codebook;
@@ -299,7 +304,10 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
 #pragma unroll
   for (int e = 0; e < SUB; ++e) {
     const int c = slot * SUB + e;
-    mu[e] = (red[0][c] + red[1][c] + red[2][c] + red[3][c]) * (1.0f / R);
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kEncWaves; ++w) sum += red[w][c];
+    mu[e] = sum * (1.0f / R);
   }
   if constexpr (DQ) {
     // 4-bit codes of the mean in groups of 32 channels (32 / SUB slots); the
@@ -422,23 +430,38 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     asm("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(0xffffff00u));
     uint32_t best0 = 0xffffffffu, best1 = 0xffffffffu;
     const float16_t zacc = {};
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    // software pipeline: the products of tile t + 1 are issued before the keys
+    // of tile t are formed, so the matrix core runs under the argmin
+    auto tile = [&](int t, float16_t& acc0, float16_t& acc1) {
       const half8_t A1t = sA1[t][lane];
-      float16_t acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1t, B0, zacc, 0, 0, 0);
-      float16_t acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1t, B1, zacc, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1t, B0, zacc, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1t, B1, zacc, 0, 0, 0);
       if constexpr (SUB == 8) {
         const half4_t A2t = sA2[t][lane];
         acc0 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2t, Bb0, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2t, Bb1, acc1, 0, 0, 0);
       }
+    };
+    // (at 1 bit the extra bias products would push the kernel past 168 VGPRs;
+    // it keeps one tile in flight)
+    constexpr bool kPipe = SUB == 4;
+    float16_t cur0, cur1, nxt0, nxt1;
+    if (kPipe) tile(0, cur0, cur1);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (!kPipe) tile(t, cur0, cur1);
+      if (kPipe && t + 1 < 8) tile(t + 1, nxt0, nxt1);
 #pragma unroll
       for (int q = 0; q < 16; q += 2) {
         // accumulator q holds codeword 32t + 8(q/4) + 4(lane/32) + q%4
         const uint32_t i0 = 32u * t + 8u * (q >> 2) + (q & 3);
         const uint32_t i1 = 32u * t + 8u * ((q + 1) >> 2) + ((q + 1) & 3);
-        best0 = min(min(best0, make_key(acc0[q], vmask, i0)), make_key(acc0[q + 1], vmask, i1));
-        best1 = min(min(best1, make_key(acc1[q], vmask, i0)), make_key(acc1[q + 1], vmask, i1));
+        best0 = min(min(best0, make_key(cur0[q], vmask, i0)), make_key(cur0[q + 1], vmask, i1));
+        best1 = min(min(best1, make_key(cur1[q], vmask, i0)), make_key(cur1[q + 1], vmask, i1));
+      }
+      if (kPipe && t + 1 < 8) {
+        cur0 = nxt0;
+        cur1 = nxt1;
       }
     }
     const uint32_t hbit = (uint32_t)(lane >> 5) << 2;
@@ -526,7 +549,7 @@ hipError_t launch_append(const AppendArgs& a, int B, hipStream_t stream) {
 
 hipError_t launch_encode(const EncodeArgs& a, int sub, int R, hipStream_t stream) {
   const bool rcopy = a.rc_r > 0 || a.lens != nullptr;
-  dim3 grid(a.nblk * a.n_units + (rcopy ? a.n_units : 0), 2), block(256);
+  dim3 grid(a.nblk * a.n_units + (rcopy ? a.n_units : 0), 2), block(64 * kEncWaves);
   if (grid.x == 0) return hipSuccess;
   if (a.dq) {
     if (sub == 4 && R == 128) hipLaunchKernelGGL((encode_kernel<4, 128, true>), grid, block, 0, stream, a);
