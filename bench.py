@@ -185,7 +185,8 @@ def measure_options(nsnq, synth, w: dict, k, v, q, codebook, dev, reps: int = 20
     return res
 
 
-def decode_step_bench(nsnq, synth, workload: str, steps: int, dev, distinct_layers: int = 2):
+def decode_step_bench(nsnq, synth, workload: str, steps: int, dev, distinct_layers: int = 2,
+                      max_layers: int = 0, with_fp16: bool = True):
     """Whole-model decode step (every layer's decode attention, one new token
     per sequence) on a multi-layer workload, against the fp16-cache comparator
     at the largest batch whose fp16 cache fits the same HBM budget.
@@ -200,6 +201,9 @@ def decode_step_bench(nsnq, synth, workload: str, steps: int, dev, distinct_laye
     import torch
     w = synth.WORKLOADS[workload]
     NL, B, Hq, Hkv, L, d, bits, R = (w["layers"], w["B"], w["Hq"], w["Hkv"], w["L"], w["d"], w["bits"], w["R"])
+    if max_layers > 0:
+        NL = min(NL, max_layers)
+        distinct_layers = min(distinct_layers, NL)
     p = nsnq.params(bits, R)
     s = nsnq.sub_dim(bits)
     _, cb, _ = nsnq.nsnq_build_codebook(p, synth.randn_samples(0, 1 << 20, s).to(dev), 50)
@@ -247,6 +251,13 @@ def decode_step_bench(nsnq, synth, workload: str, steps: int, dev, distinct_laye
     dec_b = NL * decode_bytes(bits, R, nq, r, B * Hkv, d)
     del caches
     torch.cuda.empty_cache()
+    res = {"metric": "decode-attn tokens/s", "workload": workload, "layers": NL, "batch": B, "context": L,
+           "bits": bits, "step_ms": t_c * 1e3, "tokens_per_s": B / t_c,
+           "hbm_gbs": dec_b / t_c / 1e9, "hbm_frac": dec_b / t_c / 1e9 / HBM_PEAK_GBS,
+           "compressed_cache_gb": cache_bytes / 1e9,
+           "setup": f"{distinct_layers} distinct layers encoded, caches copied to the other {NL - distinct_layers}"}
+    if not with_fp16:
+        return res
     # fp16 comparator: largest batch whose fp16 K/V for all layers fits the budget
     free, total = torch.cuda.mem_get_info()
     budget = free - 8e9
@@ -264,15 +275,10 @@ def decode_step_bench(nsnq, synth, workload: str, steps: int, dev, distinct_laye
 
     t_16 = timed(step16, steps)
     b16 = NL * B16 * Hkv * L * 2 * 2 * d
-    return {"metric": "decode-attn tokens/s", "workload": workload, "layers": NL, "batch": B, "context": L,
-            "bits": bits, "step_ms": t_c * 1e3, "tokens_per_s": B / t_c,
-            "hbm_gbs": dec_b / t_c / 1e9, "hbm_frac": dec_b / t_c / 1e9 / HBM_PEAK_GBS,
-            "compressed_cache_gb": cache_bytes / 1e9,
-            "fp16": {"batch": B16, "step_ms": t_16 * 1e3, "tokens_per_s": B16 / t_16,
-                     "hbm_gbs": b16 / t_16 / 1e9, "cache_gb": per_seq * B16 / 1e9,
-                     "budget_gb": budget / 1e9},
-            "gain_tokens_per_s": (B / t_c) / (B16 / t_16),
-            "setup": f"{distinct_layers} distinct layers encoded, caches copied to the other {NL - distinct_layers}"}
+    res["fp16"] = {"batch": B16, "step_ms": t_16 * 1e3, "tokens_per_s": B16 / t_16,
+                   "hbm_gbs": b16 / t_16 / 1e9, "cache_gb": per_seq * B16 / 1e9, "budget_gb": budget / 1e9}
+    res["gain_tokens_per_s"] = (B / t_c) / (B16 / t_16)
+    return res
 
 
 def copy_calibration(nbytes: int, reps: int):
@@ -337,6 +343,8 @@ def main():
     ap.add_argument("--no-fp16", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 1-bit layer measurement")
     ap.add_argument("--copy-bytes", type=int, default=0, help="only run a device copy of this size")
+    ap.add_argument("--decode-layers", type=int, default=0,
+                    help="multi-layer workloads: time the decode of only this many layers (profiling)")
     args = ap.parse_args()
     if args.copy_bytes:
         copy_calibration(args.copy_bytes, max(args.steps, 1))
@@ -356,7 +364,8 @@ def main():
     torch.cuda.set_device(dev)
     w = dict(synth.WORKLOADS[args.workload])
     if w["layers"] > 1:
-        print(json.dumps(decode_step_bench(nsnq, synth, args.workload, max(args.steps // 5, 3), dev)), flush=True)
+        print(json.dumps(decode_step_bench(nsnq, synth, args.workload, max(args.steps // 5, 3), dev,
+                                           max_layers=args.decode_layers, with_fp16=not args.no_fp16)), flush=True)
         return
     B, Hq, Hkv, L, d, bits, R = w["B"], w["Hq"], w["Hkv"], w["L"], w["d"], w["bits"], w["R"]
     s = nsnq.sub_dim(bits)
