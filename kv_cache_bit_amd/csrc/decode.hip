@@ -79,8 +79,10 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&cw)[S / 
   }
 }
 
+// One query head per group (no RoPE): registers capped for 4 waves per SIMD
+// (5 at 1 bit) without spilling; the wider variants keep the compiler's choice.
 template <int SUB, int GH, bool DQ, bool ROPE>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && !ROPE ? (SUB == 8 ? 5 : 4) : 1))) void decode_split_kernel(DecodeArgs a) {
   constexpr int S = kDim / SUB;
   constexpr int CW = S / 4;      // 32-bit words of codes per token
   constexpr int SPT = 16 / SUB;  // value slots per lane
