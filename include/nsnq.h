@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define NSNQ_ABI_VERSION 4
+#define NSNQ_ABI_VERSION 5
 
 typedef int32_t nsnq_status;
 enum {
@@ -99,15 +99,22 @@ enum {
  *                   device array of head_dim int8 values +1/-1: the randomised
  *                   Hadamard transform u = H diag(signs) w (technical summary
  *                   sec. 2).  Encode, dequant and attention of one cache must
- *                   use the same signs. */
+ *                   use the same signs.
+ *   vq_candidates   NULL (the encoder compares every codeword), or a device
+ *                   copy of the table nsnq_vq_candidates() builds for the
+ *                   codebook passed to the encode calls (2 bits only); the
+ *                   codes are the same, the search is shorter.
+ *   vq_tiles        0 with vq_candidates NULL, else the tile count that
+ *                   nsnq_vq_candidates() returned (1..4). */
 typedef struct {
   int32_t head_dim;
   int32_t bits;
   int32_t n_codewords;
   int32_t block_tokens;
   int32_t flags;
-  int32_t reserved; /* must be 0 */
+  int32_t vq_tiles;
   const int8_t* hadamard_signs;
+  const uint8_t* vq_candidates;
 } nsnq_params;
 
 /* One of the K or V halves of a cache (layouts above). */
@@ -195,6 +202,27 @@ nsnq_status nsnq_build_codebook(const nsnq_params* p, const float* samples, int6
 nsnq_status nsnq_finetune_codebook(const nsnq_params* p, const float* samples, int64_t n, int32_t iters, float lr,
                                    float* centroids, uint16_t* codebook, float* loss, void* ws, size_t ws_bytes,
                                    void* stream);
+
+/* Candidate lists for the 2-bit encoder's nearest-codeword search (technical
+ * summary sec. 3, "Vector Quantization": squared Euclidean distance over
+ * 4-element sub-vectors, 256 codewords; ties to the lowest index).  Each
+ * sub-vector u of a Hadamard-domain vector of norm sqrt(128) lies in one of 16
+ * orthant boxes (bit i of the orthant index set when u_i < 0; every |u_i| <=
+ * 12).  For each box the list holds, in ascending order, every codeword whose
+ * Voronoi cell meets the box, found by an exact fp64 linear programme per
+ * (codeword, box); the nearest codeword of any u in the box is on its list, so
+ * searching the list returns the same code as searching all 256.
+ *   codebook_host  fp16 [256][4], HOST memory (the codebook of the encode calls).
+ *   table_host     HOST out, NSNQ_VQ_TABLE_BYTES bytes: [16 boxes][128] codeword
+ *                  indices, each list padded by repeating its last entry.
+ *   n_tiles        out: ceil(longest list / 32), for nsnq_params.vq_tiles.
+ * Copy the table to device memory and set vq_candidates / vq_tiles in the
+ * params of the encode calls.  Host only, synchronous, about 0.1 s.
+ * NSNQ_EUNSUPPORTED for bits != 2 (1-bit boxes keep most codewords) or when a
+ * list would exceed 128 entries. */
+#define NSNQ_VQ_TABLE_BYTES 2048
+nsnq_status nsnq_vq_candidates(const nsnq_params* p, const uint16_t* codebook_host, uint8_t* table_host,
+                               int32_t* n_tiles);
 
 /* Prefill encode (technical summary secs. 1-4).  k and v are fp16 streams
  * indexed [b][h][t][c] at element offsets b*stride_b + h*stride_h +

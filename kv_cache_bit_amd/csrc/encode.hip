@@ -110,27 +110,40 @@ __device__ __forceinline__ float rtn4_code(float v, float Z, float S) {
   return fminf(fmaxf(rintf((v - Z) / S), 0.f), 15.f);
 }
 
-// Waves per encode work-group: 8 x 64 lanes share one block's LDS staging,
-// which lets 4 waves per SIMD stay resident (the 48 KB of LDS per group would
-// otherwise cap a 4-wave group at 3).
-constexpr int kEncWaves = 8;
+// Waves per encode work-group.  Exhaustive search: 8 x 64 lanes share one
+// block's LDS staging, which lets 4 waves per SIMD stay resident (the 48 KB of
+// LDS per group would otherwise cap a 4-wave group at 3).  Candidate-list
+// search: 16 waves, one group per CU, since the block's sub-vector records
+// and the boxes' operand tiles take ~150 KB of LDS.
+template <int NT>
+constexpr int enc_waves() { return NT ? 16 : 8; }
 
-template <int SUB, int R, bool DQ>
-__global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeArgs a) {
+// B operand of the bias rows for a sub-vector: (|u|^2 hi, lo, 1, 1, 0, 0, 0, 0).
+__device__ __forceinline__ half8_t bias_operand(uint32_t uu_pair) {
+  return u32x4_to_half8(uu_pair, 0x3C003C00u, 0u, 0u);
+}
+
+// NT = 0: every codeword is compared.  NT = 3 (2 bits): each sub-vector is
+// compared with the 96 entries of its orthant box's candidate list.
+template <int SUB, int R, bool DQ, int NT>
+__global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs a) {
+  constexpr int NW = enc_waves<NT>();
+  static_assert(NT == 0 || SUB == 4, "candidate lists exist for 4-element sub-vectors only");
   if ((int)blockIdx.x >= a.nblk * a.n_units) {
     resid_copy(a, blockIdx.x - a.nblk * a.n_units, blockIdx.y);
     return;
   }
   constexpr int S = kDim / SUB;      // slots = lanes per token
   constexpr int TPR = kWave / S;     // tokens per wave row
-  constexpr int TPW = R / kEncWaves;  // tokens per wave
+  constexpr int TPW = R / NW;        // tokens per wave
   constexpr int ROWS = TPW / TPR;    // rows per wave
-  static_assert(ROWS * TPR * kEncWaves == R, "block split");
+  static_assert(ROWS * TPR * NW == R, "block split");
 
-  __shared__ float red[kEncWaves][kDim];
+  __shared__ float red[NW][kDim];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int slot = lane % S;
   const int tir = lane / S;
 
@@ -151,13 +164,16 @@ __global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeArgs a) {
   const int64_t tok_base = (int64_t)unit * a.cap + dst0 + (int64_t)blk * R;
 
   // ---- codebook operands (A side), per 32-codeword tile -------------------
-  // Built once per group into LDS (lane l of tile t holds codeword
-  // 32 t + (l % 32)) and re-read per row, which keeps ~40 VGPRs free.
-  __shared__ half8_t sA1[8][kWave];
-  __shared__ half4_t sA2[8][kWave];
-  for (int i = threadIdx.x; i < 8 * kWave; i += blockDim.x) {
+  // Built once per group into LDS and re-read per row, which keeps ~40 VGPRs
+  // free.  Exhaustive search: lane l of tile t holds codeword 32 t + (l % 32).
+  // Candidate lists: tile t of box o holds list entries 32 t .. 32 t + 31, so
+  // every operand read is a sequential, conflict-free 16-byte load.
+  constexpr int NTILE = NT ? 16 * NT : 8;
+  __shared__ half8_t sA1[NTILE][kWave];
+  __shared__ half4_t sA2[SUB == 8 ? 8 : 1][kWave];
+  for (int i = tid; i < NTILE * kWave; i += blockDim.x) {
     const int t = i / kWave, l = i % kWave;
-    const int k = 32 * t + (l & 31);
+    const int k = NT ? a.cand[(t / NT) * 128 + 32 * (t % NT) + (l & 31)] : 32 * t + (l & 31);
     const uint16_t* cb = a.codebook;
     float c[SUB];
     float nrm = 0.f;
@@ -170,7 +186,6 @@ __global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeArgs a) {
     const half_t b_hi = (half_t)bsum;
     const half_t b_lo = (half_t)(bsum - (float)b_hi);
     half8_t av;
-    half4_t a2 = {(half_t)0.f, (half_t)0.f, (half_t)0.f, (half_t)0.f};
     if constexpr (SUB == 4) {
       if (l < 32) {
 #pragma unroll
@@ -185,25 +200,62 @@ __global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeArgs a) {
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) av[e] = (half_t)(-2.f * c[e]);
-      a2 = half4_t{(half_t)1.f, (half_t)1.f, b_hi, b_lo};
+      sA2[t % 8][l] = half4_t{(half_t)1.f, (half_t)1.f, b_hi, b_lo};
     }
     sA1[t][l] = av;
-    sA2[t][l] = a2;
+  }
+
+  // ---- candidate-list search state (NT > 0) -------------------------------
+  // Per sub-vector i = token * S + slot: its fp16 hi/lo parts and |u|^2 pair
+  // (plus one all-zero record for padding columns), its orthant box, later its
+  // code; the box-sorted column order; the lists; per-box counts and offsets.
+  constexpr int NSV = NT ? R * S : 1;     // sub-vectors of the block
+  constexpr int kDummy = NSV;             // the all-zero record
+  constexpr int kCols = NSV + 16 * 32;    // sorted columns, each box padded to 32
+  __shared__ half8_t recs[NT ? NSV + 1 : 1];
+  __shared__ uint32_t uus[NT ? NSV + 1 : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t boxc[NT ? NSV : 16];
+  __shared__ uint16_t sidx[NT ? kCols : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t lst[NT ? 16 * 128 : 16];
+  __shared__ uint8_t cbox[NT ? kCols / 32 : 1];
+  __shared__ uint32_t whist[NT ? NW : 1][16];  // per wave and box: count, then first column
+  __shared__ int cstart[16], ccount[16], cpad[16], ncol_blocks;
+  __shared__ float n1t[NT ? R : 1], n2t[NT ? R : 1];
+  if constexpr (NT > 0) {
+    for (int i = tid; i < 128; i += blockDim.x)
+      reinterpret_cast<uint4*>(lst)[i] = reinterpret_cast<const uint4*>(a.cand)[i];
+    if (tid < NW * 16) whist[tid / 16][tid % 16] = 0u;
+    if (tid == 0) {
+      recs[kDummy] = half8_t{};
+      uus[kDummy] = 0u;
+    }
   }
   // (visible after the first __syncthreads below)
 
   // One row = this lane's sub-vector of token `tok`: raw fp16 load, then
   // y = x / n1 with n1 = ||x|| / sqrt(d).  Pass 1 reads the block from HBM
   // once and keeps the raw fp16 rows in LDS; pass 2 recomputes y from there
-  // instead of keeping R x 128 floats in registers.
+  // instead of keeping R x 128 floats in registers.  (With candidate lists the
+  // LDS holds the sub-vector records instead, and the rows stay in registers.)
   using raw_t = typename std::conditional<SUB == 4, uint2, uint4>::type;
-  __shared__ raw_t xs[R * S];  // [token][slot], R x 256 bytes
+  __shared__ raw_t xs[NT ? 1 : R * S];  // [token][slot], R x 256 bytes
   auto load_raw = [&](int tok) -> raw_t {
     const raw_t v = *reinterpret_cast<const raw_t*>(src + (int64_t)tok * a.st + slot * SUB);
-    xs[tok * S + slot] = v;
+    if constexpr (NT == 0) xs[tok * S + slot] = v;
     return v;
   };
-  auto lds_raw = [&](int tok) -> raw_t { return xs[tok * S + slot]; };
+  auto lds_raw = [&](int tok) -> raw_t { return xs[NT ? 0 : tok * S + slot]; };
+  // candidate lists: this lane's rows stay in registers from pass 1 to pass 2
+  raw_t xr[NT ? ROWS : 1];
+  auto fetch = [&](int r, int tok) -> raw_t {
+    const raw_t v = load_raw(tok);
+    if constexpr (NT > 0) xr[r] = v;
+    return v;
+  };
+  auto row_raw = [&](int r, int tok) -> raw_t {
+    if constexpr (NT > 0) return xr[r];
+    else return lds_raw(tok);
+  };
   auto norm_raw = [&](const raw_t& raw, float (&y)[SUB], float& n1) {
     float v[SUB];
     v[0] = h2f(raw.x & 0xffff); v[1] = h2f(raw.x >> 16);
@@ -240,7 +292,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeArgs a) {
     for (int r = 0; r < ROWS; ++r) {
       const int tok = wave * TPW + r * TPR + tir;
       float y[SUB], n1;
-      norm_raw(load_raw(tok), y, n1);
+      norm_raw(fetch(r, tok), y, n1);
       if (slot == 0) n1s[tok] = n1;
     }
     __syncthreads();
@@ -268,7 +320,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeArgs a) {
       const int tok = wave * TPW + r * TPR + tir;
       const float nh = fmaf(S1, rtn4_code(n1s[tok], Z1, S1), Z1);
       const float inv = nh > 0.f ? 1.f / nh : 0.f;
-      const raw_t raw = lds_raw(tok);
+      const raw_t raw = row_raw(r, tok);
       float v[SUB];
       v[0] = h2f(raw.x & 0xffff); v[1] = h2f(raw.x >> 16);
       v[2] = h2f(raw.y & 0xffff); v[3] = h2f(raw.y >> 16);
@@ -284,12 +336,12 @@ __global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeArgs a) {
 #pragma unroll 4
     for (int r = 0; r < ROWS; ++r) {
       float y[SUB], n1;
-      norm_raw(load_raw(wave * TPW + r * TPR + tir), y, n1);
+      norm_raw(fetch(r, wave * TPW + r * TPR + tir), y, n1);
 #pragma unroll
       for (int e = 0; e < SUB; ++e) csum[e] += y[e];
     }
   }
-  // combine the TPR lanes holding the same channels, then the 4 waves
+  // combine the TPR lanes holding the same channels, then the waves
 #pragma unroll
   for (int e = 0; e < SUB; ++e) {
     if constexpr (S <= 16) csum[e] += xlane<16>(csum[e]);
@@ -300,15 +352,18 @@ __global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeArgs a) {
     for (int e = 0; e < SUB; ++e) red[wave][slot * SUB + e] = csum[e];
   }
   __syncthreads();
-  float mu[SUB];
-#pragma unroll
-  for (int e = 0; e < SUB; ++e) {
-    const int c = slot * SUB + e;
+  // channel means: one thread per channel sums the waves' partials
+  __shared__ float mus[kDim];
+  if (tid < kDim) {
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < kEncWaves; ++w) sum += red[w][c];
-    mu[e] = sum * (1.0f / R);
+    for (int w = 0; w < NW; ++w) sum += red[w][tid];
+    mus[tid] = sum * (1.0f / R);
   }
+  __syncthreads();
+  float mu[SUB];
+#pragma unroll
+  for (int e = 0; e < SUB; ++e) mu[e] = mus[slot * SUB + e];
   if constexpr (DQ) {
     // 4-bit codes of the mean in groups of 32 channels (32 / SUB slots); the
     // pass below shifts by the stored mean mu_hat
@@ -348,15 +403,12 @@ __global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeArgs a) {
 #pragma unroll
   for (int e = 0; e < SUB; ++e) sgn[e] = a.signs ? (float)a.signs[slot * SUB + e] : 1.f;
 
-  // ---- pass 2: per row: shift, second normalisation, Hadamard, VQ ---------
-#pragma unroll 1
-  for (int r = 0; r < ROWS; ++r) {
-    const int tok = wave * TPW + r * TPR + tir;
-    float u[SUB], n1;
+  // Shift, second normalisation and Hadamard transform of this lane's
+  // sub-vector of token `tok`: u (norm sqrt(d) over the token), n1, n2.
+  auto transform = [&](int tok, const raw_t& raw, float (&u)[SUB], float& n1, float& n2) {
     if constexpr (DQ) {
       n1 = n1hs[tok];
       const float inv = n1 > 0.f ? 1.f / n1 : 0.f;
-      const raw_t raw = lds_raw(tok);
       u[0] = h2f(raw.x & 0xffff) * inv; u[1] = h2f(raw.x >> 16) * inv;
       u[2] = h2f(raw.y & 0xffff) * inv; u[3] = h2f(raw.y >> 16) * inv;
       if constexpr (SUB == 8) {
@@ -364,7 +416,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeArgs a) {
         u[6] = h2f(raw.w & 0xffff) * inv; u[7] = h2f(raw.w >> 16) * inv;
       }
     } else {
-      norm_raw(lds_raw(tok), u, n1);
+      norm_raw(raw, u, n1);
     }
     float ss = 0.f;
 #pragma unroll
@@ -378,121 +430,318 @@ __global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeArgs a) {
     const float rs2 = __builtin_amdgcn_rsqf(ss);
     const bool live = ss >= kN2Floor * kN2Floor;
     const float inv2 = live ? rs2 : 0.f;
-    const float n2 = ss * inv2;
+    n2 = ss * inv2;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) u[e] *= inv2 * sgn[e];
     fwht128<SUB>(u, lane);
 #pragma unroll
     for (int e = 0; e < SUB; ++e) u[e] *= kInvSqrtD;
-
-    // hi/lo split and squared norm of this lane's sub-vector
-    half_t hi[SUB], lo[SUB];
-    float uu = 0.f;
+  };
+  // hi/lo fp16 split of u and the squared norm of this lane's sub-vector
+  auto split = [&](const float (&u)[SUB], half_t (&hi)[SUB], half_t (&lo)[SUB], half_t& uu_hi, half_t& uu_lo,
+                   float& uu) {
+    uu = 0.f;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) {
       hi[e] = (half_t)u[e];
       lo[e] = (half_t)(u[e] - (float)hi[e]);
       uu = fmaf(u[e], u[e], uu);
     }
-    const half_t uu_hi = (half_t)uu;
-    const half_t uu_lo = (half_t)(uu - (float)uu_hi);
-
-    // B operands of the two 32-column blocks (lanes 0-31 / 32-63 own data)
-    half8_t B0, B1;
-    half4_t Bb0, Bb1;
-    if constexpr (SUB == 4) {
-      const uint32_t P[4] = {pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(lo[0], lo[1]),
-                             pack_h2(lo[2], lo[3])};
-      const uint32_t Q[4] = {pack_h2(uu_hi, uu_lo), pack_h2((half_t)1.f, (half_t)1.f), 0u, 0u};
-      uint32_t b0[4], b1[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) half_swap(P[i], Q[i], b0[i], b1[i], lane);
-      B0 = u32x4_to_half8(b0[0], b0[1], b0[2], b0[3]);
-      B1 = u32x4_to_half8(b1[0], b1[1], b1[2], b1[3]);
-      Bb0 = Bb1 = half4_t{(half_t)0.f, (half_t)0.f, (half_t)0.f, (half_t)0.f};
+    uu_hi = (half_t)uu;
+    uu_lo = (half_t)(uu - (float)uu_hi);
+  };
+  // the scales of token `tok` (slot-0 lane): (n1, n2) fp16, or n2 alone in
+  // the double-quantised record
+  auto store_scales = [&](int tok, float n1, float n2s) {
+    if constexpr (DQ) {
+      *reinterpret_cast<half_t*>(srec + 2 * tok) = (half_t)n2s;
     } else {
-      const uint32_t P[4] = {pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(hi[4], hi[5]),
-                             pack_h2(hi[6], hi[7])};
-      const uint32_t Q[4] = {pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]), pack_h2(lo[4], lo[5]),
-                             pack_h2(lo[6], lo[7])};
-      uint32_t b0[4], b1[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) half_swap(P[i], Q[i], b0[i], b1[i], lane);
-      B0 = u32x4_to_half8(b0[0], b0[1], b0[2], b0[3]);
-      B1 = u32x4_to_half8(b1[0], b1[1], b1[2], b1[3]);
-      const half4_t bias = {uu_hi, uu_lo, (half_t)1.f, (half_t)1.f};
-      const half4_t zero4 = {(half_t)0.f, (half_t)0.f, (half_t)0.f, (half_t)0.f};
-      Bb0 = lane < 32 ? bias : zero4;
-      Bb1 = lane < 32 ? zero4 : bias;
+      *reinterpret_cast<uint32_t*>(scales + (tok_base + tok) * 2) = pack_h2((half_t)n1, (half_t)n2s);
     }
+  };
 
-    uint32_t vmask;  // 0xffffff00 in a VGPR (opaque so it is not folded into a literal)
-    asm("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(0xffffff00u));
-    uint32_t best0 = 0xffffffffu, best1 = 0xffffffffu;
-    const float16_t zacc = {};
-    // software pipeline: the products of tile t + 1 are issued before the keys
-    // of tile t are formed, so the matrix core runs under the argmin
-    auto tile = [&](int t, float16_t& acc0, float16_t& acc1) {
-      const half8_t A1t = sA1[t][lane];
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1t, B0, zacc, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1t, B1, zacc, 0, 0, 0);
-      if constexpr (SUB == 8) {
-        const half4_t A2t = sA2[t][lane];
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2t, Bb0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2t, Bb1, acc1, 0, 0, 0);
-      }
-    };
-    // (at 1 bit the extra bias products would push the kernel past 168 VGPRs;
-    // it keeps one tile in flight)
-    constexpr bool kPipe = SUB == 4;
-    float16_t cur0, cur1, nxt0, nxt1;
-    if (kPipe) tile(0, cur0, cur1);
+  const uint32_t hbit = (uint32_t)(lane >> 5) << 2;
+
+  if constexpr (NT == 0) {
+    // ---- pass 2: per row: shift, second normalisation, Hadamard, VQ -------
+#pragma unroll 1
+    for (int r = 0; r < ROWS; ++r) {
+      const int tok = wave * TPW + r * TPR + tir;
+      float u[SUB], n1, n2;
+      transform(tok, lds_raw(tok), u, n1, n2);
+      half_t hi[SUB], lo[SUB], uu_hi, uu_lo;
+      float uu;
+      split(u, hi, lo, uu_hi, uu_lo, uu);
+
+      // B operands of the two 32-column blocks (lanes 0-31 / 32-63 own data)
+      half8_t B0, B1;
+      half4_t Bb0, Bb1;
+      if constexpr (SUB == 4) {
+        const uint32_t P[4] = {pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(lo[0], lo[1]),
+                               pack_h2(lo[2], lo[3])};
+        const uint32_t Q[4] = {pack_h2(uu_hi, uu_lo), pack_h2((half_t)1.f, (half_t)1.f), 0u, 0u};
+        uint32_t b0[4], b1[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (!kPipe) tile(t, cur0, cur1);
-      if (kPipe && t + 1 < 8) tile(t + 1, nxt0, nxt1);
-#pragma unroll
-      for (int q = 0; q < 16; q += 2) {
-        // accumulator q holds codeword 32t + 8(q/4) + 4(lane/32) + q%4
-        const uint32_t i0 = 32u * t + 8u * (q >> 2) + (q & 3);
-        const uint32_t i1 = 32u * t + 8u * ((q + 1) >> 2) + ((q + 1) & 3);
-        best0 = min(min(best0, make_key(cur0[q], vmask, i0)), make_key(cur0[q + 1], vmask, i1));
-        best1 = min(min(best1, make_key(cur1[q], vmask, i0)), make_key(cur1[q + 1], vmask, i1));
-      }
-      if (kPipe && t + 1 < 8) {
-        cur0 = nxt0;
-        cur1 = nxt1;
-      }
-    }
-    const uint32_t hbit = (uint32_t)(lane >> 5) << 2;
-    best0 |= hbit;
-    best1 |= hbit;
-    // column n of block 0 belongs to lane n, of block 1 to lane 32 + n: one
-    // swap brings each column's other half next to it
-    uint32_t klo, khi;
-    half_swap(best0, best1, klo, khi, lane);  // klo = [b0 low, b1 low], khi = [b0 high, b1 high]
-    const uint32_t mine = min(klo, khi);
-    const uint32_t code = mine & 0xffu;
-    codes[(tok_base + tok) * S + slot] = (uint8_t)code;
-    // Strategy-3 scale: alpha = |u|^2 / (u . c_hat), folded into n2
-    float n2s = n2;
-    if (a.scale_adjust) {
-      // the codeword from the MFMA operand tiles: lanes < 32 of tile code/32
-      // hold -2 c (exact in fp16)
-      const half8_t cw = sA1[code >> 5][code & 31];
-      float uc = 0.f;
-#pragma unroll
-      for (int e = 0; e < SUB; ++e) uc = fmaf(u[e], -0.5f * (float)cw[e], uc);
-      uc = group_sum<S>(uc);
-      const float utot = group_sum<S>(uu);
-      if (uc > 0.f) n2s = n2 * (utot / uc);
-    }
-    if (slot == 0) {
-      if constexpr (DQ) {
-        *reinterpret_cast<half_t*>(srec + 2 * tok) = (half_t)n2s;
+        for (int i = 0; i < 4; ++i) half_swap(P[i], Q[i], b0[i], b1[i], lane);
+        B0 = u32x4_to_half8(b0[0], b0[1], b0[2], b0[3]);
+        B1 = u32x4_to_half8(b1[0], b1[1], b1[2], b1[3]);
+        Bb0 = Bb1 = half4_t{(half_t)0.f, (half_t)0.f, (half_t)0.f, (half_t)0.f};
       } else {
-        const uint32_t pk = pack_h2((half_t)n1, (half_t)n2s);
-        *reinterpret_cast<uint32_t*>(scales + (tok_base + tok) * 2) = pk;
+        const uint32_t P[4] = {pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(hi[4], hi[5]),
+                               pack_h2(hi[6], hi[7])};
+        const uint32_t Q[4] = {pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]), pack_h2(lo[4], lo[5]),
+                               pack_h2(lo[6], lo[7])};
+        uint32_t b0[4], b1[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) half_swap(P[i], Q[i], b0[i], b1[i], lane);
+        B0 = u32x4_to_half8(b0[0], b0[1], b0[2], b0[3]);
+        B1 = u32x4_to_half8(b1[0], b1[1], b1[2], b1[3]);
+        const half4_t bias = {uu_hi, uu_lo, (half_t)1.f, (half_t)1.f};
+        const half4_t zero4 = {(half_t)0.f, (half_t)0.f, (half_t)0.f, (half_t)0.f};
+        Bb0 = lane < 32 ? bias : zero4;
+        Bb1 = lane < 32 ? zero4 : bias;
+      }
+
+      uint32_t vmask;  // 0xffffff00 in a VGPR (opaque so it is not folded into a literal)
+      asm("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(0xffffff00u));
+      uint32_t best0 = 0xffffffffu, best1 = 0xffffffffu;
+      const float16_t zacc = {};
+      // software pipeline: the products of tile t + 1 are issued before the keys
+      // of tile t are formed, so the matrix core runs under the argmin
+      auto tile = [&](int t, float16_t& acc0, float16_t& acc1) {
+        const half8_t A1t = sA1[t][lane];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1t, B0, zacc, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1t, B1, zacc, 0, 0, 0);
+        if constexpr (SUB == 8) {
+          const half4_t A2t = sA2[t][lane];
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2t, Bb0, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x8f16(A2t, Bb1, acc1, 0, 0, 0);
+        }
+      };
+      // (at 1 bit the extra bias products would push the kernel past 168 VGPRs;
+      // it keeps one tile in flight)
+      constexpr bool kPipe = SUB == 4;
+      float16_t cur0, cur1, nxt0, nxt1;
+      if (kPipe) tile(0, cur0, cur1);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (!kPipe) tile(t, cur0, cur1);
+        if (kPipe && t + 1 < 8) tile(t + 1, nxt0, nxt1);
+#pragma unroll
+        for (int q = 0; q < 16; q += 2) {
+          // accumulator q holds codeword 32t + 8(q/4) + 4(lane/32) + q%4
+          const uint32_t i0 = 32u * t + 8u * (q >> 2) + (q & 3);
+          const uint32_t i1 = 32u * t + 8u * ((q + 1) >> 2) + ((q + 1) & 3);
+          best0 = min(min(best0, make_key(cur0[q], vmask, i0)), make_key(cur0[q + 1], vmask, i1));
+          best1 = min(min(best1, make_key(cur1[q], vmask, i0)), make_key(cur1[q + 1], vmask, i1));
+        }
+        if (kPipe && t + 1 < 8) {
+          cur0 = nxt0;
+          cur1 = nxt1;
+        }
+      }
+      best0 |= hbit;
+      best1 |= hbit;
+      // column n of block 0 belongs to lane n, of block 1 to lane 32 + n: one
+      // swap brings each column's other half next to it
+      uint32_t klo, khi;
+      half_swap(best0, best1, klo, khi, lane);  // klo = [b0 low, b1 low], khi = [b0 high, b1 high]
+      const uint32_t mine = min(klo, khi);
+      const uint32_t code = mine & 0xffu;
+      codes[(tok_base + tok) * S + slot] = (uint8_t)code;
+      // Strategy-3 scale: alpha = |u|^2 / (u . c_hat), folded into n2
+      float n2s = n2;
+      if (a.scale_adjust) {
+        // the codeword from the MFMA operand tiles: lanes < 32 of tile code/32
+        // hold -2 c (exact in fp16)
+        const half8_t cw = sA1[code >> 5][code & 31];
+        float uc = 0.f;
+#pragma unroll
+        for (int e = 0; e < SUB; ++e) uc = fmaf(u[e], -0.5f * (float)cw[e], uc);
+        uc = group_sum<S>(uc);
+        const float utot = group_sum<S>(uu);
+        if (uc > 0.f) n2s = n2 * (utot / uc);
+      }
+      if (slot == 0) store_scales(tok, n1, n2s);
+    }
+  } else {
+    // ---- pass 2 with candidate lists (2 bits) -----------------------------
+    static_assert(NW == 16, "box offsets below assume 16 waves");
+    // (a) per row: transform, hi/lo split, orthant box; the rank of the
+    // sub-vector among its wave's sub-vectors of the same box
+    uint32_t boxr[ROWS], rankr[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const int tok = wave * TPW + r * TPR + tir;
+      float u[SUB], n1, n2;
+      transform(tok, xr[r], u, n1, n2);
+      half_t hi[SUB], lo[SUB], uu_hi, uu_lo;
+      float uu;
+      split(u, hi, lo, uu_hi, uu_lo, uu);
+      const int i = tok * S + slot;
+      recs[i] = u32x4_to_half8(pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(lo[0], lo[1]),
+                               pack_h2(lo[2], lo[3]));
+      uus[i] = pack_h2(uu_hi, uu_lo);
+      boxr[r] = (u[0] < 0.f ? 1u : 0u) | (u[1] < 0.f ? 2u : 0u) | (u[2] < 0.f ? 4u : 0u) | (u[3] < 0.f ? 8u : 0u);
+      rankr[r] = atomicAdd(&whist[wave][boxr[r]], 1u);
+      if (slot == 0) {
+        if (a.scale_adjust) {
+          n1t[tok] = n1;
+          n2t[tok] = n2;
+        } else {
+          store_scales(tok, n1, n2);
+        }
+      }
+    }
+    __syncthreads();
+    // (b) box offsets: each box's columns padded to a multiple of 32 (with
+    // the zero record), then each wave's share of its boxes.  Lane
+    // (g = lane / 16, box = lane % 16) covers waves 4g .. 4g + 3.
+    if (wave == 0) {
+      const int box = lane & 15, g = lane >> 4;
+      uint32_t c[4], gsum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = whist[4 * g + j][box];
+        gsum += c[j];
+      }
+      uint32_t incl_g = gsum, t = __shfl_up(incl_g, 16, kWave);
+      if (g >= 1) incl_g += t;
+      t = __shfl_up(incl_g, 32, kWave);
+      if (g >= 2) incl_g += t;
+      const uint32_t cnt = __shfl(incl_g, 48 + box, kWave);  // the box's total
+      const uint32_t padded = (cnt + 31u) & ~31u;
+      uint32_t incl_b = padded;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const uint32_t v = __shfl_up(incl_b, off, 16);
+        if (box >= off) incl_b += v;
+      }
+      const uint32_t st = incl_b - padded;
+      uint32_t base = st + incl_g - gsum;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        whist[4 * g + j][box] = base;
+        base += c[j];
+      }
+      if (g == 0) {
+        cstart[box] = (int)st;
+        ccount[box] = (int)cnt;
+        cpad[box] = (int)padded;
+      }
+      if (lane == 15) ncol_blocks = (int)(incl_b / 32);
+    }
+    __syncthreads();
+    // (c) box order: every sub-vector to its column, padding columns to the
+    // zero record, and the box of every 32-column block
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const int tok = wave * TPW + r * TPR + tir;
+      sidx[whist[wave][boxr[r]] + rankr[r]] = (uint16_t)(tok * S + slot);
+    }
+    if (tid < 16 * 32) {
+      const int box = tid >> 5, j = tid & 31;
+      if (j < cpad[box] - ccount[box]) sidx[cstart[box] + ccount[box] + j] = (uint16_t)kDummy;
+    } else if (tid < 16 * 32 + kCols / 32) {
+      const int cb = tid - 16 * 32;
+      int box = 0;
+#pragma unroll
+      for (int o = 1; o < 16; ++o)
+        if (cstart[o] <= 32 * cb && cpad[o] > 0) box = o;
+      cbox[cb] = (uint8_t)box;
+    }
+    __syncthreads();
+    // (d) distance products over the box's list, 32 sorted columns per MFMA;
+    // lane n (< 32) holds column n's u parts, lane 32 + n its bias row; tile t
+    // of a box holds its list entries 32 t .. 32 t + 31.  Each wave takes an
+    // even share of the column blocks, two per step.
+    const int nblocks = ncol_blocks;
+    const int n = lane & 31;
+    const bool upper = lane >= 32;
+    // B operand of sorted column `col` (both loads on every lane, then a select)
+    auto operand_b = [&](int col, int& idx) -> half8_t {
+      idx = sidx[col];
+      const uint4_t rv = __builtin_bit_cast(uint4_t, recs[idx]);
+      const uint32_t q = uus[idx];
+      const uint4_t w = {upper ? q : rv[0], upper ? 0x3C003C00u : rv[1], upper ? 0u : rv[2], upper ? 0u : rv[3]};
+      return __builtin_bit_cast(half8_t, w);
+    };
+    auto search = [&](auto two, int c0) {
+      constexpr bool TWO = decltype(two)::value;
+      const int c1 = TWO ? c0 + 1 : c0;
+      const int o0 = cbox[c0], o1 = cbox[c1];
+      int i0, i1 = 0;
+      const half8_t B0 = operand_b(32 * c0 + n, i0);
+      half8_t B1 = B0;
+      if constexpr (TWO) B1 = operand_b(32 * c1 + n, i1);
+      uint32_t vmask;  // 0xffffff00 in a VGPR (opaque so it is not folded into a literal)
+      asm("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(0xffffff00u));
+      const float16_t zacc = {};
+      auto tile = [&](int t, float16_t& acc0, float16_t& acc1) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sA1[o0 * NT + t][lane], B0, zacc, 0, 0, 0);
+        if constexpr (TWO) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sA1[o1 * NT + t][lane], B1, zacc, 0, 0, 0);
+      };
+      uint32_t best0 = 0xffffffffu, best1 = 0xffffffffu;
+      float16_t cur0, cur1, nxt0, nxt1;
+      tile(0, cur0, cur1);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t + 1 < NT) tile(t + 1, nxt0, nxt1);
+#pragma unroll
+        for (int q = 0; q < 16; q += 2) {
+          // accumulator q holds list position 32t + 8(q/4) + 4(lane/32) + q%4
+          const uint32_t p0 = 32u * t + 8u * (q >> 2) + (q & 3);
+          const uint32_t p1 = 32u * t + 8u * ((q + 1) >> 2) + ((q + 1) & 3);
+          best0 = min(min(best0, make_key(cur0[q], vmask, p0)), make_key(cur0[q + 1], vmask, p1));
+          if constexpr (TWO)
+            best1 = min(min(best1, make_key(cur1[q], vmask, p0)), make_key(cur1[q + 1], vmask, p1));
+        }
+        if (t + 1 < NT) {
+          cur0 = nxt0;
+          if constexpr (TWO) cur1 = nxt1;
+        }
+      }
+      best0 |= hbit;
+      uint32_t mine;
+      if constexpr (TWO) {
+        best1 |= hbit;
+        uint32_t klo, khi;
+        half_swap(best0, best1, klo, khi, lane);  // lane n: block c0 column n; lane 32 + n: block c1 column n
+        mine = min(klo, khi);
+      } else {
+        mine = min(best0, (uint32_t)__builtin_bit_cast(uint32_t, xlane<32>(__builtin_bit_cast(float, best0))));
+      }
+      const uint32_t pos = mine & 0xffu;
+      const int idx = upper ? i1 : i0;
+      // lists are ascending, so the lowest position of a tie is the lowest index
+      if (idx != kDummy && (TWO || !upper)) boxc[idx] = lst[(upper ? o1 : o0) * 128 + pos];
+    };
+    for (int pb = wave; 2 * pb < nblocks; pb += NW) {
+      if (2 * pb + 1 < nblocks) search(std::true_type{}, 2 * pb);
+      else search(std::false_type{}, 2 * pb);
+    }
+    __syncthreads();
+    // (e) codes (the block's R x S bytes are contiguous) and Strategy-3 scales
+    for (int i = tid; i < NSV / 16; i += blockDim.x)
+      reinterpret_cast<uint4*>(codes + tok_base * S)[i] = reinterpret_cast<const uint4*>(boxc)[i];
+    if (a.scale_adjust) {
+      for (int i = tid; i < NSV; i += blockDim.x) {  // a wave covers two whole tokens
+        const int tok = i / S;
+        const half8_t r8 = recs[i];
+        const int code = boxc[i];
+        const uint2 cw = *reinterpret_cast<const uint2*>(a.codebook + code * SUB);
+        const float c[4] = {h2f(cw.x & 0xffff), h2f(cw.x >> 16), h2f(cw.y & 0xffff), h2f(cw.y >> 16)};
+        float uc = 0.f;
+#pragma unroll
+        for (int e = 0; e < SUB; ++e) uc = fmaf((float)r8[e] + (float)r8[4 + e], c[e], uc);
+        uc = group_sum<S>(uc);
+        const uint32_t q = uus[i];
+        const float utot = group_sum<S>(h2f(q & 0xffff) + h2f(q >> 16));
+        if ((i % S) == 0) {
+          float n2s = n2t[tok];
+          if (uc > 0.f) n2s *= utot / uc;
+          store_scales(tok, n1t[tok], n2s);
+        }
       }
     }
   }
@@ -547,23 +796,41 @@ hipError_t launch_append(const AppendArgs& a, int B, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int SUB, int R, bool DQ>
+static hipError_t launch_encode_nt(const EncodeArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.nt == 0) {
+    hipLaunchKernelGGL((encode_kernel<SUB, R, DQ, 0>), grid, dim3(64 * enc_waves<0>()), 0, stream, a);
+    return hipSuccess;
+  }
+  if constexpr (SUB == 4) {
+    if (a.nt <= 3) {
+      hipLaunchKernelGGL((encode_kernel<4, R, DQ, 3>), grid, dim3(64 * enc_waves<3>()), 0, stream, a);
+      return hipSuccess;
+    }
+    // a list longer than 96 entries: the box tiles would not fit in LDS
+    hipLaunchKernelGGL((encode_kernel<4, R, DQ, 0>), grid, dim3(64 * enc_waves<0>()), 0, stream, a);
+    return hipSuccess;
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_encode(const EncodeArgs& a, int sub, int R, hipStream_t stream) {
   const bool rcopy = a.rc_r > 0 || a.lens != nullptr;
-  dim3 grid(a.nblk * a.n_units + (rcopy ? a.n_units : 0), 2), block(64 * kEncWaves);
+  const dim3 grid(a.nblk * a.n_units + (rcopy ? a.n_units : 0), 2);
   if (grid.x == 0) return hipSuccess;
+  hipError_t e = hipErrorInvalidValue;
   if (a.dq) {
-    if (sub == 4 && R == 128) hipLaunchKernelGGL((encode_kernel<4, 128, true>), grid, block, 0, stream, a);
-    else if (sub == 4 && R == 64) hipLaunchKernelGGL((encode_kernel<4, 64, true>), grid, block, 0, stream, a);
-    else if (sub == 8 && R == 128) hipLaunchKernelGGL((encode_kernel<8, 128, true>), grid, block, 0, stream, a);
-    else if (sub == 8 && R == 64) hipLaunchKernelGGL((encode_kernel<8, 64, true>), grid, block, 0, stream, a);
-    else return hipErrorInvalidValue;
+    if (sub == 4 && R == 128) e = launch_encode_nt<4, 128, true>(a, grid, stream);
+    else if (sub == 4 && R == 64) e = launch_encode_nt<4, 64, true>(a, grid, stream);
+    else if (sub == 8 && R == 128) e = launch_encode_nt<8, 128, true>(a, grid, stream);
+    else if (sub == 8 && R == 64) e = launch_encode_nt<8, 64, true>(a, grid, stream);
   } else {
-    if (sub == 4 && R == 128) hipLaunchKernelGGL((encode_kernel<4, 128, false>), grid, block, 0, stream, a);
-    else if (sub == 4 && R == 64) hipLaunchKernelGGL((encode_kernel<4, 64, false>), grid, block, 0, stream, a);
-    else if (sub == 8 && R == 128) hipLaunchKernelGGL((encode_kernel<8, 128, false>), grid, block, 0, stream, a);
-    else if (sub == 8 && R == 64) hipLaunchKernelGGL((encode_kernel<8, 64, false>), grid, block, 0, stream, a);
-    else return hipErrorInvalidValue;
+    if (sub == 4 && R == 128) e = launch_encode_nt<4, 128, false>(a, grid, stream);
+    else if (sub == 4 && R == 64) e = launch_encode_nt<4, 64, false>(a, grid, stream);
+    else if (sub == 8 && R == 128) e = launch_encode_nt<8, 128, false>(a, grid, stream);
+    else if (sub == 8 && R == 64) e = launch_encode_nt<8, 64, false>(a, grid, stream);
   }
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

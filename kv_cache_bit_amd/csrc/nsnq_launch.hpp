@@ -35,6 +35,11 @@ struct EncodeArgs {
   // fl_quant[b].  Null otherwise.
   const int32_t* fl_quant;
   const int32_t* fl_resid;
+  // 2-bit nearest-codeword search over per-orthant candidate lists
+  // ([16][128] codeword indices, device) with nt 32-entry tiles; nt = 0
+  // compares every codeword
+  const uint8_t* cand;
+  int nt;
 };
 
 struct AppendArgs {

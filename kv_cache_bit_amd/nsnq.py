@@ -28,7 +28,7 @@ size_t = ctypes.c_size_t
 
 class nsnq_params(ctypes.Structure):
     _fields_ = [("head_dim", i32), ("bits", i32), ("n_codewords", i32), ("block_tokens", i32),
-                ("flags", i32), ("reserved", i32), ("hadamard_signs", P)]
+                ("flags", i32), ("vq_tiles", i32), ("hadamard_signs", P), ("vq_candidates", P)]
 
 
 class nsnq_rope(ctypes.Structure):
@@ -54,6 +54,7 @@ _SIGNATURES = {
     "nsnq_build_codebook_workspace_bytes": (size_t, [_PP]),
     "nsnq_build_codebook": (i32, [_PP, P, i64, i32, P, P, P, P, P, size_t, P]),
     "nsnq_finetune_codebook": (i32, [_PP, P, i64, i32, f32, P, P, P, P, size_t, P]),
+    "nsnq_vq_candidates": (i32, [_PP, P, P, P]),
     "nsnq_encode_kv": (i32, [_PP, P, P, P, i64, i64, i64, i32, _PC, P]),
     "nsnq_encode_kv_ragged": (i32, [_PP, P, P, P, i64, i64, i64, P, i32, _PC, P]),
     "nsnq_flush_residual": (i32, [_PP, P, _PC, P]),
@@ -118,11 +119,24 @@ def params(bits: int, block_tokens: int, head_dim: int = 128, n_codewords: int =
            signs: torch.Tensor | None = None) -> nsnq_params:
     """Format parameters.  `signs`: device int8 [head_dim] of +-1 for the
     randomised Hadamard transform (kept referenced by the returned struct)."""
-    p = nsnq_params(head_dim, bits, n_codewords, block_tokens, flags, 0, _ptr(signs))
+    p = nsnq_params(head_dim, bits, n_codewords, block_tokens, flags, 0, _ptr(signs), None)
     if signs is not None:
         assert signs.dtype == torch.int8 and signs.is_contiguous() and signs.numel() == head_dim
         p._signs_ref = signs
     return p
+
+
+def with_candidates(p: nsnq_params, codebook: torch.Tensor) -> nsnq_params:
+    """A copy of `p` whose encode calls search only the per-orthant candidate
+    lists of `codebook` (2 bits; same codes as the exhaustive search).  The
+    table is built on the host and copied next to the codebook."""
+    table, tiles = nsnq_vq_candidates(p, codebook)
+    dev = table.to(codebook.device)
+    q = nsnq_params(p.head_dim, p.bits, p.n_codewords, p.block_tokens, p.flags, tiles, p.hadamard_signs,
+                    dev.data_ptr())
+    q._signs_ref = getattr(p, "_signs_ref", None)
+    q._cand_ref = dev
+    return q
 
 
 def sub_dim(bits: int) -> int:
@@ -134,6 +148,18 @@ def sub_dim(bits: int) -> int:
 
 def nsnq_abi_version() -> int:
     return lib().nsnq_abi_version()
+
+
+def nsnq_vq_candidates(p: nsnq_params, codebook: torch.Tensor) -> tuple[torch.Tensor, int]:
+    """Candidate table (uint8 [16][128], host) and tile count for a 2-bit fp16
+    codebook [256][4] (any device; read on the host)."""
+    cb = codebook.detach().to("cpu").contiguous()
+    assert cb.dtype == torch.float16 and cb.numel() == 256 * 4
+    table = torch.empty(16, 128, dtype=torch.uint8)
+    tiles = ctypes.c_int32()
+    _check(lib().nsnq_vq_candidates(ctypes.byref(p), cb.data_ptr(), table.data_ptr(), ctypes.byref(tiles)),
+           "nsnq_vq_candidates")
+    return table, tiles.value
 
 
 def nsnq_buffer_bytes(p: nsnq_params, cap_tokens: int) -> tuple[int, int, int, int]:

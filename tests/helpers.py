@@ -37,11 +37,14 @@ def capacity(L: int, R: int, extra_blocks: int = 1) -> int:
 
 
 def gpu_encode(k: torch.Tensor, v: torch.Tensor, bits: int, R: int, cb_bits: np.ndarray, cap: int | None = None,
-               flags: int = 0, signs: torch.Tensor | None = None):
+               flags: int = 0, signs: torch.Tensor | None = None, cand: bool = False):
+    """Encode on the GPU; cand=True searches the per-orthant candidate lists."""
     p = nsnq.params(bits, R, flags=flags, signs=None if signs is None else signs.to(DEV))
     B, H, L, d = k.shape
     cache = nsnq.KVCache(p, B, H, cap or capacity(L, R), DEV)
     cb = cb_tensor(cb_bits)
+    if cand:
+        p = nsnq.with_candidates(p, cb)
     nsnq.nsnq_encode_kv(p, cb, k.to(DEV), v.to(DEV), L, cache)
     torch.cuda.synchronize()
     return p, cb, cache

@@ -26,10 +26,10 @@ def nsnq():
 
 def test_exports_every_declared_symbol(nsnq):
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(nsnq.lib(), n), n
-    assert nsnq.nsnq_abi_version() == 4
+    assert nsnq.nsnq_abi_version() == 5
     assert nsnq.lib().nsnq_status_str(1) == b"invalid argument"
 
 
@@ -50,12 +50,16 @@ def test_host_validation_rejects_before_launch(nsnq):
     assert L.nsnq_encode_kv(by(nsnq.params(2, 128, head_dim=64)), P, P, P, 0, 0, 64, 256, by(c), None) == EUNS
     assert L.nsnq_encode_kv(by(nsnq.params(2, 96)), P, P, P, 0, 0, 128, 256, by(c), None) == EUNS
     assert L.nsnq_encode_kv(by(nsnq.params(2, 128, n_codewords=16)), P, P, P, 0, 0, 128, 256, by(c), None) == EINVAL
-    # unknown flags, nonzero reserved field
+    # unknown flags; candidate-table fields that do not go together
     bad_flags = nsnq.params(2, 128, flags=4)
     assert L.nsnq_encode_kv(by(bad_flags), P, P, P, 0, 0, 128, 256, by(c), None) == EINVAL
-    bad_res = nsnq.params(2, 128)
-    bad_res.reserved = 1
-    assert L.nsnq_encode_kv(by(bad_res), P, P, P, 0, 0, 128, 256, by(c), None) == EINVAL
+    for bits, tiles, table in ((2, 1, None), (2, 0, P), (2, 5, P), (2, 3, P + 8), (1, 3, P)):
+        bad = nsnq.params(bits, 128)
+        bad.vq_tiles, bad.vq_candidates = tiles, table
+        assert L.nsnq_encode_kv(by(bad), P, P, P, 0, 0, 128, 256, by(c), None) == EINVAL, (bits, tiles, table)
+    ok = nsnq.params(2, 128)
+    ok.vq_tiles, ok.vq_candidates = 3, P
+    assert L.nsnq_encode_kv(by(ok), P, P, P, 0, 0, 128, 0, by(c), None) == nsnq.NSNQ_OK
     adj = nsnq.params(2, 128, flags=nsnq.NSNQ_SCALE_ADJUST)
     assert L.nsnq_encode_kv(by(adj), P, P, P, 0, 0, 128, 0, by(c), None) == nsnq.NSNQ_OK
     # misaligned or null pointers, bad strides, capacity, residual state

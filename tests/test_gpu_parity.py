@@ -56,6 +56,79 @@ def test_encode_degenerate_tokens(oracle_codebooks):
     assert np.all(half_np(cache, 0)["scales"][0, 0, 10, 0] == 0)
 
 
+# ------------------------------------------------ candidate-list encode --
+
+@pytest.mark.parametrize("R,B,H,L,flags,use_signs", [
+    (64, 1, 1, 512, 0, False),
+    (128, 2, 3, 300, 0, False),
+    (128, 1, 2, 1000, nsnq.NSNQ_DOUBLE_QUANT, False),
+    (128, 2, 2, 700, nsnq.NSNQ_SCALE_ADJUST, True),
+    (64, 1, 2, 450, nsnq.NSNQ_DOUBLE_QUANT | nsnq.NSNQ_SCALE_ADJUST, True),
+])
+def test_encode_candidate_lists(oracle_codebooks, R, B, H, L, flags, use_signs):
+    """2 bits, searching only the orthant box's candidate list: the oracle's
+    codes and scalars under the same bars as the exhaustive search, and the
+    same codes as the exhaustive GPU search outside the near-tie band."""
+    cb = oracle_codebooks[2]
+    k, v = _kv(150 + L, B, H, L)
+    signs = synth.hadamard_signs(15 + R) if use_signs else None
+    adjust = bool(flags & nsnq.NSNQ_SCALE_ADJUST)
+    p, cbt, cache = gpu_encode(k, v, 2, R, cb, flags=flags, signs=signs, cand=True)
+    assert p.vq_tiles in (3, 4)
+    _, _, full = gpu_encode(k, v, 2, R, cb, flags=flags, signs=signs)
+    dq = bool(flags & nsnq.NSNQ_DOUBLE_QUANT)
+    kw = dict(signs=None if signs is None else signs.numpy(), scale_adjust=adjust, dq=dq)
+    ek, ev = oracle.encode(k, R, cb, **kw), oracle.encode(v, R, cb, **kw)
+    if dq:
+        compare_encoded_dq(cache, ek, ev, R, scale_adjust=adjust)
+    else:
+        compare_encoded(cache, ek, ev, scale_adjust=adjust)
+    for which, e in ((0, ek), (1, ev)):
+        g, f = half_np(cache, which)["codes"], half_np(full, which)["codes"]
+        assert not np.any((g != f) & (e["gap"] >= 1e-4)), "pruned and exhaustive codes differ away from a tie"
+    # dequant and decode read the cache as usual
+    q = synth.queries(150 + L, 0, B, 2 * H, D)
+    ref = oracle.reference_decode(q, ek, ev, ek["n_quant"], ek["n_resid"], R, cb, signs=kw["signs"])
+    o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), cache).float().cpu().numpy()
+    same = all(np.array_equal(half_np(cache, w)["codes"], e["codes"]) for w, e in ((0, ek), (1, ev)))
+    if same and not dq:
+        check_attention(o, ref)
+
+
+def test_encode_candidate_lists_degenerate(oracle_codebooks):
+    """A zero token, a constant block (n2 = 0: u = 0 on every box's faces) and
+    a ragged prefill with a window flush, all through the candidate lists."""
+    cb = oracle_codebooks[2]
+    R = 64
+    k, v = _kv(8, 1, 1, 3 * R + 5)
+    k[0, 0, 10] = 0
+    v[0, 0, R:2 * R] = v[0, 0, R]
+    p, cbt, cache = gpu_encode(k, v, 2, R, cb, cand=True)
+    ek, ev = oracle_encode_pair(k, v, R, cb)
+    compare_encoded(cache, ek, ev)
+    assert np.all(half_np(cache, 1)["scales"][0, 0, R:2 * R, 1] == 0)
+    # ragged rows, then appends that flush a full window through the lists
+    lengths = [0, R, 2 * R + 3]
+    kk, vv = _kv(9, 3, 2, 3 * R + 2)
+    pc = nsnq.with_candidates(nsnq.params(2, R), cbt)
+    rc = nsnq.KVCache(pc, 3, 2, 4 * R, DEV, ragged=True)
+    nsnq.nsnq_encode_kv_ragged(pc, cbt, kk.to(DEV), vv.to(DEV), torch.tensor(lengths, dtype=torch.int32, device=DEV),
+                               max(lengths), rc)
+    for i in range(2):
+        idx = torch.tensor([Lb + i for Lb in lengths])
+        nsnq.nsnq_append_kv(pc, cbt, kk[torch.arange(3), :, idx].contiguous().to(DEV),
+                            vv[torch.arange(3), :, idx].contiguous().to(DEV), rc)
+    torch.cuda.synchronize()
+    flips = total = 0
+    for b, Lb in enumerate(lengths):
+        e_k = oracle.encode(kk[b:b + 1, :, :Lb + 2], R, cb)
+        e_v = oracle.encode(vv[b:b + 1, :, :Lb + 2], R, cb)
+        assert (rc.seq_quant[b].item(), rc.seq_resid[b].item()) == (e_k["n_quant"], e_k["n_resid"])
+        f, t = _check_row(rc, b, e_k, e_v)
+        flips, total = flips + f, total + t
+    check_tie_rate(flips, total)
+
+
 # ----------------------------------------------------------------- dequant --
 
 @pytest.mark.parametrize("bits,R", [(2, 64), (1, 128)])
@@ -457,14 +530,16 @@ def test_cosine_finetune_matches_oracle(bits):
 
 # ---------------------------------------------------------- full-size cases --
 
-def test_llama2_layer_2bit_full(oracle_codebooks):
+@pytest.mark.parametrize("cand", [False, True])
+def test_llama2_layer_2bit_full(oracle_codebooks, cand):
     """One LLaMA-2-7B-shaped layer: 32 heads, 4096 tokens, 2-bit, R = 128;
-    every code of every head, and the decode step."""
+    every code of every head, and the decode step (exhaustive search, and the
+    candidate-list search the bench times)."""
     cb = oracle_codebooks[2]
     w = synth.WORKLOADS["llama2-7b-layer-b1-2bit"]
     B, H, L, R = w["B"], w["Hkv"], w["L"], w["R"]
     k, v = synth.kv_layer(w["config_id"], 0, B, H, L, D)
-    p, cbt, cache = gpu_encode(k, v, 2, R, cb)
+    p, cbt, cache = gpu_encode(k, v, 2, R, cb, cand=cand)
     assert (cache.n_quant, cache.n_resid) == (3968, 128)
     ek, ev = oracle_encode_pair(k, v, R, cb)
     compare_encoded(cache, ek, ev)
