@@ -28,6 +28,7 @@
 // (SUB = 8) the hi/lo products fill K = 16 and the bias terms go through a
 // second 32x32x8 instruction.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "nsnq_device.hpp"
@@ -129,8 +130,10 @@ template <int SUB, int R, bool DQ, int NT>
 __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs a) {
   constexpr int NW = enc_waves<NT>();
   static_assert(NT == 0 || SUB == 4, "candidate lists exist for 4-element sub-vectors only");
-  if ((int)blockIdx.x >= a.nblk * a.n_units) {
-    resid_copy(a, blockIdx.x - a.nblk * a.n_units, blockIdx.y);
+  // work-groups past the encoding ones copy the residual tokens
+  const int n_enc = NT ? a.n_enc : a.nblk * a.n_units;
+  if ((int)blockIdx.x >= n_enc) {
+    resid_copy(a, blockIdx.x - n_enc, blockIdx.y);
     return;
   }
   constexpr int S = kDim / SUB;      // slots = lanes per token
@@ -146,22 +149,8 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
   const int wave = tid >> 6;
   const int slot = lane % S;
   const int tir = lane / S;
-
-  const int blk = blockIdx.x % a.nblk;
-  const int unit = blockIdx.x / a.nblk;  // b * H + h
   const int kv = blockIdx.y;
-  const int b = unit / a.H, h = unit % a.H;
-  int dst0 = a.dst_tok0;  // first destination token of this launch's blocks
-  if (a.lens) {           // ragged prefill: this row encodes L - r tokens
-    const int L = min(max(a.lens[b], 0), a.lens_max);
-    if (blk * R >= L - resid_of(L, R)) return;
-  } else if (a.fl_resid) {  // ragged flush: only full windows, each at its row's n_quant
-    dst0 = a.fl_quant[b];
-    if (a.fl_resid[b] != R || dst0 < 0 || dst0 % R != 0 || dst0 + R > a.cap) return;
-  }
 
-  const uint16_t* src = a.src[kv] + (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)blk * R * a.st;
-  const int64_t tok_base = (int64_t)unit * a.cap + dst0 + (int64_t)blk * R;
 
   // ---- codebook operands (A side), per 32-codeword tile -------------------
   // Built once per group into LDS and re-read per row, which keeps ~40 VGPRs
@@ -173,7 +162,7 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
   __shared__ half4_t sA2[SUB == 8 ? 8 : 1][kWave];
   for (int i = tid; i < NTILE * kWave; i += blockDim.x) {
     const int t = i / kWave, l = i % kWave;
-    const int k = NT ? a.cand[(t / NT) * 128 + 32 * (t % NT) + (l & 31)] : 32 * t + (l & 31);
+    const int k = NT ? a.cand[(t / (NT ? NT : 1)) * 128 + 32 * (t % (NT ? NT : 1)) + (l & 31)] : 32 * t + (l & 31);
     const uint16_t* cb = a.codebook;
     float c[SUB];
     float nrm = 0.f;
@@ -224,7 +213,6 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
   if constexpr (NT > 0) {
     for (int i = tid; i < 128; i += blockDim.x)
       reinterpret_cast<uint4*>(lst)[i] = reinterpret_cast<const uint4*>(a.cand)[i];
-    if (tid < NW * 16) whist[tid / 16][tid % 16] = 0u;
     if (tid == 0) {
       recs[kDummy] = half8_t{};
       uus[kDummy] = 0u;
@@ -239,24 +227,59 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
   // LDS holds the sub-vector records instead, and the rows stay in registers.)
   using raw_t = typename std::conditional<SUB == 4, uint2, uint4>::type;
   __shared__ raw_t xs[NT ? 1 : R * S];  // [token][slot], R x 256 bytes
+  __shared__ float n1s[DQ ? R : 1];   // double quantisation: s1 per token
+  __shared__ float n1hs[DQ ? R : 1];  // n1_hat per token
+  __shared__ float mus[kDim];         // channel means of the block
+  __shared__ float n1p[DQ ? 1 : R], invp[DQ ? 1 : R];  // pass 1's n1 and 1 / n1 per token
+  // candidate lists: this lane's rows stay in registers from pass 1 to pass 2,
+  // and the next block's rows are loaded under this block's products
+  raw_t xr[NT ? ROWS : 1], xn[NT ? ROWS : 1];
+  const int items = a.nblk * a.n_units;
+  auto row_ptr = [&](int item) -> const uint16_t* {
+    const int blk = item % a.nblk, unit = item / a.nblk;
+    return a.src[kv] + (int64_t)(unit / a.H) * a.sb + (int64_t)(unit % a.H) * a.sh + (int64_t)blk * R * a.st +
+           (int64_t)(wave * TPW + tir) * a.st + slot * SUB;
+  };
+  auto load_rows = [&](int item, raw_t (&dst)[NT ? ROWS : 1]) {
+    const uint16_t* p = row_ptr(item);
+#pragma unroll
+    for (int r = 0; r < (NT ? ROWS : 1); ++r) dst[r] = *reinterpret_cast<const raw_t*>(p + (int64_t)r * TPR * a.st);
+  };
+
+  // Encode block `blk` of stream `unit` (b * H + h); `next` is the item whose
+  // rows to prefetch (candidate lists), or past the end.  Returns whether the
+  // prefetch was issued (false when the block is skipped).
+  auto encode_block = [&](int blk, int unit, int next) -> bool {
+  const int b = unit / a.H, h = unit % a.H;
+  int dst0 = a.dst_tok0;  // first destination token of this launch's blocks
+  if (a.lens) {           // ragged prefill: this row encodes L - r tokens
+    const int L = min(max(a.lens[b], 0), a.lens_max);
+    if (blk * R >= L - resid_of(L, R)) return false;
+  } else if (a.fl_resid) {  // ragged flush: only full windows, each at its row's n_quant
+    dst0 = a.fl_quant[b];
+    if (a.fl_resid[b] != R || dst0 < 0 || dst0 % R != 0 || dst0 + R > a.cap) return false;
+  }
+
+  const uint16_t* src = a.src[kv] + (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)blk * R * a.st;
+  const int64_t tok_base = (int64_t)unit * a.cap + dst0 + (int64_t)blk * R;
+  if constexpr (NT > 0) {
+    if (tid < NW * 16) whist[tid / 16][tid % 16] = 0u;
+  }
   auto load_raw = [&](int tok) -> raw_t {
     const raw_t v = *reinterpret_cast<const raw_t*>(src + (int64_t)tok * a.st + slot * SUB);
     if constexpr (NT == 0) xs[tok * S + slot] = v;
     return v;
   };
   auto lds_raw = [&](int tok) -> raw_t { return xs[NT ? 0 : tok * S + slot]; };
-  // candidate lists: this lane's rows stay in registers from pass 1 to pass 2
-  raw_t xr[NT ? ROWS : 1];
   auto fetch = [&](int r, int tok) -> raw_t {
-    const raw_t v = load_raw(tok);
-    if constexpr (NT > 0) xr[r] = v;
-    return v;
+    if constexpr (NT > 0) return xr[r];  // loaded ahead
+    else return load_raw(tok);
   };
   auto row_raw = [&](int r, int tok) -> raw_t {
     if constexpr (NT > 0) return xr[r];
     else return lds_raw(tok);
   };
-  auto norm_raw = [&](const raw_t& raw, float (&y)[SUB], float& n1) {
+  auto norm_raw = [&](const raw_t& raw, float (&y)[SUB], float& n1, float& inv) {
     float v[SUB];
     v[0] = h2f(raw.x & 0xffff); v[1] = h2f(raw.x >> 16);
     v[2] = h2f(raw.y & 0xffff); v[3] = h2f(raw.y >> 16);
@@ -269,7 +292,7 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
     for (int e = 0; e < SUB; ++e) ss = fmaf(v[e], v[e], ss);
     ss = group_sum<S>(ss) * (1.0f / kDim);
     const float rs = __builtin_amdgcn_rsqf(ss);  // 1 / n1
-    const float inv = ss > 0.f ? rs : 0.f;
+    inv = ss > 0.f ? rs : 0.f;
     n1 = ss * inv;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) y[e] = v[e] * inv;
@@ -280,8 +303,6 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
   // tokens are divided by the stored value n1_hat (so the reconstruction from
   // stored values only carries the VQ error).
   constexpr int SR = dq_scales_bytes<R>();
-  __shared__ float n1s[DQ ? R : 1];   // s1 per token
-  __shared__ float n1hs[DQ ? R : 1];  // n1_hat per token
   uint8_t* srec = reinterpret_cast<uint8_t*>(a.scales[kv]) + ((int64_t)unit * (a.cap / R) + dst0 / R + blk) * SR;
   uint8_t* mrec = reinterpret_cast<uint8_t*>(a.mu[kv]) + ((int64_t)unit * (a.cap / R) + dst0 / R + blk) * kDqMuBytes;
   float csum[SUB];
@@ -291,8 +312,8 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
 #pragma unroll 4
     for (int r = 0; r < ROWS; ++r) {
       const int tok = wave * TPW + r * TPR + tir;
-      float y[SUB], n1;
-      norm_raw(fetch(r, tok), y, n1);
+      float y[SUB], n1, inv;
+      norm_raw(fetch(r, tok), y, n1, inv);
       if (slot == 0) n1s[tok] = n1;
     }
     __syncthreads();
@@ -335,8 +356,13 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
   } else {
 #pragma unroll 4
     for (int r = 0; r < ROWS; ++r) {
-      float y[SUB], n1;
-      norm_raw(fetch(r, wave * TPW + r * TPR + tir), y, n1);
+      const int tok = wave * TPW + r * TPR + tir;
+      float y[SUB], n1, inv;
+      norm_raw(fetch(r, tok), y, n1, inv);
+      if (slot == 0) {
+        n1p[tok] = n1;
+        invp[tok] = inv;
+      }
 #pragma unroll
       for (int e = 0; e < SUB; ++e) csum[e] += y[e];
     }
@@ -353,7 +379,6 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
   }
   __syncthreads();
   // channel means: one thread per channel sums the waves' partials
-  __shared__ float mus[kDim];
   if (tid < kDim) {
     float sum = 0.f;
 #pragma unroll
@@ -415,8 +440,15 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
         u[4] = h2f(raw.z & 0xffff) * inv; u[5] = h2f(raw.z >> 16) * inv;
         u[6] = h2f(raw.w & 0xffff) * inv; u[7] = h2f(raw.w >> 16) * inv;
       }
-    } else {
-      norm_raw(raw, u, n1);
+    } else {  // pass 1's scales, so y is the same value without a second reduction
+      n1 = n1p[tok];
+      const float inv = invp[tok];
+      u[0] = h2f(raw.x & 0xffff) * inv; u[1] = h2f(raw.x >> 16) * inv;
+      u[2] = h2f(raw.y & 0xffff) * inv; u[3] = h2f(raw.y >> 16) * inv;
+      if constexpr (SUB == 8) {
+        u[4] = h2f(raw.z & 0xffff) * inv; u[5] = h2f(raw.z >> 16) * inv;
+        u[6] = h2f(raw.w & 0xffff) * inv; u[7] = h2f(raw.w >> 16) * inv;
+      }
     }
     float ss = 0.f;
 #pragma unroll
@@ -651,6 +683,7 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
       cbox[cb] = (uint8_t)box;
     }
     __syncthreads();
+    if (next < items) load_rows(next, xn);
     // (d) distance products over the box's list, 32 sorted columns per MFMA;
     // lane n (< 32) holds column n's u parts, lane 32 + n its bias row; tile t
     // of a box holds its list entries 32 t .. 32 t + 31.  Each wave takes an
@@ -668,7 +701,7 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
     };
     auto search = [&](auto two, int c0) {
       constexpr bool TWO = decltype(two)::value;
-      const int c1 = TWO ? c0 + 1 : c0;
+      const int c1 = TWO ? c0 + NW : c0;
       const int o0 = cbox[c0], o1 = cbox[c1];
       int i0, i1 = 0;
       const half8_t B0 = operand_b(32 * c0 + n, i0);
@@ -682,11 +715,12 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
         if constexpr (TWO) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sA1[o1 * NT + t][lane], B1, zacc, 0, 0, 0);
       };
       uint32_t best0 = 0xffffffffu, best1 = 0xffffffffu;
-      float16_t cur0, cur1, nxt0, nxt1;
-      tile(0, cur0, cur1);
+      // (other waves on the SIMD cover the product latency: no software
+      // pipeline, which keeps the register count under 128)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if (t + 1 < NT) tile(t + 1, nxt0, nxt1);
+        float16_t cur0, cur1;
+        tile(t, cur0, cur1);
 #pragma unroll
         for (int q = 0; q < 16; q += 2) {
           // accumulator q holds list position 32t + 8(q/4) + 4(lane/32) + q%4
@@ -695,10 +729,6 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
           best0 = min(min(best0, make_key(cur0[q], vmask, p0)), make_key(cur0[q + 1], vmask, p1));
           if constexpr (TWO)
             best1 = min(min(best1, make_key(cur1[q], vmask, p0)), make_key(cur1[q + 1], vmask, p1));
-        }
-        if (t + 1 < NT) {
-          cur0 = nxt0;
-          if constexpr (TWO) cur1 = nxt1;
         }
       }
       best0 |= hbit;
@@ -716,9 +746,10 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
       // lists are ascending, so the lowest position of a tie is the lowest index
       if (idx != kDummy && (TWO || !upper)) boxc[idx] = lst[(upper ? o1 : o0) * 128 + pos];
     };
-    for (int pb = wave; 2 * pb < nblocks; pb += NW) {
-      if (2 * pb + 1 < nblocks) search(std::true_type{}, 2 * pb);
-      else search(std::false_type{}, 2 * pb);
+    // wave w takes blocks w, w + NW, w + 2 NW, ... two at a time
+    for (int c0 = wave; c0 < nblocks; c0 += 2 * NW) {
+      if (c0 + NW < nblocks) search(std::true_type{}, c0);
+      else search(std::false_type{}, c0);
     }
     __syncthreads();
     // (e) codes (the block's R x S bytes are contiguous) and Strategy-3 scales
@@ -741,6 +772,28 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
           float n2s = n2t[tok];
           if (uc > 0.f) n2s *= utot / uc;
           store_scales(tok, n1t[tok], n2s);
+        }
+      }
+    }
+    __syncthreads();  // the next block reuses the LDS records
+  }
+  return next < items;
+  };
+
+  if constexpr (NT == 0) {
+    encode_block(blockIdx.x % a.nblk, blockIdx.x / a.nblk, items);
+  } else {
+    // persistent: work-group g encodes items g, g + n_enc, ...
+    if ((int)blockIdx.x < items) load_rows(blockIdx.x, xr);
+    for (int item = blockIdx.x; item < items; item += n_enc) {
+      const int next = item + n_enc;
+      const bool pre = encode_block(item % a.nblk, item / a.nblk, next);
+      if (next < items) {
+        if (pre) {
+#pragma unroll
+          for (int r = 0; r < (NT ? ROWS : 1); ++r) xr[r] = xn[r];
+        } else {
+          load_rows(next, xr);
         }
       }
     }
@@ -814,9 +867,21 @@ static hipError_t launch_encode_nt(const EncodeArgs& a, dim3 grid, hipStream_t s
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_encode(const EncodeArgs& a, int sub, int R, hipStream_t stream) {
+hipError_t launch_encode(const EncodeArgs& args, int sub, int R, hipStream_t stream) {
+  EncodeArgs a = args;
   const bool rcopy = a.rc_r > 0 || a.lens != nullptr;
-  const dim3 grid(a.nblk * a.n_units + (rcopy ? a.n_units : 0), 2);
+  const int items = a.nblk * a.n_units;
+  int n_enc = items;
+  if (sub == 4 && a.nt > 0 && a.nt <= 3) {
+    // candidate lists: one persistent group per CU and K/V half
+    int dev = 0, ncu = 0;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+      ncu = 256;
+    n_enc = std::min(items, std::max(1, ncu / 2));
+  }
+  a.n_enc = n_enc;
+  const dim3 grid(n_enc + (rcopy ? a.n_units : 0), 2);
   if (grid.x == 0) return hipSuccess;
   hipError_t e = hipErrorInvalidValue;
   if (a.dq) {

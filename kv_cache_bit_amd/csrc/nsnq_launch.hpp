@@ -40,6 +40,7 @@ struct EncodeArgs {
   // compares every codeword
   const uint8_t* cand;
   int nt;
+  int n_enc;  // candidate lists: encoding work-groups per K/V half (each loops over blocks)
 };
 
 struct AppendArgs {
