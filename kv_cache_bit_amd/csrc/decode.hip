@@ -45,11 +45,11 @@ struct DecodeSmem {
   int qf, qr, cbh, lut, wbuf, total;
 };
 
-__host__ __device__ inline DecodeSmem decode_smem(int sub, int gh, int split_tokens, int R) {
+__host__ __device__ constexpr DecodeSmem decode_smem(int sub, int gh, int split_tokens, int R) {
   (void)split_tokens;
   (void)R;
   const int S = kDim / sub;
-  DecodeSmem s;
+  DecodeSmem s{};
   int o = 0;
   s.qf = o; o += gh * kDim;
   s.qr = o; o += gh * kDim;
@@ -70,6 +70,19 @@ int decode_max_split_tokens(int sub, int gh, int R) {
   return kMaxSplitBlocks * R;
 }
 
+// LDS loads at absolute byte addresses.  The split kernel has no static LDS,
+// so its dynamic segment (smem) starts at address 0: an address is the
+// shifted code byte (one SDWA shift) plus a constant folded into the
+// instruction's offset field.
+__device__ __forceinline__ float lds_f32(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) float*>(static_cast<size_t>(addr));
+}
+typedef uint32_t lds_u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 lds_u32x2(uint32_t addr) {
+  const lds_u32x2_t v = *reinterpret_cast<const __attribute__((address_space(3))) lds_u32x2_t*>(static_cast<size_t>(addr));
+  return make_uint2(v.x, v.y);
+}
+
 template <int S>
 __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&cw)[S / 4]) {
 #pragma unroll
@@ -80,14 +93,17 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&cw)[S / 
 }
 
 // One query head per group (no RoPE): registers capped for 4 waves per SIMD
-// (5 at 1 bit) without spilling; the wider variants keep the compiler's choice.
+// at 2 bits (two chunk buffers in turn) and 5 at 1 bit (one buffer, copied),
+// without spilling; the wider variants keep the compiler's choice.
 template <int SUB, int GH, bool DQ, bool ROPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && !ROPE ? (SUB == 8 ? 5 : 4) : 1))) void decode_split_kernel(DecodeArgs a) {
+  constexpr bool kPingPong = SUB == 4;
   constexpr int S = kDim / SUB;
   constexpr int CW = S / 4;      // 32-bit words of codes per token
   constexpr int SPT = 16 / SUB;  // value slots per lane
   extern __shared__ float smem[];
   const DecodeSmem L = decode_smem(SUB, GH, a.split_tokens, a.R);
+  constexpr DecodeSmem kL = decode_smem(SUB, GH, 0, 0);  // the same offsets, as constants
   float* qf = smem + L.qf;
   float* qr = smem + L.qr;
   uint16_t* cbh = reinterpret_cast<uint16_t*>(smem + L.cbh);
@@ -234,9 +250,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
     for (int e = 0; e < 8; ++e) rsg[e] = (a.signs ? (float)a.signs[8 * rj + e] : 1.f) * kInvSqrtD;
   }
 
-  for (; ch < nchunk; ch += 4) {
-    ChunkRegs nxt;
-    if (ch + 4 < nchunk) load_chunk(ch + 4, nxt);
+  // one chunk of this wave with its loads in `cur` (the next chunk's loads
+  // are already in flight into the other buffer)
+  auto chunk_step = [&](int ch, const ChunkRegs& cur) {
     float kn1, kn2, vn1, vn2, km0, km1, vm0, vm1;
     if constexpr (DQ) {
       kn1 = dq_value(cur.kpar, cur.ksc >> 16);
@@ -337,12 +353,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
         sv = a.scale_log2 * rsc[g * kChunk + lane];
       } else {
         // score of this lane's token
-        const float* lg = lut + g * S * kLutStride;
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int j = 0; j < S; j += 2) {
-          s0 += lg[j * kLutStride + ((cur.kcw[j >> 2] >> (8 * (j & 3))) & 0xffu)];
-          s1 += lg[(j + 1) * kLutStride + ((cur.kcw[(j + 1) >> 2] >> (8 * ((j + 1) & 3))) & 0xffu)];
+          constexpr uint32_t base = 4u * kL.lut;
+          const uint32_t o0 = base + 4u * (uint32_t)((g * S + j) * kLutStride);
+          const uint32_t o1 = o0 + 4u * kLutStride;
+          s0 += lds_f32(o0 + (((cur.kcw[j >> 2] >> (8 * (j & 3))) & 0xffu) << 2));
+          s1 += lds_f32(o1 + (((cur.kcw[(j + 1) >> 2] >> (8 * ((j + 1) & 3))) & 0xffu) << 2));
         }
         const float qmu = group_sum<kWave>(fmaf(q0[g], km0, q1[g] * km1));
         sv = a.scale_log2 * kn1 * fmaf(kn2, s0 + s1, qmu);
@@ -371,11 +389,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
       for (int g = 0; g < GH; ++g) wg[g] = wb[g * kChunk + 8 * tg + i];
 #pragma unroll
       for (int si = 0; si < SPT; ++si) {
-        const uint32_t code = (cur.vcw[i] >> (8 * si)) & 0xffu;
-        const uint16_t* cp = cbh + code * SUB;
+        const uint32_t caddr = ((cur.vcw[i] >> (8 * si)) & 0xffu) * (2u * SUB) + 4u * kL.cbh;
 #pragma unroll
         for (int hh = 0; hh < SUB / 4; ++hh) {
-          const uint2 c4 = *reinterpret_cast<const uint2*>(cp + 4 * hh);
+          const uint2 c4 = lds_u32x2(caddr + 8u * hh);
           const float c0 = h2f(c4.x & 0xffff), c1 = h2f(c4.x >> 16);
           const float c2 = h2f(c4.y & 0xffff), c3 = h2f(c4.y >> 16);
 #pragma unroll
@@ -392,7 +409,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    cur = nxt;
+  };
+  if constexpr (kPingPong) {
+    // two buffers in turn, so no register copies between chunks
+    ChunkRegs alt;
+    for (; ch < nchunk; ch += 8) {
+      if (ch + 4 < nchunk) load_chunk(ch + 4, alt);
+      chunk_step(ch, cur);
+      if (ch + 4 >= nchunk) break;
+      if (ch + 8 < nchunk) load_chunk(ch + 8, cur);
+      chunk_step(ch + 4, alt);
+    }
+  } else {
+    for (; ch < nchunk; ch += 4) {
+      ChunkRegs nxt;
+      if (ch + 4 < nchunk) load_chunk(ch + 4, nxt);
+      chunk_step(ch, cur);
+      cur = nxt;
+    }
   }
 
   // token-group reduction inside the wave (lane bits 3..5)
