@@ -385,7 +385,7 @@ def main():
     t_tab = time.perf_counter()
     p_enc = nsnq.with_candidates(p, codebook) if bits == 2 else p
     t_tab = time.perf_counter() - t_tab
-    search_cols = 32 * p_enc.vq_tiles if p_enc.vq_tiles else 256  # codewords compared per sub-vector
+    search_cols = p_enc.vq_span if p_enc.vq_span else 256  # codewords compared per sub-vector
     k, v = synth.kv_layer(w["config_id"], 0, B, Hkv, L, d, outlier_std=synth.outlier_std_for(args.workload, 0),
                           device=dev)
     q = synth.queries(w["config_id"], 0, B, Hq, d, device=dev)
@@ -505,7 +505,9 @@ def main():
         "fp16_decode": fp16,
         "codebook": {"build_s": t_cb, "iters": args.codebook_iters, "n": 1 << 20,
                      "final_mse_per_elem": float(dist[-1].item())},
-        "roofline": {"kernel": "encode_kernel<4, 128, false, 3>" if p_enc is not p else "encode_kernel",
+        "roofline": {"kernel": (f"encode_kernel<4, {R}, false, {(search_cols + 31) // 32}, "
+                                f"{'true' if search_cols % 32 else 'false'}>" if p_enc is not p
+                                else f"encode_kernel<{s}, {R}, false, 0, false>"),
                      "bound": "alu", "achieved": enc_alu_tops,
                      "peak": VALU_PEAK_TOPS, "unit": "Tops/s", "frac": enc_alu_tops / VALU_PEAK_TOPS,
                      "traffic": encode_traffic(os.path.join(ROOT, "kv_cache_bit_amd", "csrc", "encode.hip")),

@@ -104,15 +104,16 @@ enum {
  *                   copy of the table nsnq_vq_candidates() builds for the
  *                   codebook passed to the encode calls (2 bits only); the
  *                   codes are the same, the search is shorter.
- *   vq_tiles        0 with vq_candidates NULL, else the tile count that
- *                   nsnq_vq_candidates() returned (1..4). */
+ *   vq_span         0 with vq_candidates NULL, else the number of list entries
+ *                   to search that nsnq_vq_candidates() returned (a multiple of
+ *                   16, at most 128; spans over 96 use the exhaustive search). */
 typedef struct {
   int32_t head_dim;
   int32_t bits;
   int32_t n_codewords;
   int32_t block_tokens;
   int32_t flags;
-  int32_t vq_tiles;
+  int32_t vq_span;
   const int8_t* hadamard_signs;
   const uint8_t* vq_candidates;
 } nsnq_params;
@@ -215,14 +216,15 @@ nsnq_status nsnq_finetune_codebook(const nsnq_params* p, const float* samples, i
  *   codebook_host  fp16 [256][4], HOST memory (the codebook of the encode calls).
  *   table_host     HOST out, NSNQ_VQ_TABLE_BYTES bytes: [16 boxes][128] codeword
  *                  indices, each list padded by repeating its last entry.
- *   n_tiles        out: ceil(longest list / 32), for nsnq_params.vq_tiles.
- * Copy the table to device memory and set vq_candidates / vq_tiles in the
+ *   span           out: the longest list rounded up to a multiple of 16, for
+ *                  nsnq_params.vq_span.
+ * Copy the table to device memory and set vq_candidates / vq_span in the
  * params of the encode calls.  Host only, synchronous, about 0.1 s.
  * NSNQ_EUNSUPPORTED for bits != 2 (1-bit boxes keep most codewords) or when a
  * list would exceed 128 entries. */
 #define NSNQ_VQ_TABLE_BYTES 2048
 nsnq_status nsnq_vq_candidates(const nsnq_params* p, const uint16_t* codebook_host, uint8_t* table_host,
-                               int32_t* n_tiles);
+                               int32_t* span);
 
 /* Prefill encode (technical summary secs. 1-4).  k and v are fp16 streams
  * indexed [b][h][t][c] at element offsets b*stride_b + h*stride_h +

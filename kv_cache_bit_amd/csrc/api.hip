@@ -24,8 +24,9 @@ nsnq_status check_params(const nsnq_params* p) {
   if (p->block_tokens != 64 && p->block_tokens != 128) return NSNQ_EUNSUPPORTED;
   if ((p->flags & ~(NSNQ_SCALE_ADJUST | NSNQ_DOUBLE_QUANT)) != 0) return NSNQ_EINVAL;
   if (p->vq_candidates == nullptr) {
-    if (p->vq_tiles != 0) return NSNQ_EINVAL;
-  } else if (p->bits != 2 || p->vq_tiles < 1 || p->vq_tiles > 4 || !aligned16(p->vq_candidates)) {
+    if (p->vq_span != 0) return NSNQ_EINVAL;
+  } else if (p->bits != 2 || p->vq_span < 16 || p->vq_span > 128 || p->vq_span % 16 != 0 ||
+             !aligned16(p->vq_candidates)) {
     return NSNQ_EINVAL;
   }
   return NSNQ_OK;
@@ -91,7 +92,7 @@ nsnq_status run_encode(const nsnq_params* p, const uint16_t* cb, const uint16_t*
   a.scale_adjust = (p->flags & NSNQ_SCALE_ADJUST) ? 1 : 0;
   a.dq = (p->flags & NSNQ_DOUBLE_QUANT) ? 1 : 0;
   a.cand = p->vq_candidates;
-  a.nt = p->vq_candidates ? p->vq_tiles : 0;
+  a.span = p->vq_candidates ? p->vq_span : 0;
   return hip_status(launch_encode(a, sub_of(p), p->block_tokens, stream));
 }
 
@@ -134,7 +135,7 @@ nsnq_status run_ragged_flush(const nsnq_params* p, const uint16_t* cb, const nsn
   a.scale_adjust = (p->flags & NSNQ_SCALE_ADJUST) ? 1 : 0;
   a.dq = (p->flags & NSNQ_DOUBLE_QUANT) ? 1 : 0;
   a.cand = p->vq_candidates;
-  a.nt = p->vq_candidates ? p->vq_tiles : 0;
+  a.span = p->vq_candidates ? p->vq_span : 0;
   a.fl_quant = c->seq_quant;
   a.fl_resid = c->seq_resid;
   return hip_status(launch_encode(a, sub_of(p), R, stream));
@@ -308,7 +309,7 @@ nsnq_status nsnq_encode_kv_ragged(const nsnq_params* p, const uint16_t* codebook
   a.scale_adjust = (p->flags & NSNQ_SCALE_ADJUST) ? 1 : 0;
   a.dq = (p->flags & NSNQ_DOUBLE_QUANT) ? 1 : 0;
   a.cand = p->vq_candidates;
-  a.nt = p->vq_candidates ? p->vq_tiles : 0;
+  a.span = p->vq_candidates ? p->vq_span : 0;
   a.lens = lengths;
   a.lens_max = max_len;
   a.out_quant = cache->seq_quant;

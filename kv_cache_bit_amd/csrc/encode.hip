@@ -124,9 +124,11 @@ __device__ __forceinline__ half8_t bias_operand(uint32_t uu_pair) {
   return u32x4_to_half8(uu_pair, 0x3C003C00u, 0u, 0u);
 }
 
-// NT = 0: every codeword is compared.  NT = 3 (2 bits): each sub-vector is
-// compared with the 96 entries of its orthant box's candidate list.
-template <int SUB, int R, bool DQ, int NT>
+// NT = 0: every codeword is compared.  NT = 2, 3 (2 bits): each sub-vector is
+// compared with the first 32 NT entries of its orthant box's candidate list,
+// or with the first 32 NT - 16 when HALF (the last tile's upper rows are not
+// searched).
+template <int SUB, int R, bool DQ, int NT, bool HALF>
 __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs a) {
   constexpr int NW = enc_waves<NT>();
   static_assert(NT == 0 || SUB == 4, "candidate lists exist for 4-element sub-vectors only");
@@ -723,7 +725,9 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
         tile(t, cur0, cur1);
 #pragma unroll
         for (int q = 0; q < 16; q += 2) {
-          // accumulator q holds list position 32t + 8(q/4) + 4(lane/32) + q%4
+          // accumulator q holds list position 32t + 8(q/4) + 4(lane/32) + q%4:
+          // rows 0-15 of the tile for q < 8
+          if (HALF && t == NT - 1 && q >= 8) continue;
           const uint32_t p0 = 32u * t + 8u * (q >> 2) + (q & 3);
           const uint32_t p1 = 32u * t + 8u * ((q + 1) >> 2) + ((q + 1) & 3);
           best0 = min(min(best0, make_key(cur0[q], vmask, p0)), make_key(cur0[q + 1], vmask, p1));
@@ -849,22 +853,28 @@ hipError_t launch_append(const AppendArgs& a, int B, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The list kernel searching `span` entries per list (16, 32, ... 96), or the
+// exhaustive kernel.
 template <int SUB, int R, bool DQ>
 static hipError_t launch_encode_nt(const EncodeArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.nt == 0) {
-    hipLaunchKernelGGL((encode_kernel<SUB, R, DQ, 0>), grid, dim3(64 * enc_waves<0>()), 0, stream, a);
-    return hipSuccess;
-  }
+  const dim3 b0(64 * enc_waves<0>()), b1(64 * enc_waves<1>());
   if constexpr (SUB == 4) {
-    if (a.nt <= 3) {
-      hipLaunchKernelGGL((encode_kernel<4, R, DQ, 3>), grid, dim3(64 * enc_waves<3>()), 0, stream, a);
+    if (a.span > 0 && a.span <= 64) {
+      hipLaunchKernelGGL((encode_kernel<4, R, DQ, 2, false>), grid, b1, 0, stream, a);
       return hipSuccess;
     }
-    // a list longer than 96 entries: the box tiles would not fit in LDS
-    hipLaunchKernelGGL((encode_kernel<4, R, DQ, 0>), grid, dim3(64 * enc_waves<0>()), 0, stream, a);
-    return hipSuccess;
+    if (a.span > 64 && a.span <= 80) {
+      hipLaunchKernelGGL((encode_kernel<4, R, DQ, 3, true>), grid, b1, 0, stream, a);
+      return hipSuccess;
+    }
+    if (a.span > 80 && a.span <= 96) {
+      hipLaunchKernelGGL((encode_kernel<4, R, DQ, 3, false>), grid, b1, 0, stream, a);
+      return hipSuccess;
+    }
   }
-  return hipErrorInvalidValue;
+  // no table, or lists longer than 96 entries (their box tiles would not fit in LDS)
+  hipLaunchKernelGGL((encode_kernel<SUB, R, DQ, 0, false>), grid, b0, 0, stream, a);
+  return hipSuccess;
 }
 
 hipError_t launch_encode(const EncodeArgs& args, int sub, int R, hipStream_t stream) {
@@ -872,7 +882,7 @@ hipError_t launch_encode(const EncodeArgs& args, int sub, int R, hipStream_t str
   const bool rcopy = a.rc_r > 0 || a.lens != nullptr;
   const int items = a.nblk * a.n_units;
   int n_enc = items;
-  if (sub == 4 && a.nt > 0 && a.nt <= 3) {
+  if (sub == 4 && a.span > 0 && a.span <= 96) {
     // candidate lists: one persistent group per CU and K/V half
     int dev = 0, ncu = 0;
     if (hipStreamGetDevice(stream, &dev) != hipSuccess ||

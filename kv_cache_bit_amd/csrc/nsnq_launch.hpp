@@ -36,10 +36,10 @@ struct EncodeArgs {
   const int32_t* fl_quant;
   const int32_t* fl_resid;
   // 2-bit nearest-codeword search over per-orthant candidate lists
-  // ([16][128] codeword indices, device) with nt 32-entry tiles; nt = 0
-  // compares every codeword
+  // ([16][128] codeword indices, device), the first `span` entries of each;
+  // span = 0 compares every codeword
   const uint8_t* cand;
-  int nt;
+  int span;
   int n_enc;  // candidate lists: encoding work-groups per K/V half (each loops over blocks)
 };
 

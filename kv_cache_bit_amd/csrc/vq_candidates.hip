@@ -136,8 +136,8 @@ double cell_gap(const double (*C)[kDimS], const double* n2, int k, int orthant, 
 }  // namespace
 
 extern "C" nsnq_status nsnq_vq_candidates(const nsnq_params* p, const uint16_t* codebook_host, uint8_t* table_host,
-                                          int32_t* n_tiles) {
-  if (!p || !codebook_host || !table_host || !n_tiles) return NSNQ_EINVAL;
+                                          int32_t* span) {
+  if (!p || !codebook_host || !table_host || !span) return NSNQ_EINVAL;
   if (p->n_codewords != kNcw || p->head_dim != 128) return NSNQ_EINVAL;
   if (p->bits != 2) return NSNQ_EUNSUPPORTED;
   double C[kNcw][kDimS], n2[kNcw];
@@ -166,6 +166,6 @@ extern "C" nsnq_status nsnq_vq_candidates(const nsnq_params* p, const uint16_t* 
   }
   static_assert(sizeof(lists) == NSNQ_VQ_TABLE_BYTES, "table layout");
   memcpy(table_host, lists, sizeof(lists));
-  *n_tiles = (longest + 31) / 32;
+  *span = (longest + 15) / 16 * 16;
   return NSNQ_OK;
 }

@@ -28,7 +28,7 @@ size_t = ctypes.c_size_t
 
 class nsnq_params(ctypes.Structure):
     _fields_ = [("head_dim", i32), ("bits", i32), ("n_codewords", i32), ("block_tokens", i32),
-                ("flags", i32), ("vq_tiles", i32), ("hadamard_signs", P), ("vq_candidates", P)]
+                ("flags", i32), ("vq_span", i32), ("hadamard_signs", P), ("vq_candidates", P)]
 
 
 class nsnq_rope(ctypes.Structure):
@@ -130,9 +130,9 @@ def with_candidates(p: nsnq_params, codebook: torch.Tensor) -> nsnq_params:
     """A copy of `p` whose encode calls search only the per-orthant candidate
     lists of `codebook` (2 bits; same codes as the exhaustive search).  The
     table is built on the host and copied next to the codebook."""
-    table, tiles = nsnq_vq_candidates(p, codebook)
+    table, span = nsnq_vq_candidates(p, codebook)
     dev = table.to(codebook.device)
-    q = nsnq_params(p.head_dim, p.bits, p.n_codewords, p.block_tokens, p.flags, tiles, p.hadamard_signs,
+    q = nsnq_params(p.head_dim, p.bits, p.n_codewords, p.block_tokens, p.flags, span, p.hadamard_signs,
                     dev.data_ptr())
     q._signs_ref = getattr(p, "_signs_ref", None)
     q._cand_ref = dev
@@ -151,15 +151,15 @@ def nsnq_abi_version() -> int:
 
 
 def nsnq_vq_candidates(p: nsnq_params, codebook: torch.Tensor) -> tuple[torch.Tensor, int]:
-    """Candidate table (uint8 [16][128], host) and tile count for a 2-bit fp16
-    codebook [256][4] (any device; read on the host)."""
+    """Candidate table (uint8 [16][128], host) and the entries to search per
+    list for a 2-bit fp16 codebook [256][4] (any device; read on the host)."""
     cb = codebook.detach().to("cpu").contiguous()
     assert cb.dtype == torch.float16 and cb.numel() == 256 * 4
     table = torch.empty(16, 128, dtype=torch.uint8)
-    tiles = ctypes.c_int32()
-    _check(lib().nsnq_vq_candidates(ctypes.byref(p), cb.data_ptr(), table.data_ptr(), ctypes.byref(tiles)),
+    span = ctypes.c_int32()
+    _check(lib().nsnq_vq_candidates(ctypes.byref(p), cb.data_ptr(), table.data_ptr(), ctypes.byref(span)),
            "nsnq_vq_candidates")
-    return table, tiles.value
+    return table, span.value
 
 
 def nsnq_buffer_bytes(p: nsnq_params, cap_tokens: int) -> tuple[int, int, int, int]:

@@ -53,12 +53,12 @@ def test_host_validation_rejects_before_launch(nsnq):
     # unknown flags; candidate-table fields that do not go together
     bad_flags = nsnq.params(2, 128, flags=4)
     assert L.nsnq_encode_kv(by(bad_flags), P, P, P, 0, 0, 128, 256, by(c), None) == EINVAL
-    for bits, tiles, table in ((2, 1, None), (2, 0, P), (2, 5, P), (2, 3, P + 8), (1, 3, P)):
+    for bits, span, table in ((2, 16, None), (2, 0, P), (2, 144, P), (2, 72, P), (2, 96, P + 8), (1, 96, P)):
         bad = nsnq.params(bits, 128)
-        bad.vq_tiles, bad.vq_candidates = tiles, table
-        assert L.nsnq_encode_kv(by(bad), P, P, P, 0, 0, 128, 256, by(c), None) == EINVAL, (bits, tiles, table)
+        bad.vq_span, bad.vq_candidates = span, table
+        assert L.nsnq_encode_kv(by(bad), P, P, P, 0, 0, 128, 256, by(c), None) == EINVAL, (bits, span, table)
     ok = nsnq.params(2, 128)
-    ok.vq_tiles, ok.vq_candidates = 3, P
+    ok.vq_span, ok.vq_candidates = 80, P
     assert L.nsnq_encode_kv(by(ok), P, P, P, 0, 0, 128, 0, by(c), None) == nsnq.NSNQ_OK
     adj = nsnq.params(2, 128, flags=nsnq.NSNQ_SCALE_ADJUST)
     assert L.nsnq_encode_kv(by(adj), P, P, P, 0, 0, 128, 0, by(c), None) == nsnq.NSNQ_OK

@@ -74,7 +74,7 @@ def test_encode_candidate_lists(oracle_codebooks, R, B, H, L, flags, use_signs):
     signs = synth.hadamard_signs(15 + R) if use_signs else None
     adjust = bool(flags & nsnq.NSNQ_SCALE_ADJUST)
     p, cbt, cache = gpu_encode(k, v, 2, R, cb, flags=flags, signs=signs, cand=True)
-    assert p.vq_tiles in (3, 4)
+    assert p.vq_span in (64, 80, 96)
     _, _, full = gpu_encode(k, v, 2, R, cb, flags=flags, signs=signs)
     dq = bool(flags & nsnq.NSNQ_DOUBLE_QUANT)
     kw = dict(signs=None if signs is None else signs.numpy(), scale_adjust=adjust, dq=dq)
@@ -93,6 +93,32 @@ def test_encode_candidate_lists(oracle_codebooks, R, B, H, L, flags, use_signs):
     same = all(np.array_equal(half_np(cache, w)["codes"], e["codes"]) for w, e in ((0, ek), (1, ev)))
     if same and not dq:
         check_attention(o, ref)
+
+
+def test_encode_candidate_list_spans(oracle_codebooks):
+    """Every list-kernel variant: a constructed codebook whose lists hold 16
+    entries (the 16 points {+-1}^4; the other 240 words lie far outside the
+    region u can reach and are on no list) runs the 64-entry kernel; the
+    k-means codebook runs with its own span and with the span forced to 96
+    (searching repeated padding entries is still exact)."""
+    R, B, H, L = 128, 1, 4, 3 * 128 + 17
+    k, v = _kv(170, B, H, L)
+    grid = np.array([[1.0 if (i >> e) & 1 else -1.0 for e in range(4)] for i in range(16)])
+    far = 40.0 + np.arange(240)[:, None] * 0.25 + np.zeros((240, 4))
+    cb_grid = np.concatenate([grid, far]).astype(np.float16).view(np.uint16)
+    cases = [(cb_grid, None), (oracle_codebooks[2], None), (oracle_codebooks[2], 96)]
+    for cb, force in cases:
+        cbt = cb_tensor(cb)
+        p = nsnq.with_candidates(nsnq.params(2, R), cbt)
+        if cb is cb_grid:
+            assert p.vq_span == 16
+        if force is not None:
+            p.vq_span = force
+        cache = nsnq.KVCache(p, B, H, capacity(L, R), DEV)
+        nsnq.nsnq_encode_kv(p, cbt, k.to(DEV), v.to(DEV), L, cache)
+        torch.cuda.synchronize()
+        ek, ev = oracle_encode_pair(k, v, R, cb)
+        compare_encoded(cache, ek, ev)
 
 
 def test_encode_candidate_lists_degenerate(oracle_codebooks):

@@ -48,11 +48,11 @@ def _gap_lp(C, k, o):
 
 
 def test_table_layout(cb2):
-    tab, tiles = _table(cb2)
+    tab, span = _table(cb2)
     assert tab.shape == (16, 128)
     lists = _lists(tab)
     longest = max(len(l) for l in lists)
-    assert tiles == (longest + 31) // 32 and 1 <= tiles <= 4
+    assert span == (longest + 15) // 16 * 16 and 16 <= span <= 128
     for o in range(16):
         n = len(lists[o])
         assert np.array_equal(tab[o, :n], np.array(lists[o], np.uint8)), "ascending, no repeats before the pad"
@@ -121,5 +121,5 @@ def test_unsupported_and_invalid(cb2):
 
 def test_params_carry_the_table(cb2):
     p = nsnq.with_candidates(nsnq.params(2, 64), torch.from_numpy(cb2.view(np.float16)))
-    assert p.vq_tiles in (3, 4) and p.vq_candidates
+    assert p.vq_span in (64, 80, 96) and p.vq_candidates
     assert p._cand_ref.numel() == 2048
