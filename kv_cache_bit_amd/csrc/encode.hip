@@ -210,7 +210,6 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
   __shared__ __attribute__((aligned(16))) uint8_t lst[NT ? 16 * 128 : 16];
   __shared__ uint8_t cbox[NT ? kCols / 32 : 1];
   __shared__ uint32_t whist[NT ? NW : 1][16];  // per wave and box: count, then first column
-  __shared__ int cstart[16], ccount[16], cpad[16], ncol_blocks;
   __shared__ float n1t[NT ? R : 1], n2t[NT ? R : 1];
   if constexpr (NT > 0) {
     for (int i = tid; i < 128; i += blockDim.x)
@@ -600,7 +599,7 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
     }
   } else {
     // ---- pass 2 with candidate lists (2 bits) -----------------------------
-    static_assert(NW == 16, "box offsets below assume 16 waves");
+    static_assert(NW == 16, "wave w pads box w below: 16 waves for 16 boxes");
     // (a) per row: transform, hi/lo split, orthant box; the rank of the
     // sub-vector among its wave's sub-vectors of the same box
     uint32_t boxr[ROWS], rankr[ROWS];
@@ -628,69 +627,46 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
       }
     }
     __syncthreads();
-    // (b) box offsets: each box's columns padded to a multiple of 32 (with
-    // the zero record), then each wave's share of its boxes.  Lane
-    // (g = lane / 16, box = lane % 16) covers waves 4g .. 4g + 3.
-    if (wave == 0) {
-      const int box = lane & 15, g = lane >> 4;
-      uint32_t c[4], gsum = 0;
+    // (b) box offsets, computed by every wave for itself (no barrier): lane
+    // `box` (< 16) sums the waves' counts of its box; each box's columns are
+    // padded to a multiple of 32 (with the zero record).
+    const int nblocks = [&] {
+      const int box = lane & 15;
+      uint32_t cnt = 0, mine = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = whist[4 * g + j][box];
-        gsum += c[j];
+      for (int w = 0; w < NW; ++w) {
+        const uint32_t c = whist[w][box];
+        mine = (w == wave) ? cnt : mine;  // columns of the waves before this one
+        cnt += c;
       }
-      uint32_t incl_g = gsum, t = __shfl_up(incl_g, 16, kWave);
-      if (g >= 1) incl_g += t;
-      t = __shfl_up(incl_g, 32, kWave);
-      if (g >= 2) incl_g += t;
-      const uint32_t cnt = __shfl(incl_g, 48 + box, kWave);  // the box's total
       const uint32_t padded = (cnt + 31u) & ~31u;
-      uint32_t incl_b = padded;
+      uint32_t incl = padded;
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) {
-        const uint32_t v = __shfl_up(incl_b, off, 16);
-        if (box >= off) incl_b += v;
+        const uint32_t v = __shfl_up(incl, off, 16);
+        if (box >= off) incl += v;
       }
-      const uint32_t st = incl_b - padded;
-      uint32_t base = st + incl_g - gsum;
+      const uint32_t st = incl - padded;
+      // (c) box order: every sub-vector of this wave to its column
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        whist[4 * g + j][box] = base;
-        base += c[j];
+      for (int r = 0; r < ROWS; ++r) {
+        const int tok = wave * TPW + r * TPR + tir;
+        const uint32_t first = __shfl(st + mine, (int)boxr[r], kWave);
+        sidx[first + rankr[r]] = (uint16_t)(tok * S + slot);
       }
-      if (g == 0) {
-        cstart[box] = (int)st;
-        ccount[box] = (int)cnt;
-        cpad[box] = (int)padded;
-      }
-      if (lane == 15) ncol_blocks = (int)(incl_b / 32);
-    }
-    __syncthreads();
-    // (c) box order: every sub-vector to its column, padding columns to the
-    // zero record, and the box of every 32-column block
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const int tok = wave * TPW + r * TPR + tir;
-      sidx[whist[wave][boxr[r]] + rankr[r]] = (uint16_t)(tok * S + slot);
-    }
-    if (tid < 16 * 32) {
-      const int box = tid >> 5, j = tid & 31;
-      if (j < cpad[box] - ccount[box]) sidx[cstart[box] + ccount[box] + j] = (uint16_t)kDummy;
-    } else if (tid < 16 * 32 + kCols / 32) {
-      const int cb = tid - 16 * 32;
-      int box = 0;
-#pragma unroll
-      for (int o = 1; o < 16; ++o)
-        if (cstart[o] <= 32 * cb && cpad[o] > 0) box = o;
-      cbox[cb] = (uint8_t)box;
-    }
+      // wave w pads box w with the zero record and labels its column blocks
+      const uint32_t wst = __shfl(st, wave, kWave), wcnt = __shfl(cnt, wave, kWave);
+      const uint32_t wpad = __shfl(padded, wave, kWave);
+      if ((uint32_t)lane < wpad - wcnt) sidx[wst + wcnt + lane] = (uint16_t)kDummy;
+      for (uint32_t q = lane; q < wpad / 32; q += kWave) cbox[wst / 32 + q] = (uint8_t)wave;  // up to R S / 32 blocks
+      return (int)(__shfl(incl, 15, kWave) / 32);
+    }();
     __syncthreads();
     if (next < items) load_rows(next, xn);
     // (d) distance products over the box's list, 32 sorted columns per MFMA;
     // lane n (< 32) holds column n's u parts, lane 32 + n its bias row; tile t
     // of a box holds its list entries 32 t .. 32 t + 31.  Each wave takes an
     // even share of the column blocks, two per step.
-    const int nblocks = ncol_blocks;
     const int n = lane & 31;
     const bool upper = lane >= 32;
     // B operand of sorted column `col` (both loads on every lane, then a select)

@@ -133,6 +133,14 @@ def test_encode_candidate_lists_degenerate(oracle_codebooks):
     ek, ev = oracle_encode_pair(k, v, R, cb)
     compare_encoded(cache, ek, ev)
     assert np.all(half_np(cache, 1)["scales"][0, 0, R:2 * R, 1] == 0)
+    # R = 128: a constant block puts all 4096 sub-vectors in one box (128
+    # column blocks), next to an ordinary block
+    k2, v2 = _kv(9, 1, 1, 3 * 128 + 1)
+    v2[0, 0, 128:256] = v2[0, 0, 128]
+    p2, _, cache2 = gpu_encode(k2, v2, 2, 128, cb, cand=True)
+    e2k, e2v = oracle_encode_pair(k2, v2, 128, cb)
+    compare_encoded(cache2, e2k, e2v)
+    assert np.all(half_np(cache2, 1)["scales"][0, 0, 128:256, 1] == 0)
     # ragged rows, then appends that flush a full window through the lists
     lengths = [0, R, 2 * R + 3]
     kk, vv = _kv(9, 3, 2, 3 * R + 2)
