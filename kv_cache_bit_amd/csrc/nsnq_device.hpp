@@ -27,10 +27,10 @@ __device__ __forceinline__ uint16_t f2h(float x) { return __builtin_bit_cast(uin
 template <int M>
 __device__ __forceinline__ float xlane(float v) {
   const int iv = __builtin_bit_cast(int, v);
-  if constexpr (M == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, false));
-  else if constexpr (M == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, false));
+  if constexpr (M == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true));
+  else if constexpr (M == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true));
   else if constexpr (M == 4) return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x101F));
-  else if constexpr (M == 8) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, false));
+  else if constexpr (M == 8) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, true));
   else if constexpr (M == 16) return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x401F));
   else {
     static_assert(M == 32, "lane xor");
