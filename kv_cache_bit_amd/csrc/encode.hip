@@ -640,12 +640,13 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
         cnt += c;
       }
       const uint32_t padded = (cnt + 31u) & ~31u;
+      // inclusive prefix over the 16 boxes of each DPP row: row_shr adds,
+      // lanes shifted in from outside the row read 0
       uint32_t incl = padded;
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const uint32_t v = __shfl_up(incl, off, 16);
-        if (box >= off) incl += v;
-      }
+      incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x111, 0xF, 0xF, false);
+      incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x112, 0xF, 0xF, false);
+      incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x114, 0xF, 0xF, false);
+      incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x118, 0xF, 0xF, false);
       const uint32_t st = incl - padded;
       // (c) box order: every sub-vector of this wave to its column
 #pragma unroll
@@ -655,11 +656,11 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
         sidx[first + rankr[r]] = (uint16_t)(tok * S + slot);
       }
       // wave w pads box w with the zero record and labels its column blocks
-      const uint32_t wst = __shfl(st, wave, kWave), wcnt = __shfl(cnt, wave, kWave);
-      const uint32_t wpad = __shfl(padded, wave, kWave);
+      const uint32_t wst = __builtin_amdgcn_readlane(st, wave), wcnt = __builtin_amdgcn_readlane(cnt, wave);
+      const uint32_t wpad = __builtin_amdgcn_readlane(padded, wave);
       if ((uint32_t)lane < wpad - wcnt) sidx[wst + wcnt + lane] = (uint16_t)kDummy;
       for (uint32_t q = lane; q < wpad / 32; q += kWave) cbox[wst / 32 + q] = (uint8_t)wave;  // up to R S / 32 blocks
-      return (int)(__shfl(incl, 15, kWave) / 32);
+      return (int)(__builtin_amdgcn_readlane(incl, 15) / 32);
     }();
     __syncthreads();
     if (next < items) load_rows(next, xn);
