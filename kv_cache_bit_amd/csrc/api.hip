@@ -467,9 +467,18 @@ DecodePlan plan_decode(const nsnq_params* p, const nsnq_cache* c, int q_heads, i
     bps = (nblk + num_splits - 1) / num_splits;
   } else {
     // about 1024 work-groups over the grid, each with at least 512 tokens so
-    // each of its 4 waves streams at least two 64-token chunks
+    // each of its 4 waves streams at least two 64-token chunks.  The
+    // grouped-head kernel has long per-group set-up and only a few groups fit
+    // a CU: there the grid is sized to what the device holds at once
+    // (residual-window groups included), so every group starts in the first
+    // round instead of a short second round trailing the first.
     const int64_t units = (int64_t)c->batch * c->kv_heads * (G / pl.gh);
     int64_t want = (1024 + units - 1) / units;
+    if (pl.mfma) {
+      const int64_t cap = decode_mfma_resident_groups(sub_of(p), pl.gh, (p->flags & NSNQ_DOUBLE_QUANT) != 0);
+      const int64_t fit = (cap - (c->n_resid > 0 ? units : 0)) / units;
+      if (cap > 0 && fit >= 4) want = fit;
+    }
     if (want < 1) want = 1;
     bps = (int)((nblk + want - 1) / want);
     const int min_bps = (512 + R - 1) / R;

@@ -24,6 +24,9 @@
 //           kept in LDS and folded in once at the end of the split.
 // Up to 16 query heads share a work-group, one MFMA column each.
 
+#include <type_traits>
+#include <utility>
+
 #include "decode_common.hpp"
 
 namespace nsnq {
@@ -32,6 +35,17 @@ namespace {
 
 constexpr int kMChunk = 64;                                 // tokens per wave step
 constexpr int kMaxChunks = kMaxSplitBlocks * 128 / kMChunk;  // per split (R <= 128)
+static_assert(kMaxChunks <= 64, "the merge gives each chunk a lane");
+
+// f(std::integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -121,6 +135,9 @@ template <int SUB, int GQ, bool DQ>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   using L = MfmaSmem<SUB, GQ>;
   constexpr int S = kDim / SUB;
+  // up to 4 heads: one token per lane, scores from 4x4x4 blocks; more heads
+  // fill the columns of 16x16x32 tiles instead
+  constexpr bool T4 = GQ <= 4;
   extern __shared__ float smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m16 = lane & 15, kb = lane >> 4;
@@ -136,8 +153,19 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int64_t ws_head = (int64_t)a.nsplit * (kDim + 2);
 
   float* qf = smem + L::qf;
-  for (int i = tid; i < GQ * kDim; i += 256) qf[i] = h2f(a.q[((int64_t)b * a.Hq + h0) * kDim + i]);
+  // queries into registers first: every set-up load below is issued before
+  // any of them is waited for
+  constexpr int QPT = (GQ * kDim + 255) / 256;
+  uint16_t qh[QPT];
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int i = tid + 256 * j;
+    qh[j] = i < GQ * kDim ? a.q[((int64_t)b * a.Hq + h0) * kDim + i] : (uint16_t)0;
+  }
   if (split >= a.nsplit_q) {
+#pragma unroll
+    for (int j = 0; j < QPT; ++j)
+      if (tid + 256 * j < GQ * kDim) qf[tid + 256 * j] = h2f(qh[j]);
     decode_residual<GQ>(a, row_resid(a, b), qf, smem + L::rsc, smem + L::rov, smem + L::rred, ws_base, ws_head,
                         unit);
     return;
@@ -160,23 +188,33 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   // slot 8 kb / 4 kb), and token `lane`'s scales and V code row, which go
   // through LDS.
   constexpr int KCW = SUB == 4 ? 2 : 1;
-  struct Ld {
-    uint32_t kc[4][KCW];
+  struct LdTile {
+    uint32_t kc[4][KCW];  // K codes of token 16 tau + m16, slots KCW 4 kb ..
+  };
+  struct LdToken {
+    uint4_t kc[S / 16];   // K code row of token `lane`
+  };
+  struct Ld : std::conditional_t<T4, LdToken, LdTile> {
     uint32_t ksc, vsc;    // (n1, n2) fp16 pairs, or (q1 << 16 | n2) double-quantised
     uint32_t kpar, vpar;  // double-quantised: the chunk's block (S1, Z1)
     uint4_t vcode[S / 16];
   };
   auto load = [&](int ch, Ld& r) {
     const int64_t base = (int64_t)ch * kMChunk;
+    if constexpr (T4) {
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      const uint8_t* p = kc + (base + 16 * tau + m16) * S + KCW * 4 * kb;
-      if constexpr (SUB == 4) {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
-        r.kc[tau][0] = v.x;
-        r.kc[tau][1] = v.y;
-      } else {
-        r.kc[tau][0] = *reinterpret_cast<const uint32_t*>(p);
+      for (int i = 0; i < S / 16; ++i) r.kc[i] = *reinterpret_cast<const uint4_t*>(kc + (base + lane) * S + 16 * i);
+    } else {
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        const uint8_t* p = kc + (base + 16 * tau + m16) * S + KCW * 4 * kb;
+        if constexpr (SUB == 4) {
+          const uint2 v = *reinterpret_cast<const uint2*>(p);
+          r.kc[tau][0] = v.x;
+          r.kc[tau][1] = v.y;
+        } else {
+          r.kc[tau][0] = *reinterpret_cast<const uint32_t*>(p);
+        }
       }
     }
     if constexpr (DQ) {
@@ -198,11 +236,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   };
   Ld cur;
   int ch = wave;
-  if (ch < nchunk) load(ch, cur);
+  // randomised-Hadamard signs of channels 2 lane, 2 lane + 1
+  const float sg0 = a.signs ? (float)a.signs[2 * lane] : 1.f;
+  const float sg1 = a.signs ? (float)a.signs[2 * lane + 1] : 1.f;
 
   // ---- per-split set-up: codebook, rotated queries, q . KMU_b -------------
   uint32_t* cb32 = reinterpret_cast<uint32_t*>(smem + L::cbh);
-  for (int i = tid; i < kCodewords * SUB / 2; i += 256) cb32[i] = reinterpret_cast<const uint32_t*>(a.codebook)[i];
+  constexpr int CPT = kCodewords * SUB / 2 / 256;  // codebook words per thread
+  uint32_t cbw[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) cbw[j] = reinterpret_cast<const uint32_t*>(a.codebook)[tid + 256 * j];
   // the split's block means as fp32 (at most 16 blocks x 128 channels for K
   // and V), all loads in flight together
   {
@@ -227,15 +270,21 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         }
       }
     }
+    // the first chunk's loads queue behind the set-up loads, which are waited
+    // for first
+    if (ch < nchunk) load(ch, cur);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       kmul[tid + 256 * j] = kt[j];
       vmul[tid + 256 * j] = vt[j];
     }
   }
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) cb32[tid + 256 * j] = cbw[j];
+#pragma unroll
+  for (int j = 0; j < QPT; ++j)
+    if (tid + 256 * j < GQ * kDim) qf[tid + 256 * j] = h2f(qh[j]);
   __syncthreads();
-  const float sg0 = a.signs ? (float)a.signs[2 * lane] : 1.f;
-  const float sg1 = a.signs ? (float)a.signs[2 * lane + 1] : 1.f;
   float* qr = smem + L::qr;
   for (int g = wave; g < GQ; g += 4) {
     float x[2] = {qf[g * kDim + 2 * lane] * sg0, qf[g * kDim + 2 * lane + 1] * sg1};
@@ -243,35 +292,67 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     qr[g * kDim + 2 * lane] = x[0] * kInvSqrtD;
     qr[g * kDim + 2 * lane + 1] = x[1] * kInvSqrtD;
   }
+  // q . KMU_b: the 16 lanes of a row share block b = tid / 16, each lane
+  // takes 8 channels of every head and the row sums them
   float* qmu = smem + L::qmu;
-  for (int i = tid; i < nblk * GQ; i += 256) {
-    const int bl = i / GQ, g = i % GQ;
-    const float4* mp = reinterpret_cast<const float4*>(smem + L::kmu) + bl * (kDim / 4);
-    const float4* qg = reinterpret_cast<const float4*>(qf + g * kDim);
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < kDim / 4; ++c) {
-      const float4 m4 = mp[c], q4 = qg[c];
-      s0 = fmaf(q4.x, m4.x, s0);
-      s1 = fmaf(q4.y, m4.y, s1);
-      s0 = fmaf(q4.z, m4.z, s0);
-      s1 = fmaf(q4.w, m4.w, s1);
+  if ((tid >> 4) < nblk) {
+    const int bl = tid >> 4, c8 = tid & 15;
+    const float4* mp = reinterpret_cast<const float4*>(smem + L::kmu) + bl * (kDim / 4) + 2 * c8;
+    const float4 m0 = mp[0], m1 = mp[1];
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      const float4* qg = reinterpret_cast<const float4*>(qf + g * kDim) + 2 * c8;
+      const float4 q0 = qg[0], q1 = qg[1];
+      float d = q0.x * m0.x;
+      d = fmaf(q0.y, m0.y, d);
+      d = fmaf(q0.z, m0.z, d);
+      d = fmaf(q0.w, m0.w, d);
+      d = fmaf(q1.x, m1.x, d);
+      d = fmaf(q1.y, m1.y, d);
+      d = fmaf(q1.z, m1.z, d);
+      d = fmaf(q1.w, m1.w, d);
+      d = group_sum<16>(d);
+      if (c8 == 0) qmu[bl * GQ + g] = d;
     }
-    qmu[i] = s0 + s1;
   }
   __syncthreads();
   // B operands of the score products: lane (head m16, k-block kb), MFMA i
   // holds channels 32 kb + 8 i .. + 7 of q', as fp16 high and low parts.
   half8_t bqh[4], bql[4];
+  half4_t qa[2][2];  // [fp16 high, low part][k-slice half]
+  if constexpr (T4) {
+    // A blocks of the score products: lane 4 j + i holds channels
+    // 4 (16 h + j) .. + 3 of head i in qa[.][h]; a product broadcasts block
+    // j of the slice it needs to all 16 blocks
+    const int i = lane & 3, j = lane >> 2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int h = 0; h < 2; ++h) {
+      const float4 v = *reinterpret_cast<const float4*>(qr + (i < GQ ? i : 0) * kDim + 4 * (16 * h + j));
+      const float on = i < GQ ? 1.f : 0.f;
+      const float x[4] = {v.x * on, v.y * on, v.z * on, v.w * on};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = m16 < GQ ? qr[m16 * kDim + 32 * kb + 8 * i + e] : 0.f;
-      const half_t hi = (half_t)v;
-      bqh[i][e] = hi;
-      bql[i][e] = (half_t)(v - (float)hi);
+      for (int e = 0; e < 4; ++e) {
+        const half_t hi = (half_t)x[e];
+        qa[0][h][e] = hi;
+        qa[1][h][e] = (half_t)(x[e] - (float)hi);
+      }
     }
+  } else {
+    const float4* qrow = reinterpret_cast<const float4*>(qr + (m16 < GQ ? m16 : 0) * kDim + 32 * kb);
+    const float on = m16 < GQ ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v0 = qrow[2 * i], v1 = qrow[2 * i + 1];
+      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = v[e] * on;
+        const half_t hi = (half_t)x;
+        bqh[i][e] = hi;
+        bql[i][e] = (half_t)(x - (float)hi);
+      }
+    }
+  }
 
   float* vst = smem + L::vst + wave * L::VSTW;
   uint8_t* vcl = reinterpret_cast<uint8_t*>(vst);  // [64][S] V codes
@@ -288,13 +369,35 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) vacc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (; ch < nchunk; ch += 4) {
-    Ld nxt;
-    if (ch + 4 < nchunk) load(ch + 4, nxt);
-    // stage this chunk's V codes and token `lane`'s factors
+  if constexpr (T4) {
+    // ---- one token per lane ----------------------------------------------
+    // sacc row r, lane t: (H D q_r / sqrt d) . codewords of token t, summed
+    // over 32 slices of 4 channels (two 8-channel codewords' halves at 1 bit).
+    // The running reference mr of each head moves only when a score exceeds
+    // it by more than 2^3 (then to the exact maximum), so the cross-lane
+    // maximum and the rescale are rare; p <= 8 and p VC / 8 in fp16 keeps
+    // the range of p VC with p <= 1.
+    constexpr float kLazy = 3.f;
+    float mr[GQ], lp[GQ];
 #pragma unroll
-    for (int i = 0; i < S / 16; ++i) *reinterpret_cast<uint4_t*>(vcl + lane * S + 16 * i) = cur.vcode[i];
-    {
+    for (int r = 0; r < GQ; ++r) {
+      mr[r] = -INFINITY;
+      lp[r] = 0.f;
+    }
+    // p VC / 8 (columns 0..3) and p VD / 8 (columns 4..7) of the chunk's
+    // tokens, fp16 [8][64], in the per-token factor area
+    uint16_t* pb = reinterpret_cast<uint16_t*>(fka);
+    const uint32_t pb_lds = (uint32_t)(reinterpret_cast<uintptr_t>(fka) - reinterpret_cast<uintptr_t>(smem));
+    // A of the beta product: row 0 all ones
+    half8_t aone;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) aone[e] = (half_t)(m16 == 0 ? 1.f : 0.f);
+
+    for (; ch < nchunk; ch += 4) {
+      Ld nxt;
+      if (ch + 4 < nchunk) load(ch + 4, nxt);
+#pragma unroll
+      for (int i = 0; i < S / 16; ++i) *reinterpret_cast<uint4_t*>(vcl + lane * S + 16 * i) = cur.vcode[i];
       float kn1, kn2, vn1, vn2;
       if constexpr (DQ) {
         kn1 = dq_value(cur.kpar, cur.ksc >> 16);
@@ -307,146 +410,291 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         vn1 = h2f(cur.vsc & 0xffff);
         vn2 = h2f(cur.vsc >> 16);
       }
-      const float kas = a.scale_log2 * kn1;
-      fka[lane] = kas * kn2;
-      fkb[lane] = kas;
-      fvc[lane] = vn1 * vn2;
-      fvd[lane] = vn1;
-    }
-    wave_sync();
+      const float kas = a.scale_log2 * kn1, ka = kas * kn2;
+      const float vd8 = 0.125f * vn1, vc8 = vd8 * vn2;
 
-    // scores: tile tau covers tokens 16 tau .. 16 tau + 15 (rows), heads (columns)
-    float4_t sacc[4];
-#pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      half8_t A[4];
+      float4_t sh = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
       if constexpr (SUB == 4) {
-        uint32_t ad[8];
-        const uint32_t w0 = cur.kc[tau][0], w1 = cur.kc[tau][1];
-        ad[0] = code_shl<0, 3>(w0); ad[1] = code_shl<1, 3>(w0); ad[2] = code_shl<2, 3>(w0); ad[3] = code_shl<3, 3>(w0);
-        ad[4] = code_shl<0, 3>(w1); ad[5] = code_shl<1, 3>(w1); ad[6] = code_shl<2, 3>(w1); ad[7] = code_shl<3, 3>(w1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x2_t c0 = lds_b64(ad[2 * i]);
-          const u32x2_t c1 = lds_b64(ad[2 * i + 1]);
-          A[i] = __builtin_bit_cast(half8_t, uint4_t{c0.x, c0.y, c1.x, c1.y});
-        }
+        static_for<32>([&](auto kk_) {
+          constexpr int kk = decltype(kk_)::value;
+          const u32x2_t c = lds_b64(code_shl<kk & 3, 3>(cur.kc[kk >> 4][(kk >> 2) & 3]));
+          const half4_t B = __builtin_bit_cast(half4_t, c);
+          sh = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[0][kk >> 4], B, sh, 4, kk & 15, 0);
+          sl = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[1][kk >> 4], B, sl, 4, kk & 15, 0);
+        });
       } else {
-        const uint32_t w0 = cur.kc[tau][0];
-        uint32_t ad[4] = {code_shl<0, 4>(w0), code_shl<1, 4>(w0), code_shl<2, 4>(w0), code_shl<3, 4>(w0)};
+        static_for<16>([&](auto j_) {
+          constexpr int j = decltype(j_)::value, kk = 2 * j;
+          const uint4_t c = lds_b128(code_shl<j & 3, 4>(cur.kc[0][j >> 2]));
+          const half4_t B0 = __builtin_bit_cast(half4_t, u32x2_t{c.x, c.y});
+          const half4_t B1 = __builtin_bit_cast(half4_t, u32x2_t{c.z, c.w});
+          sh = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[0][kk >> 4], B0, sh, 4, kk & 15, 0);
+          sl = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[1][kk >> 4], B0, sl, 4, kk & 15, 0);
+          sh = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[0][kk >> 4], B1, sh, 4, (kk + 1) & 15, 0);
+          sl = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[1][kk >> 4], B1, sl, 4, (kk + 1) & 15, 0);
+        });
+      }
+      // s = KA S + KB (q . KMU_b), in log2 units
+      const int bl = (ch * kMChunk) / a.R;
+      float sc[GQ], dl[GQ];
+      bool up = false;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          A[i] = __builtin_bit_cast(half8_t, lds_b128(ad[i]));
+      for (int r = 0; r < GQ; ++r) {
+        sc[r] = fmaf(ka, sh[r] + sl[r], kas * qmu[bl * GQ + r]);
+        dl[r] = sc[r] - mr[r];
+        up = up || dl[r] > kLazy;
+      }
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        float as = 1.f;
+#pragma unroll
+        for (int r = 0; r < GQ; ++r) {
+          const float mn = fmaxf(mr[r], group_max<64>(sc[r]));
+          const float al = __builtin_amdgcn_exp2f(mr[r] - mn);
+          mr[r] = mn;
+          lp[r] *= al;
+          dl[r] = sc[r] - mn;
+          as = m16 == r ? al : as;
         }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vacc[t] *= as;
       }
-      float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], bqh[i], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], bql[i], acc, 0, 0, 0);
+      for (int r = 0; r < GQ; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(dl[r]);
+        lp[r] += pr;
+        pb[r * kMChunk + lane] = f2h(pr * vc8);
+        pb[(4 + r) * kMChunk + lane] = f2h(pr * vd8);
       }
-      sacc[tau] = acc;
-    }
-    // s = KA S + KB (q . KMU_b) for this lane's 16 tokens 16 tau + 4 kb + r
-    const int bl = (ch * kMChunk) / a.R;
-    const float qm = m16 < GQ ? qmu[bl * GQ + m16] : 0.f;
-    float s[16];
-    float cmax = -INFINITY;
-#pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      const float4 ka = *reinterpret_cast<const float4*>(fka + 16 * tau + 4 * kb);
-      const float4 kbb = *reinterpret_cast<const float4*>(fkb + 16 * tau + 4 * kb);
-      const float kav[4] = {ka.x, ka.y, ka.z, ka.w}, kbv[4] = {kbb.x, kbb.y, kbb.z, kbb.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = fmaf(kav[r], sacc[tau][r], kbv[r] * qm);
-        s[4 * tau + r] = v;
-        cmax = fmaxf(cmax, v);
-      }
-    }
-    cmax = fmaxf(cmax, xlane<16>(cmax));
-    cmax = fmaxf(cmax, xlane<32>(cmax));
-    const float mn = fmaxf(m, cmax);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    m = mn;
-    float lsum = 0.f, beta = 0.f;
-    half8_t bw[2];
-#pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      const float4 vc4 = *reinterpret_cast<const float4*>(fvc + 16 * tau + 4 * kb);
-      const float4 vd4 = *reinterpret_cast<const float4*>(fvd + 16 * tau + 4 * kb);
-      const float vcv[4] = {vc4.x, vc4.y, vc4.z, vc4.w}, vdv[4] = {vd4.x, vd4.y, vd4.z, vd4.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[4 * tau + r] - mn);
-        lsum += p;
-        beta = fmaf(p, vdv[r], beta);
-        bw[tau >> 1][4 * (tau & 1) + r] = (half_t)(p * vcv[r]);
-      }
-    }
-    l = fmaf(l, alpha, lsum);
-    beta += xlane<16>(beta);
-    beta += xlane<32>(beta);
-    if (kb == 0 && m16 < GQ) {
-      bc[ch * GQ + m16] = beta;
-      mc[ch * GQ + m16] = mn;
-    }
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // the running max moved for some head
-#pragma unroll
-      for (int t = 0; t < 8; ++t) vacc[t] *= alpha;
-    }
+      wave_sync();
 
-    // values: 32-token step c holds the rows of score tiles 2c and 2c + 1;
-    // lane (m16, kb) supplies tokens 16 (2c + e/4) + 4 kb + e%4, e = 0..7
+      // values: 32-token step c; lane (m16, kb) supplies tokens 32 c + 8 kb + e
+      float4_t db = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      int toks[8];
+      for (int c = 0; c < 2; ++c) {
+        const half8_t bw = __builtin_bit_cast(half8_t, lds_b128(pb_lds + 2 * ((m16 & 7) * kMChunk + 32 * c + 8 * kb)));
+        const uint8_t* vrow = vcl + (32 * c + 8 * kb) * S + m16;
+        if constexpr (SUB == 4) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) toks[e] = 16 * (2 * c + (e >> 2)) + 4 * kb + (e & 3);
-      if constexpr (SUB == 4) {
+          for (int g2 = 0; g2 < 2; ++g2) {
+            u32x2_t cw[8];
 #pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2) {
-          u32x2_t cw[8];
+            for (int e = 0; e < 8; ++e) cw[e] = lds_b64((uint32_t)vrow[e * S + 16 * g2] << 3);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) cw[e] = lds_b64((uint32_t)vcl[toks[e] * S + 16 * g2 + m16] << 3);
+            for (int ep = 0; ep < 4; ++ep) {
+              const uint32_t sel = (ep & 1) ? 0x07060302u : 0x05040100u;
+              uint32_t d[4];
 #pragma unroll
-          for (int ep = 0; ep < 4; ++ep) {
+              for (int jj = 0; jj < 4; ++jj) {
+                const uint32_t lo = (ep < 2) ? cw[2 * jj].x : cw[2 * jj].y;
+                const uint32_t hi = (ep < 2) ? cw[2 * jj + 1].x : cw[2 * jj + 1].y;
+                d[jj] = __builtin_amdgcn_perm(hi, lo, sel);
+              }
+              const half8_t A = __builtin_bit_cast(half8_t, uint4_t{d[0], d[1], d[2], d[3]});
+              vacc[4 * g2 + ep] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bw, vacc[4 * g2 + ep], 0, 0, 0);
+            }
+          }
+        } else {
+          uint4_t cw[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cw[e] = lds_b128((uint32_t)vrow[e * S] << 4);
+#pragma unroll
+          for (int ep = 0; ep < 8; ++ep) {
             const uint32_t sel = (ep & 1) ? 0x07060302u : 0x05040100u;
             uint32_t d[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t lo = (ep < 2) ? cw[2 * j].x : cw[2 * j].y;
-              const uint32_t hi = (ep < 2) ? cw[2 * j + 1].x : cw[2 * j + 1].y;
-              d[j] = __builtin_amdgcn_perm(hi, lo, sel);
-            }
+            for (int jj = 0; jj < 4; ++jj) d[jj] = __builtin_amdgcn_perm(cw[2 * jj + 1][ep >> 1], cw[2 * jj][ep >> 1], sel);
             const half8_t A = __builtin_bit_cast(half8_t, uint4_t{d[0], d[1], d[2], d[3]});
-            vacc[4 * g2 + ep] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bw[c], vacc[4 * g2 + ep], 0, 0, 0);
+            vacc[ep] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bw, vacc[ep], 0, 0, 0);
           }
         }
-      } else {
-        uint4_t cw[8];
+        db = __builtin_amdgcn_mfma_f32_16x16x32_f16(aone, bw, db, 0, 0, 0);
+      }
+      // beta_r = sum p VD: row 0, column 4 + r of db (lanes 4 .. 4 + GQ - 1)
+      if (m16 >= 4 && m16 < 4 + GQ && kb == 0) bc[ch * GQ + m16 - 4] = 8.f * db[0];
+      if (lane < GQ) {
+        float mm = mr[0];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cw[e] = lds_b128((uint32_t)vcl[toks[e] * S + m16] << 4);
+        for (int r = 1; r < GQ; ++r) mm = lane == r ? mr[r] : mm;
+        mc[ch * GQ + lane] = mm;
+      }
+      wave_sync();
+      cur = nxt;
+    }
+    // lane (m16 < GQ, kb): reference and sum of head m16; the value columns
+    // hold p VC / 8
+    m = mr[0];
+    l = 0.f;
 #pragma unroll
-        for (int ep = 0; ep < 8; ++ep) {
-          const uint32_t sel = (ep & 1) ? 0x07060302u : 0x05040100u;
-          uint32_t d[4];
+    for (int r = 0; r < GQ; ++r) {
+      const float lt = group_sum<64>(lp[r]);
+      m = m16 == r ? mr[r] : m;
+      l = m16 == r ? lt : l;
+    }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            d[j] = __builtin_amdgcn_perm(cw[2 * j + 1][ep >> 1], cw[2 * j][ep >> 1], sel);
+    for (int t = 0; t < 8; ++t) vacc[t] *= 8.f;
+  } else {
+  for (; ch < nchunk; ch += 4) {
+      Ld nxt;
+      if (ch + 4 < nchunk) load(ch + 4, nxt);
+      // stage this chunk's V codes and token `lane`'s factors
+  #pragma unroll
+      for (int i = 0; i < S / 16; ++i) *reinterpret_cast<uint4_t*>(vcl + lane * S + 16 * i) = cur.vcode[i];
+      {
+        float kn1, kn2, vn1, vn2;
+        if constexpr (DQ) {
+          kn1 = dq_value(cur.kpar, cur.ksc >> 16);
+          kn2 = h2f(cur.ksc & 0xffff);
+          vn1 = dq_value(cur.vpar, cur.vsc >> 16);
+          vn2 = h2f(cur.vsc & 0xffff);
+        } else {
+          kn1 = h2f(cur.ksc & 0xffff);
+          kn2 = h2f(cur.ksc >> 16);
+          vn1 = h2f(cur.vsc & 0xffff);
+          vn2 = h2f(cur.vsc >> 16);
+        }
+        const float kas = a.scale_log2 * kn1;
+        fka[lane] = kas * kn2;
+        fkb[lane] = kas;
+        fvc[lane] = vn1 * vn2;
+        fvd[lane] = vn1;
+      }
+      wave_sync();
+  
+      // scores: tile tau covers tokens 16 tau .. 16 tau + 15 (rows), heads (columns)
+      float4_t sacc[4];
+  #pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        half8_t A[4];
+        if constexpr (SUB == 4) {
+          uint32_t ad[8];
+          const uint32_t w0 = cur.kc[tau][0], w1 = cur.kc[tau][1];
+          ad[0] = code_shl<0, 3>(w0); ad[1] = code_shl<1, 3>(w0); ad[2] = code_shl<2, 3>(w0); ad[3] = code_shl<3, 3>(w0);
+          ad[4] = code_shl<0, 3>(w1); ad[5] = code_shl<1, 3>(w1); ad[6] = code_shl<2, 3>(w1); ad[7] = code_shl<3, 3>(w1);
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const u32x2_t c0 = lds_b64(ad[2 * i]);
+            const u32x2_t c1 = lds_b64(ad[2 * i + 1]);
+            A[i] = __builtin_bit_cast(half8_t, uint4_t{c0.x, c0.y, c1.x, c1.y});
           }
-          const half8_t A = __builtin_bit_cast(half8_t, uint4_t{d[0], d[1], d[2], d[3]});
-          vacc[ep] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bw[c], vacc[ep], 0, 0, 0);
+        } else {
+          const uint32_t w0 = cur.kc[tau][0];
+          uint32_t ad[4] = {code_shl<0, 4>(w0), code_shl<1, 4>(w0), code_shl<2, 4>(w0), code_shl<3, 4>(w0)};
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            A[i] = __builtin_bit_cast(half8_t, lds_b128(ad[i]));
+          }
+        }
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], bqh[i], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], bql[i], acc, 0, 0, 0);
+        }
+        sacc[tau] = acc;
+      }
+      // s = KA S + KB (q . KMU_b) for this lane's 16 tokens 16 tau + 4 kb + r
+      const int bl = (ch * kMChunk) / a.R;
+      const float qm = m16 < GQ ? qmu[bl * GQ + m16] : 0.f;
+      float s[16];
+      float cmax = -INFINITY;
+  #pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        const float4 ka = *reinterpret_cast<const float4*>(fka + 16 * tau + 4 * kb);
+        const float4 kbb = *reinterpret_cast<const float4*>(fkb + 16 * tau + 4 * kb);
+        const float kav[4] = {ka.x, ka.y, ka.z, ka.w}, kbv[4] = {kbb.x, kbb.y, kbb.z, kbb.w};
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = fmaf(kav[r], sacc[tau][r], kbv[r] * qm);
+          s[4 * tau + r] = v;
+          cmax = fmaxf(cmax, v);
         }
       }
+      cmax = fmaxf(cmax, xlane<16>(cmax));
+      cmax = fmaxf(cmax, xlane<32>(cmax));
+      const float mn = fmaxf(m, cmax);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      float lsum = 0.f, beta = 0.f;
+      half8_t bw[2];
+  #pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        const float4 vc4 = *reinterpret_cast<const float4*>(fvc + 16 * tau + 4 * kb);
+        const float4 vd4 = *reinterpret_cast<const float4*>(fvd + 16 * tau + 4 * kb);
+        const float vcv[4] = {vc4.x, vc4.y, vc4.z, vc4.w}, vdv[4] = {vd4.x, vd4.y, vd4.z, vd4.w};
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(s[4 * tau + r] - mn);
+          lsum += p;
+          beta = fmaf(p, vdv[r], beta);
+          bw[tau >> 1][4 * (tau & 1) + r] = (half_t)(p * vcv[r]);
+        }
+      }
+      l = fmaf(l, alpha, lsum);
+      beta += xlane<16>(beta);
+      beta += xlane<32>(beta);
+      if (kb == 0 && m16 < GQ) {
+        bc[ch * GQ + m16] = beta;
+        mc[ch * GQ + m16] = mn;
+      }
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // the running max moved for some head
+  #pragma unroll
+        for (int t = 0; t < 8; ++t) vacc[t] *= alpha;
+      }
+  
+      // values: 32-token step c holds the rows of score tiles 2c and 2c + 1;
+      // lane (m16, kb) supplies tokens 16 (2c + e/4) + 4 kb + e%4, e = 0..7
+  #pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        int toks[8];
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) toks[e] = 16 * (2 * c + (e >> 2)) + 4 * kb + (e & 3);
+        if constexpr (SUB == 4) {
+  #pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            u32x2_t cw[8];
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) cw[e] = lds_b64((uint32_t)vcl[toks[e] * S + 16 * g2 + m16] << 3);
+  #pragma unroll
+            for (int ep = 0; ep < 4; ++ep) {
+              const uint32_t sel = (ep & 1) ? 0x07060302u : 0x05040100u;
+              uint32_t d[4];
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const uint32_t lo = (ep < 2) ? cw[2 * j].x : cw[2 * j].y;
+                const uint32_t hi = (ep < 2) ? cw[2 * j + 1].x : cw[2 * j + 1].y;
+                d[j] = __builtin_amdgcn_perm(hi, lo, sel);
+              }
+              const half8_t A = __builtin_bit_cast(half8_t, uint4_t{d[0], d[1], d[2], d[3]});
+              vacc[4 * g2 + ep] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bw[c], vacc[4 * g2 + ep], 0, 0, 0);
+            }
+          }
+        } else {
+          uint4_t cw[8];
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) cw[e] = lds_b128((uint32_t)vcl[toks[e] * S + m16] << 4);
+  #pragma unroll
+          for (int ep = 0; ep < 8; ++ep) {
+            const uint32_t sel = (ep & 1) ? 0x07060302u : 0x05040100u;
+            uint32_t d[4];
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              d[j] = __builtin_amdgcn_perm(cw[2 * j + 1][ep >> 1], cw[2 * j][ep >> 1], sel);
+            }
+            const half8_t A = __builtin_bit_cast(half8_t, uint4_t{d[0], d[1], d[2], d[3]});
+            vacc[ep] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bw[c], vacc[ep], 0, 0, 0);
+          }
+        }
+      }
+      wave_sync();
+      cur = nxt;
     }
-    wave_sync();
-    cur = nxt;
   }
 
   // ---- merge the four waves, inverse transform, mean term ------------------
-  l += xlane<16>(l);
-  l += xlane<32>(l);
+  if constexpr (!T4) {
+    l += xlane<16>(l);
+    l += xlane<32>(l);
+  }
   __syncthreads();  // the main-loop LDS views are dead from here on
   float* mrg = smem + L::mrg;
   constexpr int MS = kDim + 2;
@@ -476,12 +724,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       x[1] = fmaf(f, r[2 + 2 * lane + 1], x[1]);
     }
     fwht128<2>(x, lane);
-    // sum over chunks of 2^(m_c - M) beta_c MU_b(c), channels 2 lane, 2 lane + 1
+    // sum over chunks of 2^(m_c - M) beta_c MU_b(c), channels 2 lane, 2 lane + 1:
+    // lane c weighs chunk c (a split has at most 32 chunks), then the weights
+    // of each block's chunks meet its mean
     const float2* vmul = reinterpret_cast<const float2*>(smem + L::vmu);
+    const float fch = lane < nchunk ? exp2f(mc[lane * GQ + g] - M) * bc[lane * GQ + g] : 0.f;
+    const int cpb = a.R / kMChunk;
     float om0 = 0.f, om1 = 0.f;
-    for (int ci = 0; ci < nchunk; ++ci) {
-      const float f = exp2f(mc[ci * GQ + g] - M) * bc[ci * GQ + g];
-      const float2 mu2 = vmul[((ci * kMChunk) / a.R) * (kDim / 2) + lane];
+    for (int bl = 0; bl < nblk; ++bl) {
+      float f = 0.f;
+      for (int j = 0; j < cpb; ++j)
+        f += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fch), bl * cpb + j));
+      const float2 mu2 = vmul[bl * (kDim / 2) + lane];
       om0 = fmaf(f, mu2.x, om0);
       om1 = fmaf(f, mu2.y, om1);
     }
@@ -505,6 +759,46 @@ size_t decode_mfma_lds_bytes(int sub, int gq) {
       : gq == 8 ? MfmaSmem<8, 8>::total : MfmaSmem<8, 16>::total;
   }
   return (size_t)w * sizeof(float);
+}
+
+template <int SUB, int GQ, bool DQ>
+static int mfma_groups_per_cu() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&decode_mfma_kernel<SUB, GQ, DQ>),
+                                                   256, (size_t)MfmaSmem<SUB, GQ>::total * sizeof(float)) != hipSuccess)
+    return 0;
+  return n;
+}
+
+template <int SUB>
+static int mfma_groups_per_cu_s(int gq, bool dq) {
+  if (gq == 2) return dq ? mfma_groups_per_cu<SUB, 2, true>() : mfma_groups_per_cu<SUB, 2, false>();
+  if (gq == 4) return dq ? mfma_groups_per_cu<SUB, 4, true>() : mfma_groups_per_cu<SUB, 4, false>();
+  if (gq == 8) return dq ? mfma_groups_per_cu<SUB, 8, true>() : mfma_groups_per_cu<SUB, 8, false>();
+  if (gq == 16) return dq ? mfma_groups_per_cu<SUB, 16, true>() : mfma_groups_per_cu<SUB, 16, false>();
+  return 0;
+}
+
+int decode_mfma_resident_groups(int sub, int gq, bool dq) {
+  // cached per device and kernel variant; 0 = unknown (no device, query failed)
+  constexpr int kDev = 16;
+  static int cache[kDev][2][5][2];  // [device][sub 4/8][log2 gq][dq], -1 stored for "unknown"
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDev) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int si = sub == 8 ? 1 : 0;
+  const int gi = gq == 2 ? 1 : gq == 4 ? 2 : gq == 8 ? 3 : gq == 16 ? 4 : 0;
+  int& slot = cache[dev][si][gi][dq ? 1 : 0];
+  if (slot == 0) {
+    int cus = 0;
+    const int per_cu = sub == 4 ? mfma_groups_per_cu_s<4>(gq, dq) : mfma_groups_per_cu_s<8>(gq, dq);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    (void)hipGetLastError();
+    slot = per_cu > 0 && cus > 0 ? per_cu * cus : -1;
+  }
+  return slot > 0 ? slot : 0;
 }
 
 template <int SUB, int GQ, bool DQ>

@@ -170,6 +170,8 @@ hipError_t launch_dequant(const DequantArgs& a, int sub, int n_units, hipStream_
 hipError_t launch_decode(const DecodeArgs& a, int sub, int gh, int B, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int sub, int gq, int B, hipStream_t stream);
 size_t decode_mfma_lds_bytes(int sub, int gq);
+// work-groups of the grouped-head kernel the device holds at once (0 if unknown)
+int decode_mfma_resident_groups(int sub, int gq, bool dq);
 hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream);
 size_t decode_lds_bytes(int sub, int gh, int split_tokens, int R);
 constexpr int kMaxSplits = 1024;  // partials one combine can merge

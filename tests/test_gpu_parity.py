@@ -252,6 +252,35 @@ def test_decode_same_cache_and_end_to_end(oracle_codebooks, bits, R, B, Hq, Hkv,
     check_attention(o, ref)
 
 
+@pytest.mark.parametrize("bits,Hq,Hkv", [(2, 8, 2), (1, 8, 2), (2, 4, 2)])
+def test_decode_late_maxima(oracle_codebooks, bits, Hq, Hkv):
+    """Tokens far into each split whose keys point along one query head, with
+    growing norms: that head's running maximum has to move several times after
+    the first chunk, and the accumulated values be rescaled each time."""
+    cb = oracle_codebooks[bits]
+    R, B, L = 128, 1, 1700
+    k, v = _kv(470 + bits, B, Hkv, L)
+    q = synth.queries(470 + bits, 0, B, Hq, D)
+    G = Hq // Hkv
+    for hk in range(Hkv):
+        d = q[0, hk * G].float()
+        d = d / d.norm()
+        for i, t in enumerate((300, 700, 1100, 1450)):
+            k[0, hk, t] = (d * (4.0 * 2 ** i) * k[0, hk, t].float().norm()).half()
+    ek, ev = oracle_encode_pair(k, v, R, cb)
+    ref = _decode_ref(q, ek, ev, cb, R)
+    p = nsnq.params(bits, R)
+    cbt = cb_tensor(cb)
+    cache = nsnq.KVCache(p, B, Hkv, capacity(L, R), DEV)
+    upload_half(cache, 0, ek)
+    upload_half(cache, 1, ev)
+    cache.n_quant, cache.n_resid = ek["n_quant"], ek["n_resid"]
+    qd = q.to(DEV)
+    for ns in (0, 1, 2, 5):
+        o = nsnq.nsnq_decode_attention(p, cbt, qd, cache, num_splits=ns).float().cpu().numpy()
+        check_attention(o, ref)
+
+
 def test_flush_then_decode(oracle_codebooks):
     """Prefill leaves a full window; the next token flushes it, is appended,
     and attention covers all tokens."""
