@@ -104,7 +104,9 @@ struct MfmaSmem {
   static constexpr int qr = qf + GQ * kDim;              // [GQ][128] H D q / sqrt(d)
   static constexpr int qmu = qr + GQ * kDim;             // [kMaxSplitBlocks][GQ] q . KMU_b
   static constexpr int kmu = qmu + kMaxSplitBlocks * GQ;  // [kMaxSplitBlocks][128] fp32 K block means
-  static constexpr int VSTW = kMChunk * S / 4 + 4 * kMChunk;  // per wave: V codes, 4 per-token factors
+  // per wave: V codes and 4 per-token factors, or (up to 4 heads) two sets
+  // of V codes and fp16 weights
+  static constexpr int VSTW = GQ <= 4 ? 2 * (kMChunk * S / 4 + 4 * kMChunk) : kMChunk * S / 4 + 4 * kMChunk;
   static constexpr int vst = kmu + kMaxSplitBlocks * kDim;
   static constexpr int main_end = vst + 4 * VSTW;
   // merge of the four waves
@@ -371,12 +373,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
   if constexpr (T4) {
     // ---- one token per lane ----------------------------------------------
-    // sacc row r, lane t: (H D q_r / sqrt d) . codewords of token t, summed
-    // over 32 slices of 4 channels (two 8-channel codewords' halves at 1 bit).
-    // The running reference mr of each head moves only when a score exceeds
-    // it by more than 2^3 (then to the exact maximum), so the cross-lane
-    // maximum and the rescale are rare; p <= 8 and p VC / 8 in fp16 keeps
-    // the range of p VC with p <= 1.
+    // Scores: row r, lane t of (sh + sl) is (H D q_r / sqrt d) . codewords
+    // of token t, summed over 32 slices of 4 channels (two 8-channel
+    // codewords' halves at 1 bit).  The running reference mr of each head
+    // moves only when a score exceeds it by more than 2^3 (then to the exact
+    // maximum), so the cross-lane maximum and the rescale are rare; p <= 8,
+    // and p VC / 8 in fp16 keeps the range of p VC with p <= 1.
+    // The loop is software-pipelined: a chunk is scored while the value
+    // products of the chunk before it run, from a second set of buffers.
     constexpr float kLazy = 3.f;
     float mr[GQ], lp[GQ];
 #pragma unroll
@@ -384,58 +388,76 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       mr[r] = -INFINITY;
       lp[r] = 0.f;
     }
-    // p VC / 8 (columns 0..3) and p VD / 8 (columns 4..7) of the chunk's
-    // tokens, fp16 [8][64], in the per-token factor area
-    uint16_t* pb = reinterpret_cast<uint16_t*>(fka);
-    const uint32_t pb_lds = (uint32_t)(reinterpret_cast<uintptr_t>(fka) - reinterpret_cast<uintptr_t>(smem));
+    // per-wave buffer pair: V codes [64][S] of a chunk, then p VC / 8
+    // (columns 0..3) and p VD / 8 (columns 4..7) of its tokens, fp16 [8][64]
+    constexpr int kBufB = kMChunk * S + 8 * kMChunk * 2;
+    uint8_t* const vbase = reinterpret_cast<uint8_t*>(vst);
+    const uint32_t vbase_lds = (uint32_t)(reinterpret_cast<uintptr_t>(vst) - reinterpret_cast<uintptr_t>(smem));
     // A of the beta product: row 0 all ones
     half8_t aone;
 #pragma unroll
     for (int e = 0; e < 8; ++e) aone[e] = (half_t)(m16 == 0 ? 1.f : 0.f);
 
-    for (; ch < nchunk; ch += 4) {
-      Ld nxt;
-      if (ch + 4 < nchunk) load(ch + 4, nxt);
+    float4_t sh, sl;
+    float kas, ka, vc8, vd8;
+    // stage chunk `c`'s V codes in buffer `bs`, score its tokens
+    auto front = [&](const Ld& c, int bs) {
+      uint8_t* vb = vbase + bs * kBufB;
 #pragma unroll
-      for (int i = 0; i < S / 16; ++i) *reinterpret_cast<uint4_t*>(vcl + lane * S + 16 * i) = cur.vcode[i];
+      for (int i = 0; i < S / 16; ++i) *reinterpret_cast<uint4_t*>(vb + lane * S + 16 * i) = c.vcode[i];
       float kn1, kn2, vn1, vn2;
       if constexpr (DQ) {
-        kn1 = dq_value(cur.kpar, cur.ksc >> 16);
-        kn2 = h2f(cur.ksc & 0xffff);
-        vn1 = dq_value(cur.vpar, cur.vsc >> 16);
-        vn2 = h2f(cur.vsc & 0xffff);
+        kn1 = dq_value(c.kpar, c.ksc >> 16);
+        kn2 = h2f(c.ksc & 0xffff);
+        vn1 = dq_value(c.vpar, c.vsc >> 16);
+        vn2 = h2f(c.vsc & 0xffff);
       } else {
-        kn1 = h2f(cur.ksc & 0xffff);
-        kn2 = h2f(cur.ksc >> 16);
-        vn1 = h2f(cur.vsc & 0xffff);
-        vn2 = h2f(cur.vsc >> 16);
+        kn1 = h2f(c.ksc & 0xffff);
+        kn2 = h2f(c.ksc >> 16);
+        vn1 = h2f(c.vsc & 0xffff);
+        vn2 = h2f(c.vsc >> 16);
       }
-      const float kas = a.scale_log2 * kn1, ka = kas * kn2;
-      const float vd8 = 0.125f * vn1, vc8 = vd8 * vn2;
-
-      float4_t sh = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
+      kas = a.scale_log2 * kn1;
+      ka = kas * kn2;
+      vd8 = 0.125f * vn1;
+      vc8 = vd8 * vn2;
+      sh = float4_t{0.f, 0.f, 0.f, 0.f};
+      sl = float4_t{0.f, 0.f, 0.f, 0.f};
       if constexpr (SUB == 4) {
-        static_for<32>([&](auto kk_) {
-          constexpr int kk = decltype(kk_)::value;
-          const u32x2_t c = lds_b64(code_shl<kk & 3, 3>(cur.kc[kk >> 4][(kk >> 2) & 3]));
-          const half4_t B = __builtin_bit_cast(half4_t, c);
-          sh = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[0][kk >> 4], B, sh, 4, kk & 15, 0);
-          sl = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[1][kk >> 4], B, sl, 4, kk & 15, 0);
+        // eight gathers in flight before their products (the scheduler would
+        // otherwise wait for each gather next to its product)
+        static_for<4>([&](auto bt_) {
+          constexpr int bt = decltype(bt_)::value;
+          u32x2_t cw[8];
+          static_for<8>([&](auto i_) {
+            constexpr int kk = 8 * bt + decltype(i_)::value;
+            cw[decltype(i_)::value] = lds_b64(code_shl<kk & 3, 3>(c.kc[kk >> 4][(kk >> 2) & 3]));
+          });
+          __builtin_amdgcn_sched_barrier(0);
+          static_for<8>([&](auto i_) {
+            constexpr int kk = 8 * bt + decltype(i_)::value;
+            const half4_t B = __builtin_bit_cast(half4_t, cw[decltype(i_)::value]);
+            sh = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[0][kk >> 4], B, sh, 4, kk & 15, 0);
+            sl = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[1][kk >> 4], B, sl, 4, kk & 15, 0);
+          });
         });
       } else {
         static_for<16>([&](auto j_) {
           constexpr int j = decltype(j_)::value, kk = 2 * j;
-          const uint4_t c = lds_b128(code_shl<j & 3, 4>(cur.kc[0][j >> 2]));
-          const half4_t B0 = __builtin_bit_cast(half4_t, u32x2_t{c.x, c.y});
-          const half4_t B1 = __builtin_bit_cast(half4_t, u32x2_t{c.z, c.w});
+          const uint4_t cw = lds_b128(code_shl<j & 3, 4>(c.kc[0][j >> 2]));
+          const half4_t B0 = __builtin_bit_cast(half4_t, u32x2_t{cw.x, cw.y});
+          const half4_t B1 = __builtin_bit_cast(half4_t, u32x2_t{cw.z, cw.w});
           sh = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[0][kk >> 4], B0, sh, 4, kk & 15, 0);
           sl = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[1][kk >> 4], B0, sl, 4, kk & 15, 0);
           sh = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[0][kk >> 4], B1, sh, 4, (kk + 1) & 15, 0);
           sl = __builtin_amdgcn_mfma_f32_4x4x4f16(qa[1][kk >> 4], B1, sl, 4, (kk + 1) & 15, 0);
         });
       }
+    };
+    // softmax of the scored chunk `chk`, its weights into buffer `bs`
+    auto weigh = [&](int chk, int bs) {
       // s = KA S + KB (q . KMU_b), in log2 units
-      const int bl = (ch * kMChunk) / a.R;
+      const int bl = (chk * kMChunk) / a.R;
       float sc[GQ], dl[GQ];
       bool up = false;
 #pragma unroll
@@ -458,6 +480,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) vacc[t] *= as;
       }
+      uint16_t* pb = reinterpret_cast<uint16_t*>(vbase + bs * kBufB + kMChunk * S);
 #pragma unroll
       for (int r = 0; r < GQ; ++r) {
         const float pr = __builtin_amdgcn_exp2f(dl[r]);
@@ -465,20 +488,33 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         pb[r * kMChunk + lane] = f2h(pr * vc8);
         pb[(4 + r) * kMChunk + lane] = f2h(pr * vd8);
       }
-      wave_sync();
-
-      // values: 32-token step c; lane (m16, kb) supplies tokens 32 c + 8 kb + e
+      if (lane == 0) {  // the references are uniform over the wave
+#pragma unroll
+        for (int r = 0; r < GQ; ++r) mc[chk * GQ + r] = mr[r];
+      }
+    };
+    // value products of the weighed chunk `chk` in buffer `bs`; lane
+    // (m16, kb) supplies tokens 32 c + 8 kb + e of step c
+    auto back = [&](int chk, int bs) {
+      const uint8_t* vb = vbase + bs * kBufB;
+      const uint32_t pb_lds = vbase_lds + bs * kBufB + kMChunk * S;
       float4_t db = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const half8_t bw = __builtin_bit_cast(half8_t, lds_b128(pb_lds + 2 * ((m16 & 7) * kMChunk + 32 * c + 8 * kb)));
-        const uint8_t* vrow = vcl + (32 * c + 8 * kb) * S + m16;
+        const uint8_t* vrow = vb + (32 * c + 8 * kb) * S + m16;
         if constexpr (SUB == 4) {
 #pragma unroll
           for (int g2 = 0; g2 < 2; ++g2) {
+            // all eight code bytes, then all eight gathers, then the products
+            uint32_t code[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) code[e] = vrow[e * S + 16 * g2];
+            __builtin_amdgcn_sched_barrier(0);
             u32x2_t cw[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) cw[e] = lds_b64((uint32_t)vrow[e * S + 16 * g2] << 3);
+            for (int e = 0; e < 8; ++e) cw[e] = lds_b64(code[e] << 3);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ep = 0; ep < 4; ++ep) {
               const uint32_t sel = (ep & 1) ? 0x07060302u : 0x05040100u;
@@ -510,15 +546,29 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         db = __builtin_amdgcn_mfma_f32_16x16x32_f16(aone, bw, db, 0, 0, 0);
       }
       // beta_r = sum p VD: row 0, column 4 + r of db (lanes 4 .. 4 + GQ - 1)
-      if (m16 >= 4 && m16 < 4 + GQ && kb == 0) bc[ch * GQ + m16 - 4] = 8.f * db[0];
-      if (lane < GQ) {
-        float mm = mr[0];
-#pragma unroll
-        for (int r = 1; r < GQ; ++r) mm = lane == r ? mr[r] : mm;
-        mc[ch * GQ + lane] = mm;
+      if (m16 >= 4 && m16 < 4 + GQ && kb == 0) bc[chk * GQ + m16 - 4] = 8.f * db[0];
+    };
+
+    if (ch < nchunk) {
+      {
+        Ld nxt;
+        if (ch + 4 < nchunk) load(ch + 4, nxt);
+        front(cur, 0);
+        weigh(ch, 0);
+        cur = nxt;
       }
-      wave_sync();
-      cur = nxt;
+      int chp = ch, bs = 1;
+      for (ch += 4; ch < nchunk; ch += 4) {
+        Ld nxt;
+        if (ch + 4 < nchunk) load(ch + 4, nxt);
+        front(cur, bs);       // score this chunk ...
+        back(chp, bs ^ 1);    // ... while the one before it meets its values
+        weigh(ch, bs);
+        chp = ch;
+        bs ^= 1;
+        cur = nxt;
+      }
+      back(chp, bs ^ 1);
     }
     // lane (m16 < GQ, kb): reference and sum of head m16; the value columns
     // hold p VC / 8
