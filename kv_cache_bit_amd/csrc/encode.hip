@@ -689,17 +689,21 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
       uint32_t vmask;  // 0xffffff00 in a VGPR (opaque so it is not folded into a literal)
       asm("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(0xffffff00u));
       const float16_t zacc = {};
-      auto tile = [&](int t, float16_t& acc0, float16_t& acc1) {
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sA1[o0 * NT + t][lane], B0, zacc, 0, 0, 0);
-        if constexpr (TWO) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sA1[o1 * NT + t][lane], B1, zacc, 0, 0, 0);
-      };
       uint32_t best0 = 0xffffffffu, best1 = 0xffffffffu;
-      // (other waves on the SIMD cover the product latency: no software
-      // pipeline, which keeps the register count under 128)
+      // the next tile's candidate operands are read while this tile's
+      // distances are reduced
+      half8_t a0 = sA1[o0 * NT][lane], a1 = a0;
+      if constexpr (TWO) a1 = sA1[o1 * NT][lane];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         float16_t cur0, cur1;
-        tile(t, cur0, cur1);
+        cur0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, B0, zacc, 0, 0, 0);
+        if constexpr (TWO) cur1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, B1, zacc, 0, 0, 0);
+        if (t + 1 < NT) {
+          a0 = sA1[o0 * NT + t + 1][lane];
+          if constexpr (TWO) a1 = sA1[o1 * NT + t + 1][lane];
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < 16; q += 2) {
           // accumulator q holds list position 32t + 8(q/4) + 4(lane/32) + q%4:
