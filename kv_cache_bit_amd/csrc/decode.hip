@@ -39,10 +39,11 @@ constexpr int kLutStride = 257;  // odd row stride: finish-step reads hit distin
 // one inverse transform, and the split's (m, l, o) partial is written.
 
 constexpr int kChunk = 64;
+constexpr float kLazyMax = 3.f;  // log2 headroom of the running softmax reference
 
 struct DecodeSmem {
   // offsets in floats
-  int qf, qr, cbh, lut, wbuf, total;
+  int qf, qr, cbh, lut, wbuf, qmu, total;
 };
 
 __host__ __device__ constexpr DecodeSmem decode_smem(int sub, int gh, int split_tokens, int R) {
@@ -56,6 +57,7 @@ __host__ __device__ constexpr DecodeSmem decode_smem(int sub, int gh, int split_
   s.cbh = o; o += kCodewords * sub / 2;      // fp16 codebook
   s.lut = o; o += gh * S * kLutStride;       // LUTs; reused for the wave merge
   s.wbuf = o; o += 4 * gh * kChunk;          // per-wave chunk weights
+  s.qmu = o; o += kMaxSplitBlocks * gh;      // q . KMU_b of the split's blocks
   s.total = o;
   return s;
 }
@@ -108,6 +110,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   float* qr = smem + L.qr;
   uint16_t* cbh = reinterpret_cast<uint16_t*>(smem + L.cbh);
   float* lut = smem + L.lut;
+  float* qmus = smem + L.qmu;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x;
@@ -149,9 +152,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
     uint32_t kcw[CW];
     uint32_t ksc, vsc;    // (n1, n2) fp16 pairs, or (q1 << 16 | n2) double-quantised
     uint32_t kpar, vpar;  // double-quantised: the block's (S1, Z1)
-    // block means of channels 2 lane, 2 lane + 1: an fp16 pair, or two fp32
+    // V block mean of channels 2 lane, 2 lane + 1: an fp16 pair, or two fp32
     // read-back values when double-quantised
-    uint32_t km[DQ ? 2 : 1], vm[DQ ? 2 : 1];
+    uint32_t vm[DQ ? 2 : 1];
     uint32_t vcw[8];
   };
   auto load_chunk = [&](int ch, ChunkRegs& r) {
@@ -167,16 +170,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
       r.kpar = dq_s1_params(kr, a.R);
       r.vpar = dq_s1_params(vr, a.R);
       float m0, m1;
-      dq_mu_pair(reinterpret_cast<const uint8_t*>(a.kmu) + (blk0 + bl) * kDqMuRecord, lane, m0, m1);
-      r.km[0] = __float_as_uint(m0);
-      r.km[DQ ? 1 : 0] = __float_as_uint(m1);
       dq_mu_pair(reinterpret_cast<const uint8_t*>(a.vmu) + (blk0 + bl) * kDqMuRecord, lane, m0, m1);
       r.vm[0] = __float_as_uint(m0);
       r.vm[DQ ? 1 : 0] = __float_as_uint(m1);
     } else {
       r.ksc = ks[tl];
       r.vsc = vs[tl];
-      r.km[0] = *reinterpret_cast<const uint32_t*>(kmu + (int64_t)bl * kDim + 2 * lane);
       r.vm[0] = *reinterpret_cast<const uint32_t*>(vmu + (int64_t)bl * kDim + 2 * lane);
     }
 #pragma unroll
@@ -219,18 +218,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
         lut[(g * S + j) * kLutStride + c] = acc;
       }
     }
+    // q . KMU_b: the 16 lanes of a row share block b = tid / 16, each lane
+    // takes 8 channels of every head and the row sums them
+    if ((tid >> 4) < ntok / a.R) {
+      const int bl = tid >> 4, c8 = tid & 15;
+      float mk[8];
+      if constexpr (DQ) {
+        const uint8_t* mr = reinterpret_cast<const uint8_t*>(a.kmu) + (blk0 + bl) * kDqMuRecord;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) dq_mu_pair(mr, 4 * c8 + e / 2, mk[e], mk[e + 1]);
+      } else {
+        const uint4 m8 = *reinterpret_cast<const uint4*>(kmu + (int64_t)bl * kDim + 8 * c8);
+        const uint32_t mw[4] = {m8.x, m8.y, m8.z, m8.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mk[e] = h2f((e & 1) ? (mw[e >> 1] >> 16) : (mw[e >> 1] & 0xffff));
+      }
+#pragma unroll
+      for (int g = 0; g < GH; ++g) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(qf[g * kDim + 8 * c8 + e], mk[e], d);
+        d = group_sum<16>(d);
+        if (c8 == 0) qmus[bl * GH + g] = d;
+      }
+    }
   }
   __syncthreads();
 
   float m[GH], l[GH], acc[GH][16], om0[GH], om1[GH];
-  float q0[GH], q1[GH];
 #pragma unroll
   for (int g = 0; g < GH; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.f;
     om0[g] = om1[g] = 0.f;
-    q0[g] = qf[g * kDim + 2 * lane];
-    q1[g] = qf[g * kDim + 2 * lane + 1];
 #pragma unroll
     for (int c = 0; c < 16; ++c) acc[g][c] = 0.f;
   }
@@ -253,14 +273,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   // one chunk of this wave with its loads in `cur` (the next chunk's loads
   // are already in flight into the other buffer)
   auto chunk_step = [&](int ch, const ChunkRegs& cur) {
-    float kn1, kn2, vn1, vn2, km0, km1, vm0, vm1;
+    float kn1, kn2, vn1, vn2, vm0, vm1;
     if constexpr (DQ) {
       kn1 = dq_value(cur.kpar, cur.ksc >> 16);
       kn2 = h2f(cur.ksc & 0xffff);
       vn1 = dq_value(cur.vpar, cur.vsc >> 16);
       vn2 = h2f(cur.vsc & 0xffff);
-      km0 = __uint_as_float(cur.km[0]);
-      km1 = __uint_as_float(cur.km[DQ ? 1 : 0]);
       vm0 = __uint_as_float(cur.vm[0]);
       vm1 = __uint_as_float(cur.vm[DQ ? 1 : 0]);
     } else {
@@ -268,8 +286,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
       kn2 = h2f(cur.ksc >> 16);
       vn1 = h2f(cur.vsc & 0xffff);
       vn2 = h2f(cur.vsc >> 16);
-      km0 = h2f(cur.km[0] & 0xffff);
-      km1 = h2f(cur.km[0] >> 16);
       vm0 = h2f(cur.vm[0] & 0xffff);
       vm1 = h2f(cur.vm[0] >> 16);
     }
@@ -362,20 +378,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
           s0 += lds_f32(o0 + (((cur.kcw[j >> 2] >> (8 * (j & 3))) & 0xffu) << 2));
           s1 += lds_f32(o1 + (((cur.kcw[(j + 1) >> 2] >> (8 * ((j + 1) & 3))) & 0xffu) << 2));
         }
-        const float qmu = group_sum<kWave>(fmaf(q0[g], km0, q1[g] * km1));
+        const float qmu = qmus[((ch * kChunk) / a.R) * GH + g];
         sv = a.scale_log2 * kn1 * fmaf(kn2, s0 + s1, qmu);
       }
-      // online softmax over the chunk
-      const float mn = fmaxf(m[g], group_max<kWave>(sv));
-      const float alpha = exp2f(m[g] - mn);
-      const float pr = exp2f(sv - mn);
-      m[g] = mn;
-      l[g] = fmaf(l[g], alpha, group_sum<kWave>(pr));
-      const float pn1 = group_sum<kWave>(pr * vn1);
-      om0[g] = fmaf(om0[g], alpha, pn1 * vm0);
-      om1[g] = fmaf(om1[g], alpha, pn1 * vm1);
+      // online softmax over the chunk.  The reference m moves only when a
+      // score exceeds it by more than 2^3 (then to the exact maximum), so the
+      // cross-lane maximum and the rescale are rare; l is a per-lane partial.
+      float dl = sv - m[g];
+      if (__builtin_amdgcn_ballot_w64(dl > kLazyMax)) {
+        const float mn = fmaxf(m[g], group_max<kWave>(sv));
+        const float alpha = exp2f(m[g] - mn);
+        m[g] = mn;
+        l[g] *= alpha;
+        om0[g] *= alpha;
+        om1[g] *= alpha;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) acc[g][c] *= alpha;
+        for (int c = 0; c < 16; ++c) acc[g][c] *= alpha;
+        dl = sv - mn;
+      }
+      const float pr = exp2f(dl);
+      l[g] += pr;
+      const float pn1 = group_sum<kWave>(pr * vn1);
+      om0[g] = fmaf(pn1, vm0, om0[g]);
+      om1[g] = fmaf(pn1, vm1, om1[g]);
       wb[g * kChunk + lane] = pr * vn1 * vn2;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -429,6 +454,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
     }
   }
 
+  // the per-lane sums of p
+#pragma unroll
+  for (int g = 0; g < GH; ++g) l[g] = group_sum<kWave>(l[g]);
   // token-group reduction inside the wave (lane bits 3..5)
 #pragma unroll
   for (int g = 0; g < GH; ++g)
