@@ -297,17 +297,28 @@ def copy_calibration(nbytes: int, reps: int):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def encode_traffic(kernel_file: str):
-    """HBM bytes per encode launch from the committed rocprofv3 counter
-    summary, or None when the kernel source has changed since it was taken."""
+ENCODE_SOURCES = ("encode.hip", "nsnq_device.hpp", "nsnq_launch.hpp")  # what the encode kernel compiles from
+
+
+def sources_sha256(names) -> str:
+    """sha256 over the named files of the kernel source folder, in order."""
     import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(ROOT, "kv_cache_bit_amd", "csrc", n), "rb").read())
+    return h.hexdigest()
+
+
+def encode_traffic():
+    """HBM bytes per encode launch from the committed rocprofv3 counter
+    summary, or None when the kernel's sources have changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "encode_kernel_llama2-7b-layer-b1-2bit_traffic.json")
     try:
         rec = json.load(open(path))
-        src = open(kernel_file, "rb").read()
+        sha = sources_sha256(ENCODE_SOURCES)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("sources") != list(ENCODE_SOURCES) or rec.get("sources_sha256") != sha:
         return None
     return rec.get("bytes_per_launch")
 
@@ -510,7 +521,7 @@ def main():
                                 else f"encode_kernel<{s}, {R}, false, 0, false>"),
                      "bound": "alu", "achieved": enc_alu_tops,
                      "peak": VALU_PEAK_TOPS, "unit": "Tops/s", "frac": enc_alu_tops / VALU_PEAK_TOPS,
-                     "traffic": encode_traffic(os.path.join(ROOT, "kv_cache_bit_amd", "csrc", "encode.hip")),
+                     "traffic": encode_traffic(),
                      "note": ("achieved = algorithmic argmin candidates per second: the nearest of 256 "
                               "codewords per sub-vector (8192 per vector at 2 bits), one 32-bit compare "
                               "each; the candidate-list search compares " + str(search_cols) +
