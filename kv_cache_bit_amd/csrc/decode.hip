@@ -514,49 +514,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   }
 }
 
-// out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.  The (m_i, l_i) pairs
-// go through LDS so every load is issued before any is consumed.
-
+// out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, one group of 128
+// lanes (channels) per (batch row, query head).  Every lane reads the splits'
+// (m_i, l_i) itself (the same addresses for the whole group) and its channel
+// of o_i, 32 splits at a time with all loads of a batch in flight together;
+// the running maximum rescales the sums between batches.
 __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
-  __shared__ float ml[2 * kMaxSplits];
-  __shared__ float red[2];
+  constexpr int kBatch = 32;
   const int bh = blockIdx.x;
   const int c = threadIdx.x;
   const float* w = a.ws + (int64_t)bh * a.nsplit * (kDim + 2);
-  float M = -INFINITY;
-  for (int i = c; i < a.nsplit; i += 128) {
-    const float mi = w[i * (kDim + 2) + kDim];
-    ml[2 * i] = mi;
-    ml[2 * i + 1] = w[i * (kDim + 2) + kDim + 1];
-    M = fmaxf(M, mi);
-  }
-  M = group_max<kWave>(M);
-  if ((c & 63) == 0) red[c >> 6] = M;
-  __syncthreads();
-  M = fmaxf(red[0], red[1]);
-  if (M == -INFINITY) {  // a row without tokens (ragged cache): zero output
-    a.out[(int64_t)bh * kDim + c] = 0;
-    return;
-  }
-  float num = 0.f, den = 0.f;
-  int i = 0;
-  for (; i + 8 <= a.nsplit; i += 8) {
-    float o[8];
+  float M = -INFINITY, num = 0.f, den = 0.f;
+  for (int i0 = 0; i0 < a.nsplit; i0 += kBatch) {
+    const int n = min(kBatch, a.nsplit - i0);
+    float mi[kBatch], li[kBatch], oi[kBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) o[u] = w[(i + u) * (kDim + 2) + c];
+    for (int u = 0; u < kBatch; ++u) {
+      const float* r = w + (int64_t)(i0 + u) * (kDim + 2);
+      mi[u] = u < n ? r[kDim] : -INFINITY;
+      li[u] = u < n ? r[kDim + 1] : 0.f;
+      oi[u] = u < n ? r[c] : 0.f;
+    }
+    float Mb = M;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float f = exp2f(ml[2 * (i + u)] - M);
-      num = fmaf(f, o[u], num);
-      den = fmaf(f, ml[2 * (i + u) + 1], den);
+    for (int u = 0; u < kBatch; ++u) Mb = fmaxf(Mb, mi[u]);
+    if (Mb == -INFINITY) continue;  // no tokens so far
+    const float sc = exp2f(M - Mb);  // 0 while M is -inf
+    num *= sc;
+    den *= sc;
+    M = Mb;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float f = exp2f(mi[u] - M);
+      num = fmaf(f, oi[u], num);
+      den = fmaf(f, li[u], den);
     }
   }
-  for (; i < a.nsplit; ++i) {
-    const float f = exp2f(ml[2 * i] - M);
-    num = fmaf(f, w[i * (kDim + 2) + c], num);
-    den = fmaf(f, ml[2 * i + 1], den);
-  }
-  a.out[(int64_t)bh * kDim + c] = f2h(num / den);
+  // a row without tokens (ragged cache): zero output
+  a.out[(int64_t)bh * kDim + c] = M == -INFINITY ? (uint16_t)0 : f2h(num / den);
 }
 
 template <int SUB, int GH, bool DQ, bool ROPE>
