@@ -465,10 +465,12 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
     const float inv2 = live ? rs2 : 0.f;
     n2 = ss * inv2;
 #pragma unroll
-    for (int e = 0; e < SUB; ++e) u[e] *= inv2 * sgn[e];
+    for (int e = 0; e < SUB; ++e) u[e] *= sgn[e];
+    // the transform is linear: the 1 / n2 scale goes after it, with 1 / sqrt(d)
     fwht128<SUB>(u, lane);
+    const float sc = inv2 * kInvSqrtD;
 #pragma unroll
-    for (int e = 0; e < SUB; ++e) u[e] *= kInvSqrtD;
+    for (int e = 0; e < SUB; ++e) u[e] *= sc;
   };
   // hi/lo fp16 split of u and the squared norm of this lane's sub-vector
   auto split = [&](const float (&u)[SUB], half_t (&hi)[SUB], half_t (&lo)[SUB], half_t& uu_hi, half_t& uu_lo,
@@ -690,20 +692,28 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
       asm("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(0xffffff00u));
       const float16_t zacc = {};
       uint32_t best0 = 0xffffffffu, best1 = 0xffffffffu;
-      // the next tile's candidate operands are read while this tile's
-      // distances are reduced
+      // where the registers allow (128 per lane for 4 waves per SIMD), the
+      // next tile's candidate operands are read while this tile's distances
+      // are reduced
+      constexpr bool kPrefetchA = !DQ && (HALF || NT == 2);
       half8_t a0 = sA1[o0 * NT][lane], a1 = a0;
       if constexpr (TWO) a1 = sA1[o1 * NT][lane];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
+        if (!kPrefetchA && t > 0) {
+          a0 = sA1[o0 * NT + t][lane];
+          if constexpr (TWO) a1 = sA1[o1 * NT + t][lane];
+        }
         float16_t cur0, cur1;
         cur0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, B0, zacc, 0, 0, 0);
         if constexpr (TWO) cur1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, B1, zacc, 0, 0, 0);
-        if (t + 1 < NT) {
-          a0 = sA1[o0 * NT + t + 1][lane];
-          if constexpr (TWO) a1 = sA1[o1 * NT + t + 1][lane];
+        if constexpr (kPrefetchA) {
+          if (t + 1 < NT) {
+            a0 = sA1[o0 * NT + t + 1][lane];
+            if constexpr (TWO) a1 = sA1[o1 * NT + t + 1][lane];
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < 16; q += 2) {
           // accumulator q holds list position 32t + 8(q/4) + 4(lane/32) + q%4:

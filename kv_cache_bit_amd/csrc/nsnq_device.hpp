@@ -44,12 +44,12 @@ __device__ __forceinline__ float xlane(float v) {
 __device__ __forceinline__ float xshfl(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
 // All-reduce over the WIDTH lanes that share lane / WIDTH (WIDTH a power of
-// two), on the VALU alone: the two quad exchanges, then the half-row and row
-// mirrors (lane 7 - i and 15 - i within the group, which pair each reduced
-// quad / half-row with the other one) by DPP, then the gfx950 row-pair swaps.
-// A swap of a value with itself may be given one register for both operands
-// (then both results hold the partner's value) or two (then one holds the
-// lane's own value): the partner is taken by lane position, as in xlane<32>.
+// two).  Within a row of 16 lanes: the two quad exchanges, then the half-row
+// and row mirrors (lane 7 - i and 15 - i, which pair each reduced quad /
+// half-row with the other one), all by DPP folded into the operation.  Across
+// rows: the LDS-crossbar swizzle for the odd/even row pair (one VALU op fewer
+// than the row swap, which needs two copies of its operand and a select) and
+// the half-wave swap of xlane<32>.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
@@ -60,17 +60,8 @@ __device__ __forceinline__ float group_reduce(float v, Op op) {
   if constexpr (WIDTH >= 4) v = op(v, dpp_f<0x4E>(v));   // quad_perm 2,3,0,1
   if constexpr (WIDTH >= 8) v = op(v, dpp_f<0x141>(v));  // row_half_mirror
   if constexpr (WIDTH >= 16) v = op(v, dpp_f<0x140>(v)); // row_mirror
-  if constexpr (WIDTH >= 32) {
-    const unsigned lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
-                                                    false, false);
-    v = op(v, __builtin_bit_cast(float, (lane & 16) ? r[0] : r[1]));
-    if constexpr (WIDTH >= 64) {
-      const auto q = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
-                                                      false, false);
-      v = op(v, __builtin_bit_cast(float, lane < 32 ? q[1] : q[0]));
-    }
-  }
+  if constexpr (WIDTH >= 32) v = op(v, xlane<16>(v));
+  if constexpr (WIDTH >= 64) v = op(v, xlane<32>(v));
   return v;
 }
 struct AddOp {
