@@ -7,22 +7,24 @@
 //   sum_t p_t v_hat_t = D H^T sum_t (p_t N1_t N2_t) c_hat_t + sum_b (sum_{t in b} p_t N1_t) MU_b.
 // Here the Hadamard-domain codewords c_hat_t are gathered once per token and
 // shared by every query head of the KV head, instead of one table lookup per
-// (token, slot, head):
-//   scores  S[t][g] = sum_c c_hat_t[c] q'_g[c]: v_mfma_f32_16x16x32_f16 over
-//           16-token x 16-head tiles; the A operand of a lane is the codeword
-//           pair (2 bits) or the codeword (1 bit) of its token read straight
-//           from the fp16 codebook in LDS; q' = H D q is split into fp16 high
-//           and low parts (two products), so the scores keep fp32 accuracy;
-//   values  O'[c][g] += sum_t c_hat_t[c] w_t[g] with w = p N1 N2 in fp16.  The
-//           contraction runs over tokens, so a lane gathers the codewords of
-//           its 8 tokens for one slot and transposes them in registers
-//           (v_perm_b32) into one A operand per channel of the slot.  The
-//           token order inside a 32-token step is the one the score tiles
-//           leave in the lanes, so the B operand (the weights) needs no
-//           exchange between lanes;
-//   means   per 64-token chunk, beta = sum_t p_t N1_t and the running max are
-//           kept in LDS and folded in once at the end of the split.
-// Up to 16 query heads share a work-group, one MFMA column each.
+// (token, slot, head).  The codewords are read straight from the fp16
+// codebook in LDS; q' = H D q is split into fp16 high and low parts (two
+// products), so the scores keep fp32 accuracy.
+//   scores, up to 4 heads: one token per lane.  v_mfma_f32_4x4x4_16b_f16 with
+//           the lane's codeword (4 channels) as the B operand and q' broadcast
+//           from one of 16 A blocks (CBSZ / ABID), so every lane ends with its
+//           token's score for each head;
+//   scores, 8 or 16 heads: v_mfma_f32_16x16x32_f16 over 16-token x 16-head
+//           tiles, the A operand of a lane being the codeword pair (2 bits) or
+//           codeword (1 bit) of its token;
+//   values  O'[c][g] += sum_t c_hat_t[c] w_t[g] with w = p N1 N2 in fp16,
+//           v_mfma_f32_16x16x32_f16 contracting over tokens: a lane gathers
+//           the codewords of its 8 tokens for one slot and transposes them in
+//           registers (v_perm_b32) into one A operand per channel of the slot;
+//   means   per 64-token chunk, beta = sum_t p_t N1_t and the softmax
+//           reference are kept in LDS and folded in once at the end of the
+//           split.
+// Up to 16 query heads share a work-group.
 
 #include <type_traits>
 #include <utility>
@@ -318,8 +320,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  // B operands of the score products: lane (head m16, k-block kb), MFMA i
-  // holds channels 32 kb + 8 i .. + 7 of q', as fp16 high and low parts.
+  // the rotated queries q' as score-product operands, in fp16 high and low parts
   half8_t bqh[4], bql[4];
   half4_t qa[2][2];  // [fp16 high, low part][k-slice half]
   if constexpr (T4) {
@@ -340,6 +341,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       }
     }
   } else {
+    // B operands: lane (head m16, k-block kb), product i holds channels
+    // 32 kb + 8 i .. + 7 of q'
     const float4* qrow = reinterpret_cast<const float4*>(qr + (m16 < GQ ? m16 : 0) * kDim + 32 * kb);
     const float on = m16 < GQ ? 1.f : 0.f;
 #pragma unroll
@@ -356,9 +359,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
+  // the wave's staging area; 8 or more heads: V codes [64][S], then the
+  // per-token factors s = KA S + KB (q . KMU), w = p VC, beta += p VD
   float* vst = smem + L::vst + wave * L::VSTW;
-  uint8_t* vcl = reinterpret_cast<uint8_t*>(vst);  // [64][S] V codes
-  // per-token factors: s = KA S + KB (q . KMU), w = p VC, beta += p VD
+  uint8_t* vcl = reinterpret_cast<uint8_t*>(vst);
   float* fka = vst + kMChunk * S / 4;
   float* fkb = fka + kMChunk;
   float* fvc = fkb + kMChunk;
