@@ -556,13 +556,9 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
 
 template <int SUB, int GH, bool DQ, bool ROPE>
 static hipError_t launch_decode_dq(const DecodeArgs& a, int B, size_t lds, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_split_kernel<SUB, GH, DQ, ROPE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool lds_set[kMaxDevices] = {};
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(&decode_split_kernel<SUB, GH, DQ, ROPE>), lds_set);
+  if (e != hipSuccess) return e;
   dim3 grid(a.nsplit, B * a.Hkv * (a.G / GH)), block(256);
   hipLaunchKernelGGL((decode_split_kernel<SUB, GH, DQ, ROPE>), grid, block, lds, stream, a);
   return hipGetLastError();
@@ -696,13 +692,9 @@ __global__ __launch_bounds__(256) void fp16_decode_kernel(Fp16DecodeArgs a) {
 
 template <int G>
 static hipError_t launch_fp16_t(const Fp16DecodeArgs& a, int B, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fp16_decode_kernel<G>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool lds_set[kMaxDevices] = {};
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(&fp16_decode_kernel<G>), lds_set);
+  if (e != hipSuccess) return e;
   const size_t lds = fp16_decode_lds_bytes(G, a.split_tokens);
   hipLaunchKernelGGL((fp16_decode_kernel<G>), dim3(a.nsplit, B * a.Hkv), dim3(256), lds, stream, a);
   return hipGetLastError();

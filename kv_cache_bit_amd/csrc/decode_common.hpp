@@ -10,6 +10,23 @@ namespace nsnq {
 // Blocks of R tokens one split may span.
 constexpr int kMaxSplitBlocks = 16;
 
+// Lets `kernel` use up to 160 KB of dynamic LDS, once per device of the
+// process (the attribute is per device); `set` is the caller's per-kernel
+// record of the devices done.
+constexpr int kMaxDevices = 64;
+inline hipError_t allow_lds(const void* kernel, bool (&set)[kMaxDevices]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!set[dev]) {
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    set[dev] = true;
+  }
+  return hipSuccess;
+}
+
 // Block-wide reduction of GH values per thread (max or sum); red is 4*GH floats.
 template <int GH, bool MAX>
 __device__ __forceinline__ void block_reduce(float (&v)[GH], float* red, int lane, int wave) {

@@ -858,13 +858,9 @@ int decode_mfma_resident_groups(int sub, int gq, bool dq) {
 template <int SUB, int GQ, bool DQ>
 static hipError_t launch_mfma_dq(const DecodeArgs& a, int B, hipStream_t stream) {
   const size_t lds = (size_t)MfmaSmem<SUB, GQ>::total * sizeof(float);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<SUB, GQ, DQ>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool lds_set[kMaxDevices] = {};
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(&decode_mfma_kernel<SUB, GQ, DQ>), lds_set);
+  if (e != hipSuccess) return e;
   dim3 grid(a.nsplit, B * a.Hkv * (a.G / GQ)), block(256);
   hipLaunchKernelGGL((decode_mfma_kernel<SUB, GQ, DQ>), grid, block, lds, stream, a);
   return hipGetLastError();
