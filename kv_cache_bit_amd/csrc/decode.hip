@@ -43,7 +43,7 @@ constexpr float kLazyMax = 3.f;  // log2 headroom of the running softmax referen
 
 struct DecodeSmem {
   // offsets in floats
-  int qf, qr, cbh, lut, wbuf, qmu, total;
+  int qf, qr, cbh, lut, wbuf, qmu, vst, total;
 };
 
 __host__ __device__ constexpr DecodeSmem decode_smem(int sub, int gh, int split_tokens, int R) {
@@ -58,6 +58,7 @@ __host__ __device__ constexpr DecodeSmem decode_smem(int sub, int gh, int split_
   s.lut = o; o += gh * S * kLutStride;       // LUTs; reused for the wave merge
   s.wbuf = o; o += 4 * gh * kChunk;          // per-wave chunk weights
   s.qmu = o; o += kMaxSplitBlocks * gh;      // q . KMU_b of the split's blocks
+  s.vst = o; o += (sub == 8 && gh == 1) ? 4 * kChunk * 16 / 4 : 0;  // per-wave V codes [64][16] (matrix-core values)
   s.total = o;
   return s;
 }
@@ -79,6 +80,9 @@ int decode_max_split_tokens(int sub, int gh, int R) {
 __device__ __forceinline__ float lds_f32(uint32_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) float*>(static_cast<size_t>(addr));
 }
+__device__ __forceinline__ uint4_t lds_u32x4(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) uint4_t*>(static_cast<size_t>(addr));
+}
 typedef uint32_t lds_u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 lds_u32x2(uint32_t addr) {
   const lds_u32x2_t v = *reinterpret_cast<const __attribute__((address_space(3))) lds_u32x2_t*>(static_cast<size_t>(addr));
@@ -98,8 +102,10 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&cw)[S / 
 // at 2 bits (two chunk buffers in turn) and 5 at 1 bit (one buffer, copied),
 // without spilling; the wider variants keep the compiler's choice.
 template <int SUB, int GH, bool DQ, bool ROPE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && !ROPE ? (SUB == 8 ? 5 : 4) : 1))) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && !ROPE ? 4 : 1))) void decode_split_kernel(DecodeArgs a) {
   constexpr bool kPingPong = SUB == 4;
+  // one head at 1 bit: the value sum on the matrix cores (see the values below)
+  constexpr bool kMV = SUB == 8 && GH == 1 && !ROPE;
   constexpr int S = kDim / SUB;
   constexpr int CW = S / 4;      // 32-bit words of codes per token
   constexpr int SPT = 16 / SUB;  // value slots per lane
@@ -178,11 +184,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
       r.vsc = vs[tl];
       r.vm[0] = *reinterpret_cast<const uint32_t*>(vmu + (int64_t)bl * kDim + 2 * lane);
     }
+    if constexpr (kMV) {
+      // the V code row of token `lane` (16 bytes), staged in LDS per chunk
+      const uint4 v4 = *reinterpret_cast<const uint4*>(vc + (int64_t)tl * S);
+      r.vcw[0] = v4.x; r.vcw[1] = v4.y; r.vcw[2] = v4.z; r.vcw[3] = v4.w;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint8_t* p = vc + (int64_t)(ch * kChunk + 8 * tg + i) * S + sq * SPT;
-      if constexpr (SPT == 4) r.vcw[i] = *reinterpret_cast<const uint32_t*>(p);
-      else r.vcw[i] = *reinterpret_cast<const uint16_t*>(p);
+      for (int i = 0; i < 8; ++i) {
+        const uint8_t* p = vc + (int64_t)(ch * kChunk + 8 * tg + i) * S + sq * SPT;
+        if constexpr (SPT == 4) r.vcw[i] = *reinterpret_cast<const uint32_t*>(p);
+        else r.vcw[i] = *reinterpret_cast<const uint16_t*>(p);
+      }
     }
   };
   ChunkRegs cur;
@@ -255,6 +267,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
     for (int c = 0; c < 16; ++c) acc[g][c] = 0.f;
   }
   float* wb = smem + L.wbuf + wave * GH * kChunk;
+  // matrix-core values: tile e, row = slot, column 0 = sum_t (p N1 N2 / 8)_t
+  // c_hat_t[8 slot + e] over the split's tokens (the other columns repeat it)
+  float4_t vacc[kMV ? 8 : 1];
+#pragma unroll
+  for (int t = 0; t < (kMV ? 8 : 1); ++t) vacc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+  uint8_t* const vstw = reinterpret_cast<uint8_t*>(smem + L.vst) + wave * kChunk * 16;
+  const uint32_t vst_lds = (uint32_t)(reinterpret_cast<uintptr_t>(vstw) - reinterpret_cast<uintptr_t>(smem));
+  const uint32_t wb_lds = (uint32_t)(reinterpret_cast<uintptr_t>(wb) - reinterpret_cast<uintptr_t>(smem));
+  const int m16 = lane & 15, kb = lane >> 4;
   // keys stored before RoPE: lane (token group tt, j) dequantises channels
   // 8 j .. 8 j + 7 of token 4 pass + tt, rotates them and dots them with the
   // queries; the per-token dot products go through LDS (the LUT space)
@@ -273,6 +294,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   // one chunk of this wave with its loads in `cur` (the next chunk's loads
   // are already in flight into the other buffer)
   auto chunk_step = [&](int ch, const ChunkRegs& cur) {
+    if constexpr (kMV)
+      *reinterpret_cast<uint4_t*>(vstw + lane * 16) = uint4_t{cur.vcw[0], cur.vcw[1], cur.vcw[2], cur.vcw[3]};
     float kn1, kn2, vn1, vn2, vm0, vm1;
     if constexpr (DQ) {
       kn1 = dq_value(cur.kpar, cur.ksc >> 16);
@@ -392,8 +415,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
         l[g] *= alpha;
         om0[g] *= alpha;
         om1[g] *= alpha;
+        if constexpr (kMV) {
 #pragma unroll
-        for (int c = 0; c < 16; ++c) acc[g][c] *= alpha;
+          for (int t = 0; t < 8; ++t) vacc[t] *= alpha;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 16; ++c) acc[g][c] *= alpha;
+        }
         dl = sv - mn;
       }
       const float pr = exp2f(dl);
@@ -401,11 +429,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
       const float pn1 = group_sum<kWave>(pr * vn1);
       om0[g] = fmaf(pn1, vm0, om0[g]);
       om1[g] = fmaf(pn1, vm1, om1[g]);
-      wb[g * kChunk + lane] = pr * vn1 * vn2;
+      if constexpr (kMV) {
+        // fp16 p N1 N2 / 8: p <= 8 keeps the range of the p <= 1 weights
+        reinterpret_cast<uint16_t*>(wb)[lane] = f2h(pr * vn1 * vn2 * 0.125f);
+      } else {
+        wb[g * kChunk + lane] = pr * vn1 * vn2;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (kMV) {
+      // values on the matrix cores, 32-token step c: lane (slot m16, kb)
+      // supplies tokens 32 c + 8 kb + e; its 8 codewords, transposed with
+      // v_perm_b32, give the A operand of each channel e of the slot
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const half8_t bw = __builtin_bit_cast(half8_t, lds_u32x4(wb_lds + 2 * (32 * c + 8 * kb)));
+        const uint8_t* vrow = vstw + (32 * c + 8 * kb) * 16 + m16;
+        uint32_t code[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) code[e] = vrow[e * 16];
+        __builtin_amdgcn_sched_barrier(0);
+        uint4_t cw[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cw[e] = lds_u32x4((code[e] << 4) + 4u * kL.cbh);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ep = 0; ep < 8; ++ep) {
+          const uint32_t sel = (ep & 1) ? 0x07060302u : 0x05040100u;
+          uint32_t d[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) d[jj] = __builtin_amdgcn_perm(cw[2 * jj + 1][ep >> 1], cw[2 * jj][ep >> 1], sel);
+          const half8_t A = __builtin_bit_cast(half8_t, uint4_t{d[0], d[1], d[2], d[3]});
+          vacc[ep] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bw, vacc[ep], 0, 0, 0);
+        }
+      }
+    } else {
     // values: tokens 8 tg .. 8 tg + 7 of the chunk, this lane's 16 channels
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -430,6 +490,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
           }
         }
       }
+    }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -459,7 +520,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   for (int g = 0; g < GH; ++g) l[g] = group_sum<kWave>(l[g]);
   // token-group reduction inside the wave (lane bits 3..5)
 #pragma unroll
-  for (int g = 0; g < GH; ++g)
+  for (int g = 0; g < (kMV ? 0 : GH); ++g)
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       float v = acc[g][c];
@@ -479,7 +540,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
       r[0] = m[g];
       r[1] = l[g];
     }
-    if (lane < 8) {
+    if constexpr (kMV) {
+      // column 0: lane (0, kb) holds slots 4 kb .. 4 kb + 3 of every tile
+      if (m16 == 0) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) r[2 + 8 * (4 * kb + rr) + t] = 8.f * vacc[t][rr];
+      }
+    } else if (lane < 8) {
 #pragma unroll
       for (int c = 0; c < 16; ++c) r[2 + sq * 16 + c] = acc[g][c];
     }

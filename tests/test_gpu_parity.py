@@ -227,6 +227,7 @@ def _decode_ref(q, ek, ev, cb, R):
     (2, 128, 1, 8, 2, 100),    # G = 4, residual tokens only (no wave has a chunk)
     (1, 64, 2, 4, 2, 50),      # G = 2, residual tokens only
     (1, 64, 1, 16, 4, 333),    # G = 4 at 1 bit: 8-channel codewords as two 4x4x4 slices
+    (1, 128, 2, 3, 3, 700),    # G = 1 at 1 bit: the value sum on the matrix cores
 ])
 def test_decode_same_cache_and_end_to_end(oracle_codebooks, bits, R, B, Hq, Hkv, L):
     cb = oracle_codebooks[bits]
