@@ -341,9 +341,19 @@ def cpu_baseline(w: dict, cb_bits, k, v, q, heads: int):
     t2 = time.perf_counter()
     scale = w["Hkv"] / heads
     step = (t2 - t0) * scale
-    return dict(step_s=step, encode_s=(t1 - t0) * scale, decode_s=(t2 - t1) * scale,
-                cores=oracle.num_threads(), sample=f"{heads} of {w['Hkv']} KV heads x batch {w['B']}, "
-                f"full context; time scaled x{scale:g}")
+    cores = oracle.num_threads()
+    # the same work on one thread, for one KV head
+    oracle.set_num_threads(1)
+    try:
+        t3 = time.perf_counter()
+        e1k, e1v = oracle.encode(kk[:, :1].contiguous(), R, cb_bits), oracle.encode(vv[:, :1].contiguous(), R, cb_bits)
+        oracle.reference_decode(qq[:, :G].contiguous(), e1k, e1v, e1k["n_quant"], e1k["n_resid"], R, cb_bits)
+        step1 = (time.perf_counter() - t3) * w["Hkv"]
+    finally:
+        oracle.set_num_threads(cores)
+    return dict(step_s=step, encode_s=(t1 - t0) * scale, decode_s=(t2 - t1) * scale, cores=cores,
+                sample=f"{heads} of {w['Hkv']} KV heads x batch {w['B']}, full context; time scaled x{scale:g}",
+                step_1t_s=step1, sample_1t=f"1 of {w['Hkv']} KV heads on one thread; time scaled x{w['Hkv']}")
 
 
 def main():
@@ -540,7 +550,9 @@ def main():
         cb_ = cpu_baseline(w, cb_bits, k, v, q, min(args.cpu_heads, Hkv))
         res["cpu_baseline"] = {"value": B * L / cb_["step_s"], "unit": "tokens/s", "cores": cb_["cores"],
                                "kind": "oracle", "sample": cb_["sample"],
-                               "encode_s": cb_["encode_s"], "decode_s": cb_["decode_s"]}
+                               "encode_s": cb_["encode_s"], "decode_s": cb_["decode_s"],
+                               "single_thread": {"value": B * L / cb_["step_1t_s"], "unit": "tokens/s",
+                                                 "cores": 1, "sample": cb_["sample_1t"]}}
     print(json.dumps(res), flush=True)
 
 

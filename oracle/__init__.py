@@ -53,6 +53,7 @@ def lib():
             "orc_attention": (None, [P, i32, i32, i32, i32, P, P, i32, f64, P]),
             "orc_kmeans": (None, [P, i64, i32, i32, i32, P, P, P, P]),
             "orc_num_threads": (i32, []),
+            "orc_set_num_threads": (None, [i32]),
             "orc_rtn4": (None, [P, i32, P, P, P, P, P]),
             "orc_cos_loss_grad": (f64, [P, i64, i32, i32, P, i32, P]),
             "orc_rope": (None, [P, i64, i32, i32, P, P, i32]),
@@ -309,6 +310,11 @@ def finetune(x, centroids, iters: int, lr: float):
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the batched routines from now on (OpenMP)."""
+    lib().orc_set_num_threads(int(n))
 
 
 def rope(k: np.ndarray, cos, sin, pos0: int = 0) -> np.ndarray:

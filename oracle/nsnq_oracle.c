@@ -800,3 +800,12 @@ int orc_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the number of OpenMP threads the batched routines use (n >= 1). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
