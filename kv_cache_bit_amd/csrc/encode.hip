@@ -49,6 +49,72 @@ __device__ __forceinline__ uint32_t make_key(float dist, uint32_t vmask, uint32_
   return (__float_as_uint(dist) & vmask) | idx;
 }
 
+// Walsh-Hadamard transform of the encoder's lane layout: E consecutive
+// channels per lane, 128 / E lanes per token (lane `l` of the token's group).
+// The in-lane stages are the usual butterflies.  Every cross-lane stage is one
+// DPP-fused multiply-add t <- t + c t', with t' the partner lane's value and
+// c = -1 on the lane whose stage bit is set (that lane keeps the negated
+// difference).  The first cross-lane stage pairs lanes l and l ^ 7 (the
+// half-row mirror: DPP has no xor-4 exchange), then l ^ 1, l ^ 2, l ^ 8 and,
+// for E = 4, l ^ 16 through the swizzle.  Composed over GF(2), the stages give
+// the Sylvester transform with lane l holding the channels of slot hslot(l),
+// in order, times hsign(l).
+__device__ __forceinline__ int hslot(int l) { return l ^ ((((l >> 1) ^ l) & 1) << 2); }  // bit 2 ^= bit 0 ^ bit 1
+__device__ __forceinline__ float hsign(int l) {
+  return ((__builtin_popcount(l) + ((l >> 2) & ((l >> 1) ^ l))) & 1) ? -1.f : 1.f;
+}
+// One DPP stage over the lane's E values: x[e] += c * partner(x[e]) as
+// v_fmac_f32_dpp (the compiler keeps a separate DPP move otherwise).  The
+// leading s_nop covers the wait a DPP read needs after a VALU write of its
+// register, which the compiler cannot see inside the block.
+#define NSNQ_HSTAGE4(DPP)                                                                    \
+  asm("s_nop 1\n\t"                                                                          \
+      "v_fmac_f32_dpp %0, %0, %4 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"        \
+      "v_fmac_f32_dpp %1, %1, %4 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"        \
+      "v_fmac_f32_dpp %2, %2, %4 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"        \
+      "v_fmac_f32_dpp %3, %3, %4 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1"              \
+      : "+v"(x[e]), "+v"(x[e + 1]), "+v"(x[e + 2]), "+v"(x[e + 3])                            \
+      : "v"(c))
+template <int BIT, int E>
+__device__ __forceinline__ void hstage(float (&x)[E], int l) {
+  const float c = ((l >> BIT) & 1) ? -1.f : 1.f;
+#pragma unroll
+  for (int e = 0; e < E; e += 4) {
+    if constexpr (BIT == 2) NSNQ_HSTAGE4("row_half_mirror");
+    else if constexpr (BIT == 0) NSNQ_HSTAGE4("quad_perm:[1,0,3,2]");
+    else if constexpr (BIT == 1) NSNQ_HSTAGE4("quad_perm:[2,3,0,1]");
+    else NSNQ_HSTAGE4("row_ror:8");
+  }
+}
+#undef NSNQ_HSTAGE4
+template <int E>
+__device__ __forceinline__ void fwht_lanes(float (&x)[E], int l) {
+  static_assert(E == 4 || E == 8, "4 or 8 channels per lane");
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if ((e & h) == 0) {
+        const float a = x[e], b = x[e + h];
+        x[e] = a + b;
+        x[e + h] = a - b;
+      }
+    }
+  }
+  hstage<2>(x, l);  // row_half_mirror: l ^ 7
+  hstage<0>(x, l);  // quad_perm 1,0,3,2: l ^ 1
+  hstage<1>(x, l);  // quad_perm 2,3,0,1: l ^ 2
+  hstage<3>(x, l);  // row_ror 8: l ^ 8
+  if constexpr (E == 4) {
+    const float c = ((l >> 4) & 1) ? -1.f : 1.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = fmaf(xlane<16>(x[e]), c, x[e]);
+  }
+}
+
+// words 2 and 3 of a token's 8-channel (1-bit) slice; a 4-channel slice has none
+__device__ __forceinline__ uint32_t raw_hi(const uint2&, int) { return 0u; }
+__device__ __forceinline__ uint32_t raw_hi(const uint4& r, int i) { return i ? r.w : r.z; }
 __device__ __forceinline__ uint32_t pack_h2(half_t a, half_t b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
@@ -150,6 +216,7 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int slot = lane % S;
+  const int oslot = hslot(slot);  // the slot this lane holds after the transform
   const int tir = lane / S;
   const int kv = blockIdx.y;
 
@@ -431,30 +498,20 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
 
   // Shift, second normalisation and Hadamard transform of this lane's
   // sub-vector of token `tok`: u (norm sqrt(d) over the token), n1, n2.
+  const float hscale = kInvSqrtD * hsign(slot);
   auto transform = [&](int tok, const raw_t& raw, float (&u)[SUB], float& n1, float& n2) {
     if constexpr (DQ) {
       n1 = n1hs[tok];
-      const float inv = n1 > 0.f ? 1.f / n1 : 0.f;
-      u[0] = h2f(raw.x & 0xffff) * inv; u[1] = h2f(raw.x >> 16) * inv;
-      u[2] = h2f(raw.y & 0xffff) * inv; u[3] = h2f(raw.y >> 16) * inv;
-      if constexpr (SUB == 8) {
-        u[4] = h2f(raw.z & 0xffff) * inv; u[5] = h2f(raw.z >> 16) * inv;
-        u[6] = h2f(raw.w & 0xffff) * inv; u[7] = h2f(raw.w >> 16) * inv;
-      }
     } else {  // pass 1's scales, so y is the same value without a second reduction
       n1 = n1p[tok];
-      const float inv = invp[tok];
-      u[0] = h2f(raw.x & 0xffff) * inv; u[1] = h2f(raw.x >> 16) * inv;
-      u[2] = h2f(raw.y & 0xffff) * inv; u[3] = h2f(raw.y >> 16) * inv;
-      if constexpr (SUB == 8) {
-        u[4] = h2f(raw.z & 0xffff) * inv; u[5] = h2f(raw.z >> 16) * inv;
-        u[6] = h2f(raw.w & 0xffff) * inv; u[7] = h2f(raw.w >> 16) * inv;
-      }
     }
+    const float inv = DQ ? (n1 > 0.f ? 1.f / n1 : 0.f) : invp[tok];
+    // z = x / n1 - mu, one mixed-precision fma per element
+    const uint32_t rw[4] = {raw.x, raw.y, SUB == 8 ? raw_hi(raw, 0) : 0u, SUB == 8 ? raw_hi(raw, 1) : 0u};
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) {
-      u[e] -= mu[e];
+      u[e] = fmaf(h2f((e & 1) ? (rw[e >> 1] >> 16) : (rw[e >> 1] & 0xffff)), inv, -mu[e]);
       ss = fmaf(u[e], u[e], ss);
     }
     ss = group_sum<S>(ss) * (1.0f / kDim);
@@ -467,8 +524,9 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
 #pragma unroll
     for (int e = 0; e < SUB; ++e) u[e] *= sgn[e];
     // the transform is linear: the 1 / n2 scale goes after it, with 1 / sqrt(d)
-    fwht128<SUB>(u, lane);
-    const float sc = inv2 * kInvSqrtD;
+    // and the lane's sign
+    fwht_lanes<SUB>(u, slot);
+    const float sc = inv2 * hscale;
 #pragma unroll
     for (int e = 0; e < SUB; ++e) u[e] *= sc;
   };
@@ -479,11 +537,11 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
 #pragma unroll
     for (int e = 0; e < SUB; ++e) {
       hi[e] = (half_t)u[e];
-      lo[e] = (half_t)(u[e] - (float)hi[e]);
+      lo[e] = (half_t)fmaf((float)hi[e], -1.f, u[e]);  // exact remainder, one mixed fma
       uu = fmaf(u[e], u[e], uu);
     }
     uu_hi = (half_t)uu;
-    uu_lo = (half_t)(uu - (float)uu_hi);
+    uu_lo = (half_t)fmaf((float)uu_hi, -1.f, uu);
   };
   // the scales of token `tok` (slot-0 lane): (n1, n2) fp16, or n2 alone in
   // the double-quantised record
@@ -583,7 +641,7 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
       half_swap(best0, best1, klo, khi, lane);  // klo = [b0 low, b1 low], khi = [b0 high, b1 high]
       const uint32_t mine = min(klo, khi);
       const uint32_t code = mine & 0xffu;
-      codes[(tok_base + tok) * S + slot] = (uint8_t)code;
+      codes[(tok_base + tok) * S + oslot] = (uint8_t)code;
       // Strategy-3 scale: alpha = |u|^2 / (u . c_hat), folded into n2
       float n2s = n2;
       if (a.scale_adjust) {
@@ -613,7 +671,7 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
       half_t hi[SUB], lo[SUB], uu_hi, uu_lo;
       float uu;
       split(u, hi, lo, uu_hi, uu_lo, uu);
-      const int i = tok * S + slot;
+      const int i = tok * S + oslot;
       recs[i] = u32x4_to_half8(pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(lo[0], lo[1]),
                                pack_h2(lo[2], lo[3]));
       uus[i] = pack_h2(uu_hi, uu_lo);
@@ -655,7 +713,7 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
       for (int r = 0; r < ROWS; ++r) {
         const int tok = wave * TPW + r * TPR + tir;
         const uint32_t first = __shfl(st + mine, (int)boxr[r], kWave);
-        sidx[first + rankr[r]] = (uint16_t)(tok * S + slot);
+        sidx[first + rankr[r]] = (uint16_t)(tok * S + oslot);
       }
       // wave w pads box w with the zero record and labels its column blocks
       const uint32_t wst = __builtin_amdgcn_readlane(st, wave), wcnt = __builtin_amdgcn_readlane(cnt, wave);
