@@ -112,6 +112,37 @@ __device__ __forceinline__ void fwht_lanes(float (&x)[E], int l) {
   }
 }
 
+// Packed fp16 pairs straight from fp32 products, each half written by one
+// mixed-precision fma (v_fma_mixlo_f16 / v_fma_mixhi_f16; the compiler
+// otherwise packs with a shift and an or per word):
+//   mix_pair:     [f16(b s), f16(a s)]
+//   mix_rem_pair: [f16(b s - h.hi), f16(a s - h.lo)], the fused remainders
+//   mix_lo:       f16(a s) in the low half (the high half is left as it was)
+//   mix_rem_lo:   [f16(a s - h.lo), h.lo]
+__device__ __forceinline__ uint32_t mix_lo(float a, float s) {
+  uint32_t w;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(w) : "v"(a), "v"(s));
+  return w;
+}
+__device__ __forceinline__ uint32_t mix_pair(float a, float b, float s) {
+  uint32_t w;
+  asm("v_fma_mixlo_f16 %0, %1, %3, 0\n\tv_fma_mixhi_f16 %0, %2, %3, 0" : "=&v"(w) : "v"(a), "v"(b), "v"(s));
+  return w;
+}
+__device__ __forceinline__ uint32_t mix_rem_pair(float a, float b, float s, uint32_t h) {
+  uint32_t w;
+  asm("v_fma_mixlo_f16 %0, %1, %3, -%4 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %2, %3, -%4 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(w)
+      : "v"(a), "v"(b), "v"(s), "v"(h));
+  return w;
+}
+__device__ __forceinline__ uint32_t mix_rem_lo(float a, float s, uint32_t h) {
+  uint32_t w = h;
+  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "+v"(w) : "v"(a), "v"(s), "v"(h));
+  return w;
+}
+
 // words 2 and 3 of a token's 8-channel (1-bit) slice; a 4-channel slice has none
 __device__ __forceinline__ uint32_t raw_hi(const uint2&, int) { return 0u; }
 __device__ __forceinline__ uint32_t raw_hi(const uint4& r, int i) { return i ? r.w : r.z; }
@@ -495,11 +526,13 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
   float sgn[SUB];
 #pragma unroll
   for (int e = 0; e < SUB; ++e) sgn[e] = a.signs ? (float)a.signs[slot * SUB + e] : 1.f;
+  const bool rht = a.signs != nullptr;
 
   // Shift, second normalisation and Hadamard transform of this lane's
-  // sub-vector of token `tok`: u (norm sqrt(d) over the token), n1, n2.
+  // sub-vector of token `tok`: n1, n2, and u before its final scale, which
+  // is returned (sc u has norm sqrt(d) over the token).
   const float hscale = kInvSqrtD * hsign(slot);
-  auto transform = [&](int tok, const raw_t& raw, float (&u)[SUB], float& n1, float& n2) {
+  auto transform_u = [&](int tok, const raw_t& raw, float (&u)[SUB], float& n1, float& n2) -> float {
     if constexpr (DQ) {
       n1 = n1hs[tok];
     } else {  // pass 1's scales, so y is the same value without a second reduction
@@ -521,12 +554,17 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
     const bool live = ss >= kN2Floor * kN2Floor;
     const float inv2 = live ? rs2 : 0.f;
     n2 = ss * inv2;
+    if (rht) {
 #pragma unroll
-    for (int e = 0; e < SUB; ++e) u[e] *= sgn[e];
+      for (int e = 0; e < SUB; ++e) u[e] *= sgn[e];
+    }
     // the transform is linear: the 1 / n2 scale goes after it, with 1 / sqrt(d)
     // and the lane's sign
     fwht_lanes<SUB>(u, slot);
-    const float sc = inv2 * hscale;
+    return inv2 * hscale;
+  };
+  auto transform = [&](int tok, const raw_t& raw, float (&u)[SUB], float& n1, float& n2) {
+    const float sc = transform_u(tok, raw, u, n1, n2);
 #pragma unroll
     for (int e = 0; e < SUB; ++e) u[e] *= sc;
   };
@@ -542,6 +580,20 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
     }
     uu_hi = (half_t)uu;
     uu_lo = (half_t)fmaf((float)uu_hi, -1.f, uu);
+  };
+  // The record of sc u (4 channels): fp16 hi and lo parts, each from one
+  // mixed-precision fma (lo = sc u - hi unrounded), and the pair
+  // (|sc u|^2 hi, lo).
+  auto split_scaled = [&](const float (&u)[SUB], float sc, uint32_t (&w)[4], uint32_t& uup) {
+    float uu = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) uu = fmaf(u[e], u[e], uu);
+    w[0] = mix_pair(u[0], u[1], sc);
+    w[1] = mix_pair(u[2], u[3], sc);
+    w[2] = mix_rem_pair(u[0], u[1], sc, w[0]);
+    w[3] = mix_rem_pair(u[2], u[3], sc, w[1]);
+    const float sc2 = sc * sc;
+    uup = mix_rem_lo(uu, sc2, mix_lo(uu, sc2));
   };
   // the scales of token `tok` (slot-0 lane): (n1, n2) fp16, or n2 alone in
   // the double-quantised record
@@ -667,15 +719,15 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
     for (int r = 0; r < ROWS; ++r) {
       const int tok = wave * TPW + r * TPR + tir;
       float u[SUB], n1, n2;
-      transform(tok, xr[r], u, n1, n2);
-      half_t hi[SUB], lo[SUB], uu_hi, uu_lo;
-      float uu;
-      split(u, hi, lo, uu_hi, uu_lo, uu);
+      const float sc = transform_u(tok, xr[r], u, n1, n2);
+      uint32_t w[4], uup;
+      split_scaled(u, sc, w, uup);
       const int i = tok * S + oslot;
-      recs[i] = u32x4_to_half8(pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(lo[0], lo[1]),
-                               pack_h2(lo[2], lo[3]));
-      uus[i] = pack_h2(uu_hi, uu_lo);
-      boxr[r] = (u[0] < 0.f ? 1u : 0u) | (u[1] < 0.f ? 2u : 0u) | (u[2] < 0.f ? 4u : 0u) | (u[3] < 0.f ? 8u : 0u);
+      recs[i] = u32x4_to_half8(w[0], w[1], w[2], w[3]);
+      uus[i] = uup;
+      // orthant box from the signs of the fp16 high parts (a zero part lies
+      // on the boundary of both boxes, whose lists both hold its nearest)
+      boxr[r] = ((w[0] >> 15) & 1u) | ((w[0] >> 30) & 2u) | ((w[1] >> 13) & 4u) | ((w[1] >> 28) & 8u);
       rankr[r] = atomicAdd(&whist[wave][boxr[r]], 1u);
       if (slot == 0) {
         if (a.scale_adjust) {
