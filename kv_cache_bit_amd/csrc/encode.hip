@@ -782,12 +782,14 @@ __global__ __launch_bounds__(64 * enc_waves<NT>()) void encode_kernel(EncodeArgs
     // even share of the column blocks, two per step.
     const int n = lane & 31;
     const bool upper = lane >= 32;
-    // B operand of sorted column `col` (both loads on every lane, then a select)
+    // B operand of sorted column `col` (both loads on every lane, then a select).
+    // The bias row's K slots 12-15 meet zeros in every candidate tile, so the
+    // upper lanes leave the record's (finite) low parts there.
     auto operand_b = [&](int col, int& idx) -> half8_t {
       idx = sidx[col];
       const uint4_t rv = __builtin_bit_cast(uint4_t, recs[idx]);
       const uint32_t q = uus[idx];
-      const uint4_t w = {upper ? q : rv[0], upper ? 0x3C003C00u : rv[1], upper ? 0u : rv[2], upper ? 0u : rv[3]};
+      const uint4_t w = {upper ? q : rv[0], upper ? 0x3C003C00u : rv[1], rv[2], rv[3]};
       return __builtin_bit_cast(half8_t, w);
     };
     auto search = [&](auto two, int c0) {
