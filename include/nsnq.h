@@ -27,9 +27,13 @@
  *  - Argument checks run on the host before anything is launched.  On error
  *    nothing is launched and a status other than NSNQ_OK is returned.  A
  *    launch failure returns NSNQ_EHIP.  Device faults surface at the caller's
- *    next synchronisation.  Inputs must be finite (not checked).
- *  - The library allocates no memory, keeps no global state and prints
- *    nothing; calls on different streams are independent.
+ *    next synchronisation.  Inputs must be finite (not checked).  Decode
+ *    attention carries per-token value weights up to n1 * n2 in fp16, so the
+ *    stored scales must keep n1 * n2 below 65504; n2 <= 2 by construction,
+ *    so every head vector of norm below 3.7e5 qualifies (not checked).
+ *  - The library allocates no memory and prints nothing.  Its only state is
+ *    per device and set once: the kernels' dynamic-LDS attribute and one
+ *    occupancy query.  Calls on different streams are independent.
  *  - Layouts are dense and row-major.  For a cache of `batch` rows,
  *    `kv_heads` heads and capacity `cap_tokens` (a multiple of R), with
  *    S = d / s slots per vector (s = 4 at 2 bits, 8 at 1 bit):
