@@ -285,6 +285,31 @@ def test_decode_late_maxima(oracle_codebooks, bits, Hq, Hkv):
         check_attention(o, ref)
 
 
+def test_decode_workspace_reuse(oracle_codebooks):
+    """One workspace serves calls of different shapes, kernels (one KV head per
+    query head, and grouped heads) and split counts in turn; every result
+    matches the oracle's attention."""
+    cases = []
+    for bits, R, B, Hq, Hkv, L in ((2, 128, 2, 4, 4, 1500), (1, 64, 1, 8, 2, 700), (2, 64, 3, 3, 3, 900)):
+        cb = oracle_codebooks[bits]
+        k, v = _kv(480 + bits + B, B, Hkv, L)
+        q = synth.queries(480 + bits + B, 0, B, Hq, D)
+        ek, ev = oracle_encode_pair(k, v, R, cb)
+        p = nsnq.params(bits, R)
+        cache = nsnq.KVCache(p, B, Hkv, capacity(L, R), DEV)
+        upload_half(cache, 0, ek)
+        upload_half(cache, 1, ev)
+        cache.n_quant, cache.n_resid = ek["n_quant"], ek["n_resid"]
+        cases.append((p, cb_tensor(cb), q.to(DEV), cache, _decode_ref(q, ek, ev, cb, R)))
+    need = max(nsnq.nsnq_decode_workspace_bytes(p, c, q.shape[1], ns)
+               for p, _, q, c, _ in cases for ns in (0, 1, 7))
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    for ns in (0, 7, 1, 0):
+        for p, cbt, qd, cache, ref in cases:
+            o = nsnq.nsnq_decode_attention(p, cbt, qd, cache, num_splits=ns, ws=ws).float().cpu().numpy()
+            check_attention(o, ref)
+
+
 def test_flush_then_decode(oracle_codebooks):
     """Prefill leaves a full window; the next token flushes it, is appended,
     and attention covers all tokens."""
