@@ -1,17 +1,21 @@
 // encode.hip -- fused NSN + Hadamard + VQ encode of R-token blocks (gfx950).
 //
-// One work-group (4 waves) encodes one block of R tokens of one (batch row,
-// head) stream, K or V.  Each lane holds one sub-vector (s = SUB elements) of
-// one token, so a token occupies S = 128/SUB consecutive lanes and a wave "row"
-// covers 64/S tokens.
+// The unit of work is one block of R tokens of one (batch row, head) stream,
+// K or V.  The exhaustive search runs one 8-wave work-group per block; the
+// candidate-list search (2 bits) runs one persistent 16-wave group per CU and
+// K/V half that loops over blocks.  Each lane holds one sub-vector (s = SUB
+// elements) of one token, so a token occupies S = 128/SUB consecutive lanes
+// and a wave "row" covers 64/S tokens.
 //
 //  1. token-wise normalisation to norm sqrt(d) (n1), kept in registers;
 //  2. channel mean over the block (wave partial sums, LDS across waves);
 //  3. second normalisation (n2), w = z / n2;
 //  4. Walsh-Hadamard transform across the S lanes of a token, scaled by
-//     1/sqrt(d);
-//  5. VQ: squared distances to all 256 codewords as an MFMA GEMM, then a
-//     per-lane argmin on packed (distance | index) keys.
+//     1/sqrt(d) (its DPP stages leave each lane with a relabelled slot and a
+//     sign: fwht_lanes below);
+//  5. VQ: squared distances to all 256 codewords (or to the candidate list
+//     of the sub-vector's orthant box) as an MFMA GEMM, then a per-lane
+//     argmin on packed (distance | index) keys.
 //
 // Distance GEMM.  Codewords are the rows (M) and sub-vectors the columns (N)
 // of v_mfma_f32_32x32x16_f16 tiles, so each lane receives 16 candidate
