@@ -287,8 +287,8 @@ def nsnq_decode_attention(p: nsnq_params, codebook, q, cache: "KVCache", softmax
         softmax_scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    need = nsnq_decode_workspace_bytes(p, cache, Hq, num_splits)
-    if ws is None:
+    if ws is None:  # (the library checks a caller's workspace size itself)
+        need = nsnq_decode_workspace_bytes(p, cache, Hq, num_splits)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     c = cache.c_struct()
     _check(lib().nsnq_decode_attention(ctypes.byref(p), _ptr(codebook), _ptr(q), Hq, ctypes.byref(c),
@@ -310,8 +310,8 @@ def nsnq_decode_attention_prerope(p: nsnq_params, codebook, q, cache: "KVCache",
         softmax_scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    need = nsnq_decode_workspace_bytes(p, cache, Hq, num_splits)
-    if ws is None:
+    if ws is None:  # (the library checks a caller's workspace size itself)
+        need = nsnq_decode_workspace_bytes(p, cache, Hq, num_splits)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     c = cache.c_struct()
     r = nsnq_rope(_ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], pos0)
