@@ -440,17 +440,15 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # per-phase HIP events on every 8th timed step (events between the phases
+    # cost ~10 us of wall time per step they bracket)
+    every = 8
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(0, args.steps, every)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        step(i, evs[i // every] if i % every == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # per-phase HIP-event times from as many steps again, after the timed region
-    # (the events are not part of the measured steps)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
     enc_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
