@@ -272,6 +272,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   float4_t vacc[kMV ? 8 : 1];
 #pragma unroll
   for (int t = 0; t < (kMV ? 8 : 1); ++t) vacc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+  // matrix-core values: the fp16 weights carry 2^(ev - 3), ev the smallest
+  // headroom exponent of the wave's chunks so far (vacc is rescaled exactly
+  // when it drops), so no N1 N2 overflows fp16 and no small one underflows;
+  // 64 is above any chunk's exponent
+  int ev = 64;
   uint8_t* const vstw = reinterpret_cast<uint8_t*>(smem + L.vst) + wave * kChunk * 16;
   const uint32_t vst_lds = (uint32_t)(reinterpret_cast<uintptr_t>(vstw) - reinterpret_cast<uintptr_t>(smem));
   const uint32_t wb_lds = (uint32_t)(reinterpret_cast<uintptr_t>(wb) - reinterpret_cast<uintptr_t>(smem));
@@ -311,6 +316,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
       vn2 = h2f(cur.vsc >> 16);
       vm0 = h2f(cur.vm[0] & 0xffff);
       vm1 = h2f(cur.vm[0] >> 16);
+    }
+    if constexpr (kMV) {
+      const int ec = f16_headroom_exp(group_max<kWave>(fabsf(vn1 * vn2)));
+      if (ec < ev) {
+        const float f = pow2f(ec - ev);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vacc[t] *= f;
+        ev = ec;
+      }
     }
     if constexpr (ROPE) {
       // the chunk's block mean for channels 8 rj .. 8 rj + 7
@@ -430,8 +444,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
       om0[g] = fmaf(pn1, vm0, om0[g]);
       om1[g] = fmaf(pn1, vm1, om1[g]);
       if constexpr (kMV) {
-        // fp16 p N1 N2 / 8: p <= 8 keeps the range of the p <= 1 weights
-        reinterpret_cast<uint16_t*>(wb)[lane] = f2h(pr * vn1 * vn2 * 0.125f);
+        // fp16 p N1 N2 2^(ev - 3) < 2^15 (p <= 8)
+        reinterpret_cast<uint16_t*>(wb)[lane] = f2h(pr * (vn1 * vn2) * pow2f(ev - 3));
       } else {
         wb[g * kChunk + lane] = pr * vn1 * vn2;
       }
@@ -546,7 +560,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) r[2 + 8 * (4 * kb + rr) + t] = 8.f * vacc[t][rr];
+          for (int rr = 0; rr < 4; ++rr) r[2 + 8 * (4 * kb + rr) + t] = pow2f(3 - ev) * vacc[t][rr];
       }
     } else if (lane < 8) {
 #pragma unroll
@@ -625,7 +639,7 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
 
 template <int SUB, int GH, bool DQ, bool ROPE>
 static hipError_t launch_decode_dq(const DecodeArgs& a, int B, size_t lds, hipStream_t stream) {
-  static bool lds_set[kMaxDevices] = {};
+  static std::atomic<bool> lds_set[kMaxDevices];
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(&decode_split_kernel<SUB, GH, DQ, ROPE>), lds_set);
   if (e != hipSuccess) return e;
   dim3 grid(a.nsplit, B * a.Hkv * (a.G / GH)), block(256);
@@ -761,7 +775,7 @@ __global__ __launch_bounds__(256) void fp16_decode_kernel(Fp16DecodeArgs a) {
 
 template <int G>
 static hipError_t launch_fp16_t(const Fp16DecodeArgs& a, int B, hipStream_t stream) {
-  static bool lds_set[kMaxDevices] = {};
+  static std::atomic<bool> lds_set[kMaxDevices];
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(&fp16_decode_kernel<G>), lds_set);
   if (e != hipSuccess) return e;
   const size_t lds = fp16_decode_lds_bytes(G, a.split_tokens);

@@ -2,6 +2,8 @@
 // kernels (LUT scoring in decode.hip, matrix-core scoring in decode_mfma.hip).
 #pragma once
 
+#include <atomic>
+
 #include "nsnq_device.hpp"
 #include "nsnq_launch.hpp"
 
@@ -12,17 +14,18 @@ constexpr int kMaxSplitBlocks = 16;
 
 // Lets `kernel` use up to 160 KB of dynamic LDS, once per device of the
 // process (the attribute is per device); `set` is the caller's per-kernel
-// record of the devices done.
-constexpr int kMaxDevices = 64;
-inline hipError_t allow_lds(const void* kernel, bool (&set)[kMaxDevices]) {
+// record of the devices done.  Threads making a first call on one device at
+// the same time may both set the attribute: the call is idempotent, and the
+// record is atomic.
+inline hipError_t allow_lds(const void* kernel, std::atomic<bool> (&set)[kMaxDevices]) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  if (!set[dev]) {
+  if (!set[dev].load(std::memory_order_acquire)) {
     e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    set[dev] = true;
+    set[dev].store(true, std::memory_order_release);
   }
   return hipSuccess;
 }

@@ -374,6 +374,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   float4_t vacc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) vacc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+  // The fp16 value weights of a chunk carry the factor 2^ev, ev the smallest
+  // headroom exponent of the wave's chunks so far (it only decreases, and
+  // vacc is rescaled exactly when it does), so that neither a large N1 N2
+  // overflows fp16 nor a small one (short value vectors, a dominant token
+  // elsewhere) underflows; vacc is scaled back at the end.  64 is above the
+  // exponent of any chunk (the smallest fp16 product gives 62).
+  int ev = 64;
 
   if constexpr (T4) {
     // ---- one token per lane ----------------------------------------------
@@ -403,7 +410,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     for (int e = 0; e < 8; ++e) aone[e] = (half_t)(m16 == 0 ? 1.f : 0.f);
 
     float4_t sh, sl;
-    float kas, ka, vc8, vd8;
+    float kas, ka, wn12, wn1;  // N1 N2 and N1 of the lane's token (V)
+    int eb0 = 0, eb1 = 0;   // beta weights' exponent of the chunk in buffer 0 / 1
     // stage chunk `c`'s V codes in buffer `bs`, score its tokens
     auto front = [&](const Ld& c, int bs) {
       uint8_t* vb = vbase + bs * kBufB;
@@ -423,8 +431,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       }
       kas = a.scale_log2 * kn1;
       ka = kas * kn2;
-      vd8 = 0.125f * vn1;
-      vc8 = vd8 * vn2;
+      wn1 = vn1;
+      wn12 = vn1 * vn2;
       sh = float4_t{0.f, 0.f, 0.f, 0.f};
       sl = float4_t{0.f, 0.f, 0.f, 0.f};
       if constexpr (SUB == 4) {
@@ -484,13 +492,27 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) vacc[t] *= as;
       }
+      // fp16 weights p N1 N2 2^(ev - 3) and p N1 2^(eb - 3): with p <= 8 they
+      // stay below 2^15; beta's exponent is the chunk's own (each chunk's
+      // beta is taken out separately)
+      const int ec = f16_headroom_exp(group_max<64>(fabsf(wn12)));
+      const int eb = f16_headroom_exp(group_max<64>(fabsf(wn1)));
+      if (ec < ev) {
+        const float f = pow2f(ec - ev);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vacc[t] *= f;
+        ev = ec;
+      }
+      if (bs) eb1 = eb;
+      else eb0 = eb;
+      const float fw = wn12 * pow2f(ev - 3), fb = wn1 * pow2f(eb - 3);
       uint16_t* pb = reinterpret_cast<uint16_t*>(vbase + bs * kBufB + kMChunk * S);
 #pragma unroll
       for (int r = 0; r < GQ; ++r) {
         const float pr = __builtin_amdgcn_exp2f(dl[r]);
         lp[r] += pr;
-        pb[r * kMChunk + lane] = f2h(pr * vc8);
-        pb[(4 + r) * kMChunk + lane] = f2h(pr * vd8);
+        pb[r * kMChunk + lane] = f2h(pr * fw);
+        pb[(4 + r) * kMChunk + lane] = f2h(pr * fb);
       }
       if (lane == 0) {  // the references are uniform over the wave
 #pragma unroll
@@ -549,8 +571,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         }
         db = __builtin_amdgcn_mfma_f32_16x16x32_f16(aone, bw, db, 0, 0, 0);
       }
-      // beta_r = sum p VD: row 0, column 4 + r of db (lanes 4 .. 4 + GQ - 1)
-      if (m16 >= 4 && m16 < 4 + GQ && kb == 0) bc[chk * GQ + m16 - 4] = 8.f * db[0];
+      // beta_r = sum p VD: row 0, column 4 + r of db (lanes 4 .. 4 + GQ - 1),
+      // scaled back by the chunk's exponent
+      if (m16 >= 4 && m16 < 4 + GQ && kb == 0) bc[chk * GQ + m16 - 4] = db[0] * pow2f(3 - (bs ? eb1 : eb0));
     };
 
     if (ch < nchunk) {
@@ -575,7 +598,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       back(chp, bs ^ 1);
     }
     // lane (m16 < GQ, kb): reference and sum of head m16; the value columns
-    // hold p VC / 8
+    // hold p VC 2^(ev - 3)
     m = mr[0];
     l = 0.f;
 #pragma unroll
@@ -584,8 +607,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       m = m16 == r ? mr[r] : m;
       l = m16 == r ? lt : l;
     }
+    {
+      const float f = pow2f(3 - ev);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) vacc[t] *= 8.f;
+      for (int t = 0; t < 8; ++t) vacc[t] *= f;
+    }
   } else {
   for (; ch < nchunk; ch += 4) {
       Ld nxt;
@@ -611,7 +637,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         fkb[lane] = kas;
         fvc[lane] = vn1 * vn2;
         fvd[lane] = vn1;
+        // the chunk's value weights p N1 N2 (p <= 1) carry 2^ev in fp16
+        const int ec = f16_headroom_exp(group_max<64>(fabsf(vn1 * vn2)));
+        if (ec < ev) {
+          const float f = pow2f(ec - ev);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) vacc[t] *= f;
+          ev = ec;
+        }
       }
+      const float fwv = pow2f(ev);
       wave_sync();
   
       // scores: tile tau covers tokens 16 tau .. 16 tau + 15 (rows), heads (columns)
@@ -680,7 +715,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
           const float p = __builtin_amdgcn_exp2f(s[4 * tau + r] - mn);
           lsum += p;
           beta = fmaf(p, vdv[r], beta);
-          bw[tau >> 1][4 * (tau & 1) + r] = (half_t)(p * vcv[r]);
+          bw[tau >> 1][4 * (tau & 1) + r] = (half_t)(p * vcv[r] * fwv);
         }
       }
       l = fmaf(l, alpha, lsum);
@@ -748,6 +783,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   if constexpr (!T4) {
     l += xlane<16>(l);
     l += xlane<32>(l);
+    const float f = pow2f(-ev);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) vacc[t] *= f;
   }
   __syncthreads();  // the main-loop LDS views are dead from here on
   float* mrg = smem + L::mrg;
@@ -834,31 +872,33 @@ static int mfma_groups_per_cu_s(int gq, bool dq) {
 }
 
 int decode_mfma_resident_groups(int sub, int gq, bool dq) {
-  // cached per device and kernel variant; 0 = unknown (no device, query failed)
-  constexpr int kDev = 16;
-  static int cache[kDev][2][5][2];  // [device][sub 4/8][log2 gq][dq], -1 stored for "unknown"
+  // cached per device and kernel variant; 0 = unknown (no device, query
+  // failed).  Concurrent first queries store the same value.
+  static std::atomic<int> cache[kMaxDevices][2][5][2];  // [device][sub 4/8][log2 gq][dq], -1 = "unknown"
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDev) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
     return 0;
   }
   const int si = sub == 8 ? 1 : 0;
   const int gi = gq == 2 ? 1 : gq == 4 ? 2 : gq == 8 ? 3 : gq == 16 ? 4 : 0;
-  int& slot = cache[dev][si][gi][dq ? 1 : 0];
-  if (slot == 0) {
+  std::atomic<int>& slot = cache[dev][si][gi][dq ? 1 : 0];
+  int v = slot.load(std::memory_order_relaxed);
+  if (v == 0) {
     int cus = 0;
     const int per_cu = sub == 4 ? mfma_groups_per_cu_s<4>(gq, dq) : mfma_groups_per_cu_s<8>(gq, dq);
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
     (void)hipGetLastError();
-    slot = per_cu > 0 && cus > 0 ? per_cu * cus : -1;
+    v = per_cu > 0 && cus > 0 ? per_cu * cus : -1;
+    slot.store(v, std::memory_order_relaxed);
   }
-  return slot > 0 ? slot : 0;
+  return v > 0 ? v : 0;
 }
 
 template <int SUB, int GQ, bool DQ>
 static hipError_t launch_mfma_dq(const DecodeArgs& a, int B, hipStream_t stream) {
   const size_t lds = (size_t)MfmaSmem<SUB, GQ>::total * sizeof(float);
-  static bool lds_set[kMaxDevices] = {};
+  static std::atomic<bool> lds_set[kMaxDevices];
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(&decode_mfma_kernel<SUB, GQ, DQ>), lds_set);
   if (e != hipSuccess) return e;
   dim3 grid(a.nsplit, B * a.Hkv * (a.G / GQ)), block(256);

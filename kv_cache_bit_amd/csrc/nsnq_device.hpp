@@ -111,4 +111,15 @@ __device__ __forceinline__ void fwht128(float (&x)[E], int lane) {
 // 1/sqrt(128)
 constexpr float kInvSqrtD = 0.088388347648318440550f;
 
+// Power-of-two scaling of fp16 weights.  For the largest magnitude xmax of a
+// set of non-negative weights, x * 2^f16_headroom_exp(xmax) < 2^15 for every
+// member: the scaled set fits fp16 (max 65504) and its largest members keep
+// full fp16 precision, whatever the magnitude of the unscaled weights.  The
+// exponent is uniform over the wave (the reduction gives every lane the same
+// maximum).
+__device__ __forceinline__ int f16_headroom_exp(float xmax) {
+  return __builtin_amdgcn_readfirstlane(15 - __builtin_amdgcn_frexp_expf(xmax));
+}
+__device__ __forceinline__ float pow2f(int e) { return __builtin_amdgcn_ldexpf(1.f, e); }
+
 }  // namespace nsnq

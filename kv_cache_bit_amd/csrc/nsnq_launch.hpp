@@ -6,6 +6,11 @@
 
 namespace nsnq {
 
+// Devices per process the library keeps per-device state for: the kernels'
+// dynamic-LDS attribute, one occupancy query per grouped-head kernel variant
+// and the address of the static decode scratch.
+constexpr int kMaxDevices = 64;
+
 struct EncodeArgs {
   const uint16_t* src[2];  // K, V fp16 streams
   int64_t sb, sh, st;      // element strides (batch, head, token)

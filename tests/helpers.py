@@ -76,15 +76,29 @@ def upload_half(cache: nsnq.KVCache, which: int, enc: dict):
     h.resid.copy_(torch.from_numpy(enc["resid"].view(np.float16)))
 
 
-def check_codes(g: np.ndarray, o: np.ndarray, gap: np.ndarray, what: str = "codes", pooled: bool = False):
+def check_codes(g: np.ndarray, o: np.ndarray, gap: np.ndarray, u: np.ndarray, cb_bits: np.ndarray,
+                what: str = "codes", pooled: bool = False):
     """Codes equal outside the near-tie band; near-tie flips within the rate
-    bound.  pooled=True leaves the rate bound to the caller, who applies it to
-    the whole test's population (check_tie_rate)."""
+    bound.  Every differing code must itself be a near-best choice: with u the
+    oracle's Hadamard-domain vectors [..., n, d] (fp64), the distance of the
+    GPU's codeword exceeds the oracle's minimum by less than 1e-4 relative.
+    pooled=True leaves the rate bound to the caller, who applies it to the
+    whole test's population (check_tie_rate)."""
     assert g.shape == o.shape, (g.shape, o.shape)
     mism = g != o
     n = int(mism.sum())
     bad = int((mism & (gap >= NEAR_TIE)).sum())
     assert bad == 0, f"{what}: {bad} mismatches outside the near-tie band (of {n} total, {g.size} codes)"
+    if n:
+        s = cb_bits.shape[1]
+        assert u.shape[:-1] == g.shape[:-1] and u.shape[-1] == g.shape[-1] * s, (u.shape, g.shape)
+        us = u.reshape(*g.shape, s)[mism]
+        cbd = np.ascontiguousarray(cb_bits).view(np.float16).astype(np.float64)
+        d_gpu = ((us - cbd[g[mism]]) ** 2).sum(-1)
+        d_best = ((us - cbd[o[mism]]) ** 2).sum(-1)
+        assert np.all(d_best > 0), f"{what}: a differing code where the oracle's distance is 0"
+        excess = (d_gpu - d_best) / d_best
+        assert excess.max() < NEAR_TIE, f"{what}: a differing GPU code is {excess.max():.2e} (relative) from the best"
     if not pooled:
         check_tie_rate(n, g.size, what)
     return n
@@ -125,10 +139,27 @@ def check_attention(g: np.ndarray, o: np.ndarray, tol: float = ATTN_TOL):
     return float(rel.max())
 
 
+def oracle_encode(x, R: int, cb_bits: np.ndarray, **kw) -> dict:
+    """The oracle's encoding of streams x, with the Hadamard-domain vectors u
+    (fp64) the code checks need and the codebook it used."""
+    e = oracle.encode(x.cpu() if hasattr(x, "cpu") else x, R, cb_bits, with_u=True, **kw)
+    e["cb"] = cb_bits
+    return e
+
+
 def oracle_encode_pair(k: torch.Tensor, v: torch.Tensor, R: int, cb_bits: np.ndarray, signs=None,
-                      scale_adjust: bool = False):
-    kw = dict(signs=signs, scale_adjust=scale_adjust)
-    return oracle.encode(k.cpu(), R, cb_bits, **kw), oracle.encode(v.cpu(), R, cb_bits, **kw)
+                      scale_adjust: bool = False, dq: bool = False):
+    kw = dict(signs=signs, scale_adjust=scale_adjust, dq=dq)
+    return oracle_encode(k, R, cb_bits, **kw), oracle_encode(v, R, cb_bits, **kw)
+
+
+def gpu_records(cache: nsnq.KVCache, which: int) -> dict:
+    """One half of a GPU cache in the oracle's dict layout (codes, scales, mu,
+    resid; the double-quantised flag), for oracle.reference_decode over the
+    GPU's own records."""
+    h = half_np(cache, which)
+    h["dq"] = bool(getattr(cache, "dq", False))
+    return h
 
 
 def compare_encoded(cache: nsnq.KVCache, ek: dict, ev: dict, units=None, scale_adjust: bool = False):
@@ -141,7 +172,7 @@ def compare_encoded(cache: nsnq.KVCache, ek: dict, ev: dict, units=None, scale_a
         gh = half_np(cache, which)
         if units is not None:
             gh = {key: np.stack([val[b, h] for b, h in units]) for key, val in gh.items()}
-        n = check_codes(gh["codes"], e["codes"], e["gap"], "K codes" if which == 0 else "V codes")
+        n = check_codes(gh["codes"], e["codes"], e["gap"], e["u"], e["cb"], "K codes" if which == 0 else "V codes")
         if scale_adjust:
             same = np.all(gh["codes"] == e["codes"], axis=-1)
             check_f16_ulp(gh["scales"][..., 0], e["scales"][..., 0], "n1")
@@ -174,11 +205,14 @@ def _dq_fields(sc: np.ndarray, mu: np.ndarray, R: int):
 
 def compare_encoded_dq(cache: nsnq.KVCache, ek: dict, ev: dict, R: int, scale_adjust: bool = False):
     """Double-quantised caches against the oracle.  Per block: the fp16 (S, Z)
-    pairs within one ulp; the 4-bit codes equal except for decisions within
-    DQ_MARGIN of a tie; a block whose 4-bit decisions all agree is then held to
-    the plain bars (codes with the near-tie rule, n2 within one ulp).  Blocks
-    with a differing decision (expected rarely) are at most 2% of blocks.
-    Returns the list of per-half boolean block masks (True = compared fully)."""
+    pairs within one ulp; every 4-bit code equal to the oracle's or one level
+    from it, and equal unless the decision is within DQ_MARGIN of a rounding
+    tie where the block's (S, Z) pair is the oracle's; a block whose 4-bit
+    decisions all agree is then held to the plain bars (codes with the
+    near-tie rule, each differing code near-best for the oracle's u; n2 within
+    one ulp).  Blocks with a differing decision (expected rarely) are at most
+    2% of blocks.  Returns the list of per-half boolean block masks (True =
+    compared fully)."""
     masks = []
     for which, e in ((0, ek), (1, ev)):
         gh = half_np(cache, which)
@@ -193,6 +227,9 @@ def compare_encoded_dq(cache: nsnq.KVCache, ek: dict, ev: dict, R: int, scale_ad
         same_par = np.all(gsz == osz, axis=-1) & np.all(gmsz == omsz, axis=(-1, -2))
         d1 = (gq1 != oq1)
         dm = (gqm != oqm)
+        # a differing 4-bit code is always the neighbouring level
+        assert np.all(np.abs(gq1.astype(np.int32) - oq1.astype(np.int32)) <= 1), "s1 code off by more than one level"
+        assert np.all(np.abs(gqm.astype(np.int32) - oqm.astype(np.int32)) <= 1), "mean code off by more than one level"
         # with equal (S, Z), differing codes only near a tie
         assert not np.any(d1 & same_par[..., None] & (m1 >= DQ_MARGIN)), "s1 code differs away from a tie"
         assert not np.any(dm & same_par[..., None] & (mmu >= DQ_MARGIN)), "mean code differs away from a tie"
@@ -202,7 +239,8 @@ def compare_encoded_dq(cache: nsnq.KVCache, ek: dict, ev: dict, R: int, scale_ad
         cg = gh["codes"].reshape(*gh["codes"].shape[:-2], nb, R, S)
         co = e["codes"].reshape(cg.shape)
         gap = e["gap"].reshape(cg.shape)
-        n = check_codes(cg[full], co[full], gap[full], "codes (double-quantised)")
+        u = e["u"].reshape(*cg.shape[:-1], -1)
+        n = check_codes(cg[full], co[full], gap[full], u[full], e["cb"], "codes (double-quantised)")
         if scale_adjust:
             same = np.all(cg[full] == co[full], axis=-1)
             check_f16_ulp(gn2[full][same], on2[full][same], "n2")

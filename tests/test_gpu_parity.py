@@ -11,8 +11,8 @@ from kv_cache_bit_amd import nsnq, synth
 
 from helpers import (DEV, capacity, check_attention, check_codes, check_dequant, check_f16_ulp, check_tie_rate,
                      compare_encoded_dq,
-                     compare_encoded, f16_bits, gpu_encode, half_np, oracle_encode_pair, token_norms,
-                     upload_half, cb_tensor)
+                     compare_encoded, f16_bits, gpu_encode, gpu_records, half_np, oracle_encode, oracle_encode_pair,
+                     token_norms, upload_half, cb_tensor)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,7 +78,7 @@ def test_encode_candidate_lists(oracle_codebooks, R, B, H, L, flags, use_signs):
     _, _, full = gpu_encode(k, v, 2, R, cb, flags=flags, signs=signs)
     dq = bool(flags & nsnq.NSNQ_DOUBLE_QUANT)
     kw = dict(signs=None if signs is None else signs.numpy(), scale_adjust=adjust, dq=dq)
-    ek, ev = oracle.encode(k, R, cb, **kw), oracle.encode(v, R, cb, **kw)
+    ek, ev = oracle_encode_pair(k, v, R, cb, **kw)
     if dq:
         compare_encoded_dq(cache, ek, ev, R, scale_adjust=adjust)
     else:
@@ -86,10 +86,20 @@ def test_encode_candidate_lists(oracle_codebooks, R, B, H, L, flags, use_signs):
     for which, e in ((0, ek), (1, ev)):
         g, f = half_np(cache, which)["codes"], half_np(full, which)["codes"]
         assert not np.any((g != f) & (e["gap"] >= 1e-4)), "pruned and exhaustive codes differ away from a tie"
-    # dequant and decode read the cache as usual
+    # decode reads the list-encoded cache as usual: against the oracle's
+    # attention over the GPU cache's own records (every case, double-quantised
+    # ones included), over the oracle's records placed in a GPU cache, and end
+    # to end where every code equals the oracle's
     q = synth.queries(150 + L, 0, B, 2 * H, D)
-    ref = oracle.reference_decode(q, ek, ev, ek["n_quant"], ek["n_resid"], R, cb, signs=kw["signs"])
     o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), cache).float().cpu().numpy()
+    gk, gv = gpu_records(cache, 0), gpu_records(cache, 1)
+    check_attention(o, oracle.reference_decode(q, gk, gv, cache.n_quant, cache.n_resid, R, cb, signs=kw["signs"]))
+    ref = oracle.reference_decode(q, ek, ev, ek["n_quant"], ek["n_resid"], R, cb, signs=kw["signs"])
+    oc = nsnq.KVCache(p, B, H, capacity(L, R), DEV)
+    upload_half(oc, 0, ek)
+    upload_half(oc, 1, ev)
+    oc.n_quant, oc.n_resid = ek["n_quant"], ek["n_resid"]
+    check_attention(nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), oc).float().cpu().numpy(), ref)
     same = all(np.array_equal(half_np(cache, w)["codes"], e["codes"]) for w, e in ((0, ek), (1, ev)))
     if same and not dq:
         check_attention(o, ref)
@@ -155,8 +165,8 @@ def test_encode_candidate_lists_degenerate(oracle_codebooks):
     torch.cuda.synchronize()
     flips = total = 0
     for b, Lb in enumerate(lengths):
-        e_k = oracle.encode(kk[b:b + 1, :, :Lb + 2], R, cb)
-        e_v = oracle.encode(vv[b:b + 1, :, :Lb + 2], R, cb)
+        e_k = oracle_encode(kk[b:b + 1, :, :Lb + 2], R, cb)
+        e_v = oracle_encode(vv[b:b + 1, :, :Lb + 2], R, cb)
         assert (rc.seq_quant[b].item(), rc.seq_resid[b].item()) == (e_k["n_quant"], e_k["n_resid"])
         f, t = _check_row(rc, b, e_k, e_v)
         flips, total = flips + f, total + t
@@ -285,6 +295,57 @@ def test_decode_late_maxima(oracle_codebooks, bits, Hq, Hkv):
         check_attention(o, ref)
 
 
+@pytest.mark.parametrize("bits,Hq,Hkv", [(2, 1, 1), (2, 4, 1), (2, 8, 1), (1, 1, 1), (1, 4, 1), (2, 32, 1)])
+@pytest.mark.parametrize("case", ["small_v_sink", "huge_v_token"])
+def test_decode_weight_range(oracle_codebooks, bits, Hq, Hkv, case):
+    """Value weights at both ends of the fp16 range, in every decode kernel
+    (LUT with FMA values, LUT with matrix-core values at 1 bit, grouped heads
+    with one token per lane and with 16-token tiles):
+      small_v_sink: values of RMS 1e-2 and one key along every query, so one
+        token takes nearly all the softmax weight and each other token of the
+        2048-token split gets p ~ 1e-5; their p N1 N2 and p N1 fall below the
+        fp16 subnormals unless scaled, and their mean term is ~1% of the output;
+      huge_v_token: a value vector of norm 4e5 (N1 N2 above the fp16 maximum).
+    One split holds all 2048 quantised tokens."""
+    cb = oracle_codebooks[bits]
+    R, B, L = 128, 1, 2049
+    k, v = _kv(560 + bits, B, Hkv, L)
+    q = synth.queries(560 + bits, 0, B, Hq, D)
+    G = Hq // Hkv
+    if case == "small_v_sink":
+        vf = v.float()
+        v = (vf * (1e-2 / vf.pow(2).mean().sqrt())).half()
+        kf = k.float()
+        k = (kf / kf.norm(dim=-1).mean()).half()  # key norms ~1: scores of order 1
+        for hk in range(Hkv):
+            qs = q[0, hk * G:(hk + 1) * G].float()
+            dirn = qs.sum(0) / qs.sum(0).norm()
+            k[0, hk, 700] = (dirn * 12.0 * G ** 0.5).half()  # score ~12 for each head
+    else:
+        sgn = torch.where(torch.arange(D) % 3 == 0, -1.0, 1.0)
+        v[0, :, 900] = (sgn * 4e5 / np.sqrt(D)).half()
+        assert float(v[0, 0, 900].float().norm()) > 3.7e5
+    ek, ev = oracle_encode_pair(k, v, R, cb)
+    assert ek["n_quant"] == 2048
+    ref = _decode_ref(q, ek, ev, cb, R)
+    assert np.all(np.isfinite(ref))
+    p = nsnq.params(bits, R)
+    cbt = cb_tensor(cb)
+    cache = nsnq.KVCache(p, B, Hkv, capacity(L, R), DEV)
+    upload_half(cache, 0, ek)
+    upload_half(cache, 1, ev)
+    cache.n_quant, cache.n_resid = ek["n_quant"], ek["n_resid"]
+    o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), cache, num_splits=1).float().cpu().numpy()
+    assert np.all(np.isfinite(o))
+    check_attention(o, ref)
+    # end to end: the GPU's own encoding, attended, against the oracle's
+    # attention over the same records
+    _, _, gc = gpu_encode(k, v, bits, R, cb)
+    o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), gc, num_splits=1).float().cpu().numpy()
+    check_attention(o, oracle.reference_decode(q, gpu_records(gc, 0), gpu_records(gc, 1), gc.n_quant,
+                                               gc.n_resid, R, cb))
+
+
 def test_decode_workspace_reuse(oracle_codebooks):
     """One workspace serves calls of different shapes, kernels (one KV head per
     query head, and grouped heads) and split counts in turn; every result
@@ -385,7 +446,7 @@ def test_double_quant_encode_dequant_decode(oracle_codebooks, bits, R, Hq, Hkv, 
     p, cbt, cache = gpu_encode(k[:, :, :L], v[:, :, :L], bits, R, cb, flags=flags)
     assert cache.dq
     kw = dict(dq=True, scale_adjust=adjust)
-    ek, ev = oracle.encode(k[:, :, :L], R, cb, **kw), oracle.encode(v[:, :, :L], R, cb, **kw)
+    ek, ev = oracle_encode(k[:, :, :L], R, cb, **kw), oracle_encode(v[:, :, :L], R, cb, **kw)
     masks = compare_encoded_dq(cache, ek, ev, R, scale_adjust=adjust)
     nq = ek["n_quant"]
     # dequant of the GPU's own records, on blocks and tokens that agree
@@ -409,7 +470,7 @@ def test_double_quant_encode_dequant_decode(oracle_codebooks, bits, R, Hq, Hkv, 
     if ek["n_resid"] == R:
         nsnq.nsnq_append_kv(p, cbt, k[:, :, L].contiguous().to(DEV), v[:, :, L].contiguous().to(DEV), cache)
         torch.cuda.synchronize()
-        ek2, ev2 = oracle.encode(k, R, cb, **kw), oracle.encode(v, R, cb, **kw)
+        ek2, ev2 = oracle_encode(k, R, cb, **kw), oracle_encode(v, R, cb, **kw)
         compare_encoded_dq(cache, ek2, ev2, R, scale_adjust=adjust)
 
 
@@ -469,7 +530,7 @@ def _check_row(cache, b, ek, ev):
     flips = total = 0
     for which, e in ((0, ek), (1, ev)):
         g = _row_state(cache, which, b, nq, r)
-        flips += check_codes(g["codes"], e["codes"], e["gap"], pooled=True)
+        flips += check_codes(g["codes"], e["codes"], e["gap"], e["u"], e["cb"], pooled=True)
         total += g["codes"].size
         check_f16_ulp(g["scales"], e["scales"], "scales")
         check_f16_ulp(g["mu"], e["mu"], "mu")
@@ -507,8 +568,8 @@ def test_ragged_prefill_append_decode(oracle_codebooks, bits, R, Hq, Hkv):
         oc = nsnq.KVCache(p, B, Hkv, cache.cap_tokens, DEV, ragged=True)
         oc.n_quant, oc.n_resid, oc.max_len = cache.n_quant, cache.n_resid, cache.max_len
         for b, Lb in enumerate(cur_len):
-            ek = oracle.encode(k[b:b + 1, :, :Lb], R, cb)
-            ev = oracle.encode(v[b:b + 1, :, :Lb], R, cb)
+            ek = oracle_encode(k[b:b + 1, :, :Lb], R, cb)
+            ev = oracle_encode(v[b:b + 1, :, :Lb], R, cb)
             assert (sq[b], sr[b]) == (ek["n_quant"], ek["n_resid"]), (b, Lb)
             assert sq[b] <= cache.n_quant and sr[b] <= cache.n_resid
             f, t = _check_row(cache, b, ek, ev)
@@ -653,7 +714,7 @@ def test_llama2_layer_1bit_b16_sampled(oracle_codebooks):
     units = [(0, 0), (5, 17), (15, 31)]
     ks = torch.stack([k[b, h] for b, h in units]).cpu()
     vs = torch.stack([v[b, h] for b, h in units]).cpu()
-    ek, ev = oracle.encode(ks, R, cb), oracle.encode(vs, R, cb)
+    ek, ev = oracle_encode(ks, R, cb), oracle_encode(vs, R, cb)
     compare_encoded(cache, ek, ev, units=units)
     for i, (b, h) in enumerate(units):
         eki = {key: (val[i:i + 1, None] if isinstance(val, np.ndarray) else val) for key, val in ek.items()}
@@ -675,7 +736,7 @@ def _sampled_layer_check(cb, w, layer, units, outlier):
     ks = torch.stack([k[b, h] for b, h in units]).cpu()
     vs = torch.stack([v[b, h] for b, h in units]).cpu()
     del k, v
-    ek, ev = oracle.encode(ks, R, cb), oracle.encode(vs, R, cb)
+    ek, ev = oracle_encode(ks, R, cb), oracle_encode(vs, R, cb)
     compare_encoded(cache, ek, ev, units=units)
     for i, (b, h) in enumerate(units):
         eki = {key: (val[i:i + 1, None] if isinstance(val, np.ndarray) else val) for key, val in ek.items()}

@@ -125,3 +125,77 @@ def test_post_transform_stats_standard_normal():
     x2 = synth.kv_unit(9, T, D).numpy()
     u2 = oracle.encode(x2[None], 128, np.zeros((256, 4), np.uint16), with_u=True)["u"][0]
     assert np.allclose(np.mean(u2 ** 2), 1.0, rtol=1e-9)
+
+
+@pytest.mark.parametrize("L,R,nq,r", [
+    (4096, 128, 3968, 128),   # the LLaMA-2-7B layer: 3968 flushed tokens, a full 128-token window
+    (128, 128, 0, 128),       # one window's worth: nothing is flushed yet
+    (129, 128, 128, 1),       # one more token: the first block is flushed
+    (1, 128, 0, 1),
+    (0, 128, 0, 0),
+    (512, 64, 448, 64),       # the tiny workload: 7 blocks
+    (32768, 128, 32640, 128),  # the LLaMA-3.1-8B context: 255 blocks
+    (300, 128, 256, 44),
+])
+def test_residual_split_literal_values(L, R, nq, r):
+    """The residual window keeps the last ((L - 1) mod R) + 1 tokens in fp16
+    and the rest are flushed in whole blocks (the window is flushed only when a
+    new token arrives at a full window): literal values, including the
+    LLaMA-2 layer's 3968 flushed tokens."""
+    assert oracle.resid_count(L, R) == r
+    if L > 0:
+        x = synth.kv_unit(3, L, D).numpy()[None]
+        enc = oracle.encode(x, R, np.zeros((256, 4), np.uint16))
+        assert (enc["n_quant"], enc["n_resid"]) == (nq, r)
+        assert enc["codes"].shape[1] == nq and nq % R == 0
+
+
+def _near_constant_block(R, ulps, chan=17, tok=5):
+    """A block of R identical fp16 tokens except token `tok`, whose channel
+    `chan` is moved by `ulps` fp16 steps; returns (x fp16 [R, d], n2 of that
+    token computed here in fp64 from the definition)."""
+    base = synth.kv_unit(21, 1, D).numpy()[0]
+    x = np.tile(base, (R, 1))
+    b = x.view(np.uint16).copy()
+    b[tok, chan] = np.uint16(int(b[tok, chan]) + ulps)
+    x = b.view(np.float16)
+    xd = x.astype(np.float64)
+    y = xd / (np.linalg.norm(xd, axis=1, keepdims=True) / np.sqrt(D))
+    z = y - y.mean(axis=0)
+    return x, np.linalg.norm(z[tok]) / np.sqrt(D), z[tok]
+
+
+def test_n2_floor_threshold():
+    """A token that differs from its block mean by relative norm n2 >= 2^-12
+    keeps its direction (w = z / n2, N2 = fp16(n2)); below 2^-12 it is stored
+    with n2 = 0 and w = 0.  Tokens at about 2^-11 and 1.2 * 2^-12 must keep
+    their direction, tokens at 0.8 * 2^-12 and about 2^-13 must not (so a
+    threshold of 2^-8 or of 2^-14 fails)."""
+    R = 64
+    found = {}
+    targets = {"2^-11": 2.0 ** -11, "1.2*2^-12": 1.2 * 2.0 ** -12, "0.8*2^-12": 0.8 * 2.0 ** -12,
+               "2^-13": 2.0 ** -13}
+    for ulps in range(1, 400):
+        x, n2, z = _near_constant_block(R, ulps)
+        for name, t in targets.items():
+            if name not in found and abs(n2 / t - 1) < 0.1:
+                found[name] = (x, n2, z)
+    assert set(found) == set(targets), sorted(found)
+    for name, (x, n2, z) in found.items():
+        o = oracle.nsn_block(x)
+        tok = 5
+        assert abs(o["n2"][tok] - (n2 if n2 >= 2.0 ** -12 else 0.0)) <= 1e-9 * n2
+        others = np.delete(np.arange(R), tok)
+        if n2 >= 2.0 ** -12:
+            assert o["n2"][tok] > 0, name
+            assert np.allclose(o["w"][tok], z / n2, rtol=1e-6, atol=1e-9), name
+            assert np.isclose(np.linalg.norm(o["w"][tok]), np.sqrt(D), rtol=1e-9)
+            # and the stored fp16 value through the encoder
+            enc = oracle.encode(np.concatenate([x, x[:1]])[None], R, np.zeros((256, 4), np.uint16))
+            assert enc["scales"][0, tok, 1] == oracle.f64_to_f16(np.array([n2]))[0]
+        else:
+            assert o["n2"][tok] == 0 and np.all(o["w"][tok] == 0), name
+            enc = oracle.encode(np.concatenate([x, x[:1]])[None], R, np.zeros((256, 4), np.uint16))
+            assert enc["scales"][0, tok, 1] == 0
+        # the other tokens sit (R-1) times closer to the mean, below the floor
+        assert np.all(o["n2"][others] == 0)
