@@ -30,9 +30,14 @@
  *    next synchronisation.  Inputs must be finite (not checked).
  *  - The library allocates no memory and prints nothing.  Its only global
  *    state is per device (up to 64 devices per process): the kernels'
- *    dynamic-LDS attribute and one occupancy query per grouped-head kernel
- *    variant, each set once on first use with atomic records (concurrent
- *    first calls are safe).  Calls on different streams are independent.
+ *    dynamic-LDS attribute, one occupancy query per grouped-head kernel
+ *    variant and the device address of the static scratch of
+ *    nsnq_decode_attention_noalloc, each set once on first use with atomic
+ *    records (concurrent first calls are safe), and that static scratch
+ *    itself (NSNQ_SCRATCH_BYTES of device memory per device, from the load
+ *    of the library to the end of the process).  Calls on different streams
+ *    are independent, except nsnq_decode_attention_noalloc calls, which
+ *    share one device's scratch.
  *  - Value weights of the decode kernels that run on the matrix cores are
  *    carried in fp16 with a power-of-two factor per 64-token chunk (undone
  *    exactly in fp32), so the stored scales may take any finite fp16 value.
@@ -67,7 +72,7 @@
 extern "C" {
 #endif
 
-#define NSNQ_ABI_VERSION 5
+#define NSNQ_ABI_VERSION 6
 
 typedef int32_t nsnq_status;
 enum {
@@ -75,7 +80,9 @@ enum {
   NSNQ_EINVAL = 1,       /* bad argument, shape, counter or alignment */
   NSNQ_EUNSUPPORTED = 2, /* valid but not implemented (e.g. d != 128) */
   NSNQ_EHIP = 3,         /* a HIP launch or runtime call failed */
-  NSNQ_EWORKSPACE = 4    /* workspace missing or too small */
+  NSNQ_EWORKSPACE = 4,   /* workspace missing or too small */
+  NSNQ_ESCRATCH = 5      /* the call needs more than NSNQ_SCRATCH_BYTES of
+                            static scratch (nsnq_decode_attention_noalloc) */
 };
 
 /* Format flags. */
@@ -303,6 +310,28 @@ nsnq_status nsnq_decode_attention(const nsnq_params* p, const uint16_t* codebook
                                   int32_t q_heads, const nsnq_cache* cache, float softmax_scale,
                                   int32_t num_splits, uint16_t* out, void* ws, size_t ws_bytes,
                                   void* stream);
+
+/* Decode attention without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc).  The same computation, kernels and launch plan as
+ * nsnq_decode_attention (same arguments, same results bit for bit), with the
+ * split partials in a static device array of NSNQ_SCRATCH_BYTES that the
+ * library holds on each device it runs on until the process ends.  Calls no
+ * hipMalloc / hipFree and allocates nothing.
+ *   Returns NSNQ_ESCRATCH, before touching the device, when the call would
+ *   need more than NSNQ_SCRATCH_BYTES (nsnq_decode_workspace_bytes() of the
+ *   same arguments gives the need: 4 (d + 2) bytes per (row, query head,
+ *   split); e.g. 12.8 MB for 256 rows x 32 heads x 3 splits).  Nothing in
+ *   the scratch has to start at zero: every call writes all it reads.
+ *   All calls on one device share that device's scratch, which keeps the last
+ *   call's contents: calls that can overlap on one device (different streams
+ *   or threads without ordering) race and must be serialised by the caller;
+ *   calls in one stream are ordered.  The first call on a device looks up the
+ *   scratch's device address (hipGetSymbolAddress) with that device current. */
+#define NSNQ_SCRATCH_BYTES (16u << 20)
+nsnq_status nsnq_decode_attention_noalloc(const nsnq_params* p, const uint16_t* codebook, const uint16_t* q,
+                                          int32_t q_heads, const nsnq_cache* cache, float softmax_scale,
+                                          int32_t num_splits, uint16_t* out, void* stream);
 
 /* Keys quantised before RoPE (technical summary sec. 4, Attention
  * Computation: NSN is applied to keys before the rotary embedding).  Token t

@@ -2,6 +2,8 @@
 // configuration and counter bookkeeping.  Every check runs before any HIP
 // call, so a rejected call touches neither the GPU nor the cache.
 
+#include <atomic>
+
 #include "../../include/nsnq.h"
 #include "nsnq_device.hpp"
 #include "nsnq_launch.hpp"
@@ -154,6 +156,7 @@ const char* nsnq_status_str(nsnq_status st) {
     case NSNQ_EUNSUPPORTED: return "unsupported parameters";
     case NSNQ_EHIP: return "HIP runtime error";
     case NSNQ_EWORKSPACE: return "workspace missing or too small";
+    case NSNQ_ESCRATCH: return "call needs more than the library's static scratch (NSNQ_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -529,6 +532,60 @@ nsnq_status nsnq_decode_attention_prerope(const nsnq_params* p, const uint16_t* 
 }
 
 }  // extern "C"
+
+// ---- decode attention without a caller workspace ---------------------------
+// The split partials go to a static device array instead of a workspace the
+// caller allocates.  Every device the library runs on holds its own copy for
+// the life of the process.  In host code `scratch` names a host-side shadow,
+// not device memory: its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and only that address is
+// handed to kernels.
+static __device__ __align__(256) unsigned char scratch[NSNQ_SCRATCH_BYTES];
+
+namespace {
+std::atomic<void*> scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch, or null (status in *st).
+void* device_scratch(nsnq_status* st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    *st = NSNQ_EHIP;
+    return nullptr;
+  }
+  void* ptr = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    // concurrent first calls on one device look up the same address
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      *st = NSNQ_EHIP;
+      return nullptr;
+    }
+    scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  *st = NSNQ_OK;
+  return ptr;
+}
+}  // namespace
+
+extern "C" nsnq_status nsnq_decode_attention_noalloc(const nsnq_params* p, const uint16_t* codebook,
+                                                     const uint16_t* q, int32_t q_heads, const nsnq_cache* cache,
+                                                     float softmax_scale, int32_t num_splits, uint16_t* out,
+                                                     void* stream) {
+  // every host check first: a call that is rejected touches no device state
+  nsnq_status s = check_params(p);
+  if (s != NSNQ_OK) return s;
+  s = check_cache(p, cache);
+  if (s != NSNQ_OK) return s;
+  if (q_heads <= 0 || q_heads % cache->kv_heads != 0 || num_splits < 0) return NSNQ_EINVAL;
+  const size_t need = nsnq_decode_workspace_bytes(p, cache, q_heads, num_splits);
+  if (need > (size_t)NSNQ_SCRATCH_BYTES) return NSNQ_ESCRATCH;
+  void* ws = device_scratch(&s);
+  if (!ws) return s;
+  // the kernels write every partial they read: nothing needs clearing
+  return run_decode(p, codebook, q, q_heads, cache, softmax_scale, nullptr, num_splits, out, ws,
+                    (size_t)NSNQ_SCRATCH_BYTES, stream);
+}
 
 namespace {
 nsnq_status run_decode(const nsnq_params* p, const uint16_t* codebook, const uint16_t* q, int32_t q_heads,

@@ -17,7 +17,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnsnq.so")
 
-NSNQ_OK, NSNQ_EINVAL, NSNQ_EUNSUPPORTED, NSNQ_EHIP, NSNQ_EWORKSPACE = range(5)
+NSNQ_OK, NSNQ_EINVAL, NSNQ_EUNSUPPORTED, NSNQ_EHIP, NSNQ_EWORKSPACE, NSNQ_ESCRATCH = range(6)
+NSNQ_SCRATCH_BYTES = 16 << 20  # static scratch of nsnq_decode_attention_noalloc, per device
 NSNQ_SCALE_ADJUST = 1
 NSNQ_DOUBLE_QUANT = 2
 
@@ -64,6 +65,7 @@ _SIGNATURES = {
     "nsnq_decode_attention": (i32, [_PP, P, P, i32, _PC, f32, i32, P, P, size_t, P]),
     "nsnq_decode_attention_prerope": (i32, [_PP, P, P, i32, _PC, f32, ctypes.POINTER(nsnq_rope), i32, P, P,
                                              size_t, P]),
+    "nsnq_decode_attention_noalloc": (i32, [_PP, P, P, i32, _PC, f32, i32, P, P]),
     "nsnq_fp16_decode_workspace_bytes": (size_t, [i32, i32, i32, i32]),
     "nsnq_fp16_decode_attention": (i32, [P, i32, P, P, i32, i32, i32, f32, i32, P, P, size_t, P]),
 }
@@ -295,6 +297,23 @@ def nsnq_decode_attention(p: nsnq_params, codebook, q, cache: "KVCache", softmax
                                        float(softmax_scale), num_splits, _ptr(out), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream(stream)),
            "nsnq_decode_attention")
+    return out
+
+
+def nsnq_decode_attention_noalloc(p: nsnq_params, codebook, q, cache: "KVCache", out,
+                                  softmax_scale: float | None = None, num_splits: int = 0, stream=None):
+    """One decode step into the caller's `out` (fp16 [B, Hq, d]) with the split
+    partials in the library's static device scratch: no allocation here or in
+    the library."""
+    B, Hq, d = q.shape
+    assert q.dtype == torch.float16 and q.is_contiguous()
+    assert out.dtype == torch.float16 and out.is_contiguous() and out.shape == q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    c = cache.c_struct()
+    _check(lib().nsnq_decode_attention_noalloc(ctypes.byref(p), _ptr(codebook), _ptr(q), Hq, ctypes.byref(c),
+                                               float(softmax_scale), num_splits, _ptr(out), _stream(stream)),
+           "nsnq_decode_attention_noalloc")
     return out
 
 

@@ -26,10 +26,10 @@ def nsnq():
 
 def test_exports_every_declared_symbol(nsnq):
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(nsnq.lib(), n), n
-    assert nsnq.nsnq_abi_version() == 5
+    assert nsnq.nsnq_abi_version() == 6
     assert nsnq.lib().nsnq_status_str(1) == b"invalid argument"
 
 
@@ -142,3 +142,24 @@ def test_buffer_bytes(nsnq):
         nsnq.nsnq_buffer_bytes(nsnq.params(2, 128), 100)
     with pytest.raises(nsnq.NsnqError):
         nsnq.nsnq_buffer_bytes(nsnq.params(2, 128, flags=8), 128)
+
+
+def test_noalloc_decode_rejects_oversize_on_the_host(nsnq):
+    """The allocation-free decode refuses, before any HIP call, a call whose
+    split partials would not fit the static scratch; it validates its
+    arguments like the workspace call does."""
+    L = nsnq.lib()
+    by = ctypes.byref
+    P = 0x1000
+    p = nsnq.params(2, 128)
+    big = _cache_struct(nsnq, B=4096, H=32, cap=4096, nq=3968, nr=128)
+    need = L.nsnq_decode_workspace_bytes(by(p), by(big), 32, 0)
+    assert need > nsnq.NSNQ_SCRATCH_BYTES
+    assert L.nsnq_decode_attention_noalloc(by(p), P, P, 32, by(big), 0.088, 0, P, None) == nsnq.NSNQ_ESCRATCH
+    assert b"static scratch" in L.nsnq_status_str(nsnq.NSNQ_ESCRATCH)
+    small = _cache_struct(nsnq, B=1, H=2, cap=256, nq=128, nr=5)
+    assert L.nsnq_decode_workspace_bytes(by(p), by(small), 2, 0) <= nsnq.NSNQ_SCRATCH_BYTES
+    assert L.nsnq_decode_attention_noalloc(by(nsnq.params(3, 128)), P, P, 2, by(small), 0.088, 0, P, None) == \
+        nsnq.NSNQ_EINVAL
+    assert L.nsnq_decode_attention_noalloc(by(p), P, P, 3, by(small), 0.088, 0, P, None) == nsnq.NSNQ_EINVAL
+    assert L.nsnq_decode_attention_noalloc(by(p), P, P, 2, by(small), 0.088, -1, P, None) == nsnq.NSNQ_EINVAL
