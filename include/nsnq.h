@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define NSNQ_ABI_VERSION 6
+#define NSNQ_ABI_VERSION 7
 
 typedef int32_t nsnq_status;
 enum {
@@ -238,6 +238,25 @@ nsnq_status nsnq_finetune_codebook(const nsnq_params* p, const float* samples, i
 #define NSNQ_VQ_TABLE_BYTES 2048
 nsnq_status nsnq_vq_candidates(const nsnq_params* p, const uint16_t* codebook_host, uint8_t* table_host,
                                int32_t* span);
+
+/* 4-bit quantisation of the codebook entries (technical summary sec. 3,
+ * "Double Quantization": besides the mean o and the scale s1, the codebook
+ * entries themselves are stored in 4 bits).  The entries in storage order
+ * ([256][s]) form groups of NSNQ_CODEBOOK_DQ_GROUP; each group keeps
+ * Z = fp16(min) and S = fp16((max - min) / 15), each entry the code
+ * q = clamp(rint((v - Z) / S), 0, 15) (0 when S = 0), all formed in double.
+ *   codebook_host      fp16 [256][s], HOST memory (s = 4 at 2 bits, 8 at 1).
+ *   record_host        HOST out, NSNQ_CODEBOOK_DQ_BYTES(bits) bytes: 128 s
+ *                      bytes of codes (entry i: byte i/2, low nibble for even
+ *                      i), then (S, Z) fp16 per group.
+ *   codebook_hat_host  HOST out, fp16 [256][s]: the read-back codebook
+ *                      fp16(Z + S q), which the encode, dequant and attention
+ *                      calls then take as their codebook.
+ * Host only, synchronous.  NSNQ_EINVAL for a non-finite entry. */
+#define NSNQ_CODEBOOK_DQ_GROUP 32
+#define NSNQ_CODEBOOK_DQ_BYTES(bits) (128 * ((bits) == 2 ? 4 : 8) + 4 * (256 * ((bits) == 2 ? 4 : 8) / 32))
+nsnq_status nsnq_codebook_dq(const nsnq_params* p, const uint16_t* codebook_host, uint8_t* record_host,
+                             uint16_t* codebook_hat_host);
 
 /* Prefill encode (technical summary secs. 1-4).  k and v are fp16 streams
  * indexed [b][h][t][c] at element offsets b*stride_b + h*stride_h +

@@ -56,6 +56,7 @@ _SIGNATURES = {
     "nsnq_build_codebook": (i32, [_PP, P, i64, i32, P, P, P, P, P, size_t, P]),
     "nsnq_finetune_codebook": (i32, [_PP, P, i64, i32, f32, P, P, P, P, size_t, P]),
     "nsnq_vq_candidates": (i32, [_PP, P, P, P]),
+    "nsnq_codebook_dq": (i32, [_PP, P, P, P]),
     "nsnq_encode_kv": (i32, [_PP, P, P, P, i64, i64, i64, i32, _PC, P]),
     "nsnq_encode_kv_ragged": (i32, [_PP, P, P, P, i64, i64, i64, P, i32, _PC, P]),
     "nsnq_flush_residual": (i32, [_PP, P, _PC, P]),
@@ -162,6 +163,23 @@ def nsnq_vq_candidates(p: nsnq_params, codebook: torch.Tensor) -> tuple[torch.Te
     _check(lib().nsnq_vq_candidates(ctypes.byref(p), cb.data_ptr(), table.data_ptr(), ctypes.byref(span)),
            "nsnq_vq_candidates")
     return table, span.value
+
+
+CODEBOOK_DQ_GROUP = 32
+
+
+def nsnq_codebook_dq(p: nsnq_params, codebook: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """4-bit quantisation of the codebook entries (double quantisation):
+    returns (record uint8 [bytes], read-back codebook fp16 [256, s]) on the
+    codebook's device; the record layout is in include/nsnq.h."""
+    cb = codebook.detach().to("cpu").contiguous()
+    s = sub_dim(p.bits)
+    assert cb.dtype == torch.float16 and cb.numel() == 256 * s
+    rec = torch.zeros(128 * s + 4 * (256 * s // CODEBOOK_DQ_GROUP), dtype=torch.uint8)
+    hat = torch.empty(256, s, dtype=torch.float16)
+    _check(lib().nsnq_codebook_dq(ctypes.byref(p), cb.data_ptr(), rec.data_ptr(), hat.data_ptr()),
+           "nsnq_codebook_dq")
+    return rec.to(codebook.device), hat.to(codebook.device)
 
 
 def nsnq_buffer_bytes(p: nsnq_params, cap_tokens: int) -> tuple[int, int, int, int]:

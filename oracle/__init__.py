@@ -61,6 +61,7 @@ def lib():
             "orc_dq_scales_bytes": (i32, [i32]),
             "orc_encode_dq": (i32, [P, i64, i32, i32, i32, i32, P, i32, P, i32, P, P, P, P, P, P, P, P, P]),
             "orc_dequant_dq": (None, [P, P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P]),
+            "orc_codebook_dq": (None, [P, i32, i32, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(_lib, name)
@@ -162,6 +163,21 @@ def rtn4(v) -> dict:
     m = np.empty(v.size, np.float64)
     lib().orc_rtn4(_p(v), v.size, ctypes.byref(Z), ctypes.byref(S), _p(q), _p(vh), _p(m))
     return dict(Z=Z.value, S=S.value, q=q, vhat=vh, margin=m)
+
+
+def codebook_dq(codebook, group: int = 32) -> dict:
+    """4-bit double quantisation of the codebook entries (groups of `group`
+    consecutive entries in storage order).  Returns record (uint8: n/2 bytes
+    of codes, then (S, Z) fp16 per group), cb_hat (fp16 bits, the read-back
+    codebook, same shape as the input) and margin (per entry)."""
+    cb = as_f16_bits(codebook)
+    n = cb.size
+    assert n % group == 0 and group % 2 == 0
+    rec = np.zeros(n // 2 + 4 * (n // group), np.uint8)
+    hat = np.zeros(cb.shape, np.uint16)
+    margin = np.zeros(cb.shape, np.float64)
+    lib().orc_codebook_dq(_p(np.ascontiguousarray(cb)), n, group, _p(rec), _p(hat), _p(margin))
+    return dict(record=rec, cb_hat=hat, margin=margin)
 
 
 def encode(x, R: int, codebook, with_u: bool = False, signs=None, scale_adjust: bool = False,

@@ -356,6 +356,45 @@ void orc_rtn4(const double* v, int n, uint16_t* Zb, uint16_t* Sb, uint8_t* q, do
   *Sb = sb;
 }
 
+/* Double quantisation of the codebook entries [P3 sec. 3, DQ: besides o and
+ * s1, the codebook entries themselves are stored in 4 bits].  The pages give
+ * no group for the codebook.  Reading taken here: the same asymmetric 4-bit
+ * round-to-nearest as orc_rtn4, over groups of `group` consecutive entries of
+ * the codebook in storage order (codeword-major [ncw][s]; the bench and tests
+ * use 32, the group the pages give for o).  The codebook the encoder and the
+ * attention use is then the read-back one, v_hat = Z + S q rounded to fp16
+ * (S q and the sum are formed in double).
+ *   cb        fp16 [n] (n = ncw * s, a multiple of group)
+ *   record    out: n/2 bytes of 4-bit codes (entry i: byte i/2, low nibble for
+ *             even i), then (S, Z) fp16 of each group (4 bytes per group)
+ *   cb_hat    out: fp16 [n], the read-back codebook
+ *   margin    out (may be NULL): per entry, the distance of its rounding
+ *             decision from a tie (orc_rtn4). */
+void orc_codebook_dq(const uint16_t* cb, int n, int group, uint8_t* record, uint16_t* cb_hat, double* margin) {
+  double* v = (double*)malloc(sizeof(double) * (size_t)group);
+  double* vh = (double*)malloc(sizeof(double) * (size_t)group);
+  uint8_t* q = (uint8_t*)malloc((size_t)group);
+  memset(record, 0, (size_t)n / 2);
+  for (int g = 0; g * group < n; ++g) {
+    for (int i = 0; i < group; ++i) v[i] = orc_h2d(cb[g * group + i]);
+    uint16_t Zb, Sb;
+    orc_rtn4(v, group, &Zb, &Sb, q, vh, margin ? margin + g * group : NULL);
+    for (int i = 0; i < group; ++i) {
+      const int e = g * group + i;
+      record[e / 2] |= (uint8_t)(q[i] << (4 * (e & 1)));
+      cb_hat[e] = orc_d2h(vh[i]);
+    }
+    uint8_t* sz = record + n / 2 + 4 * g;
+    sz[0] = (uint8_t)(Sb & 0xff);
+    sz[1] = (uint8_t)(Sb >> 8);
+    sz[2] = (uint8_t)(Zb & 0xff);
+    sz[3] = (uint8_t)(Zb >> 8);
+  }
+  free(v);
+  free(vh);
+  free(q);
+}
+
 /* Byte layout of one block of R tokens (per stream) in the double-quantised
  * format:
  *   scales record, orc_dq_scales_bytes(R) bytes:

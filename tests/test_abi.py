@@ -26,10 +26,10 @@ def nsnq():
 
 def test_exports_every_declared_symbol(nsnq):
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(nsnq.lib(), n), n
-    assert nsnq.nsnq_abi_version() == 6
+    assert nsnq.nsnq_abi_version() == 7
     assert nsnq.lib().nsnq_status_str(1) == b"invalid argument"
 
 
@@ -163,3 +163,35 @@ def test_noalloc_decode_rejects_oversize_on_the_host(nsnq):
         nsnq.NSNQ_EINVAL
     assert L.nsnq_decode_attention_noalloc(by(p), P, P, 3, by(small), 0.088, 0, P, None) == nsnq.NSNQ_EINVAL
     assert L.nsnq_decode_attention_noalloc(by(p), P, P, 2, by(small), 0.088, -1, P, None) == nsnq.NSNQ_EINVAL
+
+
+@pytest.mark.parametrize("bits", [2, 1])
+def test_codebook_dq_matches_oracle(nsnq, oracle_codebooks, bits):
+    """The library's host quantisation of the codebook entries (4 bits) gives
+    the oracle's record and read-back codebook byte for byte, on the k-means
+    codebook and on one with duplicated codewords, a constant group and
+    values near fp16 ties."""
+    import numpy as np
+    import torch
+
+    import oracle
+    cbs = [oracle_codebooks[bits]]
+    c2 = oracle_codebooks[bits].copy()
+    s = c2.shape[1]
+    c2[5] = c2[4]
+    c2[64:64 + 32 // s] = c2[64]           # a constant group
+    c2[100] = np.float16(1.0 + 2.0 ** -10).view(np.uint16)
+    cbs.append(c2)
+    for cb in cbs:
+        p = nsnq.params(bits, 128)
+        rec, hat = nsnq.nsnq_codebook_dq(p, torch.from_numpy(cb.view(np.float16)))
+        o = oracle.codebook_dq(cb, 32)
+        assert np.array_equal(rec.numpy(), o["record"])
+        assert np.array_equal(hat.numpy().view(np.uint16), o["cb_hat"])
+    L = nsnq.lib()
+    bad = cbs[0].copy()
+    bad[7, 0] = 0x7c00  # inf
+    out = np.zeros(4096, np.uint8)
+    outh = np.zeros_like(bad)
+    assert L.nsnq_codebook_dq(ctypes.byref(nsnq.params(bits, 128)), bad.ctypes.data, out.ctypes.data,
+                              outh.ctypes.data) == nsnq.NSNQ_EINVAL

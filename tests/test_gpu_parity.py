@@ -474,6 +474,71 @@ def test_double_quant_encode_dequant_decode(oracle_codebooks, bits, R, Hq, Hkv, 
         compare_encoded_dq(cache, ek2, ev2, R, scale_adjust=adjust)
 
 
+# --------------------------------------------- 4-bit codebook entries --
+
+@pytest.mark.parametrize("bits,R,flags,cand,Hq,Hkv,dup", [
+    (2, 128, 0, False, 2, 2, False),
+    (2, 128, nsnq.NSNQ_DOUBLE_QUANT, True, 8, 2, False),   # the whole double-quantised format, G = 4
+    (2, 64, nsnq.NSNQ_DOUBLE_QUANT | nsnq.NSNQ_SCALE_ADJUST, True, 2, 1, True),
+    (2, 128, 0, True, 4, 4, True),                          # duplicated codewords through the lists
+    (1, 64, nsnq.NSNQ_DOUBLE_QUANT, False, 2, 2, False),
+    (1, 128, 0, False, 1, 1, True),
+])
+def test_codebook_4bit_entries(oracle_codebooks, bits, R, flags, cand, Hq, Hkv, dup):
+    """Double quantisation of the codebook entries themselves: the library's
+    4-bit read-back codebook (equal to the oracle's, checked on the CPU) drives
+    encode, dequant and decode on the GPU, against the oracle running on the
+    oracle's own read-back codebook; with duplicated codewords (the lowest
+    index must win, through the candidate lists too)."""
+    cb = oracle_codebooks[bits].copy()
+    if dup:  # pairs inside one 32-entry group, so they stay equal in 4 bits
+        cb[9] = cb[8]
+        cb[18] = cb[17]
+    o = oracle.codebook_dq(cb, 32)
+    cbq = o["cb_hat"]
+    p = nsnq.params(bits, R, flags=flags)
+    _, hat = nsnq.nsnq_codebook_dq(p, cb_tensor(cb))
+    assert np.array_equal(f16_bits(hat), cbq)
+    if dup:
+        assert np.array_equal(cbq[9], cbq[8]) and np.array_equal(cbq[18], cbq[17])
+    B, L = 2, 4 * R + 5
+    k, v = _kv(1100 + bits + R, B, Hkv, L)
+    q = synth.queries(1100 + bits + R, 0, B, Hq, D)
+    dq = bool(flags & nsnq.NSNQ_DOUBLE_QUANT)
+    adjust = bool(flags & nsnq.NSNQ_SCALE_ADJUST)
+    pe = nsnq.with_candidates(p, hat) if cand else p
+    if cand:
+        assert pe.vq_span in (64, 80, 96)
+    cache = nsnq.KVCache(p, B, Hkv, capacity(L, R), DEV)
+    nsnq.nsnq_encode_kv(pe, hat, k.to(DEV), v.to(DEV), L, cache)
+    torch.cuda.synchronize()
+    ek, ev = oracle_encode_pair(k, v, R, cbq, scale_adjust=adjust, dq=dq)
+    if dq:
+        compare_encoded_dq(cache, ek, ev, R, scale_adjust=adjust)
+    else:
+        compare_encoded(cache, ek, ev, scale_adjust=adjust)
+    if dup:  # the higher index of a duplicated pair is never chosen
+        for w in (0, 1):
+            g = half_np(cache, w)["codes"]
+            assert not np.any(g == 9) and not np.any(g == 18)
+    nq = ek["n_quant"]
+    if not dq:
+        for which, e, x in ((0, ek, k), (1, ev, v)):
+            g = nsnq.nsnq_dequant(p, hat, cache, which, 0, nq, torch.float32).cpu().numpy()
+            ref = oracle.dequant(e["codes"], e["scales"], e["mu"], R, cbq)
+            same = np.all(half_np(cache, which)["codes"] == e["codes"], axis=-1)
+            check_dequant(g, ref, token_norms(x[:, :, :nq].numpy()), mask=same)
+    o_gpu = nsnq.nsnq_decode_attention(p, hat, q.to(DEV), cache).float().cpu().numpy()
+    check_attention(o_gpu, oracle.reference_decode(q, gpu_records(cache, 0), gpu_records(cache, 1), cache.n_quant,
+                                                   cache.n_resid, R, cbq))
+    oc = nsnq.KVCache(p, B, Hkv, capacity(L, R), DEV)
+    upload_half(oc, 0, ek)
+    upload_half(oc, 1, ev)
+    oc.n_quant, oc.n_resid = nq, ek["n_resid"]
+    check_attention(nsnq.nsnq_decode_attention(p, hat, q.to(DEV), oc, num_splits=2).float().cpu().numpy(),
+                    oracle.reference_decode(q, ek, ev, nq, ek["n_resid"], R, cbq))
+
+
 # ------------------------------------------------- keys stored before RoPE --
 
 @pytest.mark.parametrize("bits,R,B,Hq,Hkv,L,flags,ragged", [

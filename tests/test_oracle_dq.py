@@ -128,3 +128,69 @@ def test_dq_degenerate_blocks(oracle_codebooks):
     blk = x[R:2 * R].astype(np.float64)
     err = np.linalg.norm(xh[R:2 * R] - blk, axis=1) / np.linalg.norm(blk, axis=1)
     assert err.max() < 0.5
+
+
+def _parse_codebook_record(rec, n, group):
+    """Independent reading of a codebook record: n/2 bytes of 4-bit codes
+    (entry i: byte i/2, low nibble for even i), then (S, Z) fp16 per group."""
+    nib = rec[:n // 2]
+    q = np.stack([nib & 15, nib >> 4], axis=-1).reshape(n)
+    sz = rec[n // 2:].copy().view(np.float16).astype(np.float64).reshape(n // group, 2)
+    return q, sz[:, 0], sz[:, 1]
+
+
+@pytest.mark.parametrize("bits", [2, 1])
+def test_codebook_dq_nearest_level_and_layout(oracle_codebooks, bits):
+    """The codebook entries in 4 bits (technical summary sec. 3, DQ): each
+    group of 32 consecutive entries has Z = fp16(min), S = fp16(range / 15);
+    every code is the nearest of the group's 16 levels (independent search),
+    the read-back codebook is fp16(Z + S q), and it stays within half a step
+    (plus the fp16 roundings) of the input."""
+    cb = oracle_codebooks[bits]
+    n = cb.size
+    o = oracle.codebook_dq(cb, 32)
+    assert o["record"].size == n // 2 + 4 * (n // 32)
+    q, S, Z = _parse_codebook_record(o["record"], n, 32)
+    v = cb.reshape(-1).view(np.float16).astype(np.float64)
+    g = np.arange(n) // 32
+    vg = v.reshape(-1, 32)
+    assert np.array_equal(Z, vg.min(1).astype(np.float16).astype(np.float64))
+    assert np.array_equal(S, ((vg.max(1) - vg.min(1)) / 15).astype(np.float16).astype(np.float64))
+    levels = Z[:, None] + S[:, None] * np.arange(16)[None, :]
+    near = np.argmin(np.abs(v[:, None] - levels[g]), axis=1)
+    ok = o["margin"].reshape(-1) > 1e-9
+    assert np.array_equal(q[ok], near[ok])
+    hat = (Z[g] + S[g] * q).astype(np.float16)
+    assert np.array_equal(o["cb_hat"].reshape(-1), hat.view(np.uint16))
+    err = np.abs(hat.astype(np.float64) - v)
+    assert np.all(err <= S[g] / 2 + 2.0 ** -11 * (np.abs(v) + 16 * S[g]) + 2.0 ** -24)
+    # the codebook keeps its shape; 4-bit codes cost 0.5 B per entry
+    assert o["cb_hat"].shape == cb.shape
+
+
+def test_codebook_dq_exact_grid_duplicates_and_constant_group():
+    """A codebook whose groups sit exactly on 4-bit grids comes back bit for
+    bit; a constant group has step 0 (every code 0, value kept); duplicated
+    codewords stay duplicated."""
+    rng = np.random.default_rng(11)
+    n = 256 * 4
+    Z = rng.integers(-64, 0, n // 32) / 16.0          # multiples of 1/16
+    S = rng.integers(1, 8, n // 32) / 64.0            # multiples of 1/64
+    k = rng.integers(0, 16, (n // 32, 32))
+    k[:, 0], k[:, 1] = 0, 15                            # span the whole range
+    vals = (Z[:, None] + S[:, None] * k).reshape(256, 4)
+    vals[40:48] = 0.75                                  # a constant group (entries 160..191)
+    vals[3] = vals[2]                                   # duplicated codewords
+    cb = vals.astype(np.float16)
+    assert np.array_equal(cb.astype(np.float64), vals)
+    o = oracle.codebook_dq(cb.view(np.uint16), 32)
+    assert np.array_equal(o["cb_hat"], cb.view(np.uint16))
+    q, Sq, Zq = _parse_codebook_record(o["record"], n, 32)
+    kk = k.reshape(-1).copy()
+    const = np.arange(n) // 32 == 5
+    assert Sq[5] == 0.0 and Zq[5] == 0.75 and np.all(q[const] == 0)
+    grid = ~const
+    grid[8:16] = False   # codewords 2 and 3 (entries 8..15) were overwritten
+    assert np.array_equal(q[grid], kk[grid])
+    hat = o["cb_hat"].view(np.float16).reshape(256, 4)
+    assert np.array_equal(hat[2], hat[3])
