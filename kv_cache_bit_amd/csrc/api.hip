@@ -628,6 +628,7 @@ nsnq_status run_decode(const nsnq_params* p, const uint16_t* codebook, const uin
   a.G = G;
   a.cap = cache->cap_tokens;
   a.R = p->block_tokens;
+  a.lgR = __builtin_ctz((unsigned)p->block_tokens);
   a.n_quant = cache->n_quant;
   a.n_resid = cache->n_resid;
   a.split_tokens = pl.split_tokens;

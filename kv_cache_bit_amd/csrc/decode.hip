@@ -148,9 +148,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.kscales) + unit * a.cap + t0;
   const uint8_t* vc = a.vcodes + (unit * a.cap + t0) * S;
   const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.vscales) + unit * a.cap + t0;
-  const uint16_t* kmu = a.kmu + (unit * nbmu + t0 / a.R) * kDim;
-  const uint16_t* vmu = a.vmu + (unit * nbmu + t0 / a.R) * kDim;
-  const int64_t blk0 = unit * nbmu + t0 / a.R;  // first block of the split (record index)
+  const uint16_t* kmu = a.kmu + (unit * nbmu + (t0 >> a.lgR)) * kDim;
+  const uint16_t* vmu = a.vmu + (unit * nbmu + (t0 >> a.lgR)) * kDim;
+  const int64_t blk0 = unit * nbmu + (t0 >> a.lgR);  // first block of the split (record index)
 
   const int sq = lane & 7, tg = lane >> 3;
   // one chunk's loads for this lane
@@ -163,12 +163,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
     uint32_t vm[DQ ? 2 : 1];
     uint32_t vcw[8];
   };
+  // Without double quantisation the chunk loads go through buffer resources
+  // bounded by the split: a prefetch past the last chunk returns zeros without
+  // touching memory, so prefetches are unconditional and the wait before a
+  // chunk's use counts only the loads issued before it.
+  constexpr bool kBuf = !DQ;
+  const int nblk_split = (ntok + a.R - 1) >> a.lgR;
+  const buf_rsrc_t rkc = make_rsrc(kc, ntok * S), rvc = make_rsrc(vc, ntok * S);
+  const buf_rsrc_t rks = make_rsrc(ks, ntok * 4), rvs = make_rsrc(vs, ntok * 4);
+  const buf_rsrc_t rvm = make_rsrc(vmu, nblk_split * kDim * 2);
   auto load_chunk = [&](int ch, ChunkRegs& r) {
     const int tl = ch * kChunk + lane;  // this lane's token for scores
+    if constexpr (kBuf) {
+#pragma unroll
+      for (int i = 0; i < S / 16; ++i) {
+        const uint4_t v4 = buf_load_b128(rkc, tl * S + 16 * i);
+        r.kcw[4 * i] = v4[0]; r.kcw[4 * i + 1] = v4[1]; r.kcw[4 * i + 2] = v4[2]; r.kcw[4 * i + 3] = v4[3];
+      }
+      const int bl = (ch * kChunk) >> a.lgR;
+      r.ksc = buf_load_b32(rks, tl * 4);
+      r.vsc = buf_load_b32(rvs, tl * 4);
+      r.vm[0] = buf_load_b32(rvm, (bl * kDim + 2 * lane) * 2);
+      if constexpr (kMV) {
+        const uint4_t v4 = buf_load_b128(rvc, tl * S);
+        r.vcw[0] = v4[0]; r.vcw[1] = v4[1]; r.vcw[2] = v4[2]; r.vcw[3] = v4[3];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int off = (ch * kChunk + 8 * tg + i) * S + sq * SPT;
+          if constexpr (SPT == 4) r.vcw[i] = buf_load_b32(rvc, off);
+          else r.vcw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rvc, off, 0, 0);
+        }
+      }
+      return;
+    }
     load_codes<S>(kc + (int64_t)tl * S, r.kcw);
-    const int bl = (ch * kChunk) / a.R;
+    const int bl = (ch * kChunk) >> a.lgR;
     if constexpr (DQ) {
-      const int SRB = dq_record_bytes(a.R), tb = tl % a.R;
+      const int SRB = dq_record_bytes(a.R), tb = tl & (a.R - 1);
       const uint8_t* kr = reinterpret_cast<const uint8_t*>(a.kscales) + (blk0 + bl) * SRB;
       const uint8_t* vr = reinterpret_cast<const uint8_t*>(a.vscales) + (blk0 + bl) * SRB;
       r.ksc = dq_token(kr, a.R, tb);
@@ -199,7 +231,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   };
   ChunkRegs cur;
   int ch = wave;
-  if (ch < nchunk) load_chunk(ch, cur);
+  if (kBuf || ch < nchunk) load_chunk(ch, cur);
 
   for (int i = tid; i < kCodewords * SUB; i += 256) cbh[i] = a.codebook[i];
   __syncthreads();
@@ -232,7 +264,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
     }
     // q . KMU_b: the 16 lanes of a row share block b = tid / 16, each lane
     // takes 8 channels of every head and the row sums them
-    if ((tid >> 4) < ntok / a.R) {
+    if ((tid >> 4) < (ntok >> a.lgR)) {
       const int bl = tid >> 4, c8 = tid & 15;
       float mk[8];
       if constexpr (DQ) {
@@ -318,7 +350,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
       vm1 = h2f(cur.vm[0] >> 16);
     }
     if constexpr (kMV) {
-      const int ec = f16_headroom_exp(group_max<kWave>(fabsf(vn1 * vn2)));
+      const int ec = f16_headroom_exp(wave_max_nonneg(fabsf(vn1 * vn2)));
       if (ec < ev) {
         const float f = pow2f(ec - ev);
 #pragma unroll
@@ -328,7 +360,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
     }
     if constexpr (ROPE) {
       // the chunk's block mean for channels 8 rj .. 8 rj + 7
-      const int bl = (ch * kChunk) / a.R;
+      const int bl = (ch * kChunk) >> a.lgR;
       float mk[8];
       if constexpr (DQ) {
         const uint8_t* mr = reinterpret_cast<const uint8_t*>(a.kmu) + (blk0 + bl) * kDqMuRecord;
@@ -363,7 +395,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
         float tn1, tn2;
         if constexpr (DQ) {
           const uint8_t* kr = reinterpret_cast<const uint8_t*>(a.kscales) + (blk0 + bl) * dq_record_bytes(a.R);
-          const uint32_t tq = dq_token(kr, a.R, (int)(tc % a.R));
+          const uint32_t tq = dq_token(kr, a.R, (int)(tc & (a.R - 1)));
           tn1 = dq_value(dq_s1_params(kr, a.R), tq >> 16);
           tn2 = h2f(tq & 0xffff);
         } else {
@@ -415,7 +447,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
           s0 += lds_f32(o0 + (((cur.kcw[j >> 2] >> (8 * (j & 3))) & 0xffu) << 2));
           s1 += lds_f32(o1 + (((cur.kcw[(j + 1) >> 2] >> (8 * ((j + 1) & 3))) & 0xffu) << 2));
         }
-        const float qmu = qmus[((ch * kChunk) / a.R) * GH + g];
+        const float qmu = qmus[((ch * kChunk) >> a.lgR) * GH + g];
         sv = a.scale_log2 * kn1 * fmaf(kn2, s0 + s1, qmu);
       }
       // online softmax over the chunk.  The reference m moves only when a
@@ -514,16 +546,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
     // two buffers in turn, so no register copies between chunks
     ChunkRegs alt;
     for (; ch < nchunk; ch += 8) {
-      if (ch + 4 < nchunk) load_chunk(ch + 4, alt);
+      if (kBuf || ch + 4 < nchunk) load_chunk(ch + 4, alt);
       chunk_step(ch, cur);
       if (ch + 4 >= nchunk) break;
-      if (ch + 8 < nchunk) load_chunk(ch + 8, cur);
+      if (kBuf || ch + 8 < nchunk) load_chunk(ch + 8, cur);
       chunk_step(ch + 4, alt);
     }
   } else {
     for (; ch < nchunk; ch += 4) {
       ChunkRegs nxt;
-      if (ch + 4 < nchunk) load_chunk(ch + 4, nxt);
+      if (kBuf || ch + 4 < nchunk) load_chunk(ch + 4, nxt);
       chunk_step(ch, cur);
       cur = nxt;
     }
@@ -672,129 +704,6 @@ hipError_t launch_decode(const DecodeArgs& a, int sub, int gh, int B, size_t lds
 hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream) {
   hipLaunchKernelGGL(combine_kernel, dim3(B * a.Hq), dim3(128), 0, stream, a);
   return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// fp16 comparator: one work-group per (batch row, KV head, split); the G query
-// heads of the KV head share every K/V read.  Scores: each lane owns one token
-// of the wave's 64 and forms its G dot products from the token row (read as
-// 16-byte chunks) against the queries in LDS.  Values: one wave per token row,
-// lanes own 2 channels.
-template <int G>
-__global__ __launch_bounds__(256) void fp16_decode_kernel(Fp16DecodeArgs a) {
-  extern __shared__ float smem[];
-  const int TS = a.split_tokens;
-  float* qf = smem;                 // [G][128]
-  float* sc = qf + G * kDim;        // [G][TS]
-  float* ov = sc + G * TS;          // [4][G][128]
-  float* red = ov + 4 * G * kDim;   // [4][G]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x;
-  const int bk = blockIdx.y;
-  const int b = bk / a.Hkv, hk = bk % a.Hkv;
-  const int h0 = hk * G;
-  const int t0 = split * TS;
-  const int nt = min(TS, a.T - t0);
-  const uint16_t* K = a.k + ((int64_t)bk * a.T + t0) * kDim;
-  const uint16_t* V = a.v + ((int64_t)bk * a.T + t0) * kDim;
-  for (int i = tid; i < G * kDim; i += 256) qf[i] = h2f(a.q[((int64_t)b * a.Hq + h0) * kDim + i]);
-  __syncthreads();
-  for (int t = tid; t < nt; t += 256) {
-    float acc[G];
-    _Pragma("unroll") for (int g = 0; g < G; ++g) acc[g] = 0.f;
-    const uint4* row = reinterpret_cast<const uint4*>(K + (int64_t)t * kDim);
-#pragma unroll 4
-    for (int ch = 0; ch < 16; ++ch) {
-      const uint4 v4 = row[ch];
-      const uint32_t w[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float k0 = h2f(w[i] & 0xffff), k1 = h2f(w[i] >> 16);
-        const int c = ch * 8 + 2 * i;
-        _Pragma("unroll") for (int g = 0; g < G; ++g) acc[g] = fmaf(qf[g * kDim + c], k0, fmaf(qf[g * kDim + c + 1], k1, acc[g]));
-      }
-    }
-    _Pragma("unroll") for (int g = 0; g < G; ++g) sc[g * TS + t] = acc[g] * a.scale_log2;
-  }
-  __syncthreads();
-  // max and sum per head (G <= 8)
-  float m[G], l[G];
-  _Pragma("unroll") for (int g = 0; g < G; ++g) {
-    float v = -INFINITY;
-    for (int t = tid; t < nt; t += 256) v = fmaxf(v, sc[g * TS + t]);
-    m[g] = group_max<kWave>(v);
-  }
-  if (lane == 0)
-    _Pragma("unroll") for (int g = 0; g < G; ++g) red[wave * G + g] = m[g];
-  __syncthreads();
-  _Pragma("unroll") for (int g = 0; g < G; ++g)
-    m[g] = fmaxf(fmaxf(red[g], red[G + g]), fmaxf(red[2 * G + g], red[3 * G + g]));
-  __syncthreads();
-  _Pragma("unroll") for (int g = 0; g < G; ++g) {
-    float v = 0.f;
-    for (int t = tid; t < nt; t += 256) {
-      const float p = exp2f(sc[g * TS + t] - m[g]);
-      sc[g * TS + t] = p;
-      v += p;
-    }
-    l[g] = group_sum<kWave>(v);
-  }
-  if (lane == 0)
-    _Pragma("unroll") for (int g = 0; g < G; ++g) red[wave * G + g] = l[g];
-  __syncthreads();
-  _Pragma("unroll") for (int g = 0; g < G; ++g) l[g] = (red[g] + red[G + g]) + (red[2 * G + g] + red[3 * G + g]);
-  // values
-  float o0[G], o1[G];
-  _Pragma("unroll") for (int g = 0; g < G; ++g) o0[g] = o1[g] = 0.f;
-  for (int t = wave; t < nt; t += 4) {
-    const uint32_t vv = *reinterpret_cast<const uint32_t*>(V + (int64_t)t * kDim + 2 * lane);
-    const float v0 = h2f(vv & 0xffff), v1 = h2f(vv >> 16);
-    _Pragma("unroll") for (int g = 0; g < G; ++g) {
-      const float p = sc[g * TS + t];
-      o0[g] = fmaf(p, v0, o0[g]);
-      o1[g] = fmaf(p, v1, o1[g]);
-    }
-  }
-  _Pragma("unroll") for (int g = 0; g < G; ++g) {
-    ov[(wave * G + g) * kDim + 2 * lane] = o0[g];
-    ov[(wave * G + g) * kDim + 2 * lane + 1] = o1[g];
-  }
-  __syncthreads();
-  for (int o = tid; o < G * kDim; o += 256) {
-    const int g = o / kDim, c = o % kDim;
-    const float s = (ov[(0 * G + g) * kDim + c] + ov[(1 * G + g) * kDim + c]) +
-                    (ov[(2 * G + g) * kDim + c] + ov[(3 * G + g) * kDim + c]);
-    float* wo = a.ws + (((int64_t)b * a.Hq + h0 + g) * a.nsplit + split) * (kDim + 2);
-    wo[c] = s;
-    if (c == 0) {
-      wo[kDim] = m[g];
-      wo[kDim + 1] = l[g];
-    }
-  }
-}
-
-template <int G>
-static hipError_t launch_fp16_t(const Fp16DecodeArgs& a, int B, hipStream_t stream) {
-  static std::atomic<bool> lds_set[kMaxDevices];
-  const hipError_t e = allow_lds(reinterpret_cast<const void*>(&fp16_decode_kernel<G>), lds_set);
-  if (e != hipSuccess) return e;
-  const size_t lds = fp16_decode_lds_bytes(G, a.split_tokens);
-  hipLaunchKernelGGL((fp16_decode_kernel<G>), dim3(a.nsplit, B * a.Hkv), dim3(256), lds, stream, a);
-  return hipGetLastError();
-}
-
-size_t fp16_decode_lds_bytes(int G, int split_tokens) {
-  return sizeof(float) * ((size_t)G * kDim + (size_t)G * split_tokens + 4 * (size_t)G * kDim + 4 * G);
-}
-
-hipError_t launch_fp16_decode(const Fp16DecodeArgs& a, int B, hipStream_t stream) {
-  switch (a.G) {
-    case 1: return launch_fp16_t<1>(a, B, stream);
-    case 2: return launch_fp16_t<2>(a, B, stream);
-    case 4: return launch_fp16_t<4>(a, B, stream);
-    case 8: return launch_fp16_t<8>(a, B, stream);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 }  // namespace nsnq

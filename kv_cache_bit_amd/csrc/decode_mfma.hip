@@ -178,14 +178,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int t0 = split * a.split_tokens;
   const int ntok = max(0, min(a.split_tokens, row_quant(a, b) - t0));  // 0: empty partial
   const int nchunk = ntok / kMChunk;
-  const int nblk = ntok / a.R;
+  const int nblk = (ntok >> a.lgR);
   const uint8_t* kc = a.kcodes + (unit * a.cap + t0) * S;
   const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.kscales) + unit * a.cap + t0;
   const uint8_t* vc = a.vcodes + (unit * a.cap + t0) * S;
   const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.vscales) + unit * a.cap + t0;
-  const uint16_t* kmu = a.kmu + (unit * nbmu + t0 / a.R) * kDim;
-  const uint16_t* vmu = a.vmu + (unit * nbmu + t0 / a.R) * kDim;
-  const int64_t blk0 = unit * nbmu + t0 / a.R;  // first block of the split (record index)
+  const uint16_t* kmu = a.kmu + (unit * nbmu + (t0 >> a.lgR)) * kDim;
+  const uint16_t* vmu = a.vmu + (unit * nbmu + (t0 >> a.lgR)) * kDim;
+  const int64_t blk0 = unit * nbmu + (t0 >> a.lgR);  // first block of the split (record index)
 
   // One chunk's global loads for this lane: the K codes its score tiles need
   // (token 16 tau + m16, the 8 (2 bits) or 4 (1 bit) code bytes starting at
@@ -203,8 +203,39 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     uint32_t kpar, vpar;  // double-quantised: the chunk's block (S1, Z1)
     uint4_t vcode[S / 16];
   };
+  // Without double quantisation the chunk loads go through buffer resources
+  // bounded by the split's tokens: a prefetch past the last chunk returns
+  // zeros without touching memory, so every prefetch is issued unconditionally
+  // and the wait before a chunk's use counts only the loads issued before it.
+  constexpr bool kBuf = !DQ;
+  const buf_rsrc_t rkc = make_rsrc(kc, ntok * S), rvc = make_rsrc(vc, ntok * S);
+  const buf_rsrc_t rks = make_rsrc(ks, ntok * 4), rvs = make_rsrc(vs, ntok * 4);
   auto load = [&](int ch, Ld& r) {
     const int64_t base = (int64_t)ch * kMChunk;
+    if constexpr (kBuf) {
+      const int tb = ch * kMChunk;
+      if constexpr (T4) {
+#pragma unroll
+        for (int i = 0; i < S / 16; ++i) r.kc[i] = buf_load_b128(rkc, (tb + lane) * S + 16 * i);
+      } else {
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+          const int off = (tb + 16 * tau + m16) * S + KCW * 4 * kb;
+          if constexpr (SUB == 4) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rkc, off, 0, 0);
+            r.kc[tau][0] = v[0];
+            r.kc[tau][1] = v[1];
+          } else {
+            r.kc[tau][0] = buf_load_b32(rkc, off);
+          }
+        }
+      }
+      r.ksc = buf_load_b32(rks, (tb + lane) * 4);
+      r.vsc = buf_load_b32(rvs, (tb + lane) * 4);
+#pragma unroll
+      for (int i = 0; i < S / 16; ++i) r.vcode[i] = buf_load_b128(rvc, (tb + lane) * S + 16 * i);
+      return;
+    }
     if constexpr (T4) {
 #pragma unroll
       for (int i = 0; i < S / 16; ++i) r.kc[i] = *reinterpret_cast<const uint4_t*>(kc + (base + lane) * S + 16 * i);
@@ -223,8 +254,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
     if constexpr (DQ) {
       const int SRB = dq_record_bytes(a.R);
-      const int64_t rb = blk0 + (int)(base / a.R);
-      const int tb = (int)((base + lane) % a.R);
+      const int64_t rb = blk0 + (int)(base >> a.lgR);
+      const int tb = (int)((base + lane) & (a.R - 1));
       const uint8_t* kr = reinterpret_cast<const uint8_t*>(a.kscales) + rb * SRB;
       const uint8_t* vr = reinterpret_cast<const uint8_t*>(a.vscales) + rb * SRB;
       r.ksc = dq_token(kr, a.R, tb);
@@ -276,7 +307,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
     // the first chunk's loads queue behind the set-up loads, which are waited
     // for first
-    if (ch < nchunk) load(ch, cur);
+    if (kBuf || ch < nchunk) load(ch, cur);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       kmul[tid + 256 * j] = kt[j];
@@ -469,7 +500,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     // softmax of the scored chunk `chk`, its weights into buffer `bs`
     auto weigh = [&](int chk, int bs) {
       // s = KA S + KB (q . KMU_b), in log2 units
-      const int bl = (chk * kMChunk) / a.R;
+      const int bl = (chk * kMChunk) >> a.lgR;
       float sc[GQ], dl[GQ];
       bool up = false;
 #pragma unroll
@@ -495,8 +526,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       // fp16 weights p N1 N2 2^(ev - 3) and p N1 2^(eb - 3): with p <= 8 they
       // stay below 2^15; beta's exponent is the chunk's own (each chunk's
       // beta is taken out separately)
-      const int ec = f16_headroom_exp(group_max<64>(fabsf(wn12)));
-      const int eb = f16_headroom_exp(group_max<64>(fabsf(wn1)));
+      const int ec = f16_headroom_exp(wave_max_nonneg(fabsf(wn12)));
+      const int eb = f16_headroom_exp(wave_max_nonneg(fabsf(wn1)));
       if (ec < ev) {
         const float f = pow2f(ec - ev);
 #pragma unroll
@@ -579,7 +610,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     if (ch < nchunk) {
       {
         Ld nxt;
-        if (ch + 4 < nchunk) load(ch + 4, nxt);
+        if (kBuf || ch + 4 < nchunk) load(ch + 4, nxt);
         front(cur, 0);
         weigh(ch, 0);
         cur = nxt;
@@ -587,7 +618,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       int chp = ch, bs = 1;
       for (ch += 4; ch < nchunk; ch += 4) {
         Ld nxt;
-        if (ch + 4 < nchunk) load(ch + 4, nxt);
+        if (kBuf || ch + 4 < nchunk) load(ch + 4, nxt);
         front(cur, bs);       // score this chunk ...
         back(chp, bs ^ 1);    // ... while the one before it meets its values
         weigh(ch, bs);
@@ -615,7 +646,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   } else {
   for (; ch < nchunk; ch += 4) {
       Ld nxt;
-      if (ch + 4 < nchunk) load(ch + 4, nxt);
+      if (kBuf || ch + 4 < nchunk) load(ch + 4, nxt);
       // stage this chunk's V codes and token `lane`'s factors
   #pragma unroll
       for (int i = 0; i < S / 16; ++i) *reinterpret_cast<uint4_t*>(vcl + lane * S + 16 * i) = cur.vcode[i];
@@ -638,7 +669,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         fvc[lane] = vn1 * vn2;
         fvd[lane] = vn1;
         // the chunk's value weights p N1 N2 (p <= 1) carry 2^ev in fp16
-        const int ec = f16_headroom_exp(group_max<64>(fabsf(vn1 * vn2)));
+        const int ec = f16_headroom_exp(wave_max_nonneg(fabsf(vn1 * vn2)));
         if (ec < ev) {
           const float f = pow2f(ec - ev);
 #pragma unroll
@@ -682,7 +713,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         sacc[tau] = acc;
       }
       // s = KA S + KB (q . KMU_b) for this lane's 16 tokens 16 tau + 4 kb + r
-      const int bl = (ch * kMChunk) / a.R;
+      const int bl = (ch * kMChunk) >> a.lgR;
       const float qm = m16 < GQ ? qmu[bl * GQ + m16] : 0.f;
       float s[16];
       float cmax = -INFINITY;

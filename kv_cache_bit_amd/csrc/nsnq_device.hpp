@@ -122,4 +122,31 @@ __device__ __forceinline__ int f16_headroom_exp(float xmax) {
 }
 __device__ __forceinline__ float pow2f(int e) { return __builtin_amdgcn_ldexpf(1.f, e); }
 
+// Maximum over the 64 lanes of a wave of non-negative floats, through their
+// bit patterns (which order like the values): integer maxima need none of the
+// NaN canonicalisation that fmaxf carries.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_ds_swizzle((int)u, 0x401F));
+  return fmaxf(__builtin_bit_cast(float, u), xlane<32>(__builtin_bit_cast(float, u)));
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor): loads
+// at or past the end return zeros and touch no memory, so a prefetch past the
+// last chunk needs no branch.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+__device__ __forceinline__ buf_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4_t buf_load_b128(buf_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_b32(buf_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 }  // namespace nsnq

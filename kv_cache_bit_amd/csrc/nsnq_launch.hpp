@@ -113,6 +113,7 @@ struct DecodeArgs {
   float* ws;         // partials [B][Hq][nsplit][d + 2]
   int Hq, Hkv, G;    // G = Hq / Hkv
   int cap, R;
+  int lgR;           // log2 R (R is a power of two)
   int n_quant, n_resid;
   int split_tokens;  // compressed tokens per split (multiple of R)
   int nsplit_q;      // splits over the compressed tokens

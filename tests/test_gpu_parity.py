@@ -824,3 +824,23 @@ def test_llama2_b256_layer_sampled(oracle_codebooks):
     layer on the GPU, sampled streams against the oracle."""
     w = synth.WORKLOADS["llama2-7b-b256-2bit"]
     _sampled_layer_check(oracle_codebooks[2], w, 5, [(0, 0), (131, 16), (255, 31)], 10.0)
+
+
+# ------------------------------------------------- fp16-cache comparator --
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,ns", [
+    (1, 4, 4, 4096, 0),
+    (2, 8, 2, 1000, 0),     # G = 4, ragged last step
+    (1, 16, 2, 777, 3),     # G = 8
+    (3, 2, 1, 33, 0),       # G = 2, one full step and one token
+    (1, 1, 1, 1, 0),        # a single token
+    (2, 4, 4, 5000, 7),
+])
+def test_fp16_comparator_matches_oracle(B, Hq, Hkv, T, ns):
+    """The uncompressed fp16-cache decode (the comparator of the benchmark)
+    against the oracle's softmax attention over the same fp16 K/V."""
+    k, v = _kv(1500 + T, B, Hkv, T)
+    q = synth.queries(1500 + T, 0, B, Hq, D)
+    o = nsnq.nsnq_fp16_decode_attention(q.to(DEV), k.to(DEV).contiguous(), v.to(DEV).contiguous(), num_splits=ns)
+    ref = oracle.attention(q, oracle.f16_to_f64(f16_bits(k)), oracle.f16_to_f64(f16_bits(v)), 1.0 / math.sqrt(D))
+    check_attention(o.float().cpu().numpy(), ref)
