@@ -281,6 +281,21 @@ def encode_layer_timing(nsnq, p_enc, p, cb, k, v, L, B, Hkv, bits, R, dev, reps)
                       "hbm_frac": fl_b / tf / 1e9 / HBM_PEAK_GBS}}
 
 
+def encode_bench(nsnq, synth, workload: str, dev, reps: int = 5):
+    """Prefill encode of layer 0 of `workload` alone (for profiling)."""
+    import torch
+    w = synth.WORKLOADS[workload]
+    B, Hkv, L, d, bits, R = w["B"], w["Hkv"], w["L"], w["d"], w["bits"], w["R"]
+    p = nsnq.params(bits, R)
+    cb, _ = build_codebook(nsnq, synth, bits, R, dev)
+    p_enc = nsnq.with_candidates(p, cb) if bits == 2 else p
+    k, v = synth.kv_layer(w["config_id"], 0, B, Hkv, L, d, outlier_std=synth.outlier_std_for(workload, 0),
+                          device=dev)
+    res = encode_layer_timing(nsnq, p_enc, p, cb, k, v, L, B, Hkv, bits, R, dev, reps)
+    res["workload"] = workload
+    return res
+
+
 def fp16_comparator(nsnq, synth, w, NL, q, dev, steps, B, t_step):
     """The fp16-cache decode at the largest batch whose K/V of all layers fits
     the HBM left free (less an 8 GB reserve).  Two layers' caches are held and
@@ -316,7 +331,7 @@ def fp16_comparator(nsnq, synth, w, NL, q, dev, steps, B, t_step):
 
 # ------------------------------------------------------ single-layer case --
 
-def layer_bench(nsnq, synth, workload: str, dev, reps: int = 20, options: bool = False):
+def layer_bench(nsnq, synth, workload: str, dev, reps: int = 20, options: bool = False, keep_rows: int = 0):
     """One layer: prefill encode (candidate lists at 2 bits; the exhaustive
     search beside it), decode, and the fp16 comparator on the same layer.
     Inputs and caches rotate over enough copies that each rotated set exceeds
@@ -414,9 +429,10 @@ def layer_bench(nsnq, synth, workload: str, dev, reps: int = 20, options: bool =
            "codebook": cb_info}
     if options:
         res["options"] = measure_options(nsnq, synth, w, k, v, q, cb, dev)
+    host_kv = (k[:keep_rows].cpu(), v[:keep_rows].cpu()) if keep_rows > 0 else None
     del k, v
     torch.cuda.empty_cache()
-    return res
+    return res, host_kv
 
 
 def measure_options(nsnq, synth, w: dict, k, v, q, codebook, dev, reps: int = 20):
@@ -493,12 +509,12 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w: dict, host_kv, rows: int, layers: int):
+def cpu_baseline(w: dict, host_kv, rows: int, layers: int, single_thread: bool = True):
     """The CPU oracle on layer 0's first `rows` batch rows, all heads: their
     prefill encode and one decode step, timed; scaled linearly by the units of
-    the whole workload (batch x layers) and labelled as extrapolated.  The
-    codebook is the oracle's own k-means fit (its values do not change the
-    oracle's work)."""
+    the whole workload (batch x layers) and labelled as extrapolated when that
+    scale is above 1.  The codebook is the oracle's own k-means fit (its values
+    do not change the oracle's work)."""
     import numpy as np
     import oracle
     from kv_cache_bit_amd import synth
@@ -518,34 +534,37 @@ def cpu_baseline(w: dict, host_kv, rows: int, layers: int):
     scale = (B / rows) * layers
     dec_step = (t2 - t1) * scale
     enc_layer = (t1 - t0) * B / rows
-    # one KV head of one row on one thread
-    oracle.set_num_threads(1)
-    try:
-        t3 = time.perf_counter()
-        e1k = oracle.encode(k[:1, :1].contiguous(), R, cb)
-        e1v = oracle.encode(v[:1, :1].contiguous(), R, cb)
-        t4 = time.perf_counter()
-        oracle.reference_decode(q[:1, :Hq // Hkv].contiguous(), e1k, e1v, e1k["n_quant"], e1k["n_resid"], R, cb)
-        t5 = time.perf_counter()
-    finally:
-        oracle.set_num_threads(cores)
-    dec_1t = (t5 - t4) * B * Hkv * layers
     try:
         nproc = len(os.sched_getaffinity(0))
     except AttributeError:
         nproc = os.cpu_count()
-    return {"value": B / dec_step, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"layer 0, batch rows 0..{rows - 1} of {B}, all {Hkv} KV heads: prefill encode "
-                       f"{t1 - t0:.1f} s and one decode step {t2 - t1:.1f} s measured; extrapolated x{scale:g} "
-                       f"to the {layers}-layer batch-{B} step"),
-            "extrapolated": True, "measured_s": t2 - t0,
-            "encode_tokens_per_s": B * L / enc_layer,
-            "encode_layer_s_extrapolated": enc_layer,
-            "decode_step_s_extrapolated": dec_step,
-            "nproc": nproc, "cpu_model": cpu_model(),
-            "single_thread": {"value": B / dec_1t, "unit": "tokens/s", "cores": 1,
-                              "sample": (f"layer 0, row 0, one KV head on one thread ({t5 - t4:.2f} s decode); "
-                                         f"extrapolated x{B * Hkv * layers}")}}
+    res = {"value": B / dec_step, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": (f"layer 0, batch rows 0..{rows - 1} of {B}, all {Hkv} KV heads: prefill encode "
+                      f"{t1 - t0:.1f} s and one decode step {t2 - t1:.1f} s measured"
+                      + (f"; extrapolated x{scale:g} to the {layers}-layer batch-{B} step" if scale > 1 else "")),
+           "extrapolated": scale > 1, "measured_s": t2 - t0,
+           "encode_tokens_per_s": B * L / enc_layer,
+           "encode_layer_s": enc_layer,
+           "decode_step_s": dec_step,
+           "nproc": nproc, "cpu_model": cpu_model()}
+    if single_thread:
+        # one KV head of one row on one thread
+        oracle.set_num_threads(1)
+        try:
+            t3 = time.perf_counter()
+            e1k = oracle.encode(k[:1, :1].contiguous(), R, cb)
+            e1v = oracle.encode(v[:1, :1].contiguous(), R, cb)
+            t4 = time.perf_counter()
+            oracle.reference_decode(q[:1, :Hq // Hkv].contiguous(), e1k, e1v, e1k["n_quant"], e1k["n_resid"], R,
+                                    cb)
+            t5 = time.perf_counter()
+        finally:
+            oracle.set_num_threads(cores)
+        dec_1t = (t5 - t4) * B * Hkv * layers
+        res["single_thread"] = {"value": B / dec_1t, "unit": "tokens/s", "cores": 1,
+                                "sample": (f"layer 0, row 0, one KV head on one thread ({t5 - t4:.2f} s decode); "
+                                           f"extrapolated x{B * Hkv * layers}")}
+    return res
 
 
 def copy_calibration(nbytes: int, reps: int):
@@ -567,12 +586,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE, help="multi-layer workload of the headline decode step")
-    ap.add_argument("--cpu-rows", type=int, default=6,
+    ap.add_argument("--cpu-rows", type=int, default=24,
                     help="batch rows of layer 0 in the CPU-baseline sample (0: skip)")
     ap.add_argument("--no-fp16", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="headline only: skip the other workloads")
     ap.add_argument("--only", default="", help="run one part for profiling: headline, layer:<workload>, "
-                                                "step:<workload>")
+                                                "step:<workload>, encode:<workload>")
     ap.add_argument("--copy-bytes", type=int, default=0, help="only run a device copy of this size")
     ap.add_argument("--decode-layers", type=int, default=0, help="time the decode of only this many layers")
     args = ap.parse_args()
@@ -593,7 +612,10 @@ def main():
     torch.cuda.set_device(dev)
 
     if args.only.startswith("layer:"):
-        print(json.dumps(layer_bench(nsnq, synth, args.only[6:], dev, reps=max(args.steps, 4))), flush=True)
+        print(json.dumps(layer_bench(nsnq, synth, args.only[6:], dev, reps=max(args.steps, 4))[0]), flush=True)
+        return
+    if args.only.startswith("encode:"):
+        print(json.dumps(encode_bench(nsnq, synth, args.only[7:], dev, reps=max(args.steps, 3))), flush=True)
         return
     if args.only.startswith("step:"):
         r, _, _ = decode_step(nsnq, synth, args.only[5:], args.steps, args.warmup, dev,
@@ -644,16 +666,27 @@ def main():
         res["encode"] = head["encode"]
     if "fp16" in head:
         res["fp16"] = head["fp16"]
+    cpu_samples = []  # (workload, host K/V rows, rows, layers)
     if not args.no_extra and args.only != "headline":
         res["workloads"] = {}
         for wl, opts in (("llama2-7b-layer-b1-2bit", True), ("llama2-7b-layer-b16-1bit", False)):
-            res["workloads"][wl] = layer_bench(nsnq, synth, wl, dev, options=opts)
-        r4, _, _ = decode_step(nsnq, synth, "llama3.1-8b-gqa-b4-32k-2bit", args.steps, args.warmup, dev,
-                               with_fp16=not args.no_fp16)
-        res["workloads"]["llama3.1-8b-gqa-b4-32k-2bit"] = r4
+            res["workloads"][wl], hkv = layer_bench(nsnq, synth, wl, dev, options=opts,
+                                                    keep_rows=1 if args.cpu_rows > 0 else 0)
+            cpu_samples.append((wl, hkv, 1, 1))
+        wl = "llama3.1-8b-gqa-b4-32k-2bit"
+        r4, hkv, _ = decode_step(nsnq, synth, wl, args.steps, args.warmup, dev, with_fp16=not args.no_fp16,
+                                 keep_inputs_rows=1 if args.cpu_rows > 0 else 0)
+        res["workloads"][wl] = r4
+        cpu_samples.append((wl, hkv, 1, synth.WORKLOADS[wl]["layers"]))
     if args.cpu_rows > 0 and host_kv is not None:
         progress("CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w, host_kv, min(args.cpu_rows, w["B"]), head["layers"])
+        res["cpu_baseline"]["workloads"] = {}
+        for wl, hkv, rows, layers in cpu_samples:
+            if hkv is not None:
+                cb_ = cpu_baseline(synth.WORKLOADS[wl], hkv, rows, layers, single_thread=False)
+                res["cpu_baseline"]["workloads"][wl] = {key: cb_[key] for key in (
+                    "value", "unit", "sample", "extrapolated", "encode_tokens_per_s", "decode_step_s")}
     print(json.dumps(res), flush=True)
 
 
