@@ -629,44 +629,66 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   }
 }
 
-// out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, one group of 128
-// lanes (channels) per (batch row, query head).  Every lane reads the splits'
-// (m_i, l_i) itself (the same addresses for the whole group) and its channel
-// of o_i, 32 splits at a time with all loads of a batch in flight together;
-// the running maximum rescales the sums between batches.
-__global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
-  constexpr int kBatch = 32;
-  const int bh = blockIdx.x;
-  const int c = threadIdx.x;
-  const float* w = a.ws + (int64_t)bh * a.nsplit * (kDim + 2);
-  float M = -INFINITY, num = 0.f, den = 0.f;
-  for (int i0 = 0; i0 < a.nsplit; i0 += kBatch) {
-    const int n = min(kBatch, a.nsplit - i0);
-    float mi[kBatch], li[kBatch], oi[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const float* r = w + (int64_t)(i0 + u) * (kDim + 2);
-      mi[u] = u < n ? r[kDim] : -INFINITY;
-      li[u] = u < n ? r[kDim + 1] : 0.f;
-      oi[u] = u < n ? r[c] : 0.f;
+// out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i for each (batch row,
+// query head).  CPL channels per lane: one wave per head (CPL = 2) or two
+// (CPL = 1, more waves for few heads).  The splits go in batches of NB
+// (<= 64): lane u reads split u's (m_u, l_u) while the batch's o values of
+// every lane are in flight (indexes past the batch re-read its last split, so
+// no load sits behind a branch); one wave maximum and one exp2 per lane then
+// give the split factors, which the channel sums read back with v_readlane
+// (uniform split index; lanes past the batch hold factor 0).  A running
+// maximum rescales the sums between batches.
+template <int NB, int CPL>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  static_assert(NB <= kWave, "one split per lane");
+  static_assert(CPL == 1 || CPL == 2, "one or two channels per lane");
+  constexpr int WPH = 2 / CPL;  // waves per head
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int bh = blockIdx.x * ((int)(blockDim.x >> 6) / WPH) + wave / WPH;
+  if (bh >= a.nbh) return;  // the whole wave (and its partner)
+  const int c0 = (wave % WPH) * kWave * CPL + CPL * lane;  // this lane's first channel
+  constexpr int RS = kDim + 2;  // floats per partial
+  const float* w = a.ws + (int64_t)bh * a.nsplit * RS;
+  float M = -INFINITY, den = 0.f, n0 = 0.f, n1 = 0.f;
+  for (int i0 = 0; i0 < a.nsplit; i0 += NB) {
+    const int last = min(NB, a.nsplit - i0) - 1;
+    const float* wb = w + (int64_t)i0 * RS;
+    float mu = -INFINITY, lu = 0.f;
+    if (lane <= last) {
+      mu = wb[lane * RS + kDim];
+      lu = wb[lane * RS + kDim + 1];
     }
-    float Mb = M;
+    float2 o[NB];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) Mb = fmaxf(Mb, mi[u]);
+    for (int k = 0; k < NB; ++k) {
+      const float* r = wb + min(k, last) * RS + c0;
+      if constexpr (CPL == 2) o[k] = *reinterpret_cast<const float2*>(r);
+      else o[k] = float2{*r, 0.f};
+    }
+    const float Mb = fmaxf(M, group_max<kWave>(mu));
     if (Mb == -INFINITY) continue;  // no tokens so far
     const float sc = exp2f(M - Mb);  // 0 while M is -inf
-    num *= sc;
+    n0 *= sc;
+    n1 *= sc;
     den *= sc;
     M = Mb;
+    const float fu = exp2f(mu - M);  // 0 for lanes past the batch
+    den += group_sum<kWave>(fu * lu);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const float f = exp2f(mi[u] - M);
-      num = fmaf(f, oi[u], num);
-      den = fmaf(f, li[u], den);
+    for (int k = 0; k < NB; ++k) {
+      const float f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fu), k));
+      n0 = fmaf(f, o[k].x, n0);
+      if constexpr (CPL == 2) n1 = fmaf(f, o[k].y, n1);
     }
   }
   // a row without tokens (ragged cache): zero output
-  a.out[(int64_t)bh * kDim + c] = M == -INFINITY ? (uint16_t)0 : f2h(num / den);
+  uint16_t* out = a.out + (int64_t)bh * kDim + c0;
+  if constexpr (CPL == 2) {
+    const uint32_t pair = M == -INFINITY ? 0u : ((uint32_t)f2h(n0 / den) | ((uint32_t)f2h(n1 / den) << 16));
+    *reinterpret_cast<uint32_t*>(out) = pair;
+  } else {
+    *out = M == -INFINITY ? (uint16_t)0 : f2h(n0 / den);
+  }
 }
 
 template <int SUB, int GH, bool DQ, bool ROPE>
@@ -701,8 +723,21 @@ hipError_t launch_decode(const DecodeArgs& a, int sub, int gh, int B, size_t lds
   return hipErrorInvalidValue;
 }
 
+template <int CPL>
+static void launch_combine_nb(const CombineArgs& c, dim3 grid, dim3 block, hipStream_t stream) {
+  if (c.nsplit <= 4) hipLaunchKernelGGL((combine_kernel<4, CPL>), grid, block, 0, stream, c);
+  else if (c.nsplit <= 8) hipLaunchKernelGGL((combine_kernel<8, CPL>), grid, block, 0, stream, c);
+  else if (c.nsplit <= 16) hipLaunchKernelGGL((combine_kernel<16, CPL>), grid, block, 0, stream, c);
+  else hipLaunchKernelGGL((combine_kernel<32, CPL>), grid, block, 0, stream, c);
+}
+
 hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(B * a.Hq), dim3(128), 0, stream, a);
+  CombineArgs c = a;
+  c.nbh = B * a.Hq;
+  // many heads: one wave per head, four heads per group; few heads: two
+  // waves per head (one channel per lane), spread over more CUs
+  if (c.nbh >= 4096) launch_combine_nb<2>(c, dim3((c.nbh + 3) / 4), dim3(256), stream);
+  else launch_combine_nb<1>(c, dim3(c.nbh), dim3(128), stream);
   return hipGetLastError();
 }
 

@@ -145,6 +145,7 @@ struct CombineArgs {
   const float* ws;
   uint16_t* out;
   int Hq, nsplit;
+  int nbh;  // batch rows x query heads (set by the launcher)
 };
 
 struct KmeansArgs {
