@@ -512,27 +512,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
         }
       }
     } else {
-    // values: tokens 8 tg .. 8 tg + 7 of the chunk, this lane's 16 channels
+    // values: tokens 8 tg .. 8 tg + 7 of the chunk, this lane's 16 channels,
+    // two tokens at a time: all eight codeword gathers are issued before the
+    // first product (issued one by one next to their products, each gather's
+    // bank-conflicted latency stalled the wave)
+    constexpr int NG = SPT * (SUB / 4);  // 8-byte codeword pieces per token
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float wg[GH];
+    for (int i = 0; i < 8; i += 2) {
+      float wg[2][GH];
+      uint2 c4[2][NG];
 #pragma unroll
-      for (int g = 0; g < GH; ++g) wg[g] = wb[g * kChunk + 8 * tg + i];
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int si = 0; si < SPT; ++si) {
-        const uint32_t caddr = ((cur.vcw[i] >> (8 * si)) & 0xffu) * (2u * SUB) + 4u * kL.cbh;
+        for (int g = 0; g < GH; ++g) wg[t][g] = wb[g * kChunk + 8 * tg + i + t];
 #pragma unroll
-        for (int hh = 0; hh < SUB / 4; ++hh) {
-          const uint2 c4 = lds_u32x2(caddr + 8u * hh);
-          const float c0 = h2f(c4.x & 0xffff), c1 = h2f(c4.x >> 16);
-          const float c2 = h2f(c4.y & 0xffff), c3 = h2f(c4.y >> 16);
+        for (int si = 0; si < SPT; ++si) {
+          const uint32_t caddr = ((cur.vcw[i + t] >> (8 * si)) & 0xffu) * (2u * SUB) + 4u * kL.cbh;
+#pragma unroll
+          for (int hh = 0; hh < SUB / 4; ++hh) c4[t][si * (SUB / 4) + hh] = lds_u32x2(caddr + 8u * hh);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int n = 0; n < NG; ++n) {
+          const float c0 = h2f(c4[t][n].x & 0xffff), c1 = h2f(c4[t][n].x >> 16);
+          const float c2 = h2f(c4[t][n].y & 0xffff), c3 = h2f(c4[t][n].y >> 16);
 #pragma unroll
           for (int g = 0; g < GH; ++g) {
-            float* ag = &acc[g][si * SUB + 4 * hh];
-            ag[0] = fmaf(wg[g], c0, ag[0]);
-            ag[1] = fmaf(wg[g], c1, ag[1]);
-            ag[2] = fmaf(wg[g], c2, ag[2]);
-            ag[3] = fmaf(wg[g], c3, ag[3]);
+            float* ag = &acc[g][4 * n];
+            ag[0] = fmaf(wg[t][g], c0, ag[0]);
+            ag[1] = fmaf(wg[t][g], c1, ag[1]);
+            ag[2] = fmaf(wg[t][g], c2, ag[2]);
+            ag[3] = fmaf(wg[t][g], c3, ag[3]);
           }
         }
       }
