@@ -295,6 +295,37 @@ def test_decode_late_maxima(oracle_codebooks, bits, Hq, Hkv):
         check_attention(o, ref)
 
 
+@pytest.mark.parametrize("bits,Hq,Hkv", [(2, 2, 2), (2, 8, 2), (1, 4, 4)])
+def test_decode_many_splits(oracle_codebooks, bits, Hq, Hkv):
+    """More split partials than one combine batch holds (32): with one block per
+    split the combine merges 63 partials in two batches, and keys late in the
+    context pointing along a query head put that head's maximum in the second
+    batch, so the sums of the first are rescaled between batches."""
+    cb = oracle_codebooks[bits]
+    R, B, L = 64, 1, 4000
+    k, v = _kv(480 + bits, B, Hkv, L)
+    q = synth.queries(480 + bits, 0, B, Hq, D)
+    G = Hq // Hkv
+    for hk in range(Hkv):
+        d = q[0, hk * G].float()
+        d = d / d.norm()
+        for i, t in enumerate((2500, 3300, 3900)):
+            k[0, hk, t] = (d * (4.0 * 2 ** i) * k[0, hk, t].float().norm()).half()
+    ek, ev = oracle_encode_pair(k, v, R, cb)
+    assert ek["n_quant"] // R == 62
+    ref = _decode_ref(q, ek, ev, cb, R)
+    p = nsnq.params(bits, R)
+    cbt = cb_tensor(cb)
+    cache = nsnq.KVCache(p, B, Hkv, capacity(L, R), DEV)
+    upload_half(cache, 0, ek)
+    upload_half(cache, 1, ev)
+    cache.n_quant, cache.n_resid = ek["n_quant"], ek["n_resid"]
+    qd = q.to(DEV)
+    for ns in (62, 21, 0):  # 63, 22 and the planner's partials
+        o = nsnq.nsnq_decode_attention(p, cbt, qd, cache, num_splits=ns).float().cpu().numpy()
+        check_attention(o, ref)
+
+
 @pytest.mark.parametrize("bits,Hq,Hkv", [(2, 1, 1), (2, 4, 1), (2, 8, 1), (1, 1, 1), (1, 4, 1), (2, 32, 1)])
 @pytest.mark.parametrize("case", ["small_v_sink", "huge_v_token"])
 def test_decode_weight_range(oracle_codebooks, bits, Hq, Hkv, case):
