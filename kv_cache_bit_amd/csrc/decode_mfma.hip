@@ -36,6 +36,15 @@ namespace nsnq {
 namespace {
 
 constexpr int kMChunk = 64;                                 // tokens per wave step
+// Staged V code rows (up to 4 heads): token t's row sits at t S + 16 (t / 8)
+// bytes, 16 bytes of padding after every 8 rows.  The value step's lane
+// groups read rows 8 apart; without the padding those rows share banks.
+constexpr int kVRowPad = 16;
+__host__ __device__ constexpr int vcode_bytes(int S) { return kMChunk * S + kMChunk / 8 * kVRowPad; }
+// Row stride (fp16 elements) of the staged value weights [8][kMChunk]: the
+// value step reads rows m16 mod 8 at once, which with a 128-byte stride share
+// banks.
+constexpr int kPbStride = kMChunk + 8;
 constexpr int kMaxChunks = kMaxSplitBlocks * 128 / kMChunk;  // per split (R <= 128)
 static_assert(kMaxChunks <= 64, "the merge gives each chunk a lane");
 
@@ -108,7 +117,7 @@ struct MfmaSmem {
   static constexpr int kmu = qmu + kMaxSplitBlocks * GQ;  // [kMaxSplitBlocks][128] fp32 K block means
   // per wave: V codes and 4 per-token factors, or (up to 4 heads) two sets
   // of V codes and fp16 weights
-  static constexpr int VSTW = GQ <= 4 ? 2 * (kMChunk * S / 4 + 4 * kMChunk) : kMChunk * S / 4 + 4 * kMChunk;
+  static constexpr int VSTW = GQ <= 4 ? 2 * (vcode_bytes(S) / 4 + 4 * kPbStride) : kMChunk * S / 4 + 4 * kMChunk;
   static constexpr int vst = kmu + kMaxSplitBlocks * kDim;
   static constexpr int main_end = vst + 4 * VSTW;
   // merge of the four waves
@@ -430,9 +439,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       mr[r] = -INFINITY;
       lp[r] = 0.f;
     }
-    // per-wave buffer pair: V codes [64][S] of a chunk, then p VC / 8
-    // (columns 0..3) and p VD / 8 (columns 4..7) of its tokens, fp16 [8][64]
-    constexpr int kBufB = kMChunk * S + 8 * kMChunk * 2;
+    // per-wave buffer pair: V codes [64][S] of a chunk (padded rows), then
+    // p VC / 8 (columns 0..3) and p VD / 8 (columns 4..7) of its tokens, fp16
+    // [8][kPbStride]
+    constexpr int kBufB = vcode_bytes(S) + 8 * kPbStride * 2;
     uint8_t* const vbase = reinterpret_cast<uint8_t*>(vst);
     const uint32_t vbase_lds = (uint32_t)(reinterpret_cast<uintptr_t>(vst) - reinterpret_cast<uintptr_t>(smem));
     // A of the beta product: row 0 all ones
@@ -447,7 +457,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     auto front = [&](const Ld& c, int bs) {
       uint8_t* vb = vbase + bs * kBufB;
 #pragma unroll
-      for (int i = 0; i < S / 16; ++i) *reinterpret_cast<uint4_t*>(vb + lane * S + 16 * i) = c.vcode[i];
+      for (int i = 0; i < S / 16; ++i) *reinterpret_cast<uint4_t*>(vb + lane * S + (lane >> 3) * kVRowPad + 16 * i) = c.vcode[i];
       float kn1, kn2, vn1, vn2;
       if constexpr (DQ) {
         kn1 = dq_value(c.kpar, c.ksc >> 16);
@@ -537,13 +547,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       if (bs) eb1 = eb;
       else eb0 = eb;
       const float fw = wn12 * pow2f(ev - 3), fb = wn1 * pow2f(eb - 3);
-      uint16_t* pb = reinterpret_cast<uint16_t*>(vbase + bs * kBufB + kMChunk * S);
+      uint16_t* pb = reinterpret_cast<uint16_t*>(vbase + bs * kBufB + vcode_bytes(S));
 #pragma unroll
       for (int r = 0; r < GQ; ++r) {
         const float pr = __builtin_amdgcn_exp2f(dl[r]);
         lp[r] += pr;
-        pb[r * kMChunk + lane] = f2h(pr * fw);
-        pb[(4 + r) * kMChunk + lane] = f2h(pr * fb);
+        pb[r * kPbStride + lane] = f2h(pr * fw);
+        pb[(4 + r) * kPbStride + lane] = f2h(pr * fb);
       }
       if (lane == 0) {  // the references are uniform over the wave
 #pragma unroll
@@ -554,12 +564,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     // (m16, kb) supplies tokens 32 c + 8 kb + e of step c
     auto back = [&](int chk, int bs) {
       const uint8_t* vb = vbase + bs * kBufB;
-      const uint32_t pb_lds = vbase_lds + bs * kBufB + kMChunk * S;
+      const uint32_t pb_lds = vbase_lds + bs * kBufB + vcode_bytes(S);
       float4_t db = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const half8_t bw = __builtin_bit_cast(half8_t, lds_b128(pb_lds + 2 * ((m16 & 7) * kMChunk + 32 * c + 8 * kb)));
-        const uint8_t* vrow = vb + (32 * c + 8 * kb) * S + m16;
+        const half8_t bw = __builtin_bit_cast(half8_t, lds_b128(pb_lds + 2 * ((m16 & 7) * kPbStride + 32 * c + 8 * kb)));
+        const uint8_t* vrow = vb + (32 * c + 8 * kb) * S + (4 * c + kb) * kVRowPad + m16;
         if constexpr (SUB == 4) {
 #pragma unroll
           for (int g2 = 0; g2 < 2; ++g2) {
