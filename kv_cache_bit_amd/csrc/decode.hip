@@ -39,6 +39,10 @@ constexpr int kLutStride = 257;  // odd row stride: finish-step reads hit distin
 // one inverse transform, and the split's (m, l, o) partial is written.
 
 constexpr int kChunk = 64;
+// Staged V code rows of the matrix-core value sum (1 bit, one head): token
+// t's 16-byte row sits at 16 t + 16 (t / 8): the value step's lane groups
+// read rows 8 apart, which without the padding share banks.
+constexpr int kVstWave = kChunk * 16 + kChunk / 8 * 16;  // bytes per wave
 constexpr float kLazyMax = 3.f;  // log2 headroom of the running softmax reference
 
 struct DecodeSmem {
@@ -58,7 +62,7 @@ __host__ __device__ constexpr DecodeSmem decode_smem(int sub, int gh, int split_
   s.lut = o; o += gh * S * kLutStride;       // LUTs; reused for the wave merge
   s.wbuf = o; o += 4 * gh * kChunk;          // per-wave chunk weights
   s.qmu = o; o += kMaxSplitBlocks * gh;      // q . KMU_b of the split's blocks
-  s.vst = o; o += (sub == 8 && gh == 1) ? 4 * kChunk * 16 / 4 : 0;  // per-wave V codes [64][16] (matrix-core values)
+  s.vst = o; o += (sub == 8 && gh == 1) ? 4 * kVstWave / 4 : 0;  // per-wave V codes [64][16] (matrix-core values)
   s.total = o;
   return s;
 }
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   // when it drops), so no N1 N2 overflows fp16 and no small one underflows;
   // 64 is above any chunk's exponent
   int ev = 64;
-  uint8_t* const vstw = reinterpret_cast<uint8_t*>(smem + L.vst) + wave * kChunk * 16;
+  uint8_t* const vstw = reinterpret_cast<uint8_t*>(smem + L.vst) + wave * kVstWave;
   const uint32_t vst_lds = (uint32_t)(reinterpret_cast<uintptr_t>(vstw) - reinterpret_cast<uintptr_t>(smem));
   const uint32_t wb_lds = (uint32_t)(reinterpret_cast<uintptr_t>(wb) - reinterpret_cast<uintptr_t>(smem));
   const int m16 = lane & 15, kb = lane >> 4;
@@ -332,7 +336,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   // are already in flight into the other buffer)
   auto chunk_step = [&](int ch, const ChunkRegs& cur) {
     if constexpr (kMV)
-      *reinterpret_cast<uint4_t*>(vstw + lane * 16) = uint4_t{cur.vcw[0], cur.vcw[1], cur.vcw[2], cur.vcw[3]};
+      *reinterpret_cast<uint4_t*>(vstw + lane * 16 + (lane >> 3) * 16) = uint4_t{cur.vcw[0], cur.vcw[1], cur.vcw[2], cur.vcw[3]};
     float kn1, kn2, vn1, vn2, vm0, vm1;
     if constexpr (DQ) {
       kn1 = dq_value(cur.kpar, cur.ksc >> 16);
@@ -492,7 +496,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const half8_t bw = __builtin_bit_cast(half8_t, lds_u32x4(wb_lds + 2 * (32 * c + 8 * kb)));
-        const uint8_t* vrow = vstw + (32 * c + 8 * kb) * 16 + m16;
+        const uint8_t* vrow = vstw + (32 * c + 8 * kb) * 16 + (4 * c + kb) * 16 + m16;
         uint32_t code[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) code[e] = vrow[e * 16];
