@@ -36,10 +36,12 @@ namespace nsnq {
 namespace {
 
 constexpr int kMChunk = 64;                                 // tokens per wave step
-// Staged V code rows (up to 4 heads): token t's row sits at t S + 16 (t / 8)
-// bytes, 16 bytes of padding after every 8 rows.  The value step's lane
-// groups read rows 8 apart; without the padding those rows share banks.
-constexpr int kVRowPad = 16;
+// Staged V code rows (up to 4 heads): token t's row sits at t S + 32 (t / 8)
+// bytes, 32 bytes of padding after every 8 rows.  The value step's lane
+// groups read rows 8 apart; without the padding those rows share banks.  At
+// 2 bits a row holds its codes as pairs (slot j, slot j + 16), so one 16-bit
+// read gives a lane both slots it gathers for.
+constexpr int kVRowPad = 32;
 __host__ __device__ constexpr int vcode_bytes(int S) { return kMChunk * S + kMChunk / 8 * kVRowPad; }
 // Row stride (fp16 elements) of the staged value weights [8][kMChunk]: the
 // value step reads rows m16 mod 8 at once, which with a 128-byte stride share
@@ -456,8 +458,20 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     // stage chunk `c`'s V codes in buffer `bs`, score its tokens
     auto front = [&](const Ld& c, int bs) {
       uint8_t* vb = vbase + bs * kBufB;
+      uint8_t* vrw = vb + lane * S + (lane >> 3) * kVRowPad;
+      if constexpr (SUB == 4) {
+        // bytes (2 j, 2 j + 1) = (code of slot j, code of slot j + 16)
+        const uint32_t d[8] = {c.vcode[0][0], c.vcode[0][1], c.vcode[0][2], c.vcode[0][3],
+                               c.vcode[1][0], c.vcode[1][1], c.vcode[1][2], c.vcode[1][3]};
+        uint32_t pd[8];
 #pragma unroll
-      for (int i = 0; i < S / 16; ++i) *reinterpret_cast<uint4_t*>(vb + lane * S + (lane >> 3) * kVRowPad + 16 * i) = c.vcode[i];
+        for (int k = 0; k < 8; ++k) pd[k] = __builtin_amdgcn_perm(d[4 + k / 2], d[k / 2], (k & 1) ? 0x07030602u : 0x05010400u);
+        *reinterpret_cast<uint4_t*>(vrw) = uint4_t{pd[0], pd[1], pd[2], pd[3]};
+        *reinterpret_cast<uint4_t*>(vrw + 16) = uint4_t{pd[4], pd[5], pd[6], pd[7]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < S / 16; ++i) *reinterpret_cast<uint4_t*>(vrw + 16 * i) = c.vcode[i];
+      }
       float kn1, kn2, vn1, vn2;
       if constexpr (DQ) {
         kn1 = dq_value(c.kpar, c.ksc >> 16);
@@ -571,16 +585,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         const half8_t bw = __builtin_bit_cast(half8_t, lds_b128(pb_lds + 2 * ((m16 & 7) * kPbStride + 32 * c + 8 * kb)));
         const uint8_t* vrow = vb + (32 * c + 8 * kb) * S + (4 * c + kb) * kVRowPad + m16;
         if constexpr (SUB == 4) {
+          // the code pairs (slot m16, slot m16 + 16) of the eight tokens
+          const uint16_t* vrow16 = reinterpret_cast<const uint16_t*>(vrow - m16) + m16;
+          uint32_t code2[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) code2[e] = vrow16[e * (S / 2)];
 #pragma unroll
           for (int g2 = 0; g2 < 2; ++g2) {
-            // all eight code bytes, then all eight gathers, then the products
-            uint32_t code[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) code[e] = vrow[e * S + 16 * g2];
+            // all eight gathers, then the products
             __builtin_amdgcn_sched_barrier(0);
             u32x2_t cw[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) cw[e] = lds_b64(code[e] << 3);
+            for (int e = 0; e < 8; ++e) cw[e] = lds_b64(g2 ? code_shl<1, 3>(code2[e]) : code_shl<0, 3>(code2[e]));
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ep = 0; ep < 4; ++ep) {
