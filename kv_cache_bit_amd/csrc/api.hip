@@ -463,35 +463,39 @@ DecodePlan plan_decode(const nsnq_params* p, const nsnq_cache* c, int q_heads, i
   const int nblk = c->n_quant / R;
   const int max_ts = decode_max_split_tokens(sub_of(p), pl.gh, R);
   const int max_bps = max_ts / R;  // blocks per split
-  int bps;
-  if (nblk == 0) {
-    bps = 1;
-  } else if (num_splits > 0) {
-    bps = (nblk + num_splits - 1) / num_splits;
-  } else {
-    // about 1024 work-groups over the grid, each with at least 512 tokens so
-    // each of its 4 waves streams at least two 64-token chunks.  The
-    // grouped-head kernel has long per-group set-up and only a few groups fit
-    // a CU: there the grid is sized to what the device holds at once
-    // (residual-window groups included), so every group starts in the first
-    // round instead of a short second round trailing the first.
-    const int64_t units = (int64_t)c->batch * c->kv_heads * (G / pl.gh);
-    int64_t want = (1024 + units - 1) / units;
-    if (pl.mfma) {
-      const int64_t cap = decode_mfma_resident_groups(sub_of(p), pl.gh, (p->flags & NSNQ_DOUBLE_QUANT) != 0);
-      const int64_t fit = (cap - (c->n_resid > 0 ? units : 0)) / units;
-      if (cap > 0 && fit >= 4) want = fit;
+  // Split count over the compressed blocks; the splits then take nblk /
+  // nsplit_q blocks each, as evenly as whole blocks allow (no short last
+  // split), between 1 and max_bps blocks.
+  int64_t nsq = 0;
+  if (nblk > 0) {
+    if (num_splits > 0) {
+      nsq = num_splits;
+    } else {
+      // about 1024 work-groups over the grid, each with at least 512 tokens so
+      // each of its 4 waves streams at least two 64-token chunks.  The
+      // grouped-head kernel has long per-group set-up and only a few groups
+      // fit a CU: there the grid is sized to what the device holds at once
+      // (residual-window groups included), so every group starts in the first
+      // round instead of a short second round trailing the first.
+      const int64_t units = (int64_t)c->batch * c->kv_heads * (G / pl.gh);
+      int64_t want = (1024 + units - 1) / units;
+      if (pl.mfma) {
+        const int64_t cap = decode_mfma_resident_groups(sub_of(p), pl.gh, (p->flags & NSNQ_DOUBLE_QUANT) != 0);
+        const int64_t fit = (cap - (c->n_resid > 0 ? units : 0)) / units;
+        if (cap > 0 && fit >= 4) want = fit;
+      }
+      const int min_bps = (512 + R - 1) / R;
+      const int64_t most = nblk / min_bps > 0 ? nblk / min_bps : 1;
+      nsq = want < most ? want : most;
     }
-    if (want < 1) want = 1;
-    bps = (int)((nblk + want - 1) / want);
-    const int min_bps = (512 + R - 1) / R;
-    if (bps < min_bps) bps = min_bps;
+    if (nsq > nblk) nsq = nblk;
+    if (nsq > kMaxSplits - 1) nsq = kMaxSplits - 1;
+    const int64_t least = (nblk + max_bps - 1) / max_bps;
+    if (nsq < least) nsq = least;
+    if (nsq < 1) nsq = 1;
   }
-  if (bps < 1) bps = 1;
-  if (nblk > 0 && (nblk + bps - 1) / bps > kMaxSplits - 1) bps = (nblk + kMaxSplits - 2) / (kMaxSplits - 1);
-  if (bps > max_bps) bps = max_bps;
-  pl.split_tokens = bps * R;
-  pl.nsplit_q = nblk == 0 ? 0 : (nblk + bps - 1) / bps;
+  pl.nsplit_q = (int)nsq;
+  pl.split_tokens = nsq > 0 ? (int)((nblk + nsq - 1) / nsq) * R : R;  // the longest split
   pl.nsplit = pl.nsplit_q + (c->n_resid > 0 ? 1 : 0);
   pl.lds = pl.mfma ? decode_mfma_lds_bytes(sub_of(p), pl.gh) : decode_lds_bytes(sub_of(p), pl.gh, pl.split_tokens, R);
   return pl;

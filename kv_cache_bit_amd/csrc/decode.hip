@@ -145,8 +145,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
     return;
   }
 
-  const int t0 = split * a.split_tokens;
-  const int ntok = max(0, min(a.split_tokens, row_quant(a, b) - t0));  // 0: empty partial
+  const int sb0 = split_block(a, split), sb1 = split_block(a, split + 1);
+  const int t0 = sb0 << a.lgR;
+  const int ntok = max(0, min((sb1 - sb0) << a.lgR, row_quant(a, b) - t0));  // 0: empty partial
   const int nchunk = ntok / kChunk;
   const uint8_t* kc = a.kcodes + (unit * a.cap + t0) * S;
   const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.kscales) + unit * a.cap + t0;

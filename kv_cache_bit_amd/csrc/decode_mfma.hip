@@ -186,8 +186,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     return;
   }
 
-  const int t0 = split * a.split_tokens;
-  const int ntok = max(0, min(a.split_tokens, row_quant(a, b) - t0));  // 0: empty partial
+  const int sb0 = split_block(a, split), sb1 = split_block(a, split + 1);
+  const int t0 = sb0 << a.lgR;
+  const int ntok = max(0, min((sb1 - sb0) << a.lgR, row_quant(a, b) - t0));  // 0: empty partial
   const int nchunk = ntok / kMChunk;
   const int nblk = (ntok >> a.lgR);
   const uint8_t* kc = a.kcodes + (unit * a.cap + t0) * S;

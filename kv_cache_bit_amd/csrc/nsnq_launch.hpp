@@ -115,8 +115,8 @@ struct DecodeArgs {
   int cap, R;
   int lgR;           // log2 R (R is a power of two)
   int n_quant, n_resid;
-  int split_tokens;  // compressed tokens per split (multiple of R)
-  int nsplit_q;      // splits over the compressed tokens
+  int split_tokens;  // compressed tokens of the longest split (multiple of R)
+  int nsplit_q;      // splits over the compressed tokens (split_block)
   int nsplit;        // nsplit_q + (n_resid > 0)
   float scale_log2;  // softmax scale * log2(e)
   const int8_t* signs;  // randomised-Hadamard signs [128] or null
@@ -131,7 +131,13 @@ struct DecodeArgs {
   int rope_pos0;
 };
 
-// Per-row token counts of a decode launch.
+// Compressed split s of a decode launch covers blocks [split_block(a, s),
+// split_block(a, s + 1)) of the host bound n_quant: nsplit_q splits as even as
+// whole blocks allow.
+__device__ __forceinline__ int split_block(const DecodeArgs& a, int s) {
+  return (int)(((int64_t)s * (a.n_quant >> a.lgR)) / a.nsplit_q);
+}
+
 // Per-row token counts of a decode launch (ragged counters are clamped to the
 // host bounds the launch was sized for).
 __device__ __forceinline__ int row_quant(const DecodeArgs& a, int b) {
