@@ -59,7 +59,7 @@ def lib():
             "orc_rope": (None, [P, i64, i32, i32, P, P, i32]),
             "orc_finetune": (None, [P, i64, i32, i32, i32, i32, f64, P, P, P]),
             "orc_dq_scales_bytes": (i32, [i32]),
-            "orc_encode_dq": (i32, [P, i64, i32, i32, i32, i32, P, i32, P, i32, P, P, P, P, P, P, P, P, P]),
+            "orc_encode_dq": (i32, [P, i64, i32, i32, i32, i32, P, i32, P, i32, P, P, P, P, P, P, P, P, P, P, P]),
             "orc_dequant_dq": (None, [P, P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P]),
             "orc_codebook_dq": (None, [P, i32, i32, P, P, P]),
         }
@@ -181,12 +181,15 @@ def codebook_dq(codebook, group: int = 32) -> dict:
 
 
 def encode(x, R: int, codebook, with_u: bool = False, signs=None, scale_adjust: bool = False,
-           dq: bool = False) -> dict:
+           dq: bool = False, force_records=None) -> dict:
     """Encode streams x fp16 [..., L, d] (leading dims are independent units).
     signs: +-1 [d] for the randomised Hadamard transform (None: plain);
     scale_adjust: Strategy-3 scale folded into n2; dq: double-quantised format
     (scales [..., nq/R, dq_scales_bytes(R)] and mu [..., nq/R, 80] uint8
     records, plus n1hat / m1 per token and mmu per block channel).
+    force_records (dq only): (scales, mu) records of the same layout whose
+    4-bit decisions, (S, Z) and codes, every block takes instead of rounding
+    its own; n2, codes, gap and u then follow from those read-back values.
 
     Returns codes [..., nq, S] uint8, scales [..., nq, 2] (fp16 bits),
     mu [..., nq/R, d] (fp16 bits), resid [..., R, d] (fp16 bits, rows >= r
@@ -213,9 +216,14 @@ def encode(x, R: int, codebook, with_u: bool = False, signs=None, scale_adjust: 
         n1hat = np.zeros((n_units, nq), np.float64)
         m1 = np.zeros((n_units, nq), np.float64)
         mmu = np.zeros((n_units, nq // R, d), np.float64)
+        fs = fm = None
+        if force_records is not None:
+            fs = np.ascontiguousarray(force_records[0], dtype=np.uint8).reshape(n_units, nq // R, SR)
+            fm = np.ascontiguousarray(force_records[1], dtype=np.uint8).reshape(n_units, nq // R, DQ_MU_BYTES)
         lib().orc_encode_dq(_p(xb), n_units, L, d, R, s, _p(cb), ncw, _p(sg) if sg is not None else None,
                             int(scale_adjust), _p(codes), _p(scales), _p(mu), _p(resid), _p(gap),
-                            _p(u) if with_u else None, _p(n1hat), _p(m1), _p(mmu))
+                            _p(u) if with_u else None, _p(n1hat), _p(m1), _p(mmu),
+                            _p(fs) if fs is not None else None, _p(fm) if fm is not None else None)
         out = dict(codes=codes.reshape(*lead, nq, S), scales=scales.reshape(*lead, nq // R, SR),
                    mu=mu.reshape(*lead, nq // R, DQ_MU_BYTES), resid=resid.reshape(*lead, R, d),
                    gap=gap.reshape(*lead, nq, S), n1hat=n1hat.reshape(*lead, nq), m1=m1.reshape(*lead, nq),

@@ -416,11 +416,17 @@ static int get_nib(const uint8_t* p, int i) { return (p[i / 2] >> (4 * (i & 1)))
  * VQ and options as orc_encode_unit).  scales_rec: [nq/R][orc_dq_scales_bytes]
  * bytes, mu_rec: [nq/R][80] bytes.  Optional outputs per quantised token:
  * n1hat, m1 (margin of its q1); per block and channel: mmu (margin of its mu
- * code).  Returns nq. */
+ * code).  force_sr / force_mr (optional, laid out like scales_rec / mu_rec):
+ * take every block's 4-bit decisions for s1 and the mean, (S, Z) and codes,
+ * from these records instead of rounding, and run the rest of the encode from
+ * their read-back values (a test compares another encoder's blocks whose
+ * rounding decisions differ near a tie this way); their n2 bytes are ignored,
+ * and m1 / mmu are 1/2.  Returns nq. */
 int orc_encode_unit_dq(const uint16_t* x, int L, int d, int R, int s,
                        const uint16_t* cb, int ncw, const double* signs, int scale_adjust,
                        uint8_t* codes, uint8_t* scales_rec, uint8_t* mu_rec, uint16_t* resid,
-                       double* gap, double* u_out, double* n1hat_out, double* m1_out, double* mmu_out) {
+                       double* gap, double* u_out, double* n1hat_out, double* m1_out, double* mmu_out,
+                       const uint8_t* force_sr, const uint8_t* force_mr) {
   int r = orc_resid_count(L, R);
   int nq = L - r;
   int S = d / s;
@@ -457,7 +463,18 @@ int orc_encode_unit_dq(const uint16_t* x, int L, int d, int R, int s,
       n1[t] = sqrt(ss) / sqrt_d;
     }
     uint16_t Z1, S1;
-    orc_rtn4(n1, R, &Z1, &S1, q1, n1h, m1);
+    if (force_sr) {
+      const uint8_t* fr = force_sr + (size_t)blk * SR;
+      S1 = get_h(fr + 2 * R + R / 2);
+      Z1 = get_h(fr + 2 * R + R / 2 + 2);
+      for (int t = 0; t < R; ++t) {
+        q1[t] = (uint8_t)get_nib(fr + 2 * R, t);
+        n1h[t] = orc_h2d(Z1) + orc_h2d(S1) * (double)q1[t];
+        m1[t] = 0.5;
+      }
+    } else {
+      orc_rtn4(n1, R, &Z1, &S1, q1, n1h, m1);
+    }
     for (int t = 0; t < R; ++t) sr[2 * R + t / 2] |= (uint8_t)(q1[t] << (4 * (t & 1)));
     put_h(sr + 2 * R + R / 2, S1);
     put_h(sr + 2 * R + R / 2 + 2, Z1);
@@ -474,7 +491,18 @@ int orc_encode_unit_dq(const uint16_t* x, int L, int d, int R, int s,
     }
     for (int g = 0; g < d / 32; ++g) {
       uint16_t Zm, Sm;
-      orc_rtn4(mu + 32 * g, 32, &Zm, &Sm, qm + 32 * g, muh + 32 * g, mm + 32 * g);
+      if (force_mr) {
+        const uint8_t* fm = force_mr + (size_t)blk * ORC_DQ_MU_BYTES;
+        Sm = get_h(fm + 64 + 4 * g);
+        Zm = get_h(fm + 64 + 4 * g + 2);
+        for (int c = 32 * g; c < 32 * g + 32; ++c) {
+          qm[c] = (uint8_t)get_nib(fm, c);
+          muh[c] = orc_h2d(Zm) + orc_h2d(Sm) * (double)qm[c];
+          mm[c] = 0.5;
+        }
+      } else {
+        orc_rtn4(mu + 32 * g, 32, &Zm, &Sm, qm + 32 * g, muh + 32 * g, mm + 32 * g);
+      }
       put_h(mr + 64 + 4 * g, Sm);
       put_h(mr + 64 + 4 * g + 2, Zm);
     }
@@ -523,7 +551,8 @@ int orc_encode_unit_dq(const uint16_t* x, int L, int d, int R, int s,
 int orc_encode_dq(const uint16_t* x, int64_t n_units, int L, int d, int R, int s,
                   const uint16_t* cb, int ncw, const double* signs, int scale_adjust,
                   uint8_t* codes, uint8_t* scales_rec, uint8_t* mu_rec, uint16_t* resid,
-                  double* gap, double* u_out, double* n1hat, double* m1, double* mmu) {
+                  double* gap, double* u_out, double* n1hat, double* m1, double* mmu,
+                  const uint8_t* force_sr, const uint8_t* force_mr) {
   int r = orc_resid_count(L, R);
   int nq = L - r;
   int S = d / s;
@@ -536,7 +565,9 @@ int orc_encode_dq(const uint16_t* x, int64_t n_units, int L, int d, int R, int s
                        mu_rec + (size_t)i * (nq / R) * ORC_DQ_MU_BYTES, resid + (size_t)i * R * d,
                        gap ? gap + (size_t)i * nq * S : NULL, u_out ? u_out + (size_t)i * nq * d : NULL,
                        n1hat ? n1hat + (size_t)i * nq : NULL, m1 ? m1 + (size_t)i * nq : NULL,
-                       mmu ? mmu + (size_t)i * (nq / R) * d : NULL);
+                       mmu ? mmu + (size_t)i * (nq / R) * d : NULL,
+                       force_sr ? force_sr + (size_t)i * (nq / R) * SR : NULL,
+                       force_mr ? force_mr + (size_t)i * (nq / R) * ORC_DQ_MU_BYTES : NULL);
   }
   return nq;
 }

@@ -142,8 +142,10 @@ def check_attention(g: np.ndarray, o: np.ndarray, tol: float = ATTN_TOL):
 def oracle_encode(x, R: int, cb_bits: np.ndarray, **kw) -> dict:
     """The oracle's encoding of streams x, with the Hadamard-domain vectors u
     (fp64) the code checks need and the codebook it used."""
-    e = oracle.encode(x.cpu() if hasattr(x, "cpu") else x, R, cb_bits, with_u=True, **kw)
+    xc = x.cpu() if hasattr(x, "cpu") else x
+    e = oracle.encode(xc, R, cb_bits, with_u=True, **kw)
     e["cb"] = cb_bits
+    e["x"], e["kw"] = xc, kw  # for re-encodes with another encoder's 4-bit decisions
     return e
 
 
@@ -211,8 +213,10 @@ def compare_encoded_dq(cache: nsnq.KVCache, ek: dict, ev: dict, R: int, scale_ad
     decisions all agree is then held to the plain bars (codes with the
     near-tie rule, each differing code near-best for the oracle's u; n2 within
     one ulp).  Blocks with a differing decision (expected rarely) are at most
-    2% of blocks.  Returns the list of per-half boolean block masks (True =
-    compared fully)."""
+    2% of blocks; the oracle re-encodes them with the GPU's own 4-bit records
+    (its decisions taken as given), and their codes and n2 are held to the
+    same bars against that re-encode.  Returns the list of per-half boolean
+    block masks (True = the 4-bit decisions agree)."""
     masks = []
     for which, e in ((0, ek), (1, ev)):
         gh = half_np(cache, which)
@@ -247,5 +251,18 @@ def compare_encoded_dq(cache: nsnq.KVCache, ek: dict, ev: dict, R: int, scale_ad
         else:
             check_f16_ulp(gn2[full], on2[full], "n2")
         assert np.array_equal(gh["resid"][..., :e["n_resid"], :], e["resid"][..., :e["n_resid"], :])
+        if (~full).any():
+            fe = oracle.encode(e["x"], R, e["cb"], with_u=True, force_records=(gh["scales"], gh["mu"]), **e["kw"])
+            fn2 = _dq_fields(fe["scales"], fe["mu"], R)[0]
+            fc = fe["codes"].reshape(cg.shape)
+            fgap = fe["gap"].reshape(cg.shape)
+            fu = fe["u"].reshape(*cg.shape[:-1], -1)
+            part = ~full
+            check_codes(cg[part], fc[part], fgap[part], fu[part], e["cb"], "codes (double-quantised, GPU's 4-bit records)")
+            if scale_adjust:
+                same = np.all(cg[part] == fc[part], axis=-1)
+                check_f16_ulp(gn2[part][same], fn2[part][same], "n2 (GPU's 4-bit records)")
+            else:
+                check_f16_ulp(gn2[part], fn2[part], "n2 (GPU's 4-bit records)")
         masks.append(full)
     return masks

@@ -98,6 +98,56 @@ def test_dq_records_and_exact_inverse(oracle_codebooks, bits, R):
     assert np.allclose(np.linalg.norm(xd - xh, axis=1), pred, rtol=1e-2)
 
 
+@pytest.mark.parametrize("bits,R", [(2, 64), (1, 128)])
+def test_dq_forced_records(oracle_codebooks, bits, R):
+    """Encoding with given 4-bit records: its own records reproduce the plain
+    encode byte for byte; records with some decisions moved by one level are
+    taken as given (n1_hat and mu_hat read back from them), and the rest of the
+    encode then follows from those values exactly as it does from rounded ones:
+    x = n1_hat (n2 H^T u + mu_hat), with the codes the nearest codewords of u."""
+    cb = oracle_codebooks[bits]
+    L = 3 * R + 7
+    x = synth.kv_unit(61 + bits, L, D).numpy()
+    enc = oracle.encode(x[None], R, cb, with_u=True, dq=True)
+    same = oracle.encode(x[None], R, cb, with_u=True, dq=True, force_records=(enc["scales"], enc["mu"]))
+    for k in ("codes", "scales", "mu", "resid", "n1hat", "u"):
+        assert np.array_equal(same[k], enc[k]), k
+    # move some s1 and mean codes one level (kept within 0..15)
+    sc, mu = enc["scales"].copy(), enc["mu"].copy()
+    nb = sc.shape[1]
+    rng = np.random.default_rng(5)
+    for b in range(nb):
+        for t in rng.choice(R, 5, replace=False):
+            byte = 2 * R + t // 2
+            q = (sc[0, b, byte] >> (4 * (t & 1))) & 15
+            q2 = q + 1 if q < 15 else q - 1
+            sc[0, b, byte] = (sc[0, b, byte] & (0xF0 if t & 1 == 0 else 0x0F)) | (q2 << (4 * (t & 1)))
+        for c in rng.choice(D, 7, replace=False):
+            q = (mu[0, b, c // 2] >> (4 * (c & 1))) & 15
+            q2 = q + 1 if q < 15 else q - 1
+            mu[0, b, c // 2] = (mu[0, b, c // 2] & (0xF0 if c & 1 == 0 else 0x0F)) | (q2 << (4 * (c & 1)))
+    f = oracle.encode(x[None], R, cb, with_u=True, dq=True, force_records=(sc, mu))
+    n2_st, n1hat, muhat = _parse(f, R)
+    # the records came through unchanged apart from the n2 bytes
+    assert np.array_equal(f["scales"][..., 2 * R:], sc[..., 2 * R:]) and np.array_equal(f["mu"], mu)
+    assert np.array_equal(n1hat, f["n1hat"][0])
+    assert not np.array_equal(n1hat, enc["n1hat"][0])
+    nq = f["n_quant"]
+    Hs = scipy.linalg.hadamard(D).astype(np.float64) / np.sqrt(D)
+    xd = x[:nq].astype(np.float64)
+    mub = np.repeat(muhat, R, axis=0)
+    n2 = np.linalg.norm(xd / n1hat[:, None] - mub, axis=1) / np.sqrt(D)
+    rec = n1hat[:, None] * (n2[:, None] * (f["u"][0] @ Hs) + mub)
+    assert np.allclose(rec, xd, rtol=0, atol=1e-10 * np.abs(xd).max())
+    assert np.allclose(n2_st, n2, rtol=2.0 ** -11)
+    # codes: the nearest codeword of each sub-vector of u (brute force)
+    c64 = oracle.f16_to_f64(cb)
+    s = c64.shape[1]
+    sub = f["u"][0].reshape(-1, s)
+    dist = ((sub[:, None, :] - c64[None, :, :]) ** 2).sum(-1)
+    assert np.array_equal(f["codes"][0].reshape(-1), np.argmin(dist, axis=1).astype(np.uint8))
+
+
 def test_dq_bits_per_element():
     """Overhead of the stored NSN parameters per element (d = 128): at R = 64
     the unpadded records cost 0.238 bits (n2 fp16, s1 in 4 bits with its
