@@ -144,6 +144,32 @@ def test_buffer_bytes(nsnq):
         nsnq.nsnq_buffer_bytes(nsnq.params(2, 128, flags=8), 128)
 
 
+def test_decode_split_plan(nsnq):
+    """Split planning (host, read back through the workspace size, which holds
+    one (d + 2)-float partial per row, query head and split): a requested split
+    count is honoured between one block per split and 16 blocks per split, the
+    residual window adds one split, and the default plan for one head keeps at
+    least 512 tokens per split."""
+    L = nsnq.lib()
+    by = ctypes.byref
+    p = nsnq.params(2, 128)
+
+    def nsplit(nq, nr, ns, B=1, H=2):
+        c = _cache_struct(nsnq, B=B, H=H, cap=nq + 128, nq=nq, nr=nr)
+        per = 4 * (128 + 2) * B * H
+        ws = L.nsnq_decode_workspace_bytes(by(p), by(c), H, ns)
+        assert ws % per == 0
+        return ws // per
+
+    assert nsplit(31 * 128, 128, 7) == 8     # 7 splits of 4-5 blocks + the residual window
+    assert nsplit(31 * 128, 128, 40) == 32   # one block each, no more
+    assert nsplit(31 * 128, 0, 1) == 2       # 16 blocks at most: two splits
+    assert nsplit(5 * 128, 3, 3) == 4
+    assert nsplit(0, 5, 0) == 1              # residual tokens only
+    assert nsplit(31 * 128, 128, 0, B=1, H=32) == 8   # default: 512 tokens or more per split
+    assert nsplit(31 * 128, 128, 0, B=256, H=32) == 3  # default at batch 256: the 16-block cap
+
+
 def test_noalloc_decode_rejects_oversize_on_the_host(nsnq):
     """The allocation-free decode refuses, before any HIP call, a call whose
     split partials would not fit the static scratch; it validates its

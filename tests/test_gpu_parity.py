@@ -254,7 +254,7 @@ def test_decode_same_cache_and_end_to_end(oracle_codebooks, bits, R, B, Hq, Hkv,
     cache.n_quant, cache.n_resid = ek["n_quant"], ek["n_resid"]
     qd = q.to(DEV)
     outs = []
-    for ns in (0, 1, 3):
+    for ns in (0, 1, 3, 40):  # 40: more splits than blocks (one block each)
         o = nsnq.nsnq_decode_attention(p, cbt, qd, cache, num_splits=ns).float().cpu().numpy()
         check_attention(o, ref)
         outs.append(o)
