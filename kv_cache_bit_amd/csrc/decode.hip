@@ -123,10 +123,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   float* qmus = smem + L.qmu;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x;
+  const int split = a.split_slow ? blockIdx.y : blockIdx.x;
+  const int ux = a.split_slow ? blockIdx.x : blockIdx.y;
   const int groups = a.G / GH;
-  const int hg = blockIdx.y % groups;
-  const int bk = blockIdx.y / groups;
+  const int hg = ux % groups;
+  const int bk = ux / groups;
   const int b = bk / a.Hkv, hk = bk % a.Hkv;
   const int h0 = hk * a.G + hg * GH;
   const int64_t unit = (int64_t)b * a.Hkv + hk;
@@ -709,13 +710,42 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
 }
 
+// Work-groups of a kernel variant the device holds at once (0 if unknown),
+// cached per device in `cache` (0 = not asked yet, -1 = unknown).
+static int resident_groups(const void* kernel, size_t lds, std::atomic<int> (&cache)[kMaxDevices]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess) per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    (void)hipGetLastError();
+    v = per_cu > 0 && cus > 0 ? per_cu * cus : -1;
+    cache[dev].store(v, std::memory_order_relaxed);  // concurrent first queries store the same value
+  }
+  return v > 0 ? v : 0;
+}
+
 template <int SUB, int GH, bool DQ, bool ROPE>
 static hipError_t launch_decode_dq(const DecodeArgs& a, int B, size_t lds, hipStream_t stream) {
   static std::atomic<bool> lds_set[kMaxDevices];
-  const hipError_t e = allow_lds(reinterpret_cast<const void*>(&decode_split_kernel<SUB, GH, DQ, ROPE>), lds_set);
+  static std::atomic<int> resident[kMaxDevices];
+  const void* k = reinterpret_cast<const void*>(&decode_split_kernel<SUB, GH, DQ, ROPE>);
+  const hipError_t e = allow_lds(k, lds_set);
   if (e != hipSuccess) return e;
-  dim3 grid(a.nsplit, B * a.Hkv * (a.G / GH)), block(256);
-  hipLaunchKernelGGL((decode_split_kernel<SUB, GH, DQ, ROPE>), grid, block, lds, stream, a);
+  // When every compressed split fits the device at once, they go first and
+  // the short residual groups fill in behind them; otherwise each row's
+  // groups go together, so residual reads overlap the compressed splits.
+  DecodeArgs c = a;
+  const int units = B * a.Hkv * (a.G / GH);
+  const int cap = resident_groups(k, lds, resident);
+  c.split_slow = (cap > 0 && (int64_t)a.nsplit_q * units <= cap) || units > 65535 ? 1 : 0;  // grid y <= 65535
+  const dim3 grid = c.split_slow ? dim3(units, a.nsplit) : dim3(a.nsplit, units), block(256);
+  hipLaunchKernelGGL((decode_split_kernel<SUB, GH, DQ, ROPE>), grid, block, lds, stream, c);
   return hipGetLastError();
 }
 

@@ -156,10 +156,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m16 = lane & 15, kb = lane >> 4;
-  const int split = blockIdx.x;
+  const int split = a.split_slow ? blockIdx.y : blockIdx.x;
+  const int ux = a.split_slow ? blockIdx.x : blockIdx.y;
   const int groups = a.G / GQ;
-  const int hg = blockIdx.y % groups;
-  const int bk = blockIdx.y / groups;
+  const int hg = ux % groups;
+  const int bk = ux / groups;
   const int b = bk / a.Hkv, hk = bk % a.Hkv;
   const int h0 = hk * a.G + hg * GQ;
   const int64_t unit = (int64_t)b * a.Hkv + hk;
@@ -959,8 +960,14 @@ static hipError_t launch_mfma_dq(const DecodeArgs& a, int B, hipStream_t stream)
   static std::atomic<bool> lds_set[kMaxDevices];
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(&decode_mfma_kernel<SUB, GQ, DQ>), lds_set);
   if (e != hipSuccess) return e;
-  dim3 grid(a.nsplit, B * a.Hkv * (a.G / GQ)), block(256);
-  hipLaunchKernelGGL((decode_mfma_kernel<SUB, GQ, DQ>), grid, block, lds, stream, a);
+  // compressed splits first when they all fit the device at once (see the
+  // LUT kernel's launcher)
+  DecodeArgs c = a;
+  const int units = B * a.Hkv * (a.G / GQ);
+  const int cap = decode_mfma_resident_groups(SUB, GQ, DQ);
+  c.split_slow = (cap > 0 && (int64_t)a.nsplit_q * units <= cap) || units > 65535 ? 1 : 0;  // grid y <= 65535
+  const dim3 grid = c.split_slow ? dim3(units, a.nsplit) : dim3(a.nsplit, units), block(256);
+  hipLaunchKernelGGL((decode_mfma_kernel<SUB, GQ, DQ>), grid, block, lds, stream, c);
   return hipGetLastError();
 }
 

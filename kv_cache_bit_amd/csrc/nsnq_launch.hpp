@@ -116,6 +116,10 @@ struct DecodeArgs {
   int lgR;           // log2 R (R is a power of two)
   int n_quant, n_resid;
   int split_tokens;  // compressed tokens of the longest split (multiple of R)
+  // grid order, set by the launchers: 0 = blockIdx.x is the split (each row's
+  // splits, residual group included, dispatch together), 1 = blockIdx.y is
+  // the split (all compressed splits dispatch before the residual groups)
+  int split_slow;
   int nsplit_q;      // splits over the compressed tokens (split_block)
   int nsplit;        // nsplit_q + (n_resid > 0)
   float scale_log2;  // softmax scale * log2(e)
