@@ -1,5 +1,6 @@
-// decode.hip -- split-K decode attention over the NSNQuant-compressed cache,
-// the LSE combine, and an fp16-cache comparator (gfx950).
+// decode.hip -- split-K decode attention over the NSNQuant-compressed cache
+// with per-query lookup tables, and the LSE combine of the split partials
+// (gfx950).
 //
 // For a key stored as codes c_t, scales (N1, N2) and block mean MU_b,
 //   q . k_hat_t = N1 (N2 (Hq) . c_hat_t + q . MU_b),
@@ -316,7 +317,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   // 64 is above any chunk's exponent
   int ev = 64;
   uint8_t* const vstw = reinterpret_cast<uint8_t*>(smem + L.vst) + wave * kVstWave;
-  const uint32_t vst_lds = (uint32_t)(reinterpret_cast<uintptr_t>(vstw) - reinterpret_cast<uintptr_t>(smem));
   const uint32_t wb_lds = (uint32_t)(reinterpret_cast<uintptr_t>(wb) - reinterpret_cast<uintptr_t>(smem));
   const int m16 = lane & 15, kb = lane >> 4;
   // keys stored before RoPE: lane (token group tt, j) dequantises channels
