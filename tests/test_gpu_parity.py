@@ -857,6 +857,31 @@ def test_llama2_b256_layer_sampled(oracle_codebooks):
     _sampled_layer_check(oracle_codebooks[2], w, 5, [(0, 0), (131, 16), (255, 31)], 10.0)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv", [(2100, 32, 32), (8200, 32, 8)])
+def test_decode_more_units_than_grid_rows(oracle_codebooks, B, Hq, Hkv):
+    """More than 65535 (row, head-group) units: the split must then be the
+    slow grid dimension (the other one is limited to 65535).  Short contexts
+    keep the caches small; sampled rows and heads, first and last included,
+    are checked against the oracle's attention over the GPU's own records."""
+    R, L = 64, 200
+    G = Hq // Hkv
+    cb = oracle_codebooks[2]
+    k, v = synth.kv_layer(7, 0, B, Hkv, L, D, device=DEV)
+    p, cbt, cache = gpu_encode(k, v, 2, R, cb)
+    del k, v
+    q = synth.queries(7, 0, B, Hq, D, device=DEV)
+    o = nsnq.nsnq_decode_attention(p, cbt, q, cache).float().cpu().numpy()
+    nq = cache.n_quant
+
+    def rec(hv, b, h):  # one (row, KV head) of a half, in the oracle's layout
+        return dict(codes=hv.codes[b:b + 1, h:h + 1, :nq].cpu().numpy(), scales=f16_bits(hv.scales[b:b + 1, h:h + 1, :nq]),
+                    mu=f16_bits(hv.mu[b:b + 1, h:h + 1, :nq // R]), resid=f16_bits(hv.resid[b:b + 1, h:h + 1]))
+    for b, h in [(0, 0), (B // 2, Hkv // 2), (B - 1, Hkv - 1)]:
+        ref = oracle.reference_decode(q[b:b + 1, h * G:(h + 1) * G].cpu(), rec(cache.k, b, h), rec(cache.v, b, h),
+                                      nq, cache.n_resid, R, cb)
+        check_attention(o[b:b + 1, h * G:(h + 1) * G], ref)
+
+
 # ------------------------------------------------- fp16-cache comparator --
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,ns", [
