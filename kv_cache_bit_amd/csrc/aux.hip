@@ -80,53 +80,224 @@ hipError_t launch_dequant(const DequantArgs& a, int sub, int n_units, hipStream_
 }
 
 // ---------------------------------------------------------------------------
-// k-means (Lloyd).  Iteration = assign (fp32 squared distances in difference
-// form, ties to the lowest index) with per-group LDS accumulation of member
-// sums (fp64), counts and distortion, flushed to global fp64 accumulators;
-// then a one-group update that moves non-empty centroids to their means and
-// clears the accumulators for the next iteration.
+// k-means (Lloyd).  Iteration = assign (nearest centroid, ties to the lowest
+// index) with per-group LDS accumulation of member sums (fp64), counts and
+// distortion, flushed to global fp64 accumulators; then a one-group update
+// that moves non-empty centroids to their means and clears the accumulators
+// for the next iteration.
+//
+// Assignment on the matrix cores, as the encoder's distance products:
+// centroids are the rows and samples the columns of v_mfma_f32_32x32x16_f16
+// tiles, and K carries
+//   [x_hi, x_hi, x_lo] . [-2 c_hi, -2 c_lo, -2 c_hi] + [xx_hi, xx_lo, 1, 1] . [1, 1, cc_hi, cc_lo]
+// with the fp32 sample x and centroid c split into fp16 halves (x = x_hi +
+// x_lo), xx = |x|^2 and cc = |c|^2 + 2^-12 likewise, so a tile holds
+// D = |x - c|^2 + 2^-12 up to the rounding of the fp32 sums and the dropped
+// x_lo c_lo term (~1e-6 absolute for unit-scale data).  D's bits with the low
+// byte replaced by the centroid index give packed keys whose unsigned minimum
+// is the argmin (ties, and distances within 2^-15 relative, to the lowest
+// index).  The winner's distortion is then recomputed in fp32 difference form.
+// Samples with an element of magnitude >= 2^5 or |x|^2 >= 2^10, and every
+// sample when a centroid is outside those bounds, take a per-lane fp32 loop
+// over the centroids instead, where fp16 halves or the expanded form would
+// lose accuracy.  At 1 bit (SUB = 8) the terms fill two K = 16 products.
+constexpr float kKmMaxAbs = 32.f, kKmMaxSq = 1024.f;
+constexpr float kKmEps = 0.000244140625f;  // 2^-12: keeps D > 0 through rounding
+
+__device__ __forceinline__ uint32_t km_pack(half_t a, half_t b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ half8_t km_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(half8_t, uint4_t{a, b, c, d});
+}
+// (hi, lo) fp16 halves of v
+__device__ __forceinline__ void km_split(float v, half_t& hi, half_t& lo) {
+  hi = (half_t)v;
+  lo = (half_t)(v - (float)hi);
+}
 
 template <int SUB>
 __global__ __launch_bounds__(256) void kmeans_assign_kernel(KmeansArgs a) {
+  constexpr int KS = SUB / 4;  // K = 16 products per 32-centroid tile
   __shared__ float cent[kCodewords * SUB];
   __shared__ double lsum[kCodewords * SUB];
   __shared__ double lcnt[kCodewords];
   __shared__ double ldist[4];
-  const int tid = threadIdx.x;
+  __shared__ half8_t sA[8][KS][kWave];  // A operands, [tile][product][lane]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kCodewords * SUB; i += 256) {
     cent[i] = a.cent[i];
     lsum[i] = 0.0;
   }
   lcnt[tid] = 0.0;
   __syncthreads();
-  double dl = 0.0;
-  for (int64_t p = (int64_t)blockIdx.x * 256 + tid; p < a.n; p += (int64_t)gridDim.x * 256) {
-    float x[SUB];
+  // any centroid outside the products' range?  (one block-wide vote)
+  bool cbad;
+  {
+    float cc = 0.f, mx = 0.f;
 #pragma unroll
-    for (int e = 0; e < SUB; ++e) x[e] = a.samples[p * SUB + e];
-    float bd = INFINITY;
-    int best = 0;
-    for (int k = 0; k < kCodewords; ++k) {
+    for (int e = 0; e < SUB; ++e) {
+      const float v = cent[tid * SUB + e];
+      cc = fmaf(v, v, cc);
+      mx = fmaxf(mx, fabsf(v));
+    }
+    cbad = __syncthreads_or(!(mx < kKmMaxAbs && cc < kKmMaxSq));
+  }
+  // A operands: tile t, lane (row i = lane % 32, K half kb = lane / 32),
+  // centroid 32 t + i; wave w builds tiles 2 w, 2 w + 1
+  const int ri = lane & 31, kb = lane >> 5;
+#pragma unroll
+  for (int t = 2 * wave; t < 2 * wave + 2; ++t) {
+    const float* c = cent + (32 * t + ri) * SUB;
+    half_t h[SUB], l[SUB];
+    float cc = 0.f;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) {
+      km_split(c[e], h[e], l[e]);
+      cc = fmaf(c[e], c[e], cc);
+    }
+    half_t cch, ccl;
+    km_split(cc + kKmEps, cch, ccl);
+    const half_t one = (half_t)1.f, zero = (half_t)0.f;
+    if constexpr (SUB == 4) {
+      // kb 0: [-2 c_hi, -2 c_lo]; kb 1: [-2 c_hi, 1, 1, cc_hi, cc_lo]
+      const uint32_t w0 = km_pack(-2 * h[0], -2 * h[1]), w1 = km_pack(-2 * h[2], -2 * h[3]);
+      sA[t][0][lane] = kb == 0 ? km_half8(w0, w1, km_pack(-2 * l[0], -2 * l[1]), km_pack(-2 * l[2], -2 * l[3]))
+                               : km_half8(w0, w1, km_pack(one, one), km_pack(cch, ccl));
+    } else {
+      // product 0: kb 0 [-2 c_hi], kb 1 [-2 c_lo]; product 1: kb 0 [-2 c_hi], kb 1 [1, 1, cc_hi, cc_lo, 0 ..]
+      const half8_t hh = km_half8(km_pack(-2 * h[0], -2 * h[1]), km_pack(-2 * h[2], -2 * h[3]),
+                                  km_pack(-2 * h[4], -2 * h[5]), km_pack(-2 * h[6], -2 * h[7]));
+      const half8_t ll = km_half8(km_pack(-2 * l[0], -2 * l[1]), km_pack(-2 * l[2], -2 * l[3]),
+                                  km_pack(-2 * l[4], -2 * l[5]), km_pack(-2 * l[6], -2 * l[7]));
+      sA[t][0][lane] = kb == 0 ? hh : ll;
+      sA[t][KS - 1][lane] = kb == 0 ? hh : km_half8(km_pack(one, one), km_pack(cch, ccl), km_pack(zero, zero), 0u);
+    }
+  }
+  __syncthreads();
+  const float16_t zacc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  double dl = 0.0;
+  // each wave takes 64 samples per step, one per lane
+  for (int64_t p0 = ((int64_t)blockIdx.x * 4 + wave) * 64; p0 < a.n; p0 += (int64_t)gridDim.x * 256) {
+    const int64_t p = p0 + lane;
+    const bool valid = p < a.n;
+    float x[SUB];
+    float xx = 0.f, mx = 0.f;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) {
+      x[e] = valid ? a.samples[p * SUB + e] : 0.f;
+      xx = fmaf(x[e], x[e], xx);
+      mx = fmaxf(mx, fabsf(x[e]));
+    }
+    const bool fast = !cbad && mx < kKmMaxAbs && xx < kKmMaxSq;
+    // this lane's K halves: P (K 0-7), Q (K 8-15) of each product
+    uint32_t P[KS][4], Q[KS][4];
+    {
+      half_t h[SUB], l[SUB], xh, xl;
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) km_split(fast ? x[e] : 0.f, h[e], l[e]);
+      km_split(fast ? xx : 0.f, xh, xl);
+      const half_t one = (half_t)1.f, zero = (half_t)0.f;
+      if constexpr (SUB == 4) {
+        P[0][0] = km_pack(h[0], h[1]);
+        P[0][1] = km_pack(h[2], h[3]);
+        P[0][2] = P[0][0];
+        P[0][3] = P[0][1];
+        Q[0][0] = km_pack(l[0], l[1]);
+        Q[0][1] = km_pack(l[2], l[3]);
+        Q[0][2] = km_pack(xh, xl);
+        Q[0][3] = km_pack(one, one);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          P[0][i] = Q[0][i] = km_pack(h[2 * i], h[2 * i + 1]);
+          P[KS - 1][i] = km_pack(l[2 * i], l[2 * i + 1]);
+        }
+        Q[KS - 1][0] = km_pack(xh, xl);
+        Q[KS - 1][1] = km_pack(one, one);
+        Q[KS - 1][2] = Q[KS - 1][3] = km_pack(zero, zero);
+      }
+    }
+    // B operands: columns = the samples of lanes 0-31 (B0) and 32-63 (B1);
+    // lane (n, kb) holds K 8 kb .. 8 kb + 7 of column n
+    half8_t B0[KS], B1[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      uint32_t b0[4], b1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto r = __builtin_amdgcn_permlane32_swap(P[k][i], Q[k][i], false, false);
+        b0[i] = r[0];
+        b1[i] = r[1];
+      }
+      B0[k] = km_half8(b0[0], b0[1], b0[2], b0[3]);
+      B1[k] = km_half8(b1[0], b1[1], b1[2], b1[3]);
+    }
+    // keys carry the index within the lane's rows (a constant per
+    // accumulator); the lane's row offset 4 kb is added before the two
+    // halves meet.  The mask sits in a VGPR so each key is one v_and_or_b32
+    // with the index as its scalar operand.
+    uint32_t vmask;
+    asm("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(0xffffff00u));
+    uint32_t best0 = 0xffffffffu, best1 = 0xffffffffu;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      float16_t d0 = zacc, d1 = zacc;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const half8_t A = sA[t][k][lane];
+        d0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B0[k], d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B1[k], d1, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        // accumulator q holds centroid 32 t + 8 (q / 4) + 4 kb + q % 4
+        const uint32_t k = 32u * t + 8u * (q >> 2) + (q & 3);
+        best0 = min(best0, (__float_as_uint(d0[q]) & vmask) | k);
+        best1 = min(best1, (__float_as_uint(d1[q]) & vmask) | k);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one tile's accumulators live at a time
+    }
+    // lane l: the two half-lists of sample p0 + l
+    uint32_t key;
+    {
+      const auto r = __builtin_amdgcn_permlane32_swap(best0 + 4u * kb, best1 + 4u * kb, false, false);
+      key = min(r[0], r[1]);
+    }
+    int best = (int)(key & 0xffu);
+    if (!fast && valid) {
+      float bd = INFINITY;
+      best = 0;
+      for (int k = 0; k < kCodewords; ++k) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < SUB; ++e) {
+          const float df = x[e] - cent[k * SUB + e];
+          d = fmaf(df, df, d);
+        }
+        if (d < bd) {
+          bd = d;
+          best = k;
+        }
+      }
+    }
+    if (valid) {
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < SUB; ++e) {
-        const float df = x[e] - cent[k * SUB + e];
+        const float df = x[e] - cent[best * SUB + e];
         d = fmaf(df, df, d);
       }
-      if (d < bd) {
-        bd = d;
-        best = k;
-      }
-    }
 #pragma unroll
-    for (int e = 0; e < SUB; ++e) atomicAdd(&lsum[best * SUB + e], (double)x[e]);
-    atomicAdd(&lcnt[best], 1.0);
-    dl += (double)bd;
+      for (int e = 0; e < SUB; ++e) atomicAdd(&lsum[best * SUB + e], (double)x[e]);
+      atomicAdd(&lcnt[best], 1.0);
+      dl += (double)d;
+    }
   }
   // wave sum of the distortion
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) dl += __shfl_xor(dl, m, kWave);
-  if ((tid & 63) == 0) ldist[tid >> 6] = dl;
+  if (lane == 0) ldist[wave] = dl;
   __syncthreads();
   for (int i = tid; i < kCodewords * SUB; i += 256)
     if (lsum[i] != 0.0) atomicAdd(&a.sums[i], lsum[i]);
@@ -161,8 +332,10 @@ __global__ void kmeans_finish_kernel(KmeansArgs a, int total) {
 }
 
 hipError_t launch_kmeans_iter(const KmeansArgs& a, int sub, hipStream_t stream) {
+  // two groups per CU: each group flushes 256 (SUB + 1) fp64 sums with global
+  // atomics, which at 2048 groups cost more than the assignment itself
   const int64_t want = (a.n + 255) / 256;
-  const int grid = (int)(want < 2048 ? want : 2048);
+  const int grid = (int)(want < 512 ? want : 512);
   if (sub == 4) {
     hipLaunchKernelGGL(kmeans_assign_kernel<4>, dim3(grid), dim3(256), 0, stream, a);
     hipLaunchKernelGGL(kmeans_update_kernel<4>, dim3(1), dim3(256), 0, stream, a);

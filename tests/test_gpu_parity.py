@@ -757,6 +757,32 @@ def test_kmeans_matches_oracle(bits):
 
 
 @pytest.mark.parametrize("bits", [2, 1])
+@pytest.mark.parametrize("case", ["some_wide", "all_wide"])
+def test_kmeans_wide_samples(bits, case):
+    """Samples the matrix-core assignment does not take (an element of
+    magnitude >= 32 or a squared norm >= 1024) go through the per-sample fp32
+    search; with such a centroid every sample does.  "some_wide": every 7th
+    sample after the first 256 (the initial centroids) scaled by 40;
+    "all_wide": every sample scaled by 40."""
+    s = nsnq.sub_dim(bits)
+    x = synth.randn_samples(960 + bits, 1 << 13, s).numpy().astype(np.float32)
+    if case == "all_wide":
+        x *= 40.0
+    else:
+        x[256::7] *= 40.0
+    p = nsnq.params(bits, 128)
+    cent1, _, dist1 = nsnq.nsnq_build_codebook(p, torch.from_numpy(x).to(DEV), 1)
+    ocent1, _, odist1 = oracle.kmeans(x, 256, 1)
+    assert dist1.item() == pytest.approx(odist1[0], rel=1e-5)
+    scale = 40.0 if case == "all_wide" else 1.0
+    dev = np.abs(cent1.cpu().numpy().astype(np.float64) - ocent1).max(axis=1) / scale
+    assert (dev > 1e-5).sum() <= 4, f"{(dev > 1e-5).sum()} centroids differ"
+    _, _, dist = nsnq.nsnq_build_codebook(p, torch.from_numpy(x).to(DEV), 5)
+    _, _, odist = oracle.kmeans(x, 256, 5)
+    assert np.allclose(dist.cpu().numpy(), odist, rtol=1e-3)
+
+
+@pytest.mark.parametrize("bits", [2, 1])
 def test_cosine_finetune_matches_oracle(bits):
     """Same start (the oracle's k-means centroids in fp32), same training head
     vectors: the loss curve and the refined centroids agree (assignments are
