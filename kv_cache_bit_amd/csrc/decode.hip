@@ -378,43 +378,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
 #pragma unroll
         for (int e = 0; e < 8; ++e) mk[e] = h2f((e & 1) ? (mw[e >> 1] >> 16) : (mw[e >> 1] & 0xffff));
       }
-#pragma unroll 2
-      for (int pass = 0; pass < kChunk / 4; ++pass) {
+      // the chunk's K code rows and (N1, N2) per token, staged in LDS (a
+      // pass reads the tokens of other lanes); the LUT space is free here
+      uint8_t* kst = reinterpret_cast<uint8_t*>(lut + 4 * GH * kChunk) + wave * (kChunk * (S + 8));
+      float2* sst = reinterpret_cast<float2*>(kst + kChunk * S);
+#pragma unroll
+      for (int i = 0; i < S / 16; ++i)
+        *reinterpret_cast<uint4_t*>(kst + lane * S + 16 * i) =
+            uint4_t{cur.kcw[4 * i], cur.kcw[4 * i + 1], cur.kcw[4 * i + 2], cur.kcw[4 * i + 3]};
+      sst[lane] = float2{kn1, kn2};
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // RoPE rows of a pass's token (channels 8 (rj % 8) .. + 7), requested
+      // one pass ahead
+      struct RopeRow {
+        float4 ca, cb, sa, sb;
+      };
+      auto rope_row = [&](int pass, RopeRow& r) {
+        const int64_t pos = (int64_t)a.rope_pos0 + t0 + (int64_t)ch * kChunk + 4 * pass + rtt;
+        const float4* cs4 = reinterpret_cast<const float4*>(a.rope_cos + pos * (kDim / 2) + 8 * (rj & 7));
+        const float4* sn4 = reinterpret_cast<const float4*>(a.rope_sin + pos * (kDim / 2) + 8 * (rj & 7));
+        r.ca = cs4[0];
+        r.cb = cs4[1];
+        r.sa = sn4[0];
+        r.sb = sn4[1];
+      };
+      auto pass_step = [&](int pass, const RopeRow& rr) {
         const int tok = 4 * pass + rtt;
-        const int64_t tc = (int64_t)ch * kChunk + tok;  // token in the split
         float x[8];
         if constexpr (SUB == 4) {
-          const uint32_t c2 = *reinterpret_cast<const uint16_t*>(kc + tc * S + 2 * rj);
+          const uint32_t c2 = *reinterpret_cast<const uint16_t*>(kst + tok * S + 2 * rj);
           const uint2 w0 = *reinterpret_cast<const uint2*>(cbh + (c2 & 0xffu) * 4);
           const uint2 w1 = *reinterpret_cast<const uint2*>(cbh + (c2 >> 8) * 4);
           const uint32_t w[4] = {w0.x, w0.y, w1.x, w1.y};
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = h2f((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffff));
         } else {
-          const uint32_t c1 = kc[tc * S + rj];
+          const uint32_t c1 = kst[tok * S + rj];
           const uint4 w4 = *reinterpret_cast<const uint4*>(cbh + c1 * 8);
           const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = h2f((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffff));
         }
         fwht128<8>(x, lane);
-        float tn1, tn2;
-        if constexpr (DQ) {
-          const uint8_t* kr = reinterpret_cast<const uint8_t*>(a.kscales) + (blk0 + bl) * dq_record_bytes(a.R);
-          const uint32_t tq = dq_token(kr, a.R, (int)(tc & (a.R - 1)));
-          tn1 = dq_value(dq_s1_params(kr, a.R), tq >> 16);
-          tn2 = h2f(tq & 0xffff);
-        } else {
-          const uint32_t sc = ks[tc];
-          tn1 = h2f(sc & 0xffff);
-          tn2 = h2f(sc >> 16);
-        }
-        const int64_t pos = (int64_t)a.rope_pos0 + t0 + tc;
-        const float4* cs4 = reinterpret_cast<const float4*>(a.rope_cos + pos * (kDim / 2) + 8 * (rj & 7));
-        const float4* sn4 = reinterpret_cast<const float4*>(a.rope_sin + pos * (kDim / 2) + 8 * (rj & 7));
-        const float4 ca = cs4[0], cb = cs4[1], sa = sn4[0], sb = sn4[1];
-        const float cv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
-        const float sv8[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+        const float2 tsc = sst[tok];
+        const float tn1 = tsc.x, tn2 = tsc.y;
+        const float cv[8] = {rr.ca.x, rr.ca.y, rr.ca.z, rr.ca.w, rr.cb.x, rr.cb.y, rr.cb.z, rr.cb.w};
+        const float sv8[8] = {rr.sa.x, rr.sa.y, rr.sa.z, rr.sa.w, rr.sb.x, rr.sb.y, rr.sb.z, rr.sb.w};
         // rotate-half pairs (c, c + 64): lanes rj < 8 hold c < 64, the partner is rj ^ 8
         const float ssg = rj < 8 ? -1.f : 1.f;
         float r[8];
@@ -432,6 +443,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
           d = group_sum<16>(d);
           if (rj == 0) rsc[g * kChunk + tok] = d;
         }
+      };
+      RopeRow r0, r1;
+      rope_row(0, r0);
+      for (int pass = 0; pass < kChunk / 4; pass += 2) {
+        rope_row(pass + 1, r1);
+        pass_step(pass, r0);
+        if (pass + 2 < kChunk / 4) rope_row(pass + 2, r0);
+        pass_step(pass + 1, r1);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
