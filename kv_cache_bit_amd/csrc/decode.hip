@@ -319,19 +319,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
   uint8_t* const vstw = reinterpret_cast<uint8_t*>(smem + L.vst) + wave * kVstWave;
   const uint32_t wb_lds = (uint32_t)(reinterpret_cast<uintptr_t>(wb) - reinterpret_cast<uintptr_t>(smem));
   const int m16 = lane & 15, kb = lane >> 4;
-  // keys stored before RoPE: lane (token group tt, j) dequantises channels
-  // 8 j .. 8 j + 7 of token 4 pass + tt, rotates them and dots them with the
-  // queries; the per-token dot products go through LDS (the LUT space)
+  // Keys stored before RoPE are rebuilt 16 tokens at a time on the matrix
+  // cores: H c_hat = (H_4 (x) H_32) c_hat, the 32-point factor as
+  // v_mfma_f32_16x16x32_f16 products of the gathered codewords (A: token rows)
+  // with +-1 operands, the 4-point factor over the four 32-channel blocks in
+  // registers.  Lane (rj, rtt) then holds channels 32 ch + 2 rj + j (value
+  // 2 ch + j, ch = 0..3, j = 0, 1) of tokens 4 rtt .. 4 rtt + 3 of the tile:
+  // the RoPE pairs (c, c + 64) and their tables' columns (2 rj, 2 rj + 1 and
+  // 32 + 2 rj, 33 + 2 rj) stay in the lane.  It scales, adds the block mean,
+  // rotates and dots the pairs with the queries; a 16-lane sum gives each
+  // token's score, which goes through LDS (the LUT space) to the softmax.
   const int rj = lane & 15, rtt = lane >> 4;
   float* rsc = lut + wave * GH * kChunk;
   float rq[ROPE ? GH : 1][8], rsg[8];
+  half8_t hb[ROPE ? 2 : 1];  // B operands: H_32[8 rtt + e][2 rj + j]
+  auto rch = [&](int v) { return 32 * (v >> 1) + 2 * rj + (v & 1); };  // channel of value v
   if constexpr (ROPE) {
 #pragma unroll
     for (int g = 0; g < GH; ++g)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rq[g][e] = qf[g * kDim + 8 * rj + e];
+      for (int v = 0; v < 8; ++v) rq[g][v] = qf[g * kDim + rch(v)];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rsg[e] = (a.signs ? (float)a.signs[8 * rj + e] : 1.f) * kInvSqrtD;
+    for (int v = 0; v < 8; ++v) rsg[v] = (a.signs ? (float)a.signs[rch(v)] : 1.f) * kInvSqrtD;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        hb[j][e] = (__builtin_popcount((8 * rtt + e) & (2 * rj + j)) & 1) ? (half_t)-1.f : (half_t)1.f;
   }
 
   // one chunk of this wave with its loads in `cur` (the next chunk's loads
@@ -365,21 +379,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
       }
     }
     if constexpr (ROPE) {
-      // the chunk's block mean for channels 8 rj .. 8 rj + 7
+      // the chunk's block mean for this lane's channels (pairs 32 ch + 2 rj, + 1)
       const int bl = (ch * kChunk) >> a.lgR;
       float mk[8];
       if constexpr (DQ) {
         const uint8_t* mr = reinterpret_cast<const uint8_t*>(a.kmu) + (blk0 + bl) * kDqMuRecord;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) dq_mu_pair(mr, 4 * rj + e / 2, mk[e], mk[e + 1]);
+        for (int c = 0; c < 4; ++c) dq_mu_pair(mr, 16 * c + rj, mk[2 * c], mk[2 * c + 1]);
       } else {
-        const uint4 m8 = *reinterpret_cast<const uint4*>(kmu + (int64_t)bl * kDim + 8 * rj);
-        const uint32_t mw[4] = {m8.x, m8.y, m8.z, m8.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mk[e] = h2f((e & 1) ? (mw[e >> 1] >> 16) : (mw[e >> 1] & 0xffff));
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t m2 = *reinterpret_cast<const uint32_t*>(kmu + (int64_t)bl * kDim + 32 * c + 2 * rj);
+          mk[2 * c] = h2f(m2 & 0xffff);
+          mk[2 * c + 1] = h2f(m2 >> 16);
+        }
       }
-      // the chunk's K code rows and (N1, N2) per token, staged in LDS (a
-      // pass reads the tokens of other lanes); the LUT space is free here
+      // the chunk's K code rows and (N1, N2) per token, staged in LDS (the
+      // products read the codes of other lanes' tokens); the LUT space is
+      // free here
       uint8_t* kst = reinterpret_cast<uint8_t*>(lut + 4 * GH * kChunk) + wave * (kChunk * (S + 8));
       float2* sst = reinterpret_cast<float2*>(kst + kChunk * S);
 #pragma unroll
@@ -390,67 +407,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // RoPE rows of a pass's token (channels 8 (rj % 8) .. + 7), requested
-      // one pass ahead
-      struct RopeRow {
-        float4 ca, cb, sa, sb;
-      };
-      auto rope_row = [&](int pass, RopeRow& r) {
-        const int64_t pos = (int64_t)a.rope_pos0 + t0 + (int64_t)ch * kChunk + 4 * pass + rtt;
-        const float4* cs4 = reinterpret_cast<const float4*>(a.rope_cos + pos * (kDim / 2) + 8 * (rj & 7));
-        const float4* sn4 = reinterpret_cast<const float4*>(a.rope_sin + pos * (kDim / 2) + 8 * (rj & 7));
-        r.ca = cs4[0];
-        r.cb = cs4[1];
-        r.sa = sn4[0];
-        r.sb = sn4[1];
-      };
-      auto pass_step = [&](int pass, const RopeRow& rr) {
-        const int tok = 4 * pass + rtt;
-        float x[8];
-        if constexpr (SUB == 4) {
-          const uint32_t c2 = *reinterpret_cast<const uint16_t*>(kst + tok * S + 2 * rj);
-          const uint2 w0 = *reinterpret_cast<const uint2*>(cbh + (c2 & 0xffu) * 4);
-          const uint2 w1 = *reinterpret_cast<const uint2*>(cbh + (c2 >> 8) * 4);
-          const uint32_t w[4] = {w0.x, w0.y, w1.x, w1.y};
+      const float4_t zacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+      for (int tt = 0; tt < kChunk / 16; ++tt) {
+        // RoPE rows of this lane's four tokens, requested before the products
+        float2 rc[4][2], rs[4][2];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = h2f((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffff));
-        } else {
-          const uint32_t c1 = kst[tok * S + rj];
-          const uint4 w4 = *reinterpret_cast<const uint4*>(cbh + c1 * 8);
-          const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = h2f((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffff));
+        for (int r = 0; r < 4; ++r) {
+          const int64_t pos = (int64_t)a.rope_pos0 + t0 + (int64_t)ch * kChunk + 16 * tt + 4 * rtt + r;
+          const float* cp = a.rope_cos + pos * (kDim / 2) + 2 * rj;
+          const float* sp = a.rope_sin + pos * (kDim / 2) + 2 * rj;
+          rc[r][0] = *reinterpret_cast<const float2*>(cp);
+          rc[r][1] = *reinterpret_cast<const float2*>(cp + 32);
+          rs[r][0] = *reinterpret_cast<const float2*>(sp);
+          rs[r][1] = *reinterpret_cast<const float2*>(sp + 32);
         }
-        fwht128<8>(x, lane);
-        const float2 tsc = sst[tok];
-        const float tn1 = tsc.x, tn2 = tsc.y;
-        const float cv[8] = {rr.ca.x, rr.ca.y, rr.ca.z, rr.ca.w, rr.cb.x, rr.cb.y, rr.cb.z, rr.cb.w};
-        const float sv8[8] = {rr.sa.x, rr.sa.y, rr.sa.z, rr.sa.w, rr.sb.x, rr.sb.y, rr.sb.z, rr.sb.w};
-        // rotate-half pairs (c, c + 64): lanes rj < 8 hold c < 64, the partner is rj ^ 8
-        const float ssg = rj < 8 ? -1.f : 1.f;
-        float r[8];
+        // P[s][j]: token rows 16 tt + rj (A), 32-channel block s, columns 2 rj + j
+        float4_t P[4][2];
+        const int ta = 16 * tt + rj;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float kk = tn1 * fmaf(tn2, x[e] * rsg[e], mk[e]);
-          const float pk = xlane<8>(kk);
-          r[e] = fmaf(kk, cv[e], ssg * pk * sv8[e]);
+        for (int sb = 0; sb < 4; ++sb) {
+          half8_t A;
+          if constexpr (SUB == 4) {
+            const uint32_t c2 = *reinterpret_cast<const uint16_t*>(kst + ta * S + 8 * sb + 2 * rtt);
+            const uint2 w0 = *reinterpret_cast<const uint2*>(cbh + (c2 & 0xffu) * 4);
+            const uint2 w1 = *reinterpret_cast<const uint2*>(cbh + (c2 >> 8) * 4);
+            A = __builtin_bit_cast(half8_t, uint4_t{w0.x, w0.y, w1.x, w1.y});
+          } else {
+            const uint32_t c1 = kst[ta * S + 4 * sb + rtt];
+            A = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t*>(cbh + c1 * 8));
+          }
+          P[sb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, hb[0], zacc, 0, 0, 0);
+          P[sb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, hb[1], zacc, 0, 0, 0);
         }
 #pragma unroll
-        for (int g = 0; g < GH; ++g) {
-          float d = 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int tok = 16 * tt + 4 * rtt + r;
+          const float2 tsc = sst[tok];
+          // 4-point transform over the blocks: value 2 ch + j
+          float kk[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) d = fmaf(r[e], rq[g][e], d);
-          d = group_sum<16>(d);
-          if (rj == 0) rsc[g * kChunk + tok] = d;
+          for (int j = 0; j < 2; ++j) {
+            const float a0 = P[0][j][r] + P[1][j][r], a1 = P[0][j][r] - P[1][j][r];
+            const float a2 = P[2][j][r] + P[3][j][r], a3 = P[2][j][r] - P[3][j][r];
+            kk[j] = a0 + a2;
+            kk[2 + j] = a1 + a3;
+            kk[4 + j] = a0 - a2;
+            kk[6 + j] = a1 - a3;
+          }
+          // k / N1 = N2 D H c_hat / sqrt(d) + mu, then the rotation of the pairs (ch, ch + 2)
+#pragma unroll
+          for (int v = 0; v < 8; ++v) kk[v] = fmaf(tsc.y * rsg[v], kk[v], mk[v]);
+          float kr[8];
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const float lo = kk[2 * c + j], hi = kk[2 * c + 4 + j];
+              const float cs = j ? rc[r][c].y : rc[r][c].x, sn = j ? rs[r][c].y : rs[r][c].x;
+              kr[2 * c + j] = fmaf(lo, cs, -hi * sn);
+              kr[2 * c + 4 + j] = fmaf(hi, cs, lo * sn);
+            }
+#pragma unroll
+          for (int g = 0; g < GH; ++g) {
+            float d = 0.f;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) d = fmaf(kr[v], rq[g][v], d);
+            d = group_sum<16>(d);
+            if (rj == 0) rsc[g * kChunk + tok] = tsc.x * d;
+          }
         }
-      };
-      RopeRow r0, r1;
-      rope_row(0, r0);
-      for (int pass = 0; pass < kChunk / 4; pass += 2) {
-        rope_row(pass + 1, r1);
-        pass_step(pass, r0);
-        if (pass + 2 < kChunk / 4) rope_row(pass + 2, r0);
-        pass_step(pass + 1, r1);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();

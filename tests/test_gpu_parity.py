@@ -611,6 +611,32 @@ def test_prerope_decode(oracle_codebooks, bits, R, B, Hq, Hkv, L, flags, ragged)
         assert not np.allclose(plain, out, rtol=1e-2)
 
 
+@pytest.mark.parametrize("bits,R,B,Hq,Hkv,L,use_signs,flags,ns", [
+    (2, 128, 2, 4, 2, 5 * 128 + 9, True, 0, 3),                # randomised Hadamard, 3 splits
+    (1, 64, 1, 2, 1, 700, True, 2, 0),                         # 1 bit, signs, double-quantised records
+    (2, 128, 2, 8, 8, 2500, False, 0, 0),                      # one head per KV head, several splits
+])
+def test_prerope_decode_signs_and_splits(oracle_codebooks, bits, R, B, Hq, Hkv, L, use_signs, flags, ns):
+    """Keys stored before RoPE with a sign vector, double quantisation and
+    several splits per row, against the oracle's rotated-key attention."""
+    cb = oracle_codebooks[bits]
+    pos0 = 3
+    cos, sin = synth.rope_tables(pos0 + L + 1, 10000.0, D)
+    k, v = _kv(1100 + bits, B, Hkv, L)
+    q = synth.queries(1100 + bits, 0, B, Hq, D)
+    signs = synth.hadamard_signs(110 + bits) if use_signs else None
+    dq = bool(flags & nsnq.NSNQ_DOUBLE_QUANT)
+    p, cbt, cache = gpu_encode(k, v, bits, R, cb, flags=flags, signs=signs)
+    out = nsnq.nsnq_decode_attention_prerope(p, cbt, q.to(DEV), cache, cos.to(DEV), sin.to(DEV), pos0,
+                                             num_splits=ns).float().cpu().numpy()
+    sg = None if signs is None else signs.numpy()
+    ek = oracle.encode(k, R, cb, dq=dq, signs=sg)
+    ev = oracle.encode(v, R, cb, dq=dq, signs=sg)
+    ref = oracle.reference_decode(q, ek, ev, ek["n_quant"], ek["n_resid"], R, cb, signs=sg,
+                                  rope_tables=(cos, sin), pos0=pos0)
+    check_attention(out, ref)
+
+
 # ------------------------------------------------------------ ragged rows --
 
 def _row_state(cache: nsnq.KVCache, which: int, b: int, nq: int, r: int) -> dict:
