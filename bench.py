@@ -218,7 +218,30 @@ def decode_step(nsnq, synth, workload: str, steps: int, warmup: int, dev, with_f
     cache_bytes = sum(c.nbytes() for c in caches)
     call_b = decode_bytes(bits, R, nq, r, units, d)
     dec_b = NL * call_b
-    del caches, ws, outs
+    # the same step with the keys read as stored before RoPE (the pages' key
+    # order): standard RoPE tables, positions 0 .. L - 1
+    cos, sin = (t.to(dev).contiguous() for t in synth.rope_tables(L + 8))
+
+    def call_pre(layer):
+        return lambda: nsnq.nsnq_decode_attention_prerope(p, cb, qs[layer], caches[layer], cos, sin, 0,
+                                                          out=outs[layer], ws=ws, stream=stream)
+    calls_pre = [call_pre(layer) for layer in range(NL)]
+    progress(f"{workload}: timing {min(steps, 5)} decode steps with keys stored before RoPE")
+    for f in calls_pre:
+        f()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(min(steps, 5)):
+        for f in calls_pre:
+            f()
+    torch.cuda.synchronize()
+    t_pre = (time.perf_counter() - t0) / min(steps, 5)
+    prerope = {"step_ms": t_pre * 1e3, "tokens_per_s": B / t_pre, "hbm_gbs": dec_b / t_pre / 1e9,
+               "hbm_frac": dec_b / t_pre / 1e9 / HBM_PEAK_GBS, "vs_post_rope": t_pre / t_step,
+               "steps": min(steps, 5),
+               "note": "keys rebuilt per token (codewords, Hadamard on the matrix cores, scale, mean) and rotated "
+                       "with fp32 tables before the product; values as in the post-RoPE step"}
+    del caches, ws, outs, cos, sin
     torch.cuda.empty_cache()
     res = {"workload": workload, "layers": NL, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "context": L,
            "bits": bits, "residual": R, "encoded_tokens": nq, "residual_tokens": r,
@@ -231,7 +254,7 @@ def decode_step(nsnq, synth, workload: str, steps: int, warmup: int, dev, with_f
                     "bytes": call_b, "hbm_gbs": call_b / t_call / 1e9,
                     "hbm_frac": call_b / t_call / 1e9 / HBM_PEAK_GBS,
                     "step_ms_events_median": float(np.median(step_s)) * 1e3},
-           "codebook": cb_info,
+           "codebook": cb_info, "prerope": prerope,
            "setup": f"{distinct_layers} distinct layers encoded, caches copied to the other {NL - distinct_layers}"}
     if enc is not None:
         res["encode"] = enc
@@ -659,7 +682,7 @@ def main():
                               "tokens) / the call's mean HIP-event duration over 20 passes of all layers")},
         "decode_step": {k: head[k] for k in ("step_ms", "tokens_per_s", "kv_tokens_per_s", "hbm_gbs",
                                              "hbm_frac", "bytes_per_step", "compressed_cache_gb", "call",
-                                             "setup")},
+                                             "prerope", "setup")},
         "codebook": head["codebook"],
     }
     if "encode" in head:
