@@ -785,10 +785,12 @@ static hipError_t launch_decode_dq(const DecodeArgs& a, int B, size_t lds, hipSt
   // When every compressed split fits the device at once, they go first and
   // the short residual groups fill in behind them; otherwise each row's
   // groups go together, so residual reads overlap the compressed splits.
+  // Keys stored before RoPE: compressed splits first in every case (their
+  // groups are long, so the residual groups are better left to the end).
   DecodeArgs c = a;
   const int units = B * a.Hkv * (a.G / GH);
   const int cap = resident_groups(k, lds, resident);
-  c.split_slow = (cap > 0 && (int64_t)a.nsplit_q * units <= cap) || units > 65535 ? 1 : 0;  // grid y <= 65535
+  c.split_slow = ROPE || (cap > 0 && (int64_t)a.nsplit_q * units <= cap) || units > 65535 ? 1 : 0;  // grid y <= 65535
   const dim3 grid = c.split_slow ? dim3(units, a.nsplit) : dim3(a.nsplit, units), block(256);
   hipLaunchKernelGGL((decode_split_kernel<SUB, GH, DQ, ROPE>), grid, block, lds, stream, c);
   return hipGetLastError();
