@@ -784,6 +784,21 @@ def test_kmeans_matches_oracle(bits):
     assert d2.item() == pytest.approx(od2[0], rel=1e-5)
 
 
+@pytest.mark.parametrize("bits,n", [(2, 300), (1, 1000), (2, 64 * 517 + 13)])
+def test_kmeans_sample_count_not_a_multiple_of_the_wave(bits, n):
+    """The assignment takes 64 samples per wave step; a count that leaves a
+    partial last step gives the oracle's iteration (the tail lanes add
+    nothing)."""
+    s = nsnq.sub_dim(bits)
+    x = synth.randn_samples(970 + bits, n, s)
+    p = nsnq.params(bits, 128)
+    cent1, _, dist1 = nsnq.nsnq_build_codebook(p, x.to(DEV), 1)
+    ocent1, _, odist1 = oracle.kmeans(x.numpy(), 256, 1)
+    assert dist1.item() == pytest.approx(odist1[0], rel=1e-5)
+    dev = np.abs(cent1.cpu().numpy().astype(np.float64) - ocent1).max(axis=1)
+    assert (dev > 1e-5).sum() <= 2, f"{(dev > 1e-5).sum()} centroids differ"
+
+
 @pytest.mark.parametrize("bits", [2, 1])
 @pytest.mark.parametrize("case", ["some_wide", "all_wide"])
 def test_kmeans_wide_samples(bits, case):
