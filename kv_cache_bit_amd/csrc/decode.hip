@@ -347,6 +347,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
       for (int e = 0; e < 8; ++e)
         hb[j][e] = (__builtin_popcount((8 * rtt + e) & (2 * rj + j)) & 1) ? (half_t)-1.f : (half_t)1.f;
   }
+  // One head: the scale, the sign and the two 4-point outputs of each RoPE
+  // pair fold into the query.  For pair p = (c, j) (values 2 c + j and
+  // 2 c + 4 + j, the blocks' transform outputs e0 + e1 and e0 - e1 with
+  // (e0, e1) = (a0, a2) or (a1, a3)), q . rot(k) / N1 =
+  //   cos (N2 A_W + A_M) + sin (N2 B_W + B_M),
+  //   A_W = qa[p][0] e0 + qa[p][1] e1,  B_W = qa[p][2] e0 + qa[p][3] e1,
+  // with A_M, B_M the block mean's share (per chunk).
+  float qa[ROPE && GH == 1 ? 4 : 1][4];
+  if constexpr (ROPE && GH == 1) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int vl = 2 * (p >> 1) + (p & 1), vh = vl + 4;
+      const float Ql = rq[0][vl] * rsg[vl], Qh = rq[0][vh] * rsg[vh];
+      const float Xl = rq[0][vh] * rsg[vl], Xh = -rq[0][vl] * rsg[vh];
+      qa[p][0] = Ql + Qh;
+      qa[p][1] = Ql - Qh;
+      qa[p][2] = Xl + Xh;
+      qa[p][3] = Xl - Xh;
+    }
+  }
 
   // one chunk of this wave with its loads in `cur` (the next chunk's loads
   // are already in flight into the other buffer)
@@ -392,6 +412,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
           const uint32_t m2 = *reinterpret_cast<const uint32_t*>(kmu + (int64_t)bl * kDim + 32 * c + 2 * rj);
           mk[2 * c] = h2f(m2 & 0xffff);
           mk[2 * c + 1] = h2f(m2 >> 16);
+        }
+      }
+      // one head: the block mean's share per RoPE pair (see qa)
+      float mam[GH == 1 ? 4 : 1][2];
+      if constexpr (GH == 1) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int vl = 2 * (p >> 1) + (p & 1), vh = vl + 4;
+          mam[p][0] = fmaf(rq[0][vl], mk[vl], rq[0][vh] * mk[vh]);
+          mam[p][1] = fmaf(rq[0][vh], mk[vl], -rq[0][vl] * mk[vh]);
         }
       }
       // the chunk's K code rows and (N1, N2) per token, staged in LDS (the
@@ -440,41 +470,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GH == 1 && 
           P[sb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, hb[0], zacc, 0, 0, 0);
           P[sb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, hb[1], zacc, 0, 0, 0);
         }
+        if constexpr (GH == 1) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tok = 16 * tt + 4 * rtt + r;
-          const float2 tsc = sst[tok];
-          // 4-point transform over the blocks: value 2 ch + j
-          float kk[8];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float a0 = P[0][j][r] + P[1][j][r], a1 = P[0][j][r] - P[1][j][r];
-            const float a2 = P[2][j][r] + P[3][j][r], a3 = P[2][j][r] - P[3][j][r];
-            kk[j] = a0 + a2;
-            kk[2 + j] = a1 + a3;
-            kk[4 + j] = a0 - a2;
-            kk[6 + j] = a1 - a3;
-          }
-          // k / N1 = N2 D H c_hat / sqrt(d) + mu, then the rotation of the pairs (ch, ch + 2)
-#pragma unroll
-          for (int v = 0; v < 8; ++v) kk[v] = fmaf(tsc.y * rsg[v], kk[v], mk[v]);
-          float kr[8];
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
+          for (int r = 0; r < 4; ++r) {
+            const int tok = 16 * tt + 4 * rtt + r;
+            const float2 tsc = sst[tok];
+            float aw = 0.f, am = 0.f;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-              const float lo = kk[2 * c + j], hi = kk[2 * c + 4 + j];
-              const float cs = j ? rc[r][c].y : rc[r][c].x, sn = j ? rs[r][c].y : rs[r][c].x;
-              kr[2 * c + j] = fmaf(lo, cs, -hi * sn);
-              kr[2 * c + 4 + j] = fmaf(hi, cs, lo * sn);
+              const float a0 = P[0][j][r] + P[1][j][r], a1 = P[0][j][r] - P[1][j][r];
+              const float a2 = P[2][j][r] + P[3][j][r], a3 = P[2][j][r] - P[3][j][r];
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {
+                const int p = 2 * c + j;
+                const float e0 = c ? a1 : a0, e1 = c ? a3 : a2;
+                const float AW = fmaf(qa[p][0], e0, qa[p][1] * e1);
+                const float BW = fmaf(qa[p][2], e0, qa[p][3] * e1);
+                const float cs = j ? rc[r][c].y : rc[r][c].x, sn = j ? rs[r][c].y : rs[r][c].x;
+                aw = fmaf(cs, AW, aw);
+                aw = fmaf(sn, BW, aw);
+                am = fmaf(cs, mam[p][0], am);
+                am = fmaf(sn, mam[p][1], am);
+              }
             }
+            const float d = group_sum<16>(fmaf(tsc.y, aw, am));
+            if (rj == 0) rsc[tok] = tsc.x * d;
+          }
+        } else {
 #pragma unroll
-          for (int g = 0; g < GH; ++g) {
-            float d = 0.f;
+          for (int r = 0; r < 4; ++r) {
+            const int tok = 16 * tt + 4 * rtt + r;
+            const float2 tsc = sst[tok];
+            // 4-point transform over the blocks: value 2 ch + j
+            float kk[8];
 #pragma unroll
-            for (int v = 0; v < 8; ++v) d = fmaf(kr[v], rq[g][v], d);
-            d = group_sum<16>(d);
-            if (rj == 0) rsc[g * kChunk + tok] = tsc.x * d;
+            for (int j = 0; j < 2; ++j) {
+              const float a0 = P[0][j][r] + P[1][j][r], a1 = P[0][j][r] - P[1][j][r];
+              const float a2 = P[2][j][r] + P[3][j][r], a3 = P[2][j][r] - P[3][j][r];
+              kk[j] = a0 + a2;
+              kk[2 + j] = a1 + a3;
+              kk[4 + j] = a0 - a2;
+              kk[6 + j] = a1 - a3;
+            }
+            // k / N1 = N2 D H c_hat / sqrt(d) + mu, then the rotation of the pairs (ch, ch + 2)
+#pragma unroll
+            for (int v = 0; v < 8; ++v) kk[v] = fmaf(tsc.y * rsg[v], kk[v], mk[v]);
+            float kr[8];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+              for (int j = 0; j < 2; ++j) {
+                const float lo = kk[2 * c + j], hi = kk[2 * c + 4 + j];
+                const float cs = j ? rc[r][c].y : rc[r][c].x, sn = j ? rs[r][c].y : rs[r][c].x;
+                kr[2 * c + j] = fmaf(lo, cs, -hi * sn);
+                kr[2 * c + 4 + j] = fmaf(hi, cs, lo * sn);
+              }
+#pragma unroll
+            for (int g = 0; g < GH; ++g) {
+              float d = 0.f;
+#pragma unroll
+              for (int v = 0; v < 8; ++v) d = fmaf(kr[v], rq[g][v], d);
+              d = group_sum<16>(d);
+              if (rj == 0) rsc[g * kChunk + tok] = tsc.x * d;
+            }
           }
         }
       }
