@@ -851,8 +851,9 @@ def test_cosine_finetune_matches_oracle(bits):
 @pytest.mark.parametrize("cand", [False, True])
 def test_llama2_layer_2bit_full(oracle_codebooks, cand):
     """One LLaMA-2-7B-shaped layer: 32 heads, 4096 tokens, 2-bit, R = 128;
-    every code of every head, and the decode step (exhaustive search, and the
-    candidate-list search the bench times)."""
+    every code of every head, and the decode step, post-RoPE and with the keys
+    read as stored before RoPE (exhaustive search, and the candidate-list
+    search the bench times)."""
     cb = oracle_codebooks[2]
     w = synth.WORKLOADS["llama2-7b-layer-b1-2bit"]
     B, H, L, R = w["B"], w["Hkv"], w["L"], w["R"]
@@ -864,6 +865,11 @@ def test_llama2_layer_2bit_full(oracle_codebooks, cand):
     q = synth.queries(w["config_id"], 0, B, w["Hq"], D)
     o = nsnq.nsnq_decode_attention(p, cbt, q.to(DEV), cache).float().cpu().numpy()
     check_attention(o, _decode_ref(q, ek, ev, cb, R))
+    # the same cache read as keys stored before RoPE (positions 0 .. L - 1)
+    cos, sin = synth.rope_tables(L + 1, 10000.0, D)
+    o = nsnq.nsnq_decode_attention_prerope(p, cbt, q.to(DEV), cache, cos.to(DEV), sin.to(DEV), 0)
+    check_attention(o.float().cpu().numpy(), oracle.reference_decode(q, ek, ev, ek["n_quant"], ek["n_resid"], R, cb,
+                                                                     rope_tables=(cos, sin)))
 
 
 def test_llama2_layer_1bit_b16_sampled(oracle_codebooks):
@@ -891,13 +897,17 @@ def test_llama2_layer_1bit_b16_sampled(oracle_codebooks):
 def _sampled_layer_check(cb, w, layer, units, outlier):
     """Encode and attend one whole layer on the GPU (the bench's launch
     configuration), then check sampled (b, kv-head) streams and their query
-    heads against the oracle."""
+    heads against the oracle, for the post-RoPE decode and for the decode
+    that reads the same cache as keys stored before RoPE (positions 0 ..
+    L - 1, standard tables)."""
     B, Hq, Hkv, L, R, bits = w["B"], w["Hq"], w["Hkv"], w["L"], w["R"], w["bits"]
     G = Hq // Hkv
     k, v = synth.kv_layer(w["config_id"], layer, B, Hkv, L, D, outlier_std=outlier, device=DEV)
     p, cbt, cache = gpu_encode(k, v, bits, R, cb)
     q = synth.queries(w["config_id"], layer, B, Hq, D, device=DEV)
     o = nsnq.nsnq_decode_attention(p, cbt, q, cache).float().cpu().numpy()
+    cos, sin = synth.rope_tables(L + 8)
+    o_pre = nsnq.nsnq_decode_attention_prerope(p, cbt, q, cache, cos.to(DEV), sin.to(DEV), 0).float().cpu().numpy()
     ks = torch.stack([k[b, h] for b, h in units]).cpu()
     vs = torch.stack([v[b, h] for b, h in units]).cpu()
     del k, v
@@ -909,6 +919,8 @@ def _sampled_layer_check(cb, w, layer, units, outlier):
         qh = q[b:b + 1, h * G:(h + 1) * G].cpu()
         ref = oracle.reference_decode(qh, eki, evi, ek["n_quant"], ek["n_resid"], R, cb)
         check_attention(o[b:b + 1, h * G:(h + 1) * G], ref)
+        ref = oracle.reference_decode(qh, eki, evi, ek["n_quant"], ek["n_resid"], R, cb, rope_tables=(cos, sin))
+        check_attention(o_pre[b:b + 1, h * G:(h + 1) * G], ref)
 
 
 def test_llama31_gqa_32k_layer0_sampled(oracle_codebooks):
