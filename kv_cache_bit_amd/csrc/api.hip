@@ -444,22 +444,29 @@ struct DecodePlan {
 
 // Query heads per work-group.  Matrix-core kernel: G itself for G = 2, 4, 8,
 // 16, else 16 when G is a multiple of 16.  LUT kernel (G = 1 and the rest):
-// the largest of 4, 2, 1 dividing G.
+// the largest of 4, 2, 1 dividing G; with keys stored before RoPE at most 2:
+// the four-head variant needs more than 256 registers (one wave per SIMD),
+// and two-head groups at two waves per SIMD are faster even though each
+// rebuilds the keys.
 int mfma_heads_per_group(int G) {
   if (G == 2 || G == 4 || G == 8 || G == 16) return G;
   if (G > 16 && G % 16 == 0) return 16;
   return 0;
 }
-int heads_per_group(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
+int heads_per_group(int G, bool rope) {
+  if (G % 4 == 0 && !rope) return 4;
+  return (G % 2 == 0) ? 2 : 1;
+}
 
+// prerope: keys stored before RoPE (LUT kernel only, at most 2 heads per group)
 DecodePlan plan_decode(const nsnq_params* p, const nsnq_cache* c, int q_heads, int num_splits,
-                       bool lut_only = false) {
+                       bool prerope = false) {
   DecodePlan pl{};
   const int G = q_heads / c->kv_heads;
   const int R = p->block_tokens;
-  const int gq = lut_only ? 0 : mfma_heads_per_group(G);
+  const int gq = prerope ? 0 : mfma_heads_per_group(G);
   pl.mfma = gq > 0;
-  pl.gh = pl.mfma ? gq : heads_per_group(G);
+  pl.gh = pl.mfma ? gq : heads_per_group(G, prerope);
   const int nblk = c->n_quant / R;
   const int max_ts = decode_max_split_tokens(sub_of(p), pl.gh, R);
   const int max_bps = max_ts / R;  // blocks per split

@@ -856,9 +856,13 @@ static hipError_t launch_decode_dq(const DecodeArgs& a, int B, size_t lds, hipSt
 
 template <int SUB, int GH>
 static hipError_t launch_decode_t(const DecodeArgs& a, int B, size_t lds, hipStream_t stream) {
-  if (a.rope_cos)
-    return a.dq ? launch_decode_dq<SUB, GH, true, true>(a, B, lds, stream)
-                : launch_decode_dq<SUB, GH, false, true>(a, B, lds, stream);
+  if (a.rope_cos) {
+    // keys stored before RoPE: groups of at most 2 heads (the planner's choice)
+    if constexpr (GH > 2) return hipErrorInvalidValue;
+    else
+      return a.dq ? launch_decode_dq<SUB, GH, true, true>(a, B, lds, stream)
+                  : launch_decode_dq<SUB, GH, false, true>(a, B, lds, stream);
+  }
   return a.dq ? launch_decode_dq<SUB, GH, true, false>(a, B, lds, stream)
               : launch_decode_dq<SUB, GH, false, false>(a, B, lds, stream);
 }

@@ -615,7 +615,7 @@ def test_prerope_decode(oracle_codebooks, bits, R, B, Hq, Hkv, L, flags, ragged)
     (2, 128, 2, 4, 2, 5 * 128 + 9, True, 0, 3),                # randomised Hadamard, 3 splits
     (1, 64, 1, 2, 1, 700, True, 2, 0),                         # 1 bit, signs, double-quantised records
     (2, 128, 2, 8, 8, 2500, False, 0, 0),                      # one head per KV head, several splits
-    (2, 64, 1, 8, 1, 500, False, 0, 0),                        # G = 8: two 4-head groups per KV head
+    (2, 64, 1, 8, 1, 500, False, 0, 0),                        # G = 8: four 2-head groups per KV head
     (1, 128, 1, 3, 1, 600, True, 0, 0),                        # G = 3: three one-head groups
 ])
 def test_prerope_decode_signs_and_splits(oracle_codebooks, bits, R, B, Hq, Hkv, L, use_signs, flags, ns):
