@@ -1,8 +1,10 @@
-"""CPU checks of the parity helpers themselves: a double-quantised cache whose
-4-bit decisions differ from the oracle's in one block is compared against the
-oracle's re-encode with those decisions, and a wrong code there is caught.
-The caches live in host memory (the records are plain tensors); no kernel
-runs."""
+"""CPU checks of the parity helpers themselves, with mistakes planted on the
+CPU: a double-quantised cache whose 4-bit decisions differ from the oracle's
+in one block is compared against the oracle's re-encode with those
+decisions, and a wrong code there is caught; the VQ code check accepts a
+near-tie flip to the runner-up and rejects a far code at a near tie, any
+change outside the near-tie band, and flips beyond the rate bound.  The
+caches live in host memory (the records are plain tensors); no kernel runs."""
 import numpy as np
 import pytest
 
@@ -55,3 +57,69 @@ def test_dq_block_with_other_decisions(oracle_codebooks):
     codes[0, 0, t, j] = far
     with pytest.raises(AssertionError, match="GPU's 4-bit records"):
         compare_encoded_dq(cache, ek, ev, R)
+
+
+def _near_tie_point(cb_bits, rng):
+    """A 4-element point between a codeword and its nearest neighbour, just
+    nearer the first: the oracle's gap is far inside the near-tie band."""
+    c = oracle.f16_to_f64(cb_bits)
+    for _ in range(200):
+        a = int(rng.integers(len(c)))
+        d = ((c - c[a]) ** 2).sum(-1)
+        d[a] = np.inf
+        b = int(np.argmin(d))
+        u = 0.5 * (c[a] + c[b]) + 1e-7 * (c[a] - c[b])
+        code, _, gap = oracle.vq(u, cb_bits)
+        if code == a and 0 < gap < 1e-5:
+            return u, a, b
+    raise AssertionError("no near-tie point found")
+
+
+def test_check_codes_catches_planted_mistakes(oracle_codebooks):
+    """check_codes against codes planted on the CPU: a near-tie flip to the
+    runner-up passes; a far code at a near tie, any change outside the band,
+    and more flips than the rate bound allows all fail."""
+    from helpers import check_codes
+    cb = oracle_codebooks[2]
+    rng = np.random.default_rng(5)
+    n_tok, S, s = 40, 32, 4
+    u = rng.standard_normal((n_tok, S * s))
+    ties = [(3, 5), (17, 30)]
+    runner_up = {}
+    for t, j in ties:
+        p, a, b = _near_tie_point(cb, rng)
+        u[t, s * j:s * (j + 1)] = p
+        runner_up[(t, j)] = b
+    o = np.zeros((n_tok, S), np.uint8)
+    gap = np.zeros((n_tok, S))
+    for t in range(n_tok):
+        for j in range(S):
+            code, _, g = oracle.vq(u[t, s * j:s * (j + 1)], cb)
+            o[t, j], gap[t, j] = code, g
+    assert all(gap[t, j] < 1e-4 for t, j in ties)
+
+    assert check_codes(o.copy(), o, gap, u, cb) == 0
+    g = o.copy()
+    g[ties[0]] = runner_up[ties[0]]
+    assert check_codes(g, o, gap, u, cb) == 1  # one flip in 1280 codes: within the bound of max(0.0001 n, 1)
+
+    c64 = oracle.f16_to_f64(cb)
+    t, j = ties[0]
+    far = int(np.argmax(((c64 - u[t, s * j:s * (j + 1)]) ** 2).sum(-1)))
+    g = o.copy()
+    g[t, j] = far
+    with pytest.raises(AssertionError, match="from the best"):
+        check_codes(g, o, gap, u, cb)
+
+    t2, j2 = next((t, j) for t in range(n_tok) for j in range(S) if gap[t, j] >= 1e-4)
+    g = o.copy()
+    g[t2, j2] = (int(o[t2, j2]) + 1) % 256
+    with pytest.raises(AssertionError, match="outside the near-tie band"):
+        check_codes(g, o, gap, u, cb)
+
+    g = o.copy()
+    for tj in ties:
+        g[tj] = runner_up[tj]
+    with pytest.raises(AssertionError, match="near-tie mismatches"):
+        check_codes(g, o, gap, u, cb)
+    assert check_codes(g, o, gap, u, cb, pooled=True) == 2
