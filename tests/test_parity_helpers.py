@@ -3,8 +3,9 @@ CPU: a double-quantised cache whose 4-bit decisions differ from the oracle's
 in one block is compared against the oracle's re-encode with those
 decisions, and a wrong code there is caught; the VQ code check accepts a
 near-tie flip to the runner-up and rejects a far code at a near tie, any
-change outside the near-tie band, and flips beyond the rate bound.  The
-caches live in host memory (the records are plain tensors); no kernel runs."""
+change outside the near-tie band, and flips beyond the rate bound; the
+attention, dequant and fp16-ulp checks sit at their stated bars.  The caches
+live in host memory (the records are plain tensors); no kernel runs."""
 import numpy as np
 import pytest
 
@@ -123,3 +124,46 @@ def test_check_codes_catches_planted_mistakes(oracle_codebooks):
     with pytest.raises(AssertionError, match="near-tie mismatches"):
         check_codes(g, o, gap, u, cb)
     assert check_codes(g, o, gap, u, cb, pooled=True) == 2
+
+
+def test_tolerance_checks_sit_at_the_stated_bars():
+    """The attention check (2e-3 relative L2 per output row), the dequant check
+    (1e-3 of the token norm, max-abs per token) and the one-ulp check of the
+    stored fp16 scalars, each against errors planted just inside and just
+    outside its bar."""
+    from helpers import check_attention, check_dequant, check_f16_ulp
+    rng = np.random.default_rng(11)
+    o = rng.standard_normal((6, 128))
+    e = rng.standard_normal((6, 128))
+    e /= np.linalg.norm(e, axis=-1, keepdims=True)
+    nrm = np.linalg.norm(o, axis=-1, keepdims=True)
+    assert check_attention(o + 1.9e-3 * nrm * e, o) < 2e-3
+    bad = o.copy()
+    bad[4] += 2.1e-3 * nrm[4] * e[4]
+    with pytest.raises(AssertionError, match="attention"):
+        check_attention(bad, o)
+
+    x = rng.standard_normal((5, 128))
+    norms = np.linalg.norm(x, axis=-1)
+    g = x.copy()
+    g[:, 7] += 0.9e-3 * norms
+    assert check_dequant(g, x, norms) < 1e-3
+    g[2, 9] -= 1.1e-3 * norms[2]
+    with pytest.raises(AssertionError, match="dequant"):
+        check_dequant(g, x, norms)
+    # tokens outside the mask (a near-tie flip moved a codeword) are not held to the bar
+    assert check_dequant(g, x, norms, mask=np.arange(5) != 2) < 1e-3
+
+    vals = np.abs(rng.standard_normal(4000)).astype(np.float16) + np.float16(0.01)
+    ob = vals.view(np.uint16)
+    gb = ob.copy()
+    gb[:40] += 1  # one ulp up on 1 % of the values
+    assert check_f16_ulp(gb, ob, "n1") == 40
+    two = ob.copy()
+    two[3] += 2
+    with pytest.raises(AssertionError, match="exceeds one fp16 ulp"):
+        check_f16_ulp(two, ob, "n1")
+    many = ob.copy()
+    many[:41] += 1
+    with pytest.raises(AssertionError, match="off by one ulp"):
+        check_f16_ulp(many, ob, "n1")
