@@ -58,6 +58,12 @@ def encode_bytes_per_vector(bits: int, R: int, d: int = 128) -> float:
     return 2 * d + S + 4 + 2 * d / R
 
 
+def dequant_bytes_per_vector(bits: int, R: int, d: int = 128) -> float:
+    """Dequant, per head vector: codes S + (n1, n2) 4 + the block mean's share
+    2d/R read, 2d written (fp16)."""
+    return d // (4 if bits == 2 else 8) + 4 + 2 * d / R + 2 * d
+
+
 def decode_bytes(bits: int, R: int, n_quant: int, n_resid: int, units: int, d: int = 128) -> float:
     """Algorithmic bytes of one decode call: K and V codes + scalars + means of
     the compressed tokens, and the fp16 residual tokens, for `units` (b, h)."""
@@ -414,7 +420,22 @@ def layer_bench(nsnq, synth, workload: str, dev, reps: int = 20, options: bool =
         nsnq.nsnq_decode_attention(p, cb, q, c, out=out, ws=ws, stream=stream)
     t_dec = event_time(stream, dec, max(reps, 2 * n_c))
     dec_b = decode_bytes(bits, R, nq, r, units, d)
-    del caches, ws
+    # dequant of every compressed token, K and V, to fp16, over the rotated
+    # caches and rotated output buffers
+    progress(f"{workload}: dequant")
+    out_b = units * nq * d * 2
+    n_o = max(4, math.ceil(1e9 / out_b))
+    outs = [torch.empty(B, Hkv, nq, d, dtype=torch.float16, device=dev) for _ in range(n_o)]
+    it[0] = 0
+
+    def deq():
+        c, o = caches[it[0] % n_c], outs[it[0] % n_o]
+        it[0] += 1
+        nsnq.nsnq_dequant(p, cb, c, 0, 0, nq, out=o, stream=stream)
+        nsnq.nsnq_dequant(p, cb, c, 1, 0, nq, out=o, stream=stream)
+    t_deq = event_time(stream, deq, max(reps, 2 * max(n_c, n_o)))
+    deq_b = 2 * units * nq * dequant_bytes_per_vector(bits, R, d)
+    del caches, ws, outs
     torch.cuda.empty_cache()
     # fp16 comparator over rotated copies of the layer's K/V
     kf, vf = k.contiguous(), v.contiguous()
@@ -446,6 +467,9 @@ def layer_bench(nsnq, synth, workload: str, dev, reps: int = 20, options: bool =
            "decode": {"us": t_dec * 1e6, "tokens_per_s": B / t_dec, "kv_tokens_per_s": units * L / t_dec,
                       "hbm_gbs": dec_b / t_dec / 1e9, "hbm_frac": dec_b / t_dec / 1e9 / HBM_PEAK_GBS,
                       "bytes": dec_b, "rotated_copies": n_c},
+           "dequant": {"us": t_deq * 1e6, "vectors_per_s": 2 * units * nq / t_deq, "hbm_gbs": deq_b / t_deq / 1e9,
+                       "hbm_frac": deq_b / t_deq / 1e9 / HBM_PEAK_GBS, "bytes": deq_b,
+                       "note": "K and V of every compressed token to fp16, one call each"},
            "fp16_decode": {"us": t16 * 1e6, "tokens_per_s": B / t16, "hbm_gbs": b16 / t16 / 1e9,
                            "hbm_frac": b16 / t16 / 1e9 / HBM_PEAK_GBS, "bytes": b16, "rotated_copies": n16,
                            "compressed_speedup": t16 / t_dec},

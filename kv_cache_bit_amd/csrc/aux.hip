@@ -18,8 +18,42 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   __shared__ float cbf[kCodewords * SUB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = lane % S, tir = lane / S;
+  // lane `slot` takes the codeword of its slot; the transform (DPP stages,
+  // as in the encoder) leaves it holding the channels of output slot
+  // hslot(slot) times hsign(slot), which the scale undoes
+  const int oslot = hslot(slot);
   const int unit = blockIdx.y;
+  // every row's codes, scales and block-mean channels are requested before
+  // the codebook goes to LDS, so their latency overlaps the codebook's
+  uint32_t code[ROWS], s2[ROWS], mw[ROWS][SUB / 2];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const int i = blockIdx.x * TPB + wave * (TPB / 4) + r * TPR + tir;
+    const int t = a.tok0 + (i < a.ntok ? i : 0);
+    const int64_t ct = (int64_t)unit * a.cap + t;
+    code[r] = a.codes[ct * S + slot];
+    if (!a.dq) {
+      s2[r] = reinterpret_cast<const uint32_t*>(a.scales)[ct];
+      // the block mean's SUB channels of the output slot, one 8- or 16-byte load
+      const uint16_t* mp = a.mu + ((int64_t)unit * (a.cap / a.R) + t / a.R) * kDim + oslot * SUB;
+      if constexpr (SUB == 4) {
+        const uint2 m2 = *reinterpret_cast<const uint2*>(mp);
+        mw[r][0] = m2.x;
+        mw[r][1] = m2.y;
+      } else {
+        const uint4 m4 = *reinterpret_cast<const uint4*>(mp);
+        mw[r][0] = m4.x;
+        mw[r][1] = m4.y;
+        mw[r][2] = m4.z;
+        mw[r][3] = m4.w;
+      }
+    }
+  }
   for (int i = threadIdx.x; i < kCodewords * SUB; i += 256) cbf[i] = h2f(a.codebook[i]);
+  float sc[SUB];  // 1/sqrt(d), the lane's transform sign and the randomised-Hadamard sign of each output channel
+#pragma unroll
+  for (int e = 0; e < SUB; ++e)
+    sc[e] = kInvSqrtD * hsign(slot) * (a.signs ? (float)a.signs[oslot * SUB + e] : 1.f);
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
@@ -27,9 +61,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
     const bool act = i < a.ntok;
     const bool live = !a.seq_quant || a.tok0 + i < a.seq_quant[unit / a.H];  // ragged: past the row's end -> 0
     const int t = a.tok0 + (act ? i : 0);                               // cache token
-    const int64_t ct = (int64_t)unit * a.cap + t;
     const int64_t blk = (int64_t)unit * (a.cap / a.R) + t / a.R;
-    const uint32_t code = a.codes[ct * S + slot];
     float n1, n2, mv[SUB];
     if (a.dq) {
       const uint8_t* rec = reinterpret_cast<const uint8_t*>(a.scales) + blk * dq_record_bytes(a.R);
@@ -38,34 +70,37 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
       n2 = h2f(tq & 0xffff);
       const uint8_t* mrec = reinterpret_cast<const uint8_t*>(a.mu) + blk * kDqMuRecord;
 #pragma unroll
-      for (int e = 0; e < SUB; e += 2) dq_mu_pair(mrec, (slot * SUB + e) / 2, mv[e], mv[e + 1]);
+      for (int e = 0; e < SUB; e += 2) dq_mu_pair(mrec, (oslot * SUB + e) / 2, mv[e], mv[e + 1]);
     } else {
-      const uint32_t sc = reinterpret_cast<const uint32_t*>(a.scales)[ct];
-      n1 = h2f(sc & 0xffff);
-      n2 = h2f(sc >> 16);
-      const uint16_t* mp = a.mu + blk * kDim + slot * SUB;
+      n1 = h2f(s2[r] & 0xffff);
+      n2 = h2f(s2[r] >> 16);
 #pragma unroll
-      for (int e = 0; e < SUB; ++e) mv[e] = h2f(mp[e]);
+      for (int e = 0; e < SUB; e += 2) {
+        mv[e] = h2f(mw[r][e / 2] & 0xffff);
+        mv[e + 1] = h2f(mw[r][e / 2] >> 16);
+      }
     }
     float x[SUB];
 #pragma unroll
-    for (int e = 0; e < SUB; ++e) x[e] = cbf[code * SUB + e];
-    fwht128<SUB>(x, lane);
+    for (int e = 0; e < SUB; ++e) x[e] = cbf[code[r] * SUB + e];
+    fwht_lanes<SUB>(x, slot);
 #pragma unroll
-    for (int e = 0; e < SUB; ++e) {
-      const float sg = a.signs ? (float)a.signs[slot * SUB + e] : 1.f;
-      x[e] = live ? n1 * fmaf(n2, x[e] * (kInvSqrtD * sg), mv[e]) : 0.f;
-    }
+    for (int e = 0; e < SUB; ++e) x[e] = live ? n1 * fmaf(n2, x[e] * sc[e], mv[e]) : 0.f;
     if (act) {
-      const int64_t o = ((int64_t)unit * a.ntok + i) * kDim + slot * SUB;
+      // the output slot's SUB values in one store per lane; the lanes of a
+      // token cover its 256 (fp16) or 512 (fp32) bytes
+      const int64_t o = ((int64_t)unit * a.ntok + i) * kDim + oslot * SUB;
       if (a.out_f16) {
+        uint32_t w[SUB / 2];
+#pragma unroll
+        for (int e = 0; e < SUB; e += 2) w[e / 2] = (uint32_t)f2h(x[e]) | ((uint32_t)f2h(x[e + 1]) << 16);
         uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + o;
-#pragma unroll
-        for (int e = 0; e < SUB; ++e) out[e] = f2h(x[e]);
+        if constexpr (SUB == 4) *reinterpret_cast<uint2*>(out) = uint2{w[0], w[1]};
+        else *reinterpret_cast<uint4*>(out) = uint4{w[0], w[1], w[2], w[3]};
       } else {
-        float* out = reinterpret_cast<float*>(a.out) + o;
+        float4* out = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + o);
 #pragma unroll
-        for (int e = 0; e < SUB; ++e) out[e] = x[e];
+        for (int e = 0; e < SUB; e += 4) out[e / 4] = float4{x[e], x[e + 1], x[e + 2], x[e + 3]};
       }
     }
   }

@@ -108,6 +108,69 @@ __device__ __forceinline__ void fwht128(float (&x)[E], int lane) {
   if constexpr (LANES >= 64) fwht_stage<32>(x, lane);
 }
 
+// Walsh-Hadamard transform in the encoder's lane layout: E consecutive
+// channels per lane, 128 / E lanes per token (lane `l` of the token's group).
+// The in-lane stages are the usual butterflies.  Every cross-lane stage is one
+// DPP-fused multiply-add t <- t + c t', with t' the partner lane's value and
+// c = -1 on the lane whose stage bit is set (that lane keeps the negated
+// difference).  The first cross-lane stage pairs lanes l and l ^ 7 (the
+// half-row mirror: DPP has no xor-4 exchange), then l ^ 1, l ^ 2, l ^ 8 and,
+// for E = 4, l ^ 16 through the swizzle.  Composed over GF(2), the stages give
+// the Sylvester transform with lane l holding the channels of slot hslot(l),
+// in order, times hsign(l).
+__device__ __forceinline__ int hslot(int l) { return l ^ ((((l >> 1) ^ l) & 1) << 2); }  // bit 2 ^= bit 0 ^ bit 1
+__device__ __forceinline__ float hsign(int l) {
+  return ((__builtin_popcount(l) + ((l >> 2) & ((l >> 1) ^ l))) & 1) ? -1.f : 1.f;
+}
+// One DPP stage over the lane's E values: x[e] += c * partner(x[e]) as
+// v_fmac_f32_dpp (the compiler keeps a separate DPP move otherwise).  The
+// leading s_nop covers the wait a DPP read needs after a VALU write of its
+// register, which the compiler cannot see inside the block.
+#define NSNQ_HSTAGE4(DPP)                                                                    \
+  asm("s_nop 1\n\t"                                                                          \
+      "v_fmac_f32_dpp %0, %0, %4 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"        \
+      "v_fmac_f32_dpp %1, %1, %4 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"        \
+      "v_fmac_f32_dpp %2, %2, %4 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"        \
+      "v_fmac_f32_dpp %3, %3, %4 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1"              \
+      : "+v"(x[e]), "+v"(x[e + 1]), "+v"(x[e + 2]), "+v"(x[e + 3])                            \
+      : "v"(c))
+template <int BIT, int E>
+__device__ __forceinline__ void hstage(float (&x)[E], int l) {
+  const float c = ((l >> BIT) & 1) ? -1.f : 1.f;
+#pragma unroll
+  for (int e = 0; e < E; e += 4) {
+    if constexpr (BIT == 2) NSNQ_HSTAGE4("row_half_mirror");
+    else if constexpr (BIT == 0) NSNQ_HSTAGE4("quad_perm:[1,0,3,2]");
+    else if constexpr (BIT == 1) NSNQ_HSTAGE4("quad_perm:[2,3,0,1]");
+    else NSNQ_HSTAGE4("row_ror:8");
+  }
+}
+#undef NSNQ_HSTAGE4
+template <int E>
+__device__ __forceinline__ void fwht_lanes(float (&x)[E], int l) {
+  static_assert(E == 4 || E == 8, "4 or 8 channels per lane");
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if ((e & h) == 0) {
+        const float a = x[e], b = x[e + h];
+        x[e] = a + b;
+        x[e + h] = a - b;
+      }
+    }
+  }
+  hstage<2>(x, l);  // row_half_mirror: l ^ 7
+  hstage<0>(x, l);  // quad_perm 1,0,3,2: l ^ 1
+  hstage<1>(x, l);  // quad_perm 2,3,0,1: l ^ 2
+  hstage<3>(x, l);  // row_ror 8: l ^ 8
+  if constexpr (E == 4) {
+    const float c = ((l >> 4) & 1) ? -1.f : 1.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = fmaf(xlane<16>(x[e]), c, x[e]);
+  }
+}
+
 // 1/sqrt(128)
 constexpr float kInvSqrtD = 0.088388347648318440550f;
 
