@@ -23,19 +23,25 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   // hslot(slot) times hsign(slot), which the scale undoes
   const int oslot = hslot(slot);
   const int unit = blockIdx.y;
+  // per-lane bases, then 32-bit token offsets per row (R is 64 or 128: the
+  // block of token t is t >> lgR)
+  const int lgR = __builtin_ctz(a.R);
+  const int i0 = blockIdx.x * TPB + wave * (TPB / 4) + tir;  // output token of row 0
+  const int tlast = a.tok0 + a.ntok - 1;                      // loads of rows past the end re-read the last token
+  const uint8_t* codes_u = a.codes + (int64_t)unit * a.cap * S + slot;
+  const uint32_t* scales_u = reinterpret_cast<const uint32_t*>(a.scales) + (int64_t)unit * a.cap;
+  const uint16_t* mu_u = a.mu + (int64_t)unit * (a.cap >> lgR) * kDim + oslot * SUB;
   // every row's codes, scales and block-mean channels are requested before
   // the codebook goes to LDS, so their latency overlaps the codebook's
   uint32_t code[ROWS], s2[ROWS], mw[ROWS][SUB / 2];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    const int i = blockIdx.x * TPB + wave * (TPB / 4) + r * TPR + tir;
-    const int t = a.tok0 + (i < a.ntok ? i : 0);
-    const int64_t ct = (int64_t)unit * a.cap + t;
-    code[r] = a.codes[ct * S + slot];
+    const int t = min(a.tok0 + i0 + r * TPR, tlast);
+    code[r] = codes_u[t * S];
     if (!a.dq) {
-      s2[r] = reinterpret_cast<const uint32_t*>(a.scales)[ct];
+      s2[r] = scales_u[t];
       // the block mean's SUB channels of the output slot, one 8- or 16-byte load
-      const uint16_t* mp = a.mu + ((int64_t)unit * (a.cap / a.R) + t / a.R) * kDim + oslot * SUB;
+      const uint16_t* mp = mu_u + (t >> lgR) * kDim;
       if constexpr (SUB == 4) {
         const uint2 m2 = *reinterpret_cast<const uint2*>(mp);
         mw[r][0] = m2.x;
@@ -55,17 +61,18 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   for (int e = 0; e < SUB; ++e)
     sc[e] = kInvSqrtD * hsign(slot) * (a.signs ? (float)a.signs[oslot * SUB + e] : 1.f);
   __syncthreads();
+  const int64_t o_u = ((int64_t)unit * a.ntok + i0) * kDim + oslot * SUB;  // output element of row 0
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    const int i = blockIdx.x * TPB + wave * (TPB / 4) + r * TPR + tir;  // output token
+    const int i = i0 + r * TPR;  // output token
     const bool act = i < a.ntok;
     const bool live = !a.seq_quant || a.tok0 + i < a.seq_quant[unit / a.H];  // ragged: past the row's end -> 0
-    const int t = a.tok0 + (act ? i : 0);                               // cache token
-    const int64_t blk = (int64_t)unit * (a.cap / a.R) + t / a.R;
+    const int t = min(a.tok0 + i, tlast);                                   // cache token
+    const int64_t blk = (int64_t)unit * (a.cap >> lgR) + (t >> lgR);
     float n1, n2, mv[SUB];
     if (a.dq) {
       const uint8_t* rec = reinterpret_cast<const uint8_t*>(a.scales) + blk * dq_record_bytes(a.R);
-      const uint32_t tq = dq_token(rec, a.R, t % a.R);
+      const uint32_t tq = dq_token(rec, a.R, t & (a.R - 1));
       n1 = dq_value(dq_s1_params(rec, a.R), tq >> 16);
       n2 = h2f(tq & 0xffff);
       const uint8_t* mrec = reinterpret_cast<const uint8_t*>(a.mu) + blk * kDqMuRecord;
@@ -89,7 +96,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
     if (act) {
       // the output slot's SUB values in one store per lane; the lanes of a
       // token cover its 256 (fp16) or 512 (fp32) bytes
-      const int64_t o = ((int64_t)unit * a.ntok + i) * kDim + oslot * SUB;
+      const int64_t o = o_u + (int64_t)(r * TPR) * kDim;
       if (a.out_f16) {
         uint32_t w[SUB / 2];
 #pragma unroll
